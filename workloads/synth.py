@@ -1,0 +1,132 @@
+"""Seeded input generators (NumPy PCG64), shared by the oracle's tests and the HIP path.
+
+Every draw comes from ``numpy.random.default_rng([seed, stream, index])`` so any
+step or round can be regenerated on its own, in any order:
+
+  stream 0            A = -exp(U(0,1)) per head (computed in fp64, stored fp32)
+  stream 1, step t    x (Bt,H,P), B (Bt,G,N), C (Bt,G,N), z (Bt,H): standard
+                      normals drawn in that order as float32; dt = softplus(z - 2)
+                      computed in fp64 and stored fp32
+  stream 2, round r   the same four draws for a speculative round, shaped
+                      (Bt,K+1,H,P), (Bt,K+1,G,N), (Bt,K+1,G,N), (Bt,K+1,H)
+  stream 3, round r   accepted drafts n_acc ~ Uniform{0..K}, one per sequence
+  stream 4            S0 ~ N(0,1) (Bt,H,P,N) float32, for the "normal" S0 variant
+  stream 5, step t    gated-DeltaNet inputs (see ``gdn_step_inputs``)
+
+Inputs stored as bf16 are rounded from the float32 draw with round-to-nearest-
+even; the returned float32 arrays are the exact values of those bf16 numbers, so
+an fp64 consumer sees the very bits the device reads.
+
+Nothing here is part of the method: no decay, update or output is computed.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .shapes import Workload
+
+
+def _rng(seed: int, stream: int, idx: int | None = None) -> np.random.Generator:
+    key = [seed, stream] if idx is None else [seed, stream, idx]
+    return np.random.default_rng(key)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
+
+    Inputs are finite normal draws here; NaN and Inf are not handled."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> their exact float32 values."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _softplus64(u: np.ndarray) -> np.ndarray:
+    u = u.astype(np.float64)
+    return np.maximum(u, 0.0) + np.log1p(np.exp(-np.abs(u)))
+
+
+def _store(a: np.ndarray, dtype: str) -> dict:
+    """Round a float32 draw to the storage dtype; return values (+ bits for bf16)."""
+    if dtype == "f32":
+        return {"val": np.ascontiguousarray(a, dtype=np.float32), "bits": None}
+    if dtype == "bf16":
+        bits = bf16_bits(a)
+        return {"val": bf16_value(bits), "bits": bits}
+    raise ValueError(dtype)
+
+
+def params(wl: Workload) -> dict:
+    """Per-head parameters: A (H,) float32, A = -exp(U(0,1))."""
+    u = _rng(wl.seed, 0).random(wl.nheads)
+    return {"A": (-np.exp(u)).astype(np.float32)}
+
+
+def initial_state(wl: Workload) -> np.ndarray:
+    """S0 (Bt,H,P,N) float32: zeros, or N(0,1) for the "normal" variant."""
+    shape = (wl.batch, wl.nheads, wl.headdim, wl.dstate)
+    if wl.s0 == "zeros":
+        return np.zeros(shape, np.float32)
+    return _rng(wl.seed, 4).standard_normal(shape, dtype=np.float32)
+
+
+def _draw_tokens(rng: np.random.Generator, wl: Workload, lead: tuple) -> dict:
+    Bt, H, P, N, G = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    x = rng.standard_normal((Bt, *lead, H, P), dtype=np.float32)
+    B = rng.standard_normal((Bt, *lead, G, N), dtype=np.float32)
+    C = rng.standard_normal((Bt, *lead, G, N), dtype=np.float32)
+    z = rng.standard_normal((Bt, *lead, H), dtype=np.float32)
+    out = {}
+    for k, v in (("x", x), ("B", B), ("C", C)):
+        s = _store(v, wl.in_dtype)
+        out[k] = s["val"]
+        out[k + "_bits"] = s["bits"]
+    out["dt"] = _softplus64(z.astype(np.float64) - 2.0).astype(np.float32)
+    return out
+
+
+def step_inputs(wl: Workload, t: int) -> dict:
+    """Inputs of plain decode step t (0-based).
+
+    Returns float32 arrays x (Bt,H,P), B (Bt,G,N), C (Bt,G,N), dt (Bt,H) holding
+    the exact stored values, and x_bits/B_bits/C_bits (uint16) when stored bf16."""
+    return _draw_tokens(_rng(wl.seed, 1, t), wl, ())
+
+
+def draft_inputs(wl: Workload, r: int) -> dict:
+    """Inputs of speculative round r: K+1 tokens per sequence (the last sampled
+    token followed by K drafts), shaped (Bt,K+1,...)."""
+    return _draw_tokens(_rng(wl.seed, 2, r), wl, (wl.draft + 1,))
+
+
+def accepted_drafts(wl: Workload, r: int) -> np.ndarray:
+    """n_acc (Bt,) int32 ~ Uniform{0..K}: drafts the target model accepts in round r."""
+    return _rng(wl.seed, 3, r).integers(0, wl.draft + 1, wl.batch).astype(np.int32)
+
+
+def gdn_step_inputs(wl: Workload, t: int) -> dict:
+    """Gated-DeltaNet inputs of step t (0-based), all float32.
+
+    q, k (Bt,H,d_k): N(0,1) draws scaled to unit L2 norm (in fp64);
+    v (Bt,H,d_v) ~ N(0,1); beta = sigmoid(N(0,1)); alpha = exp(-softplus(N(0,1))),
+    beta and alpha shaped (Bt,H). Draw order: q, k, v, beta's normal, alpha's."""
+    Bt, H, dk, dv = wl.batch, wl.nheads, wl.dstate, wl.headdim
+    rng = _rng(wl.seed, 5, t)
+    q = rng.standard_normal((Bt, H, dk), dtype=np.float32).astype(np.float64)
+    k = rng.standard_normal((Bt, H, dk), dtype=np.float32).astype(np.float64)
+    v = rng.standard_normal((Bt, H, dv), dtype=np.float32)
+    zb = rng.standard_normal((Bt, H), dtype=np.float32).astype(np.float64)
+    za = rng.standard_normal((Bt, H), dtype=np.float32).astype(np.float64)
+    q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True))
+    k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
+    return {
+        "q": q.astype(np.float32),
+        "k": k.astype(np.float32),
+        "v": v,
+        "beta": (1.0 / (1.0 + np.exp(-zb))).astype(np.float32),
+        "alpha": np.exp(-_softplus64(za)).astype(np.float32),
+    }
