@@ -1,0 +1,83 @@
+// Internal launch interface between the C ABI (rss_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "limits.h"
+
+namespace rss {
+
+// Decode (nt = 1) and speculative verify (nt = K+1) by replay.
+struct ReplayArgs {
+  const float* ckpt;       // [Bt,H,P,N] fp32 master
+  const void* ckpt_lo;     // [Bt,H,P,N] bf16 read copy (dual mode)
+  void* ring_x;            // [Bt,H,R,P]
+  void* ring_B;            // [Bt,G,R,N]
+  float2* ring_dl;         // [Bt,H,R] (dt, dt*A)
+  int4* ptr;               // [Bt,H] (head, len, n_tent, 0)
+  const float* A;          // [H]
+  int* err;                // sticky device word
+  const void* x;           // [Bt,nt,H,P]
+  const void* B;           // [Bt,nt,G,N]
+  const void* C;           // [Bt,nt,G,N]
+  const float* dt;         // [Bt,nt,H]
+  float* y;                // [Bt,nt,H,P]
+  int H, P, G, R, nt, set_tent;
+};
+hipError_t launch_replay(const ReplayArgs& a, int batch, int N, bool bf16_in, bool low_copy,
+                         hipStream_t s);
+
+// Fold the window into the checkpoint for sequences with len >= min_len.
+struct FlushArgs {
+  float* ckpt;
+  void* ckpt_lo;           // written in dual mode
+  const void* ring_x;
+  const void* ring_B;
+  const float2* ring_dl;
+  int4* ptr;
+  int* err;
+  int H, P, G, R, min_len;
+};
+hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, bool low_copy,
+                        hipStream_t s);
+
+// ckpt <- S0 (or 0), read copy <- bf16(ckpt), pointers and error word <- 0.
+struct InitArgs {
+  float* ckpt;
+  void* ckpt_lo;
+  const float* S0;
+  int4* ptr;
+  int* err;
+  size_t n_state;          // Bt*H*P*N (a multiple of 4)
+  size_t n_ptr;            // Bt*H
+};
+hipError_t launch_init(const InitArgs& a, hipStream_t s);
+
+// len -= n_drop[b], n_tent = 0 for every (b, h) with 0 <= n_drop[b] <= n_tent.
+struct RollbackArgs {
+  int4* ptr;
+  const int* n_drop;
+  int* err;
+  int H;
+  size_t n_ptr;
+};
+hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
+
+// Eager baseline: T tokens in place (src_slot == nullptr) or from pool slot
+// src_slot[b] with a snapshot written to slot i after token i.
+struct EagerArgs {
+  float* S;                // in-place state [Bt,H,P,N], or the pool [Bt,slots,H,P,N]
+  const int* src_slot;     // nullptr: in place
+  const void* x;           // [Bt,T,H,P]
+  const void* B;           // [Bt,T,G,N]
+  const void* C;           // [Bt,T,G,N]
+  const float* dt;         // [Bt,T,H]
+  const float* A;          // [H]
+  float* y;                // [Bt,T,H,P]
+  int H, P, G, T, slots;
+};
+hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, hipStream_t s);
+
+}  // namespace rss

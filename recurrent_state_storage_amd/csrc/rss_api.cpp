@@ -1,0 +1,274 @@
+// C ABI of librss: argument validation, call-order tracking and dispatch to the
+// gfx950 kernels. Every check that the host can make happens here, before any
+// launch, so a failing call leaves device state untouched.
+#include <hip/hip_runtime_api.h>
+
+#include <new>
+
+#include "../../include/rss.h"
+#include "launch.h"
+
+struct rss_layer {
+  rss_config cfg;
+  rss_buffers dev;
+  int pending_verify;  // a verify round is waiting for its rollback
+};
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_n(int32_t n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+
+int32_t check_shape(const rss_config* c) {
+  if (!c) return RSS_E_INVALID;
+  if (c->batch < 0 || c->nheads < 1 || c->ngroups < 1) return RSS_E_SHAPE;
+  if (c->nheads % c->ngroups) return RSS_E_SHAPE;
+  if (c->headdim < 1 || c->headdim > rss::kMaxP) return RSS_E_SHAPE;
+  if (!supported_n(c->dstate)) return RSS_E_SHAPE;
+  if ((int64_t)c->batch * c->nheads > 0x7fffffffLL) return RSS_E_SHAPE;
+  if (c->in_dtype != RSS_DTYPE_F32 && c->in_dtype != RSS_DTYPE_BF16) return RSS_E_DTYPE;
+  return RSS_OK;
+}
+
+int32_t check_config(const rss_config* c) {
+  int32_t st = check_shape(c);
+  if (st) return st;
+  if (c->read_copy != RSS_COPY_NONE && c->read_copy != RSS_COPY_BF16) return RSS_E_DTYPE;
+  if (c->window < 1 || c->capacity < c->window || c->capacity > rss::kMaxRing) return RSS_E_SHAPE;
+  if (c->max_draft < 0 || c->max_draft > rss::kMaxNew - 1) return RSS_E_CAPACITY;
+  if (c->capacity < c->window + c->max_draft) return RSS_E_CAPACITY;
+  return RSS_OK;
+}
+
+size_t in_bytes(const rss_config* c) { return c->in_dtype == RSS_DTYPE_BF16 ? 2 : 4; }
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? RSS_OK : RSS_E_HIP; }
+
+bool inputs_ok(const void* x, const void* B, const void* C, const void* dt, const void* y) {
+  return x && B && C && dt && y && aligned16(x) && aligned16(B) && aligned16(C) &&
+         aligned16(dt) && aligned16(y);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t rss_version(void) { return 10000; }
+
+const char* rss_status_string(int32_t s) {
+  switch (s) {
+    case RSS_OK: return "ok";
+    case RSS_E_INVALID: return "invalid argument (null or misaligned pointer, bad value)";
+    case RSS_E_SHAPE: return "unsupported or inconsistent sizes";
+    case RSS_E_DTYPE: return "unknown dtype or read-copy mode";
+    case RSS_E_CAPACITY: return "ring capacity too small (R < W + K_max) or K > K_max";
+    case RSS_E_ORDER: return "call order violated (verify round uncommitted, or no round to roll back)";
+    case RSS_E_HIP: return "HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t rss_buffer_sizes(const rss_config* c, rss_sizes* out) {
+  if (!out) return RSS_E_INVALID;
+  const int32_t st = check_config(c);
+  if (st) return st;
+  const size_t Bt = c->batch, H = c->nheads, P = c->headdim, N = c->dstate, G = c->ngroups,
+               R = c->capacity;
+  out->ckpt = Bt * H * P * N * 4;
+  out->ckpt_lo = c->read_copy == RSS_COPY_BF16 ? Bt * H * P * N * 2 : 0;
+  out->ring_x = Bt * H * R * P * in_bytes(c);
+  out->ring_B = Bt * G * R * N * in_bytes(c);
+  out->ring_dl = Bt * H * R * 2 * 4;
+  out->ptr = Bt * H * 4 * 4;
+  out->A = H * 4;
+  out->dev_err = 4;
+  return RSS_OK;
+}
+
+int32_t rss_layer_bind(const rss_config* c, const rss_buffers* d, rss_layer** out) {
+  if (!out) return RSS_E_INVALID;
+  *out = nullptr;
+  const int32_t st = check_config(c);
+  if (st) return st;
+  if (!d) return RSS_E_INVALID;
+  if (!d->A || !aligned16(d->A) || !d->dev_err || !aligned16(d->dev_err)) return RSS_E_INVALID;
+  if (c->batch > 0) {  // with no sequences the per-sequence buffers may be empty (NULL)
+    const void* req[] = {d->ckpt, d->ring_x, d->ring_B, d->ring_dl, d->ptr};
+    for (const void* p : req)
+      if (!p || !aligned16(p)) return RSS_E_INVALID;
+    if (c->read_copy == RSS_COPY_BF16 && (!d->ckpt_lo || !aligned16(d->ckpt_lo)))
+      return RSS_E_INVALID;
+  }
+  rss_layer* l = new (std::nothrow) rss_layer;
+  if (!l) return RSS_E_INVALID;
+  l->cfg = *c;
+  l->dev = *d;
+  if (c->read_copy != RSS_COPY_BF16) l->dev.ckpt_lo = nullptr;
+  l->pending_verify = 0;
+  *out = l;
+  return RSS_OK;
+}
+
+int32_t rss_layer_free(rss_layer* l) {
+  delete l;
+  return RSS_OK;
+}
+
+int32_t rss_init_state(rss_layer* l, const float* S0, void* stream) {
+  if (!l) return RSS_E_INVALID;
+  if (S0 && !aligned16(S0)) return RSS_E_INVALID;
+  const rss_config& c = l->cfg;
+  rss::InitArgs a;
+  a.ckpt = l->dev.ckpt;
+  a.ckpt_lo = l->dev.ckpt_lo;
+  a.S0 = S0;
+  a.ptr = reinterpret_cast<int4*>(l->dev.ptr);
+  a.err = l->dev.dev_err;
+  a.n_state = (size_t)c.batch * c.nheads * c.headdim * c.dstate;
+  a.n_ptr = (size_t)c.batch * c.nheads;
+  l->pending_verify = 0;
+  return launch_status(rss::launch_init(a, static_cast<hipStream_t>(stream)));
+}
+
+static int32_t replay_call(rss_layer* l, int nt, int set_tent, const void* x, const void* B,
+                           const void* C, const float* dt, float* y, void* stream) {
+  const rss_config& c = l->cfg;
+  if (c.batch == 0) return RSS_OK;
+  rss::ReplayArgs a;
+  a.ckpt = l->dev.ckpt;
+  a.ckpt_lo = l->dev.ckpt_lo;
+  a.ring_x = l->dev.ring_x;
+  a.ring_B = l->dev.ring_B;
+  a.ring_dl = reinterpret_cast<float2*>(l->dev.ring_dl);
+  a.ptr = reinterpret_cast<int4*>(l->dev.ptr);
+  a.A = l->dev.A;
+  a.err = l->dev.dev_err;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt = dt;
+  a.y = y;
+  a.H = c.nheads;
+  a.P = c.headdim;
+  a.G = c.ngroups;
+  a.R = c.capacity;
+  a.nt = nt;
+  a.set_tent = set_tent;
+  return launch_status(rss::launch_replay(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
+                                          c.read_copy == RSS_COPY_BF16,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int32_t rss_decode_step(rss_layer* l, const void* x, const void* B, const void* C, const float* dt,
+                        float* y, void* stream) {
+  if (!l) return RSS_E_INVALID;
+  if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
+  if (l->pending_verify) return RSS_E_ORDER;
+  return replay_call(l, 1, 0, x, B, C, dt, y, stream);
+}
+
+int32_t rss_verify_k_tokens(rss_layer* l, int32_t K, const void* x, const void* B, const void* C,
+                            const float* dt, float* y, void* stream) {
+  if (!l) return RSS_E_INVALID;
+  if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
+  if (K < 0) return RSS_E_INVALID;
+  if (K > l->cfg.max_draft) return RSS_E_CAPACITY;
+  if (l->pending_verify) return RSS_E_ORDER;
+  const int32_t st = replay_call(l, K + 1, 1, x, B, C, dt, y, stream);
+  if (st == RSS_OK) l->pending_verify = 1;
+  return st;
+}
+
+int32_t rss_rollback(rss_layer* l, const int32_t* n_drop, void* stream) {
+  if (!l) return RSS_E_INVALID;
+  if (l->cfg.batch > 0 && (!n_drop || !aligned16(n_drop))) return RSS_E_INVALID;
+  if (!l->pending_verify) return RSS_E_ORDER;
+  const rss_config& c = l->cfg;
+  l->pending_verify = 0;
+  if (c.batch == 0) return RSS_OK;
+  rss::RollbackArgs a;
+  a.ptr = reinterpret_cast<int4*>(l->dev.ptr);
+  a.n_drop = n_drop;
+  a.err = l->dev.dev_err;
+  a.H = c.nheads;
+  a.n_ptr = (size_t)c.batch * c.nheads;
+  return launch_status(rss::launch_rollback(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t rss_flush_checkpoint(rss_layer* l, int32_t min_len, void* stream) {
+  if (!l) return RSS_E_INVALID;
+  if (min_len < 1) return RSS_E_INVALID;
+  if (l->pending_verify) return RSS_E_ORDER;
+  const rss_config& c = l->cfg;
+  if (c.batch == 0) return RSS_OK;
+  rss::FlushArgs a;
+  a.ckpt = l->dev.ckpt;
+  a.ckpt_lo = l->dev.ckpt_lo;
+  a.ring_x = l->dev.ring_x;
+  a.ring_B = l->dev.ring_B;
+  a.ring_dl = reinterpret_cast<const float2*>(l->dev.ring_dl);
+  a.ptr = reinterpret_cast<int4*>(l->dev.ptr);
+  a.err = l->dev.dev_err;
+  a.H = c.nheads;
+  a.P = c.headdim;
+  a.G = c.ngroups;
+  a.R = c.capacity;
+  a.min_len = min_len;
+  return launch_status(rss::launch_flush(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
+                                         c.read_copy == RSS_COPY_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int32_t rss_get_device_error(rss_layer* l, int32_t* host_code, void* stream) {
+  if (!l || !host_code) return RSS_E_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, l->dev.dev_err, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return RSS_E_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return RSS_E_HIP;
+  *host_code = v;
+  return RSS_OK;
+}
+
+static int32_t eager_call(const rss_config* c, float* S, const int32_t* src_slot, int32_t slots,
+                          int32_t T, const void* x, const void* B, const void* C, const float* dt,
+                          const float* A, float* y, void* stream) {
+  const int32_t st = check_shape(c);
+  if (st) return st;
+  if (T < 1 || T > rss::kMaxNew) return RSS_E_INVALID;
+  if (!A || !aligned16(A)) return RSS_E_INVALID;
+  if (c->batch == 0) return RSS_OK;
+  if (!S || !aligned16(S) || !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
+  rss::EagerArgs a;
+  a.S = S;
+  a.src_slot = src_slot;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt = dt;
+  a.A = A;
+  a.y = y;
+  a.H = c->nheads;
+  a.P = c->headdim;
+  a.G = c->ngroups;
+  a.T = T;
+  a.slots = slots;
+  return launch_status(rss::launch_eager(a, c->batch, c->dstate, c->in_dtype == RSS_DTYPE_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int32_t rss_eager_step(const rss_config* c, float* S, const void* x, const void* B, const void* C,
+                       const float* dt, const float* A, float* y, int32_t T, void* stream) {
+  return eager_call(c, S, nullptr, 0, T, x, B, C, dt, A, y, stream);
+}
+
+int32_t rss_eager_verify(const rss_config* c, float* pool, const int32_t* src_slot, int32_t K,
+                         const void* x, const void* B, const void* C, const float* dt,
+                         const float* A, float* y, void* stream) {
+  if (K < 0 || K > rss::kMaxNew - 1) return RSS_E_INVALID;
+  if (c && c->batch > 0 && (!src_slot || !aligned16(src_slot))) return RSS_E_INVALID;
+  return eager_call(c, pool, src_slot, K + 1, K + 1, x, B, C, dt, A, y, stream);
+}
+
+}  // extern "C"

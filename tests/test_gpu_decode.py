@@ -1,0 +1,190 @@
+"""GPU parity of plain decode: replay + flush and the eager kernel against the
+fp64 oracle at every step, pointers bit-exact against the ring model, ring
+contents bit-exact against the inputs, across shapes, dtypes and both
+precision modes. All calls go through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mamba2
+from oracle.ring import PointerModel
+import workloads
+from workloads import synth
+from recurrent_state_storage_amd import rss
+from gpu_util import DEV, cfg_of, dev_inputs, rel_l2, log
+
+pytestmark = pytest.mark.gpu
+
+TINY = workloads.get("tiny_b2_h4_p16_n16_w8")
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.contiguous().cpu()
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).numpy()
+
+
+def _run_decode(wl, steps, flush_every_step=True, check_ring=True, check_eager=True):
+    """Drive replay (+eager) for `steps` tokens; compare with the oracle each step.
+
+    Returns a dict of the worst errors seen."""
+    log(f"[decode] {wl.name} P={wl.headdim} N={wl.dstate} H={wl.nheads} G={wl.ngroups} "
+        f"W={wl.window} R={wl.capacity} in={wl.in_dtype} copy={wl.read_copy} s0={wl.s0}")
+    cfg = cfg_of(wl)
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    S0 = synth.initial_state(wl)
+    layer = rss.ReplayLayer(cfg, A, DEV)
+    layer.init_state(torch.from_numpy(S0).to(DEV))
+    S_eag = torch.from_numpy(S0).to(DEV).clone()
+    S_ref = S0.astype(np.float64)
+    dual_ref = mamba2.ReplayModel(S0, A_np, wl.ngroups, wl.capacity, read_copy=wl.read_copy) \
+        if wl.read_copy == "bf16" else None
+    pm = PointerModel(wl.batch, wl.capacity)
+    Bt, H, P = wl.batch, wl.nheads, wl.headdim
+    hist = []
+    worst = {"step": 0.0, "eager": 0.0, "ckpt": 0.0, "dual_emul": 0.0}
+    ys, yrefs = [], []
+    for t in range(steps):
+        s = synth.step_inputs(wl, t)
+        hist.append(s)
+        d = dev_inputs(s, wl.in_dtype)
+        y = torch.full((Bt, H, P), float("nan"), device=DEV)
+        layer.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+        for b in range(Bt):
+            pm.append(b, 1)
+        S_ref, y_ref = mamba2.eager_step(S_ref, A_np, s["x"], s["B"], s["C"], s["dt"])
+        if check_eager:
+            ye = torch.full((Bt, H, P), float("nan"), device=DEV)
+            rss.rss_eager_step(cfg, S_eag, d["x"], d["B"], d["C"], d["dt"], A, ye)
+            worst["eager"] = max(worst["eager"], rel_l2(ye.double().cpu().numpy(), y_ref))
+        yg = y.double().cpu().numpy()
+        assert np.isfinite(yg).all(), f"non-finite output at step {t}"
+        worst["step"] = max(worst["step"], rel_l2(yg, y_ref))
+        ys.append(yg)
+        yrefs.append(y_ref)
+        if dual_ref is not None:
+            y_em = dual_ref.decode(s["x"], s["B"], s["C"], s["dt"])
+            worst["dual_emul"] = max(worst["dual_emul"], rel_l2(yg, y_em))
+        flushed = False
+        if flush_every_step or (t + 1) % wl.window == 0:
+            layer.flush_checkpoint(wl.window)
+            for b in range(Bt):
+                flushed |= pm.flush(b, wl.window)
+            if dual_ref is not None:
+                dual_ref.flush(wl.window)
+        # pointers: every head holds the sequence's values
+        ptr = layer.ptr.cpu().numpy()
+        want = pm.as_array()
+        for h in range(H):
+            assert np.array_equal(ptr[:, h, :3], want), f"pointers differ at step {t}, head {h}"
+        assert (ptr[:, :, 3] == 0).all()
+        if flushed:
+            worst["ckpt"] = max(worst["ckpt"], rel_l2(layer.ckpt.double().cpu().numpy(), S_ref))
+            if dual_ref is not None:   # the copy is torch's RNE bf16 cast of the master
+                assert torch.equal(layer.ckpt_lo.cpu(), layer.ckpt.cpu().to(torch.bfloat16)), \
+                    "read copy is not RNE-bf16 of the master"
+        if check_ring:
+            rx, rB = _bits(layer.ring_x), _bits(layer.ring_B)
+            for b in range(Bt):
+                c = t + 1 - int(pm.len[b])
+                for j in range(int(pm.len[b])):
+                    slot = pm.slot(b, j)
+                    src = hist[c + j]
+                    xb = src["x_bits"] if wl.in_dtype == "bf16" else src["x"]
+                    Bb = src["B_bits"] if wl.in_dtype == "bf16" else src["B"]
+                    assert np.array_equal(rx[b, :, slot].view(xb.dtype), xb[b]), (t, b, j)
+                    assert np.array_equal(rB[b, :, slot].view(Bb.dtype), Bb[b]), (t, b, j)
+    assert layer.device_error() == 0
+    worst["run"] = rel_l2(np.stack(ys), np.stack(yrefs))
+    return worst, layer
+
+
+@pytest.mark.parametrize("groups", [4, 2, 1])
+@pytest.mark.parametrize("s0", ["zeros", "normal"])
+def test_tiny_workload_every_step(s0, groups):
+    wl = TINY.replace(s0=s0, ngroups=groups)
+    w, _ = _run_decode(wl, wl.steps)
+    log(f"  worst {w}")
+    assert w["step"] < 1e-5 and w["run"] < 1e-5
+    assert w["eager"] < 1e-5
+    assert w["ckpt"] < 1e-5
+
+
+def test_tiny_flush_only_at_window():
+    wl = TINY.replace(s0="normal", capacity=11)
+    w, _ = _run_decode(wl, wl.steps, flush_every_step=False)
+    assert w["step"] < 1e-5 and w["ckpt"] < 1e-5
+
+
+SHAPES = [
+    # P, N, H, G, W, R, in_dtype, copy
+    (37, 32, 3, 1, 5, 7, "f32", "none"),
+    (64, 128, 4, 2, 16, 16, "bf16", "none"),
+    (64, 128, 4, 4, 16, 16, "bf16", "bf16"),
+    (100, 64, 2, 2, 6, 9, "bf16", "none"),
+    (100, 256, 2, 2, 4, 4, "f32", "none"),
+    (128, 128, 2, 2, 8, 8, "f32", "bf16"),
+    (256, 16, 2, 1, 3, 3, "f32", "none"),
+    (1, 16, 1, 1, 1, 1, "f32", "none"),
+    (64, 32, 8, 2, 8, 12, "bf16", "none"),
+    (48, 256, 2, 1, 7, 8, "bf16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "P%dN%dH%dG%dW%dR%d-%s-%s" % s)
+def test_shapes(shape):
+    P, N, H, G, W, R, idt, copy = shape
+    wl = TINY.replace(name="sweep", batch=3, headdim=P, dstate=N, nheads=H, ngroups=G, window=W,
+                      capacity=R, in_dtype=idt, read_copy=copy, s0="normal", seed=2000 + P + N)
+    w, layer = _run_decode(wl, 3 * W + 2)
+    log(f"  worst {w}")
+    if copy == "none":
+        assert w["step"] < 1e-5 and w["run"] < 1e-5
+    else:
+        assert w["run"] < 2e-2 and w["dual_emul"] < 1e-3
+    assert w["eager"] < 1e-5
+    assert w["ckpt"] < 1e-5       # the fp32 master is exact in both modes
+
+
+def test_dual_master_equals_fp32_checkpoint():
+    """The bf16 read copy never feeds back: the dual-mode master is bitwise the
+    fp32-mode checkpoint after the same tokens."""
+    base = TINY.replace(name="dual", batch=4, headdim=64, dstate=128, nheads=4, ngroups=4,
+                        window=8, capacity=8, in_dtype="bf16", s0="normal", seed=3001)
+    layers = {}
+    for copy in ("none", "bf16"):
+        wl = base.replace(read_copy=copy)
+        cfg = cfg_of(wl)
+        A = torch.from_numpy(synth.params(wl)["A"]).to(DEV)
+        L = rss.ReplayLayer(cfg, A, DEV)
+        L.init_state(torch.from_numpy(synth.initial_state(wl)).to(DEV))
+        layers[copy] = (L, A)
+    y = torch.empty((4, 4, 64), device=DEV)
+    for t in range(27):
+        d = dev_inputs(synth.step_inputs(base, t), "bf16")
+        for L, _ in layers.values():
+            L.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+            L.flush_checkpoint(8)
+    torch.cuda.synchronize()
+    assert torch.equal(layers["none"][0].ckpt, layers["bf16"][0].ckpt)
+    assert torch.equal(layers["none"][0].ptr, layers["bf16"][0].ptr)
+
+
+def test_deterministic():
+    wl = TINY.replace(name="det", batch=4, headdim=64, dstate=128, nheads=8, ngroups=8,
+                      window=16, capacity=16, in_dtype="bf16", s0="normal", seed=3002)
+    outs = []
+    for _ in range(2):
+        cfg = cfg_of(wl)
+        A = torch.from_numpy(synth.params(wl)["A"]).to(DEV)
+        L = rss.ReplayLayer(cfg, A, DEV)
+        L.init_state(torch.from_numpy(synth.initial_state(wl)).to(DEV))
+        ys = []
+        for t in range(40):
+            d = dev_inputs(synth.step_inputs(wl, t), "bf16")
+            y = torch.empty((4, 8, 64), device=DEV)
+            L.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+            L.flush_checkpoint(16)
+            ys.append(y)
+        outs.append((torch.stack(ys).cpu(), L.ckpt.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

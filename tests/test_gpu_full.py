@@ -1,0 +1,174 @@
+"""Full-size parity, in the launch configuration the benchmark times.
+
+Sizes: batch 256 x 128 heads x P=64 x N=128 (4 MiB fp32 state per sequence),
+bf16 x/B/C, W=16; batch 512 speculative rounds with K=4; dual precision over
+1024 steps. The oracle checks sampled (sequence, head) pairs one by one (pairs
+are independent); properties that hold at any size (replay == eager on the
+whole batch, pointers on every sequence, untouched checkpoint bytes) are
+checked in full."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mamba2
+from oracle.ring import PointerModel
+import workloads
+from workloads import synth
+from recurrent_state_storage_amd import rss
+from gpu_util import DEV, PairGather, cfg_of, dev_inputs, rel_l2, sample_pairs, log
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def test_decode_b256_full_size():
+    wl = workloads.get("mamba2_b256_h128_p64_n128_w16")
+    log(f"[full] {wl.name}: {wl.steps} steps, flush every {wl.window}")
+    cfg = cfg_of(wl)
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    layer = rss.ReplayLayer(cfg, A, DEV)
+    layer.init_state()
+    S_eag = torch.zeros((wl.batch, wl.nheads, wl.headdim, wl.dstate), device=DEV)
+    pg = PairGather(wl, sample_pairs(wl, 24, seed=11))
+    S_ref = np.zeros((1, len(pg.pairs), wl.headdim, wl.dstate))      # S0 = 0
+    A_pair = pg.A(A_np)
+    y = torch.empty((wl.batch, wl.nheads, wl.headdim), device=DEV)
+    ye = torch.empty_like(y)
+    worst_pair = worst_eager = worst_ckpt = 0.0
+    ys, refs = [], []
+    for t in range(wl.steps):
+        s = synth.step_inputs(wl, t)
+        d = dev_inputs(s, wl.in_dtype)
+        layer.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+        rss.rss_eager_step(cfg, S_eag, d["x"], d["B"], d["C"], d["dt"], A, ye)
+        ps = pg.step(s)
+        S_ref, y_ref = mamba2.eager_step(S_ref, A_pair, ps["x"], ps["B"], ps["C"], ps["dt"])
+        got = pg.out(y)
+        worst_pair = max(worst_pair, rel_l2(got, y_ref))
+        ys.append(got)
+        refs.append(y_ref)
+        worst_eager = max(worst_eager, float(torch.linalg.vector_norm(y - ye) / torch.linalg.vector_norm(ye)))
+        if (t + 1) % wl.window == 0:
+            layer.flush_checkpoint(wl.window)
+            ck = layer.ckpt[torch.as_tensor(pg.b, device=DEV), torch.as_tensor(pg.h, device=DEV)]
+            worst_ckpt = max(worst_ckpt, rel_l2(ck.double().cpu().numpy()[None], S_ref))
+            st = layer.ptr.cpu()
+            assert (st[:, :, 1] == 0).all() and (st[:, :, 0] == 0).all()   # R = W: head returns to 0
+        if t % 64 == 0:
+            log(f"  step {t}: pair rel-L2 {worst_pair:.2e}, replay vs eager {worst_eager:.2e}")
+    run = rel_l2(np.stack(ys), np.stack(refs))
+    log(f"  pairs worst/run {worst_pair:.3e}/{run:.3e}; replay vs eager {worst_eager:.3e}; ckpt {worst_ckpt:.3e}")
+    assert layer.device_error() == 0
+    assert worst_pair < 1e-5 and run < 1e-5
+    assert worst_eager < 1e-5
+    assert worst_ckpt < 1e-5
+    # the eager kernel's own state against the oracle on the pairs
+    se = S_eag[torch.as_tensor(pg.b, device=DEV), torch.as_tensor(pg.h, device=DEV)]
+    assert rel_l2(se.double().cpu().numpy()[None], S_ref) < 1e-5
+
+
+def test_spec_b512_full_size():
+    wl = workloads.get("mamba2_spec_b512_h128_p64_n128_w16_k4")
+    rounds = 6
+    log(f"[full] {wl.name}: {rounds} rounds")
+    cfg = cfg_of(wl)
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    Bt, H, P, N, K = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.draft
+    layer = rss.ReplayLayer(cfg, A, DEV)
+    layer.init_state()
+    pool = torch.zeros((Bt, K + 1, H, P, N), device=DEV)
+    src = torch.zeros((Bt,), dtype=torch.int32, device=DEV)
+    pm = PointerModel(Bt, wl.capacity)
+    pg = PairGather(wl, sample_pairs(wl, 24, seed=12))
+    S_ref = np.zeros((1, len(pg.pairs), P, N))
+    A_pair = pg.A(A_np)
+    y = torch.empty((Bt, K + 1, H, P), device=DEV)
+    ye = torch.empty_like(y)
+    bidx, hidx = torch.as_tensor(pg.b, device=DEV), torch.as_tensor(pg.h, device=DEV)
+    for r in range(rounds):
+        rin = synth.draft_inputs(wl, r)
+        nacc = synth.accepted_drafts(wl, r)
+        d = dev_inputs(rin, wl.in_dtype)
+        ck = layer.ckpt.clone()
+        layer.verify_k_tokens(K, d["x"], d["B"], d["C"], d["dt"], y)
+        rss.rss_eager_verify(cfg, pool, src, K, d["x"], d["B"], d["C"], d["dt"], A, ye)
+        # oracle on the pairs: K+1 eager steps from the committed state
+        pr = pg.draft(rin)
+        states, refs = [], []
+        S_run = S_ref
+        for i in range(K + 1):
+            S_run, yi = mamba2.eager_step(S_run, A_pair, pr["x"][:, i], pr["B"][:, i], pr["C"][:, i], pr["dt"][:, i])
+            states.append(S_run)
+            refs.append(yi)
+        y_ref = np.stack(refs, axis=1)                                   # (1,K+1,n,P)
+        got = y[bidx, :, hidx].permute(1, 0, 2).double().cpu().numpy()[None]
+        goe = ye[bidx, :, hidx].permute(1, 0, 2).double().cpu().numpy()[None]
+        e1, e2 = rel_l2(got, y_ref), rel_l2(goe, y_ref)
+        log(f"  round {r}: replay {e1:.2e}, eager+snapshots {e2:.2e}")
+        assert e1 < 1e-5 and e2 < 1e-5
+        n_drop = torch.from_numpy((K - nacc).astype(np.int32)).to(DEV)
+        layer.rollback(n_drop)
+        for b in range(Bt):
+            pm.append(b, K + 1)
+            pm.mark_tentative(b, K + 1)
+            pm.rollback(b, int(K - nacc[b]))
+        assert torch.equal(layer.ckpt, ck), "verify/rollback changed checkpoint bytes"
+        del ck
+        ptr = layer.ptr.cpu().numpy()
+        want = pm.as_array()
+        assert all(np.array_equal(ptr[:, h, :3], want) for h in range(H))
+        layer.flush_checkpoint(wl.window)
+        for b in range(Bt):
+            pm.flush(b, wl.window)
+        ptr = layer.ptr.cpu().numpy()
+        assert all(np.array_equal(ptr[:, h, :3], pm.as_array()) for h in range(H))
+        keep = nacc[pg.b]
+        S_ref = np.stack([states[keep[i]][0, i] for i in range(len(pg.pairs))])[None]
+        src = torch.from_numpy(nacc.astype(np.int32)).to(DEV)
+    assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("window", [8, 16, 32])
+def test_dual_precision_drift(window):
+    """fp32 master + bf16 read copy over 1024 steps on 16 sequences of the
+    batch-256 shape: output drift vs the fp64 recurrence stays within 2e-2, the
+    master matches the recurrence to 1e-5, and is bitwise the fp32-mode checkpoint."""
+    wl = workloads.get(f"mamba2_dual_b256_h128_p64_n128_w{window}").replace(batch=16)
+    log(f"[full] {wl.name} (16 sequences), {wl.steps} steps")
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    dual = rss.ReplayLayer(cfg_of(wl), A, DEV)
+    ref32 = rss.ReplayLayer(cfg_of(wl.replace(read_copy="none")), A, DEV)
+    dual.init_state()
+    ref32.init_state()
+    pg = PairGather(wl, sample_pairs(wl, 24, seed=13))
+    S_ref = np.zeros((1, len(pg.pairs), wl.headdim, wl.dstate))
+    A_pair = pg.A(A_np)
+    y = torch.empty((wl.batch, wl.nheads, wl.headdim), device=DEV)
+    y32 = torch.empty_like(y)
+    drift, ys, refs, master = 0.0, [], [], 0.0
+    bidx, hidx = torch.as_tensor(pg.b, device=DEV), torch.as_tensor(pg.h, device=DEV)
+    for t in range(wl.steps):
+        s = synth.step_inputs(wl, t)
+        d = dev_inputs(s, wl.in_dtype)
+        dual.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+        ref32.decode_step(d["x"], d["B"], d["C"], d["dt"], y32)
+        ps = pg.step(s)
+        S_ref, y_ref = mamba2.eager_step(S_ref, A_pair, ps["x"], ps["B"], ps["C"], ps["dt"])
+        got = pg.out(y)
+        drift = max(drift, rel_l2(got, y_ref))
+        ys.append(got)
+        refs.append(y_ref)
+        if (t + 1) % window == 0:
+            dual.flush_checkpoint(window)
+            ref32.flush_checkpoint(window)
+            ck = dual.ckpt[bidx, hidx].double().cpu().numpy()[None]
+            master = max(master, rel_l2(ck, S_ref))
+    torch.cuda.synchronize()
+    final = rel_l2(ys[-1], refs[-1])
+    run = rel_l2(np.stack(ys), np.stack(refs))
+    log(f"  W={window}: drift max {drift:.3e}, final {final:.3e}, run {run:.3e}, master {master:.3e}")
+    assert torch.equal(dual.ckpt, ref32.ckpt)
+    assert drift < 2e-2 and run < 2e-2
+    assert master < 1e-5
