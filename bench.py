@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the ReplaySSM hot path on one MI355X.
+
+Workload: one Mamba-2 SSM layer in decode, batch 256, 128 heads x P=64 x N=128
+(a 4 MiB fp32 state per sequence), bf16 x/B/C, fp32 dt and A, flush window
+W=16, synthetic seeded inputs (workloads.synth; 256 distinct decode steps
+resident in HBM before timing, cycled when more steps are timed).
+
+A step is one decode token for the whole batch through the replay path: the
+replay decode kernel every step, plus the checkpoint fold every W steps (the
+fold's cost is part of the timed region). The eager-rewrite kernel on the same
+inputs is timed too, so the state-traffic cut is measured.
+
+Output: one JSON line with tokens/s per layer (whole-job throughput, inputs
+already in HBM), the dominant kernel's roofline (algorithmic bytes per launch
+over the HIP-event-measured launch duration, against 8 TB/s), and the fp64 CPU
+oracle timed on a bounded sample on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+from workloads import synth  # noqa: E402
+
+WORKLOAD = "mamba2_b256_h128_p64_n128_w16"
+METRIC = "SSM decode tokens/s per layer + achieved HBM GB/s (% of peak), batch 256"
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "replay_decode_b256_hbm_counters.txt")
+KERNEL_SOURCES = ["replay.hip", "device.h", "limits.h", "launch.h"]
+
+
+# ---- algorithmic bytes (what the method must move, per (sequence, head)) ----
+def replay_bytes(wl, n0: int) -> int:
+    """Replay decode of one token with n0 entries already in the window."""
+    P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
+    tile = P * N * (2 if wl.read_copy == "bf16" else 4)
+    entry = P * ib + N * ib + 8                     # x, B, (dt, dt*A)
+    inputs = P * ib + 2 * N * ib + 4                 # x_t, B_t, C_t, dt_t
+    return tile + n0 * entry + inputs + P * 4 + entry + 32 + 4   # + y, append, pointers, A
+
+
+def flush_bytes(wl, n: int) -> int:
+    """Fold of n window entries into one checkpoint tile (read + write)."""
+    P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
+    lo = P * N * 2 if wl.read_copy == "bf16" else 0
+    return 2 * P * N * 4 + lo + n * (P * ib + N * ib + 8) + 32
+
+
+def eager_bytes(wl) -> int:
+    P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
+    return 2 * P * N * 4 + P * ib + 2 * N * ib + 4 + P * 4 + 4
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "recurrent_state_storage_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per replay launch from the committed rocprofv3 counter summary,
+    or None when the summary is absent or the kernel changed since."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            m = re.match(r"^(\w+)\s*=\s*(\S+)", line.strip())
+            if m:
+                vals[m.group(1)] = m.group(2)
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["replay_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---- inputs -------------------------------------------------------------------
+def _gen_step(args):
+    name, t = args
+    s = synth.step_inputs(workloads.get(name), t)
+    return t, s["x_bits"], s["B_bits"], s["C_bits"], s["dt"]
+
+
+def gen_pool(wl, T: int, workers: int):
+    xs = np.empty((T, wl.batch, wl.nheads, wl.headdim), np.uint16)
+    Bs = np.empty((T, wl.batch, wl.ngroups, wl.dstate), np.uint16)
+    Cs = np.empty_like(Bs)
+    dts = np.empty((T, wl.batch, wl.nheads), np.float32)
+    with concurrent.futures.ProcessPoolExecutor(max_workers=workers) as ex:
+        for t, x, B, C, dt in ex.map(_gen_step, [(wl.name, t) for t in range(T)]):
+            xs[t], Bs[t], Cs[t], dts[t] = x, B, C, dt
+    return xs, Bs, Cs, dts
+
+
+# ---- CPU baseline: the fp64 oracle as it stands ----------------------------------
+def cpu_baseline(wl, pool, budget_s: float):
+    from threadpoolctl import threadpool_limits
+    from oracle import mamba2
+    nseq = 16
+    xs, Bs, Cs, dts = pool
+    A = synth.params(wl)["A"]
+    S = np.zeros((nseq, wl.nheads, wl.headdim, wl.dstate))
+    bf = synth.bf16_value
+    steps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            i = steps % xs.shape[0]
+            S, _ = mamba2.eager_step(S, A, bf(xs[i, :nseq]), bf(Bs[i, :nseq]), bf(Cs[i, :nseq]),
+                                     dts[i, :nseq])
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or steps >= 256:
+                break
+    return {"value": nseq * steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 eager recurrence, {nseq} of {wl.batch} sequences x {wl.nheads} heads, "
+                      f"{steps} decode steps ({el:.1f} s, 1 thread)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--pool", type=int, default=256, help="distinct decode steps kept in HBM")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-eager", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU step, and every "
+              "(sequence, head) shard runs the same kernel at a smaller batch. Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from recurrent_state_storage_amd import rss
+
+    wl = workloads.get(WORKLOAD)
+    Bt, H, P, N, G, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window
+    dev = torch.device("cuda:0")
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    pool = gen_pool(wl, args.pool, workers)
+    gen_s = time.perf_counter() - t0
+    X = torch.from_numpy(pool[0].view(np.int16)).view(torch.bfloat16).to(dev)
+    Bm = torch.from_numpy(pool[1].view(np.int16)).view(torch.bfloat16).to(dev)
+    Cm = torch.from_numpy(pool[2].view(np.int16)).view(torch.bfloat16).to(dev)
+    DT = torch.from_numpy(pool[3]).to(dev)
+    A = torch.from_numpy(synth.params(wl)["A"]).to(dev)
+    cfg = rss.make_config(Bt, H, P, N, G, W, wl.capacity, 0, rss.RSS_DTYPE_BF16, rss.RSS_COPY_NONE)
+    layer = rss.ReplayLayer(cfg, A, dev)
+    layer.init_state()
+    y = torch.empty((Bt, H, P), device=dev)
+    T = args.pool
+
+    def replay_step(k, ev=None):
+        i = k % T
+        if ev is not None:
+            ev[0].record()
+        layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
+        if ev is not None:
+            ev[1].record()
+        if (k + 1) % W == 0:
+            if ev is not None:
+                ev[2].record()
+            layer.flush_checkpoint(W)
+            if ev is not None:
+                ev[3].record()
+
+    k = 0
+    for _ in range(args.warmup):
+        replay_step(k)
+        k += 1
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        replay_step(k)
+        k += 1
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    tok_s = Bt * args.steps / (ms / 1e3)
+
+    # Per-kernel durations: HIP events around every launch on the launch stream,
+    # in a second pass of the same length (so the timed pass above is unperturbed).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    phase = []
+    for j in range(args.steps):
+        phase.append(k % W)
+        replay_step(k, ev[j])
+        k += 1
+    torch.cuda.synchronize()
+    rep_ms, rep_bytes, fl_ms, fl_bytes, n_fl = 0.0, 0, 0.0, 0, 0
+    for j in range(args.steps):
+        rep_ms += ev[j][0].elapsed_time(ev[j][1])
+        rep_bytes += replay_bytes(wl, phase[j]) * Bt * H
+        if phase[j] == W - 1:
+            fl_ms += ev[j][2].elapsed_time(ev[j][3])
+            fl_bytes += flush_bytes(wl, W) * Bt * H
+            n_fl += 1
+    rep_avg_us = rep_ms / args.steps * 1e3
+    rep_gbs = rep_bytes / (rep_ms / 1e3) / 1e9
+    assert layer.device_error() == 0
+
+    out_eager = None
+    if not args.no_eager:
+        S = torch.zeros((Bt, H, P, N), device=dev)
+        ye = torch.empty_like(y)
+
+        def eager_step(k):
+            i = k % T
+            rss.rss_eager_step(cfg, S, X[i], Bm[i], Cm[i], DT[i], A, ye)
+        for j in range(args.warmup):
+            eager_step(j)
+        torch.cuda.synchronize()
+        e0.record()
+        for j in range(args.steps):
+            eager_step(j)
+        e1.record()
+        torch.cuda.synchronize()
+        ems = e0.elapsed_time(e1)
+        eev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for j in range(args.steps):
+            eev[j][0].record()
+            eager_step(j)
+            eev[j][1].record()
+        torch.cuda.synchronize()
+        eag_ms = sum(a.elapsed_time(b) for a, b in eev)
+        out_eager = {
+            "tokens_per_s": Bt * args.steps / (ems / 1e3), "ms_per_step": ems / args.steps,
+            "kernel_avg_us": eag_ms / args.steps * 1e3,
+            "kernel_GBps": eager_bytes(wl) * Bt * H * args.steps / (eag_ms / 1e3) / 1e9,
+            "bytes_per_token": eager_bytes(wl) * H,
+        }
+        del S
+
+    if args.calibrate_copy:
+        src = torch.ones((1 << 28,), device=dev)      # 1 GiB fp32
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # Bytes per decoded token per layer (analytic): state tiles, and everything.
+    st_replay = P * N * 4 * H + 2 * P * N * 4 * H / W
+    st_eager = 2 * P * N * 4 * H
+    tot_replay = (sum(replay_bytes(wl, n) for n in range(W)) / W + flush_bytes(wl, W) / W) * H
+    traffic = counter_traffic()
+    rec = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": Bt, "heads": H, "headdim": P, "dstate": N,
+                   "groups": G, "window": W, "xBC_storage": "bf16", "state": "f32",
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": rep_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": rep_gbs / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "replay decode", "avg_launch_us": rep_avg_us,
+                     "algorithmic_bytes_per_launch": rep_bytes / args.steps},
+        "kernels": {
+            "replay_decode": {"avg_us": rep_avg_us, "GBps": rep_gbs},
+            "flush": {"avg_us": fl_ms / max(n_fl, 1) * 1e3,
+                      "GBps": fl_bytes / (fl_ms / 1e3) / 1e9 if n_fl else None, "launches": n_fl},
+        },
+        "eager_baseline": out_eager,
+        "bytes_per_token": {"replay_state": st_replay, "eager_state": st_eager,
+                            "state_ratio": st_replay / st_eager, "replay_total": tot_replay,
+                            "eager_total": eager_bytes(wl) * H,
+                            "total_ratio": tot_replay / (eager_bytes(wl) * H)},
+        "input_generation_s": gen_s,
+    }
+    if out_eager:
+        rec["speedup_vs_eager_gpu"] = tok_s / out_eager["tokens_per_s"]
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, pool, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -34,9 +34,11 @@ def _rng(seed: int, stream: int, idx: int | None = None) -> np.random.Generator:
 def bf16_bits(a: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
 
-    Inputs are finite normal draws here; NaN and Inf are not handled."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    Adds half of the dropped 16 bits (minus one when the kept part is even) and
+    truncates. Exact for every finite value (overflow rounds to Inf); NaN inputs
+    are not handled (the generators never draw them)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 
