@@ -80,8 +80,71 @@ template <> struct Frag<true> {
   }
 };
 
-__device__ __forceinline__ float4 ld16(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ uint4 ld16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte loads of checkpoint tiles: each byte is used once, so they
+// are marked non-temporal to keep the caches for the small, reused data.
+__device__ __forceinline__ float4 ld16(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16(const bf16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(float* p, const float4& v) {
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// Reverse exclusive scan over the 64 lanes of a wavefront:
+// returns sum_{m > lane} v_m, summed as a fixed tree (deterministic).
+__device__ __forceinline__ float wave_suffix_excl(float v, int lane) {
+  float s = __shfl_down(v, 1, 64);
+  if (lane == 63) s = 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_down(s, off, 64);
+    if (lane + off < 64) s += t;
+  }
+  return s;
+}
+
+// 16-byte vectors of input elements (8 bf16 or 4 fp32) and their fp32 unpacking
+// into LDS. Window rows are staged through these: row lengths are multiples of
+// the vector width, so a vector never straddles two rows.
+template <typename Tin> struct V16;
+template <> struct V16<float> {
+  typedef float4 T;
+  static constexpr int VE = 4;
+};
+template <> struct V16<bf16_t> {
+  typedef uint4 T;
+  static constexpr int VE = 8;
+};
+
+template <typename Tin>
+__device__ __forceinline__ typename V16<Tin>::T ldv(const Tin* p) {
+  return *reinterpret_cast<const typename V16<Tin>::T*>(p);
+}
+
+__device__ __forceinline__ void st_lds_f32(float* d, const float4& v) {
+  *reinterpret_cast<float4*>(d) = v;
+}
+__device__ __forceinline__ void st_lds_f32(float* d, const uint4& v) {
+  *reinterpret_cast<float4*>(d) =
+      make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                  __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+  *reinterpret_cast<float4*>(d + 4) =
+      make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
+                  __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+}
+
+__host__ __device__ constexpr int align4(int n) { return (n + 3) & ~3; }
 
 // Ring slot of window position j (0 <= head < R, 0 <= j < R).
 __device__ __forceinline__ int ring_slot(int head, int j, int R) {

@@ -19,21 +19,31 @@
 
 namespace rss {
 
-constexpr int kFlushChunk = 16;  // window entries staged in LDS at a time
+constexpr int kFlushStage = 2;  // 16-byte loads per thread per staging round and array
+
+// Dynamic LDS layout of the flush kernel, in floats.
+struct FlushLds {
+  int oX, oB, oCF, total;
+  __host__ __device__ FlushLds(int R, int P, int N) {
+    oX = 0;                  // window x rows [R][P]
+    oB = align4(R * P);      // window B rows [R][N]
+    oCF = oB + R * N;        // c_j = exp(lam_j) dt_j [R], then exp(Lam)
+    total = oCF + R + 1;
+  }
+};
 
 template <int N, typename Tin, bool DUAL>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
-  constexpr int EC = kFlushChunk;
+  constexpr int VE = V16<Tin>::VE;
+  constexpr int NV = N / VE;
+  using VT = typename V16<Tin>::T;
 
-  __shared__ float sl[kMaxRing];
-  __shared__ float sdt[kMaxRing];
-  __shared__ float sc[kMaxRing];
-  __shared__ float sD;
-  extern __shared__ __align__(16) float dyn[];  // xs[EC][P] (c_j x_j), then Bs[EC][N]
+  extern __shared__ __align__(16) float lds[];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int H = a.H, P = a.P, G = a.G, R = a.R;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh - b * H;
@@ -49,11 +59,16 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (tid == 0) atomicOr(a.err, kDevUncommitted);
     return;
   }
-  float* xs = dyn;
-  float* Bs = dyn + EC * P;
+  const FlushLds lay(R, P, N);
+  float* sX = lds + lay.oX;
+  float* sB = lds + lay.oB;
+  float* sCF = lds + lay.oCF;
   const Tin* rx = static_cast<const Tin*>(a.ring_x);
   const Tin* rB = static_cast<const Tin*>(a.ring_B);
+  auto xrow = [&](int j) { return rx + ((size_t)bh * R + ring_slot(head, j, R)) * P; };
+  auto brow = [&](int j) { return rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N; };
 
+  // 1. Tile loads (fp32 master).
   const int col = tid % TPR, rsub = tid / TPR;
   float* tile = a.ckpt + (size_t)bh * P * N;
   Frag<false> fr[kMaxPass];
@@ -67,25 +82,63 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   };
   load_chunk(0);
 
-  if (tid < n) {
-    const float2 v = a.ring_dl[(size_t)bh * R + ring_slot(head, tid, R)];
-    sdt[tid] = v.x;
-    sl[tid] = v.y;
+  // 2. Window rows and (dt, l) in one round of loads, unpacked into LDS.
+  const bool xvec = (P % VE) == 0;
+  const int PV = xvec ? P / VE : 0;
+  const int totXV = n * PV, totBV = n * NV;
+  float2 dl = make_float2(0.f, 0.f);
+  if (tid < n) dl = a.ring_dl[(size_t)bh * R + ring_slot(head, tid, R)];
+  for (int q0 = 0; q0 < totBV; q0 += kFlushStage * kThreads) {
+    VT vb[kFlushStage];
+#pragma unroll
+    for (int m = 0; m < kFlushStage; ++m) {
+      const int q = q0 + m * kThreads + tid;
+      if (q < totBV) { const int j = q / NV; vb[m] = ldv<Tin>(brow(j) + (q - j * NV) * VE); }
+    }
+    VT vx[kFlushStage];
+    if (xvec && q0 < totXV) {
+#pragma unroll
+      for (int m = 0; m < kFlushStage; ++m) {
+        const int q = q0 + m * kThreads + tid;
+        if (q < totXV) { const int j = q / PV; vx[m] = ldv<Tin>(xrow(j) + (q - j * PV) * VE); }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kFlushStage; ++m) {
+      const int q = q0 + m * kThreads + tid;
+      if (q < totBV) st_lds_f32(sB + q * VE, vb[m]);
+    }
+    if (xvec && q0 < totXV) {
+#pragma unroll
+      for (int m = 0; m < kFlushStage; ++m) {
+        const int q = q0 + m * kThreads + tid;
+        if (q < totXV) st_lds_f32(sX + q * VE, vx[m]);
+      }
+    }
+  }
+  if (xvec) {  // x vectors beyond what the B rounds above covered
+    const int covered = (totBV + kFlushStage * kThreads - 1) / (kFlushStage * kThreads) *
+                        (kFlushStage * kThreads);
+    for (int q = covered + tid; q < totXV; q += kThreads) {
+      const int j = q / PV;
+      st_lds_f32(sX + q * VE, ldv<Tin>(xrow(j) + (q - j * PV) * VE));
+    }
+  } else {
+    for (int e = tid; e < n * P; e += kThreads) {
+      const int j = e / P;
+      sX[e] = to_f32(xrow(j)[e - j * P]);
+    }
+  }
+  if (wave == 0) {  // c_j = exp(sum_{j<m<n} l_m) dt_j and exp(Lam), tree-summed
+    const float u = lane < n ? dl.y : 0.f;
+    const float lam = wave_suffix_excl(u, lane);
+    if (lane < n) sCF[lane] = expf(lam) * dl.x;
+    if (lane == 0) sCF[R] = expf(lam + u);
   }
   __syncthreads();
-  if (tid < n) {
-    float lam = 0.f;
-    for (int m = n - 1; m > tid; --m) lam += sl[m];
-    sc[tid] = expf(lam) * sdt[tid];
-  }
-  if (tid == kThreads - 1) {
-    float lam = 0.f;
-    for (int m = n - 1; m >= 0; --m) lam += sl[m];
-    sD = expf(lam);
-  }
-  __syncthreads();
-  const float D = sD;
+  const float D = sCF[R];
 
+  // 3. S <- D S + sum_j (c_j x_j) outer B_j, in registers; write back.
   for (int base = 0; base < P; base += RPP * kMaxPass) {
     if (base > 0) load_chunk(base);
     float4 acc[kMaxPass];
@@ -96,39 +149,25 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
       acc[k].z = D * fr[k].v.z;
       acc[k].w = D * fr[k].v.w;
     }
-    for (int j0 = 0; j0 < n; j0 += EC) {
-      const int ne = min(EC, n - j0);
-      if (j0 > 0 || base > 0) __syncthreads();  // earlier readers of xs/Bs are done
-      for (int e = tid; e < ne * P; e += kThreads) {
-        const int jj = e / P, p = e - jj * P;
-        const int slot = ring_slot(head, j0 + jj, R);
-        xs[jj * P + p] = sc[j0 + jj] * to_f32(rx[((size_t)bh * R + slot) * P + p]);
-      }
-      for (int e = tid; e < ne * N; e += kThreads) {
-        const int jj = e / N, c = e - jj * N;
-        const int slot = ring_slot(head, j0 + jj, R);
-        Bs[jj * N + c] = to_f32(rB[(((size_t)b * G + g) * R + slot) * N + c]);
-      }
-      __syncthreads();
-      for (int jj = 0; jj < ne; ++jj) {
-        const float4 bv = *reinterpret_cast<const float4*>(&Bs[jj * N + col * 4]);
+    for (int j = 0; j < n; ++j) {
+      const float cj = sCF[j];
+      const float4 bv = *reinterpret_cast<const float4*>(&sB[j * N + col * 4]);
 #pragma unroll
-        for (int k = 0; k < kMaxPass; ++k) {
-          if (base + k * RPP >= P) break;
-          const int row = base + k * RPP + rsub;
-          const float xv = row < P ? xs[jj * P + row] : 0.f;
-          acc[k].x = fmaf(xv, bv.x, acc[k].x);
-          acc[k].y = fmaf(xv, bv.y, acc[k].y);
-          acc[k].z = fmaf(xv, bv.z, acc[k].z);
-          acc[k].w = fmaf(xv, bv.w, acc[k].w);
-        }
+      for (int k = 0; k < kMaxPass; ++k) {
+        if (base + k * RPP >= P) break;
+        const int row = base + k * RPP + rsub;
+        const float xv = row < P ? cj * sX[j * P + row] : 0.f;
+        acc[k].x = fmaf(xv, bv.x, acc[k].x);
+        acc[k].y = fmaf(xv, bv.y, acc[k].y);
+        acc[k].z = fmaf(xv, bv.z, acc[k].z);
+        acc[k].w = fmaf(xv, bv.w, acc[k].w);
       }
     }
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
       const int row = base + k * RPP + rsub;
       if (row < P) {
-        *reinterpret_cast<float4*>(tile + (size_t)row * N + col * 4) = acc[k];
+        st16(tile + (size_t)row * N + col * 4, acc[k]);
         if (DUAL) {
           bf16_t* lo = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N + (size_t)row * N + col * 4;
           uint2 pk;
@@ -142,18 +181,23 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   if (tid == 0) a.ptr[bh] = make_int4(ring_slot(head, n, R), 0, 0, 0);
 }
 
-template <int N, typename Tin>
-static hipError_t flush_dual(const FlushArgs& a, int batch, bool low, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)batch * a.H)), block(kThreads);
-  const size_t lds = (size_t)kFlushChunk * (a.P + N) * sizeof(float);
-  if (low) hipLaunchKernelGGL((flush_kernel<N, Tin, true>), grid, block, lds, s, a);
-  else hipLaunchKernelGGL((flush_kernel<N, Tin, false>), grid, block, lds, s, a);
+template <int N, typename Tin, bool DUAL>
+static hipError_t flush_one(const FlushArgs& a, int batch, hipStream_t s) {
+  const size_t lds = (size_t)FlushLds(a.R, a.P, N).total * sizeof(float);
+  auto kern = flush_kernel<N, Tin, DUAL>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)batch * a.H)), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 template <int N>
 static hipError_t flush_n(const FlushArgs& a, int batch, bool bf16_in, bool low, hipStream_t s) {
-  return bf16_in ? flush_dual<N, bf16_t>(a, batch, low, s) : flush_dual<N, float>(a, batch, low, s);
+  if (bf16_in) return low ? flush_one<N, bf16_t, true>(a, batch, s) : flush_one<N, bf16_t, false>(a, batch, s);
+  return low ? flush_one<N, float, true>(a, batch, s) : flush_one<N, float, false>(a, batch, s);
 }
 
 hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, bool low_copy,

@@ -12,14 +12,19 @@
 // from checkpoint and buffer without writing a new state). Nothing of size
 // P x N is written.
 //
-// One workgroup per (sequence, head):
-//   1. issue the 16-byte loads of the checkpoint tile (the only large read);
-//   2. while they fly: C_i into LDS, the window's (dt, l) pairs, the dot
-//      products B_j . C_i (one wavefront per entry), the coefficients
-//      exp(lam) dt (B.C) and the sums sum_j w_ij x_j, all in LDS; append the
-//      new tokens to the ring;
-//   3. consume the tile: per row a 16-byte fragment dot C_i, a butterfly over
-//      the lanes of the row, and y = exp(Lam) * dot + ring part.
+// One workgroup per (sequence, head). Every global load is issued in the first
+// two memory round trips (the pointer word, then everything else), so a
+// workgroup lives about two latencies whatever the window length:
+//   1. read the (head, len) pointer word; issue the 16-byte non-temporal loads
+//      of the checkpoint tile (the only large read);
+//   2. issue, all at once, the window's x and B rows, the new tokens' C and the
+//      window's (dt, l) pairs; then unpack them into LDS as fp32, and scan the
+//      log-decays in one wavefront (a reverse tree sum: no prefix differences);
+//   3. per (i, j) pair, one wavefront: w_ij = exp(lam) dt (B_j . C_i), and the
+//      wavefront's share of sum_j w_ij x_j (wavefront w takes j = w mod 4);
+//   4. consume the tile: per row a 16-byte fragment dot C_i, a butterfly over
+//      the lanes sharing the row, y = exp(Lam) * dot + the four ring shares.
+// The new tokens' x and B go to the ring straight from the staging registers.
 // The checkpoint tile is read exactly once per call for all nt outputs.
 #include <type_traits>
 
@@ -28,20 +33,37 @@
 
 namespace rss {
 
+// Dynamic LDS layout of the replay kernel, in floats.
+struct ReplayLds {
+  int oX, oB, oC, oCF, oDC, oRing, total;
+  __host__ __device__ ReplayLds(int R, int P, int N, int ntmax) {
+    oX = 0;                          // window x rows    [R][P]
+    oB = align4(R * P);              // window B rows    [R][N]
+    oC = oB + R * N;                 // new tokens' C    [ntmax][N]
+    oCF = oC + ntmax * N;            // exp(lam) * dt    [ntmax][R]
+    oDC = oCF + ntmax * R;           // exp(Lam)         [ntmax]
+    oRing = align4(oDC + ntmax);     // ring part, one share per wavefront [4][ntmax][P]
+    total = oRing + 4 * ntmax * P;
+  }
+};
+
+constexpr int kStageS = 4;  // scalar loads per thread and round (x rows when P % VE != 0)
+
 template <int N, typename Tin, bool LOW, int NTMAX>
 __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   using Geo = TileGeom<N, LOW>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, RPP = Geo::RPP;
-  constexpr int EPL = N >= 64 ? N / 64 : 1;
+  constexpr int VE = V16<Tin>::VE;
+  constexpr int NV = N / VE;                                   // vectors per B or C row
+  constexpr int kStageC = (NTMAX * NV + kThreads - 1) / kThreads;
+  // 16-byte loads per thread per staging round. One round holds a 16-entry
+  // window of x and B at P = 64, N = 128 in bf16; longer windows take more rounds.
+  constexpr int kStageX = NTMAX == 1 ? 1 : 2;
+  constexpr int kStageB = NTMAX == 1 ? 1 : 2;
   using TileT = typename std::conditional<LOW, bf16_t, float>::type;
+  using VT = typename V16<Tin>::T;
 
-  __shared__ __align__(16) float sC[NTMAX][N];
-  __shared__ float sl[kMaxRing];
-  __shared__ float sdt[kMaxRing];
-  __shared__ float sdot[NTMAX][kMaxRing];
-  __shared__ float sw[NTMAX][kMaxRing];
-  __shared__ float sdc[NTMAX];
-  __shared__ float sring[NTMAX][kMaxP];
+  extern __shared__ __align__(16) float lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -63,11 +85,27 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     return;
   }
 
+  const ReplayLds lay(R, P, N, NTMAX);
+  float* sX = lds + lay.oX;
+  float* sB = lds + lay.oB;
+  float* sC = lds + lay.oC;
+  float* sCF = lds + lay.oCF;
+  float* sDC = lds + lay.oDC;
+  float* sRing = lds + lay.oRing;
+
   const Tin* xin = static_cast<const Tin*>(a.x);
   const Tin* Bin = static_cast<const Tin*>(a.B);
   const Tin* Cin = static_cast<const Tin*>(a.C);
   Tin* rx = static_cast<Tin*>(a.ring_x);
   Tin* rB = static_cast<Tin*>(a.ring_B);
+  auto xrow = [&](int j) -> const Tin* {
+    return j < n0 ? rx + ((size_t)bh * R + ring_slot(head, j, R)) * P
+                  : xin + ((size_t)(b * nt + (j - n0)) * H + h) * P;
+  };
+  auto brow = [&](int j) -> const Tin* {
+    return j < n0 ? rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N
+                  : Bin + ((size_t)(b * nt + (j - n0)) * G + g) * N;
+  };
 
   // 1. Checkpoint tile: first chunk of rows into registers.
   const int col = tid % TPR, rsub = tid / TPR;
@@ -84,14 +122,50 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   };
   load_chunk(0);
 
-  // 2a. C of the new tokens, and (dt, l) of every window entry.
-  const float Ah = a.A[h];
-  for (int e = tid; e < nt * N; e += kThreads) {
-    const int i = e / N, n = e - i * N;
-    sC[i][n] = to_f32(Cin[((size_t)(b * nt + i) * G + g) * N + n]);
+  // 2. Everything else in one round of loads, then unpack into LDS.
+  const bool xvec = (P % VE) == 0;
+  const int PV = xvec ? P / VE : 0;
+  const int totXV = L * PV, totBV = L * NV, totCV = nt * NV;
+  VT vx[kStageX], vb[kStageB], vc[kStageC];
+  Tin sxs[kStageS];
+#pragma unroll
+  for (int m = 0; m < kStageB; ++m) {
+    const int q = m * kThreads + tid;
+    if (q < totBV) {
+      const int j = q / NV, c = q - j * NV;
+      vb[m] = ldv<Tin>(brow(j) + c * VE);
+    }
   }
-  if (tid < L) {
-    float dtj, lj;
+#pragma unroll
+  for (int m = 0; m < kStageC; ++m) {
+    const int q = m * kThreads + tid;
+    if (q < totCV) {
+      const int i = q / NV, c = q - i * NV;
+      vc[m] = ldv<Tin>(Cin + ((size_t)(b * nt + i) * G + g) * N + c * VE);
+    }
+  }
+  if (xvec) {
+#pragma unroll
+    for (int m = 0; m < kStageX; ++m) {
+      const int q = m * kThreads + tid;
+      if (q < totXV) {
+        const int j = q / PV, c = q - j * PV;
+        vx[m] = ldv<Tin>(xrow(j) + c * VE);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < kStageS; ++m) {
+      const int e = m * kThreads + tid;
+      if (e < L * P) {
+        const int j = e / P;
+        sxs[m] = xrow(j)[e - j * P];
+      }
+    }
+  }
+  const float Ah = a.A[h];
+  float dtj = 0.f, lj = 0.f;
+  if (tid < L) {  // wavefront 0: lane j holds window entry j's (dt, l)
     if (tid < n0) {
       const float2 v = a.ring_dl[(size_t)bh * R + ring_slot(head, tid, R)];
       dtj = v.x;
@@ -100,82 +174,143 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
       dtj = a.dt[(size_t)(b * nt + (tid - n0)) * H + h];
       lj = dtj * Ah;
     }
-    sdt[tid] = dtj;
-    sl[tid] = lj;
   }
-  __syncthreads();
 
-  // 2b. B_j . C_i, one wavefront per window entry.
-  for (int j = wave; j < L; j += kWaves) {
-    const Tin* Bj = j < n0 ? rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N
-                           : Bin + ((size_t)(b * nt + (j - n0)) * G + g) * N;
-    float bv[EPL];
+  const bool keepB = h == g * hpg;  // the group's first head keeps the group's B
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int n = lane * EPL + e;
-      bv[e] = n < N ? to_f32(Bj[n]) : 0.f;
+  for (int m = 0; m < kStageB; ++m) {
+    const int q = m * kThreads + tid;
+    if (q < totBV) {
+      st_lds_f32(sB + q * VE, vb[m]);
+      const int j = q / NV;
+      if (keepB && j >= n0)
+        *reinterpret_cast<VT*>(rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N +
+                               (q - j * NV) * VE) = vb[m];
     }
+  }
+#pragma unroll
+  for (int m = 0; m < kStageC; ++m) {
+    const int q = m * kThreads + tid;
+    if (q < totCV) st_lds_f32(sC + q * VE, vc[m]);
+  }
+  if (xvec) {
+#pragma unroll
+    for (int m = 0; m < kStageX; ++m) {
+      const int q = m * kThreads + tid;
+      if (q < totXV) {
+        st_lds_f32(sX + q * VE, vx[m]);
+        const int j = q / PV;
+        if (j >= n0)
+          *reinterpret_cast<VT*>(rx + ((size_t)bh * R + ring_slot(head, j, R)) * P +
+                                 (q - j * PV) * VE) = vx[m];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < kStageS; ++m) {
+      const int e = m * kThreads + tid;
+      if (e < L * P) {
+        sX[e] = to_f32(sxs[m]);
+        const int j = e / P;
+        if (j >= n0) rx[((size_t)bh * R + ring_slot(head, j, R)) * P + (e - j * P)] = sxs[m];
+      }
+    }
+  }
+  // Long windows (rare): further staging rounds, loads then stores.
+  for (int q0 = kStageB * kThreads; q0 < totBV; q0 += kStageB * kThreads) {
+#pragma unroll
+    for (int m = 0; m < kStageB; ++m) {
+      const int q = q0 + m * kThreads + tid;
+      if (q < totBV) { const int j = q / NV; vb[m] = ldv<Tin>(brow(j) + (q - j * NV) * VE); }
+    }
+#pragma unroll
+    for (int m = 0; m < kStageB; ++m) {
+      const int q = q0 + m * kThreads + tid;
+      if (q < totBV) {
+        st_lds_f32(sB + q * VE, vb[m]);
+        const int j = q / NV;
+        if (keepB && j >= n0)
+          *reinterpret_cast<VT*>(rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N +
+                                 (q - j * NV) * VE) = vb[m];
+      }
+    }
+  }
+  if (xvec) {
+    for (int q0 = kStageX * kThreads; q0 < totXV; q0 += kStageX * kThreads) {
+#pragma unroll
+      for (int m = 0; m < kStageX; ++m) {
+        const int q = q0 + m * kThreads + tid;
+        if (q < totXV) { const int j = q / PV; vx[m] = ldv<Tin>(xrow(j) + (q - j * PV) * VE); }
+      }
+#pragma unroll
+      for (int m = 0; m < kStageX; ++m) {
+        const int q = q0 + m * kThreads + tid;
+        if (q < totXV) {
+          st_lds_f32(sX + q * VE, vx[m]);
+          const int j = q / PV;
+          if (j >= n0)
+            *reinterpret_cast<VT*>(rx + ((size_t)bh * R + ring_slot(head, j, R)) * P +
+                                   (q - j * PV) * VE) = vx[m];
+        }
+      }
+    }
+  } else {
+    for (int e0 = kStageS * kThreads; e0 < L * P; e0 += kStageS * kThreads) {
+#pragma unroll
+      for (int m = 0; m < kStageS; ++m) {
+        const int e = e0 + m * kThreads + tid;
+        if (e < L * P) { const int j = e / P; sxs[m] = xrow(j)[e - j * P]; }
+      }
+#pragma unroll
+      for (int m = 0; m < kStageS; ++m) {
+        const int e = e0 + m * kThreads + tid;
+        if (e < L * P) {
+          sX[e] = to_f32(sxs[m]);
+          const int j = e / P;
+          if (j >= n0) rx[((size_t)bh * R + ring_slot(head, j, R)) * P + (e - j * P)] = sxs[m];
+        }
+      }
+    }
+  }
+
+  // Log-decay scan in wavefront 0: lam_i(j) = sum_{j < m <= t_i} l_m, tree-summed.
+  if (wave == 0) {
 #pragma unroll
     for (int i = 0; i < NTMAX; ++i) {
       if (i >= nt) break;
+      const int ti = n0 + i;
+      const float u = lane <= ti ? lj : 0.f;
+      const float lam = wave_suffix_excl(u, lane);
+      if (lane < L) sCF[i * R + lane] = lane <= ti ? expf(lam) * dtj : 0.f;
+      if (lane == 0) sDC[i] = expf(lam + u);
+    }
+    if (lane >= n0 && lane < L)  // the new tokens' (dt, l) into the ring
+      a.ring_dl[(size_t)bh * R + ring_slot(head, lane, R)] = make_float2(dtj, lj);
+  }
+  __syncthreads();
+
+  // 3. Wavefront w takes the window entries j = w (mod 4) of every output i:
+  // w_ij = coef_ij (B_j . C_i), and its share of sum_j w_ij x_j, row p on lane p mod 64.
+  constexpr int kRowsPerLane = kMaxP / 64;
+  for (int i = 0; i < nt; ++i) {
+    const int ti = n0 + i;
+    float share[kRowsPerLane] = {};
+    for (int j = wave; j <= ti; j += kWaves) {
       float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int n = lane * EPL + e;
-        if (n < N) part = fmaf(bv[e], sC[i][n], part);
-      }
-      part = wave_sum(part);
-      if (lane == 0) sdot[i][j] = part;
+      for (int n = lane; n < N; n += 64) part = fmaf(sB[j * N + n], sC[i * N + n], part);
+      const float w = sCF[i * R + j] * wave_sum(part);
+#pragma unroll
+      for (int r = 0; r < kRowsPerLane; ++r)
+        if (r * 64 + lane < P) share[r] = fmaf(w, sX[j * P + r * 64 + lane], share[r]);
     }
+#pragma unroll
+    for (int r = 0; r < kRowsPerLane; ++r)
+      if (r * 64 + lane < P) sRing[(wave * NTMAX + i) * P + r * 64 + lane] = share[r];
   }
   __syncthreads();
 
-  // 2c. Coefficients w_ij = exp(lam_i(j)) dt_j (B_j.C_i) and exp(Lam_i), with
-  // the log-decays summed from the newest entry backwards.
-  for (int e = tid; e < nt * L; e += kThreads) {
-    const int i = e / L, j = e - i * L;
-    const int ti = n0 + i;
-    float w = 0.f;
-    if (j <= ti) {
-      float lam = 0.f;
-      for (int m = ti; m > j; --m) lam += sl[m];
-      w = expf(lam) * sdt[j] * sdot[i][j];
-    }
-    sw[i][j] = w;
-  }
-  if (tid >= kThreads - NTMAX && tid - (kThreads - NTMAX) < nt) {
-    const int i = tid - (kThreads - NTMAX);
-    float lam = 0.f;
-    for (int m = n0 + i; m >= 0; --m) lam += sl[m];
-    sdc[i] = expf(lam);
-  }
-  __syncthreads();
-
-  // 2d. Ring part sum_j w_ij x_j[p]; append the new tokens to the ring.
-  for (int e = tid; e < nt * P; e += kThreads) {
-    const int i = e / P, p = e - i * P;
-    const int ti = n0 + i;
-    float acc = 0.f;
-    for (int j = 0; j <= ti; ++j) {
-      const float xv = j < n0 ? to_f32(rx[((size_t)bh * R + ring_slot(head, j, R)) * P + p])
-                              : to_f32(xin[((size_t)(b * nt + (j - n0)) * H + h) * P + p]);
-      acc = fmaf(sw[i][j], xv, acc);
-    }
-    sring[i][p] = acc;
-    rx[((size_t)bh * R + ring_slot(head, ti, R)) * P + p] = xin[((size_t)(b * nt + i) * H + h) * P + p];
-  }
-  if (h == g * hpg) {  // the group's first head keeps the group's B
-    for (int e = tid; e < nt * N; e += kThreads) {
-      const int i = e / N, n = e - i * N;
-      rB[(((size_t)b * G + g) * R + ring_slot(head, n0 + i, R)) * N + n] =
-          Bin[((size_t)(b * nt + i) * G + g) * N + n];
-    }
-  }
-  if (tid < nt)
-    a.ring_dl[(size_t)bh * R + ring_slot(head, n0 + tid, R)] = make_float2(sdt[n0 + tid], sl[n0 + tid]);
-  __syncthreads();
-
-  // 3. Consume the tile.
+  // 4. Consume the tile.
   for (int base = 0; base < P; base += RPP * kMaxPass) {
     if (base > 0) load_chunk(base);
 #pragma unroll
@@ -187,10 +322,13 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
         if (i >= nt) break;
         float part = 0.f;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) part = fmaf(fr[k].get(v), sC[i][col * VEC + v], part);
+        for (int v = 0; v < VEC; ++v) part = fmaf(fr[k].get(v), sC[i * N + col * VEC + v], part);
         part = row_sum<TPR>(part);
-        if (col == 0 && row < P)
-          a.y[((size_t)(b * nt + i) * H + h) * P + row] = fmaf(sdc[i], part, sring[i][row]);
+        if (col == 0 && row < P) {
+          const float ring = (sRing[i * P + row] + sRing[(NTMAX + i) * P + row]) +
+                             (sRing[(2 * NTMAX + i) * P + row] + sRing[(3 * NTMAX + i) * P + row]);
+          a.y[((size_t)(b * nt + i) * H + h) * P + row] = fmaf(sDC[i], part, ring);
+        }
       }
     }
   }
@@ -198,14 +336,23 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   if (tid == 0) a.ptr[bh] = make_int4(head, L, a.set_tent ? nt : pt.z, 0);
 }
 
+template <int N, typename Tin, bool LOW, int NTMAX>
+static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
+  const size_t lds = (size_t)ReplayLds(a.R, a.P, N, NTMAX).total * sizeof(float);
+  auto kern = replay_kernel<N, Tin, LOW, NTMAX>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)batch * a.H)), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int N, typename Tin, bool LOW>
 static hipError_t launch_nt(const ReplayArgs& a, int batch, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)batch * a.H)), block(kThreads);
-  if (a.nt == 1)
-    hipLaunchKernelGGL((replay_kernel<N, Tin, LOW, 1>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((replay_kernel<N, Tin, LOW, kMaxNew>), grid, block, 0, s, a);
-  return hipGetLastError();
+  return a.nt == 1 ? launch_one<N, Tin, LOW, 1>(a, batch, s)
+                   : launch_one<N, Tin, LOW, kMaxNew>(a, batch, s);
 }
 
 template <int N>
