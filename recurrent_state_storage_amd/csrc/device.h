@@ -50,19 +50,81 @@ struct TileGeom {
   static_assert((TPR & (TPR - 1)) == 0, "N/VEC must be a power of two");
 };
 
-// Sum over the TPR consecutive lanes that share a row (fixed butterfly order).
-template <int TPR>
-__device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+// ---- cross-lane exchanges ----------------------------------------------------
+// xchg<BIT>(v) returns v of a partner lane whose id has the opposite bit BIT and
+// the same higher bits: lane ^ 1 and lane ^ 2 (DPP quad permutes), lane ^ 7
+// (DPP half-row mirror), lane ^ 8 (DPP row rotate by 8), lane ^ 16 (LDS-free
+// ds_swizzle bit mode) and lane ^ 32 (ds_bpermute). The DPP forms are folded
+// into the consuming add, so a butterfly step costs one VALU instruction.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <int BIT> __device__ __forceinline__ float xchg(float v);
+template <> __device__ __forceinline__ float xchg<0>(float v) { return dpp_f<0xB1>(v); }
+template <> __device__ __forceinline__ float xchg<1>(float v) { return dpp_f<0x4E>(v); }
+template <> __device__ __forceinline__ float xchg<2>(float v) { return dpp_f<0x141>(v); }
+template <> __device__ __forceinline__ float xchg<3>(float v) { return dpp_f<0x128>(v); }
+template <> __device__ __forceinline__ float xchg<4>(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+template <> __device__ __forceinline__ float xchg<5>(float v) { return __shfl_xor(v, 32, 64); }
+
+// Butterfly sum over the 2^NBITS lanes that agree in every bit >= NBITS, low
+// bit first (with bits 0 and 1 already summed, the lane ^ 7 partner of bit 2
+// holds the same value as lane ^ 4). Fixed order, so results are deterministic.
+template <int NBITS>
+__device__ __forceinline__ float lanes_sum(float v) {
+  if constexpr (NBITS > 0) {
+    v = lanes_sum<NBITS - 1>(v);
+    v += xchg<NBITS - 1>(v);
+  }
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+template <int X> struct Log2 { static constexpr int v = 1 + Log2<X / 2>::v; };
+template <> struct Log2<1> { static constexpr int v = 0; };
+
+// Sum over the TPR consecutive lanes that share a row.
+template <int TPR>
+__device__ __forceinline__ float row_sum(float v) { return lanes_sum<Log2<TPR>::v>(v); }
+
+__device__ __forceinline__ float wave_sum(float v) { return lanes_sum<6>(v); }
+
+// Reduce-scatter of the 8 tile passes over a row group of TPR = 2^T lanes.
+// On entry a[k] is this lane's partial dot for the row of pass k. Each step
+// halves the values a lane keeps (by one lane-id bit, highest first) and adds
+// the partner's copy of the half it keeps; after min(T, 3) steps the remaining
+// low bits are summed by butterfly. On return a[0 .. NOUT-1], NOUT = 8 >> min(T,3),
+// are complete row sums for passes kbase .. kbase + NOUT - 1; the lanes whose
+// low T - min(T, 3) bits are zero own distinct rows and write them.
+template <int BIT, int NV>
+__device__ __forceinline__ void rs_step(float* a, int lr, int& kbase) {
+  constexpr int H = NV / 2;
+  const bool hi = (lr >> BIT) & 1;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  for (int m = 0; m < H; ++m) {
+    const float send = hi ? a[m] : a[m + H];
+    const float keep = hi ? a[m + H] : a[m];
+    a[m] = keep + xchg<BIT>(send);
+  }
+  if (hi) kbase += H;
 }
+
+template <int TPR>
+struct RowScatter {
+  static constexpr int T = Log2<TPR>::v;
+  static constexpr int S = T < 3 ? T : 3;
+  static constexpr int NOUT = 8 >> S;
+  static constexpr int WMASK = (1 << (T - S)) - 1;   // writer lanes: (lr & WMASK) == 0
+  __device__ static __forceinline__ void run(float (&a)[8], int lr, int& kbase) {
+    kbase = 0;
+    if constexpr (T >= 1) rs_step<T - 1, 8>(a, lr, kbase);
+    if constexpr (T >= 2) rs_step<T - 2, 4>(a, lr, kbase);
+    if constexpr (T >= 3) rs_step<T - 3, 2>(a, lr, kbase);
+    if constexpr (T > 3) a[0] = lanes_sum<T - 3>(a[0]);
+  }
+};
 
 // 16-byte tile fragment: 4 fp32 or 8 bf16 values.
 template <bool LOW> struct Frag;

@@ -25,6 +25,8 @@ struct ReplayArgs {
   const float* dt;         // [Bt,nt,H]
   float* y;                // [Bt,nt,H,P]
   int H, P, G, R, nt, set_tent;
+  uint64_t xdiv;           // ceil(2^32 / d): q / d == (q * xdiv) >> 32 for q < 2^16,
+                           // d = P/VE (16-byte x vectors per row) or P (element path)
 };
 hipError_t launch_replay(const ReplayArgs& a, int batch, int N, bool bf16_in, bool low_copy,
                          hipStream_t s);

@@ -115,8 +115,9 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   auto load_chunk = [&](int base) {
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
-      const int row = base + k * RPP + rsub;
-      if (row < P) fr[k].v = ld16(tile + (size_t)row * N + col * VEC);
+      const int r0 = base + k * RPP;
+      if (r0 + RPP <= P) fr[k].v = ld16(tile + (size_t)(r0 + rsub) * N + col * VEC);  // whole pass
+      else if (r0 + rsub < P) fr[k].v = ld16(tile + (size_t)(r0 + rsub) * N + col * VEC);
       else fr[k].v = decltype(fr[k].v){};
     }
   };
@@ -125,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   // 2. Everything else in one round of loads, then unpack into LDS.
   const bool xvec = (P % VE) == 0;
   const int PV = xvec ? P / VE : 0;
+  auto xdiv = [&](int q) { return (int)(((uint64_t)(uint32_t)q * a.xdiv) >> 32); };
   const int totXV = L * PV, totBV = L * NV, totCV = nt * NV;
   VT vx[kStageX], vb[kStageB], vc[kStageC];
   Tin sxs[kStageS];
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     for (int m = 0; m < kStageX; ++m) {
       const int q = m * kThreads + tid;
       if (q < totXV) {
-        const int j = q / PV, c = q - j * PV;
+        const int j = xdiv(q), c = q - j * PV;
         vx[m] = ldv<Tin>(xrow(j) + c * VE);
       }
     }
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     for (int m = 0; m < kStageS; ++m) {
       const int e = m * kThreads + tid;
       if (e < L * P) {
-        const int j = e / P;
+        const int j = xdiv(e);
         sxs[m] = xrow(j)[e - j * P];
       }
     }
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
       const int q = m * kThreads + tid;
       if (q < totXV) {
         st_lds_f32(sX + q * VE, vx[m]);
-        const int j = q / PV;
+        const int j = xdiv(q);
         if (j >= n0)
           *reinterpret_cast<VT*>(rx + ((size_t)bh * R + ring_slot(head, j, R)) * P +
                                  (q - j * PV) * VE) = vx[m];
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
       const int e = m * kThreads + tid;
       if (e < L * P) {
         sX[e] = to_f32(sxs[m]);
-        const int j = e / P;
+        const int j = xdiv(e);
         if (j >= n0) rx[((size_t)bh * R + ring_slot(head, j, R)) * P + (e - j * P)] = sxs[m];
       }
     }
@@ -240,14 +242,14 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
 #pragma unroll
       for (int m = 0; m < kStageX; ++m) {
         const int q = q0 + m * kThreads + tid;
-        if (q < totXV) { const int j = q / PV; vx[m] = ldv<Tin>(xrow(j) + (q - j * PV) * VE); }
+        if (q < totXV) { const int j = xdiv(q); vx[m] = ldv<Tin>(xrow(j) + (q - j * PV) * VE); }
       }
 #pragma unroll
       for (int m = 0; m < kStageX; ++m) {
         const int q = q0 + m * kThreads + tid;
         if (q < totXV) {
           st_lds_f32(sX + q * VE, vx[m]);
-          const int j = q / PV;
+          const int j = xdiv(q);
           if (j >= n0)
             *reinterpret_cast<VT*>(rx + ((size_t)bh * R + ring_slot(head, j, R)) * P +
                                    (q - j * PV) * VE) = vx[m];
@@ -259,14 +261,14 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
 #pragma unroll
       for (int m = 0; m < kStageS; ++m) {
         const int e = e0 + m * kThreads + tid;
-        if (e < L * P) { const int j = e / P; sxs[m] = xrow(j)[e - j * P]; }
+        if (e < L * P) { const int j = xdiv(e); sxs[m] = xrow(j)[e - j * P]; }
       }
 #pragma unroll
       for (int m = 0; m < kStageS; ++m) {
         const int e = e0 + m * kThreads + tid;
         if (e < L * P) {
           sX[e] = to_f32(sxs[m]);
-          const int j = e / P;
+          const int j = xdiv(e);
           if (j >= n0) rx[((size_t)bh * R + ring_slot(head, j, R)) * P + (e - j * P)] = sxs[m];
         }
       }
@@ -310,24 +312,36 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   }
   __syncthreads();
 
-  // 4. Consume the tile.
+  // 4. Consume the tile: per pass a 16-byte fragment dot C_i, reduce-scattered
+  // over the row's lanes so that each writer lane finishes one row.
+  using RS = RowScatter<TPR>;
   for (int base = 0; base < P; base += RPP * kMaxPass) {
     if (base > 0) load_chunk(base);
 #pragma unroll
-    for (int k = 0; k < kMaxPass; ++k) {
-      if (base + k * RPP >= P) break;
-      const int row = base + k * RPP + rsub;
+    for (int i = 0; i < NTMAX; ++i) {
+      if (i >= nt) break;
+      float cv[VEC];
 #pragma unroll
-      for (int i = 0; i < NTMAX; ++i) {
-        if (i >= nt) break;
-        float part = 0.f;
+      for (int v = 0; v < VEC; ++v) cv[v] = sC[i * N + col * VEC + v];
+      float part[kMaxPass];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) part = fmaf(fr[k].get(v), sC[i * N + col * VEC + v], part);
-        part = row_sum<TPR>(part);
-        if (col == 0 && row < P) {
-          const float ring = (sRing[i * P + row] + sRing[(NTMAX + i) * P + row]) +
-                             (sRing[(2 * NTMAX + i) * P + row] + sRing[(3 * NTMAX + i) * P + row]);
-          a.y[((size_t)(b * nt + i) * H + h) * P + row] = fmaf(sDC[i], part, ring);
+      for (int k = 0; k < kMaxPass; ++k) {
+        float acc = 0.f;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc = fmaf(fr[k].get(v), cv[v], acc);
+        part[k] = acc;
+      }
+      int kbase;
+      RS::run(part, col, kbase);
+      if ((col & RS::WMASK) == 0) {
+#pragma unroll
+        for (int m = 0; m < RS::NOUT; ++m) {
+          const int row = base + (kbase + m) * RPP + rsub;
+          if (row < P) {
+            const float ring = (sRing[i * P + row] + sRing[(NTMAX + i) * P + row]) +
+                               (sRing[(2 * NTMAX + i) * P + row] + sRing[(3 * NTMAX + i) * P + row]);
+            a.y[((size_t)(b * nt + i) * H + h) * P + row] = fmaf(sDC[i], part[m], ring);
+          }
         }
       }
     }

@@ -155,6 +155,9 @@ static int32_t replay_call(rss_layer* l, int nt, int set_tent, const void* x, co
   a.R = c.capacity;
   a.nt = nt;
   a.set_tent = set_tent;
+  const int ve = c.in_dtype == RSS_DTYPE_BF16 ? 8 : 4;  // elements per 16-byte vector
+  const uint64_t d = c.headdim % ve == 0 ? (uint64_t)(c.headdim / ve) : (uint64_t)c.headdim;
+  a.xdiv = ((1ull << 32) + d - 1) / d;
   return launch_status(rss::launch_replay(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
                                           c.read_copy == RSS_COPY_BF16,
                                           static_cast<hipStream_t>(stream)));
