@@ -19,14 +19,17 @@
 
 namespace rss {
 
-constexpr int kFlushStage = 2;  // 16-byte loads per thread per staging round and array
+constexpr int kFlushStage = 2;  // 16-byte B loads per thread per staging round
 
-// Dynamic LDS layout of the flush kernel, in floats.
+// Dynamic LDS layout of the flush kernel, in floats. x is stored transposed
+// (row p holds entries j = 0..R-1 contiguously, padded to a multiple of 4) so
+// that one 16-byte read gives a row's x for four consecutive entries.
 struct FlushLds {
-  int oX, oB, oCF, total;
+  int RS, oXT, oB, oCF, total;
   __host__ __device__ FlushLds(int R, int P, int N) {
-    oX = 0;                  // window x rows [R][P]
-    oB = align4(R * P);      // window B rows [R][N]
+    RS = align4(R);
+    oXT = 0;                 // x transposed  [P][RS]
+    oB = P * RS;             // window B rows [R][N]
     oCF = oB + R * N;        // c_j = exp(lam_j) dt_j [R], then exp(Lam)
     total = oCF + R + 1;
   }
@@ -60,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     return;
   }
   const FlushLds lay(R, P, N);
-  float* sX = lds + lay.oX;
+  const int RS = lay.RS;
+  float* sXT = lds + lay.oXT;
   float* sB = lds + lay.oB;
   float* sCF = lds + lay.oCF;
   const Tin* rx = static_cast<const Tin*>(a.ring_x);
@@ -75,19 +79,18 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   auto load_chunk = [&](int base) {
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
-      const int row = base + k * RPP + rsub;
-      if (row < P) fr[k].v = ld16(tile + (size_t)row * N + col * 4);
+      const int r0 = base + k * RPP;
+      if (r0 + RPP <= P) fr[k].v = ld16(tile + (size_t)(r0 + rsub) * N + col * 4);
+      else if (r0 + rsub < P) fr[k].v = ld16(tile + (size_t)(r0 + rsub) * N + col * 4);
       else fr[k].v = float4{};
     }
   };
   load_chunk(0);
 
-  // 2. Window rows and (dt, l) in one round of loads, unpacked into LDS.
-  const bool xvec = (P % VE) == 0;
-  const int PV = xvec ? P / VE : 0;
-  const int totXV = n * PV, totBV = n * NV;
+  // 2. Window B rows, x (transposed) and (dt, l), unpacked into LDS.
   float2 dl = make_float2(0.f, 0.f);
   if (tid < n) dl = a.ring_dl[(size_t)bh * R + ring_slot(head, tid, R)];
+  const int totBV = n * NV;
   for (int q0 = 0; q0 < totBV; q0 += kFlushStage * kThreads) {
     VT vb[kFlushStage];
 #pragma unroll
@@ -95,39 +98,36 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
       const int q = q0 + m * kThreads + tid;
       if (q < totBV) { const int j = q / NV; vb[m] = ldv<Tin>(brow(j) + (q - j * NV) * VE); }
     }
-    VT vx[kFlushStage];
-    if (xvec && q0 < totXV) {
-#pragma unroll
-      for (int m = 0; m < kFlushStage; ++m) {
-        const int q = q0 + m * kThreads + tid;
-        if (q < totXV) { const int j = q / PV; vx[m] = ldv<Tin>(xrow(j) + (q - j * PV) * VE); }
-      }
-    }
 #pragma unroll
     for (int m = 0; m < kFlushStage; ++m) {
       const int q = q0 + m * kThreads + tid;
       if (q < totBV) st_lds_f32(sB + q * VE, vb[m]);
     }
-    if (xvec && q0 < totXV) {
+  }
+  // x: thread -> (entry j = tid mod JP, column block tid / JP), JP = 2^ceil(log2 n),
+  // so consecutive lanes write consecutive entries of a transposed row.
+  const int lgJP = n > 1 ? 32 - __clz(n - 1) : 0;
+  const int JP = 1 << lgJP;
+  const int jx = tid & (JP - 1);
+  if ((P % VE) == 0) {
+    const int PV = P / VE;
+    for (int c = tid >> lgJP; c < PV; c += kThreads >> lgJP) {
+      if (jx < n) {
+        float xv[VE];
+        const VT v = ldv<Tin>(xrow(jx) + c * VE);
+        st_lds_f32(xv, v);
 #pragma unroll
-      for (int m = 0; m < kFlushStage; ++m) {
-        const int q = q0 + m * kThreads + tid;
-        if (q < totXV) st_lds_f32(sX + q * VE, vx[m]);
+        for (int e = 0; e < VE; ++e) sXT[(c * VE + e) * RS + jx] = xv[e];
       }
     }
-  }
-  if (xvec) {  // x vectors beyond what the B rounds above covered
-    const int covered = (totBV + kFlushStage * kThreads - 1) / (kFlushStage * kThreads) *
-                        (kFlushStage * kThreads);
-    for (int q = covered + tid; q < totXV; q += kThreads) {
-      const int j = q / PV;
-      st_lds_f32(sX + q * VE, ldv<Tin>(xrow(j) + (q - j * PV) * VE));
-    }
   } else {
-    for (int e = tid; e < n * P; e += kThreads) {
-      const int j = e / P;
-      sX[e] = to_f32(xrow(j)[e - j * P]);
-    }
+    for (int p = tid >> lgJP; p < P; p += kThreads >> lgJP)
+      if (jx < n) sXT[p * RS + jx] = to_f32(xrow(jx)[p]);
+  }
+  const int n4 = align4(n);  // zero the padding entries n..n4-1 read by the last group of 4
+  for (int e = tid; e < P * (n4 - n); e += kThreads) {
+    const int p = e / (n4 - n);
+    sXT[p * RS + n + (e - p * (n4 - n))] = 0.f;
   }
   if (wave == 0) {  // c_j = exp(sum_{j<m<n} l_m) dt_j and exp(Lam), tree-summed
     const float u = lane < n ? dl.y : 0.f;
@@ -138,41 +138,55 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   __syncthreads();
   const float D = sCF[R];
 
-  // 3. S <- D S + sum_j (c_j x_j) outer B_j, in registers; write back.
+  // 3. S <- D S + sum_j x_j outer (c_j B_j), four entries per step, in place.
   for (int base = 0; base < P; base += RPP * kMaxPass) {
     if (base > 0) load_chunk(base);
-    float4 acc[kMaxPass];
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
-      acc[k].x = D * fr[k].v.x;
-      acc[k].y = D * fr[k].v.y;
-      acc[k].z = D * fr[k].v.z;
-      acc[k].w = D * fr[k].v.w;
+      fr[k].v.x *= D;
+      fr[k].v.y *= D;
+      fr[k].v.z *= D;
+      fr[k].v.w *= D;
     }
-    for (int j = 0; j < n; ++j) {
-      const float cj = sCF[j];
-      const float4 bv = *reinterpret_cast<const float4*>(&sB[j * N + col * 4]);
+    for (int j4 = 0; j4 < n; j4 += 4) {
+      float4 bv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if (j4 + jj < n) {
+          const float cj = sCF[j4 + jj];
+          const float4 t = *reinterpret_cast<const float4*>(&sB[(j4 + jj) * N + col * 4]);
+          bv[jj] = make_float4(cj * t.x, cj * t.y, cj * t.z, cj * t.w);
+        } else {
+          bv[jj] = float4{};
+        }
+      }
 #pragma unroll
       for (int k = 0; k < kMaxPass; ++k) {
-        if (base + k * RPP >= P) break;
-        const int row = base + k * RPP + rsub;
-        const float xv = row < P ? cj * sX[j * P + row] : 0.f;
-        acc[k].x = fmaf(xv, bv.x, acc[k].x);
-        acc[k].y = fmaf(xv, bv.y, acc[k].y);
-        acc[k].z = fmaf(xv, bv.z, acc[k].z);
-        acc[k].w = fmaf(xv, bv.w, acc[k].w);
+        const int r0 = base + k * RPP;
+        if (r0 >= P) break;
+        const int row = r0 + rsub < P ? r0 + rsub : P - 1;   // rows past P: any valid row, result unused
+        const float4 xv = *reinterpret_cast<const float4*>(&sXT[row * RS + j4]);
+        float4& s = fr[k].v;
+        s.x = fmaf(xv.x, bv[0].x, s.x); s.y = fmaf(xv.x, bv[0].y, s.y);
+        s.z = fmaf(xv.x, bv[0].z, s.z); s.w = fmaf(xv.x, bv[0].w, s.w);
+        s.x = fmaf(xv.y, bv[1].x, s.x); s.y = fmaf(xv.y, bv[1].y, s.y);
+        s.z = fmaf(xv.y, bv[1].z, s.z); s.w = fmaf(xv.y, bv[1].w, s.w);
+        s.x = fmaf(xv.z, bv[2].x, s.x); s.y = fmaf(xv.z, bv[2].y, s.y);
+        s.z = fmaf(xv.z, bv[2].z, s.z); s.w = fmaf(xv.z, bv[2].w, s.w);
+        s.x = fmaf(xv.w, bv[3].x, s.x); s.y = fmaf(xv.w, bv[3].y, s.y);
+        s.z = fmaf(xv.w, bv[3].z, s.z); s.w = fmaf(xv.w, bv[3].w, s.w);
       }
     }
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
       const int row = base + k * RPP + rsub;
       if (row < P) {
-        st16(tile + (size_t)row * N + col * 4, acc[k]);
+        st16(tile + (size_t)row * N + col * 4, fr[k].v);
         if (DUAL) {
           bf16_t* lo = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N + (size_t)row * N + col * 4;
           uint2 pk;
-          pk.x = (uint32_t)f32_to_bf16(acc[k].x) | ((uint32_t)f32_to_bf16(acc[k].y) << 16);
-          pk.y = (uint32_t)f32_to_bf16(acc[k].z) | ((uint32_t)f32_to_bf16(acc[k].w) << 16);
+          pk.x = (uint32_t)f32_to_bf16(fr[k].v.x) | ((uint32_t)f32_to_bf16(fr[k].v.y) << 16);
+          pk.y = (uint32_t)f32_to_bf16(fr[k].v.z) | ((uint32_t)f32_to_bf16(fr[k].v.w) << 16);
           *reinterpret_cast<uint2*>(lo) = pk;
         }
       }
