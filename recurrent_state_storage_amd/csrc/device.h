@@ -208,6 +208,16 @@ __device__ __forceinline__ void st_lds_f32(float* d, const uint4& v) {
 
 __host__ __device__ constexpr int align4(int n) { return (n + 3) & ~3; }
 
+// Direct global -> LDS 16-byte load (gfx950 global_load_lds_dwordx4): lane l of
+// the wavefront writes its 16 bytes at lds_wave_base + 16 l. lds_wave_base must
+// be uniform across the wavefront and 16-byte aligned. Completion is tracked by
+// the vector-memory counter; wait for it before reading the LDS bytes.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
 // Ring slot of window position j (0 <= head < R, 0 <= j < R).
 __device__ __forceinline__ int ring_slot(int head, int j, int R) {
   int s = head + j;

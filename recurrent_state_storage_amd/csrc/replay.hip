@@ -13,18 +13,18 @@
 // P x N is written.
 //
 // One workgroup per (sequence, head). Every global load is issued in the first
-// two memory round trips (the pointer word, then everything else), so a
+// two memory round trips (tile and pointer word, then everything else), so a
 // workgroup lives about two latencies whatever the window length:
-//   1. read the (head, len) pointer word; issue the 16-byte non-temporal loads
-//      of the checkpoint tile (the only large read);
-//   2. issue, all at once, the window's x and B rows, the new tokens' C and the
-//      window's (dt, l) pairs; then unpack them into LDS as fp32, and scan the
+//   1. issue the 16-byte non-temporal loads of the checkpoint tile (the only
+//      large read), and read the (head, len) pointer word beside them;
+//   2. issue, all at once, the window's x and B rows (direct global->LDS loads,
+//      kept raw), the new tokens' C and the window's (dt, l) pairs; scan the
 //      log-decays in one wavefront (a reverse tree sum: no prefix differences);
 //   3. per (i, j) pair, one wavefront: w_ij = exp(lam) dt (B_j . C_i), and the
 //      wavefront's share of sum_j w_ij x_j (wavefront w takes j = w mod 4);
 //   4. consume the tile: per row a 16-byte fragment dot C_i, a butterfly over
 //      the lanes sharing the row, y = exp(Lam) * dot + the four ring shares.
-// The new tokens' x and B go to the ring straight from the staging registers.
+// The new tokens' x and B rows are copied from LDS to the ring.
 // The checkpoint tile is read exactly once per call for all nt outputs.
 #include <type_traits>
 
@@ -33,16 +33,18 @@
 
 namespace rss {
 
-// Dynamic LDS layout of the replay kernel, in floats.
+// Dynamic LDS layout of the replay kernel, in 4-byte words. The window's x and
+// B rows are kept raw (input dtype), exactly as the direct global->LDS loads
+// deliver them; everything else is fp32.
 struct ReplayLds {
   int oX, oB, oC, oCF, oDC, oRing, total;
-  __host__ __device__ ReplayLds(int R, int P, int N, int ntmax) {
-    oX = 0;                          // window x rows    [R][P]
-    oB = align4(R * P);              // window B rows    [R][N]
-    oC = oB + R * N;                 // new tokens' C    [ntmax][N]
-    oCF = oC + ntmax * N;            // exp(lam) * dt    [ntmax][R]
-    oDC = oCF + ntmax * R;           // exp(Lam)         [ntmax]
-    oRing = align4(oDC + ntmax);     // ring part, one share per wavefront [4][ntmax][P]
+  __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes) {
+    oX = 0;                                            // raw window x [R][P]
+    oB = align4((R * P * tin_bytes + 3) / 4);          // raw window B [R][N]
+    oC = oB + align4((R * N * tin_bytes + 3) / 4);     // new tokens' C [ntmax][N]
+    oCF = oC + ntmax * N;                              // exp(lam) * dt [ntmax][R]
+    oDC = oCF + ntmax * R;                             // exp(Lam) [ntmax]
+    oRing = align4(oDC + ntmax);                       // ring shares [4][ntmax][P]
     total = oRing + 4 * ntmax * P;
   }
 };
@@ -54,28 +56,45 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   using Geo = TileGeom<N, LOW>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, RPP = Geo::RPP;
   constexpr int VE = V16<Tin>::VE;
-  constexpr int NV = N / VE;                                   // vectors per B or C row
+  constexpr int NV = N / VE;                                   // 16-byte vectors per B or C row
   constexpr int kStageC = (NTMAX * NV + kThreads - 1) / kThreads;
-  // 16-byte loads per thread per staging round. One round holds a 16-entry
-  // window of x and B at P = 64, N = 128 in bf16; longer windows take more rounds.
-  constexpr int kStageX = NTMAX == 1 ? 1 : 2;
-  constexpr int kStageB = NTMAX == 1 ? 1 : 2;
+  constexpr int EPL = N >= 64 ? N / 64 : 1;                    // B elements per lane in a dot
   using TileT = typename std::conditional<LOW, bf16_t, float>::type;
   using VT = typename V16<Tin>::T;
 
   extern __shared__ __align__(16) float lds[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, P = a.P, G = a.G, R = a.R, nt = a.nt;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh - b * H;
   const int hpg = H / G, g = h / hpg;
 
+  // 1. Checkpoint tile: its address needs no pointer word, so its loads go
+  // out first, in parallel with the pointer read.
+  const TileT* tile = static_cast<const TileT*>(LOW ? a.ckpt_lo : static_cast<const void*>(a.ckpt)) +
+                      (size_t)bh * P * N;
+  const float Ah = a.A[h];
+  const int col = tid % TPR, rsub = tid / TPR;
+  const int toff = rsub * N + col * VEC;
+  Frag<LOW> fr[kMaxPass];
+  auto load_chunk = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < kMaxPass; ++k) {
+      const int r0 = base + k * RPP;
+      const TileT* pk = tile + r0 * N;
+      if (r0 + RPP <= P) fr[k].v = ld16(pk + toff);  // whole pass in range
+      else if (r0 + rsub < P) fr[k].v = ld16(pk + toff);
+      else fr[k].v = decltype(fr[k].v){};
+    }
+  };
+  load_chunk(0);
+
   const int4 pt = a.ptr[bh];
   const int head = pt.x, n0 = pt.y;
   const int L = n0 + nt;
-
   if (head < 0 || head >= R || n0 < 0 || L > R) {  // ring full (no flush), or corrupt pointers
     if (tid == 0) atomicOr(a.err, kDevRingOverflow);
     for (int e = tid; e < nt * P; e += kThreads) {
@@ -85,74 +104,53 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     return;
   }
 
-  const ReplayLds lay(R, P, N, NTMAX);
-  float* sX = lds + lay.oX;
-  float* sB = lds + lay.oB;
+  const ReplayLds lay(R, P, N, NTMAX, (int)sizeof(Tin));
+  Tin* sX = reinterpret_cast<Tin*>(lds + lay.oX);
+  Tin* sB = reinterpret_cast<Tin*>(lds + lay.oB);
   float* sC = lds + lay.oC;
   float* sCF = lds + lay.oCF;
   float* sDC = lds + lay.oDC;
   float* sRing = lds + lay.oRing;
 
-  const Tin* xin = static_cast<const Tin*>(a.x);
-  const Tin* Bin = static_cast<const Tin*>(a.B);
-  const Tin* Cin = static_cast<const Tin*>(a.C);
-  Tin* rx = static_cast<Tin*>(a.ring_x);
-  Tin* rB = static_cast<Tin*>(a.ring_B);
+  // Per-workgroup base pointers (uniform, held in scalar registers); every
+  // per-lane offset below is a 32-bit int.
+  Tin* rx = static_cast<Tin*>(a.ring_x) + (size_t)bh * R * P;           // this head's x rows
+  Tin* rB = static_cast<Tin*>(a.ring_B) + ((size_t)b * G + g) * R * N;   // this group's B rows
+  float2* rdl = a.ring_dl + (size_t)bh * R;
+  const Tin* xin = static_cast<const Tin*>(a.x) + ((size_t)b * nt * H + h) * P;
+  const Tin* Bin = static_cast<const Tin*>(a.B) + ((size_t)b * nt * G + g) * N;
+  const Tin* Cin = static_cast<const Tin*>(a.C) + ((size_t)b * nt * G + g) * N;
+  const float* dtin = a.dt + (size_t)b * nt * H + h;
+  float* yout = a.y + ((size_t)b * nt * H + h) * P;
+  const int xstr = H * P, bstr = G * N;   // per-token strides of x and of B, C
   auto xrow = [&](int j) -> const Tin* {
-    return j < n0 ? rx + ((size_t)bh * R + ring_slot(head, j, R)) * P
-                  : xin + ((size_t)(b * nt + (j - n0)) * H + h) * P;
+    return j < n0 ? rx + ring_slot(head, j, R) * P : xin + (j - n0) * xstr;
   };
   auto brow = [&](int j) -> const Tin* {
-    return j < n0 ? rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N
-                  : Bin + ((size_t)(b * nt + (j - n0)) * G + g) * N;
+    return j < n0 ? rB + ring_slot(head, j, R) * N : Bin + (j - n0) * bstr;
   };
 
-  // 1. Checkpoint tile: first chunk of rows into registers.
-  const int col = tid % TPR, rsub = tid / TPR;
-  const TileT* tile = static_cast<const TileT*>(LOW ? a.ckpt_lo : static_cast<const void*>(a.ckpt))
-                      + (size_t)bh * P * N;
-  Frag<LOW> fr[kMaxPass];
-  auto load_chunk = [&](int base) {
-#pragma unroll
-    for (int k = 0; k < kMaxPass; ++k) {
-      const int r0 = base + k * RPP;
-      if (r0 + RPP <= P) fr[k].v = ld16(tile + (size_t)(r0 + rsub) * N + col * VEC);  // whole pass
-      else if (r0 + rsub < P) fr[k].v = ld16(tile + (size_t)(r0 + rsub) * N + col * VEC);
-      else fr[k].v = decltype(fr[k].v){};
-    }
-  };
-  load_chunk(0);
-
-  // 2. Everything else in one round of loads, then unpack into LDS.
+  // 2. Window rows straight into LDS (direct global->LDS 16-byte loads: lane l
+  // of a wavefront lands at the wavefront's LDS base + 16 l), C and (dt, l)
+  // through registers. All issued before any wait.
   const bool xvec = (P % VE) == 0;
   const int PV = xvec ? P / VE : 0;
   auto xdiv = [&](int q) { return (int)(((uint64_t)(uint32_t)q * a.xdiv) >> 32); };
   const int totXV = L * PV, totBV = L * NV, totCV = nt * NV;
-  VT vx[kStageX], vb[kStageB], vc[kStageC];
-  Tin sxs[kStageS];
-#pragma unroll
-  for (int m = 0; m < kStageB; ++m) {
-    const int q = m * kThreads + tid;
+  for (int q0 = wave * 64; q0 < totBV; q0 += kThreads) {
+    const int q = q0 + lane;
     if (q < totBV) {
-      const int j = q / NV, c = q - j * NV;
-      vb[m] = ldv<Tin>(brow(j) + c * VE);
+      const int j = q / NV;
+      dma16(brow(j) + (q - j * NV) * VE, sB + q0 * VE);
     }
   }
-#pragma unroll
-  for (int m = 0; m < kStageC; ++m) {
-    const int q = m * kThreads + tid;
-    if (q < totCV) {
-      const int i = q / NV, c = q - i * NV;
-      vc[m] = ldv<Tin>(Cin + ((size_t)(b * nt + i) * G + g) * N + c * VE);
-    }
-  }
+  Tin sxs[kStageS];
   if (xvec) {
-#pragma unroll
-    for (int m = 0; m < kStageX; ++m) {
-      const int q = m * kThreads + tid;
+    for (int q0 = wave * 64; q0 < totXV; q0 += kThreads) {
+      const int q = q0 + lane;
       if (q < totXV) {
-        const int j = xdiv(q), c = q - j * PV;
-        vx[m] = ldv<Tin>(xrow(j) + c * VE);
+        const int j = xdiv(q);
+        dma16(xrow(j) + (q - j * PV) * VE, sX + q0 * VE);
       }
     }
   } else {
@@ -165,99 +163,36 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
       }
     }
   }
-  const float Ah = a.A[h];
-  float dtj = 0.f, lj = 0.f;
-  if (tid < L) {  // wavefront 0: lane j holds window entry j's (dt, l)
-    if (tid < n0) {
-      const float2 v = a.ring_dl[(size_t)bh * R + ring_slot(head, tid, R)];
-      dtj = v.x;
-      lj = v.y;
-    } else {
-      dtj = a.dt[(size_t)(b * nt + (tid - n0)) * H + h];
-      lj = dtj * Ah;
-    }
-  }
-
-  const bool keepB = h == g * hpg;  // the group's first head keeps the group's B
+  VT vc[kStageC];
 #pragma unroll
-  for (int m = 0; m < kStageB; ++m) {
+  for (int m = 0; m < kStageC; ++m) {
     const int q = m * kThreads + tid;
-    if (q < totBV) {
-      st_lds_f32(sB + q * VE, vb[m]);
-      const int j = q / NV;
-      if (keepB && j >= n0)
-        *reinterpret_cast<VT*>(rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N +
-                               (q - j * NV) * VE) = vb[m];
+    if (q < totCV) {
+      const int i = q / NV, c = q - i * NV;
+      vc[m] = ldv<Tin>(Cin + i * bstr + c * VE);
     }
   }
+  // Wavefront 0: lane j holds window entry j's (dt, l). The new tokens' l =
+  // dt * A is formed only after every load is in flight: consuming a load
+  // waits for all loads issued before it.
+  // (Separate registers for the two loads: one register written by two loads
+  // in flight would serialise them.)
+  float2 dl_ring = make_float2(0.f, 0.f);
+  float dt_new = 0.f;
+  if (tid < n0) dl_ring = rdl[ring_slot(head, tid, R)];
+  if (tid >= n0 && tid < L) dt_new = dtin[(tid - n0) * H];
 #pragma unroll
   for (int m = 0; m < kStageC; ++m) {
     const int q = m * kThreads + tid;
     if (q < totCV) st_lds_f32(sC + q * VE, vc[m]);
   }
-  if (xvec) {
-#pragma unroll
-    for (int m = 0; m < kStageX; ++m) {
-      const int q = m * kThreads + tid;
-      if (q < totXV) {
-        st_lds_f32(sX + q * VE, vx[m]);
-        const int j = xdiv(q);
-        if (j >= n0)
-          *reinterpret_cast<VT*>(rx + ((size_t)bh * R + ring_slot(head, j, R)) * P +
-                                 (q - j * PV) * VE) = vx[m];
-      }
-    }
-  } else {
+  if (!xvec) {
 #pragma unroll
     for (int m = 0; m < kStageS; ++m) {
       const int e = m * kThreads + tid;
-      if (e < L * P) {
-        sX[e] = to_f32(sxs[m]);
-        const int j = xdiv(e);
-        if (j >= n0) rx[((size_t)bh * R + ring_slot(head, j, R)) * P + (e - j * P)] = sxs[m];
-      }
+      if (e < L * P) sX[e] = sxs[m];
     }
-  }
-  // Long windows (rare): further staging rounds, loads then stores.
-  for (int q0 = kStageB * kThreads; q0 < totBV; q0 += kStageB * kThreads) {
-#pragma unroll
-    for (int m = 0; m < kStageB; ++m) {
-      const int q = q0 + m * kThreads + tid;
-      if (q < totBV) { const int j = q / NV; vb[m] = ldv<Tin>(brow(j) + (q - j * NV) * VE); }
-    }
-#pragma unroll
-    for (int m = 0; m < kStageB; ++m) {
-      const int q = q0 + m * kThreads + tid;
-      if (q < totBV) {
-        st_lds_f32(sB + q * VE, vb[m]);
-        const int j = q / NV;
-        if (keepB && j >= n0)
-          *reinterpret_cast<VT*>(rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N +
-                                 (q - j * NV) * VE) = vb[m];
-      }
-    }
-  }
-  if (xvec) {
-    for (int q0 = kStageX * kThreads; q0 < totXV; q0 += kStageX * kThreads) {
-#pragma unroll
-      for (int m = 0; m < kStageX; ++m) {
-        const int q = q0 + m * kThreads + tid;
-        if (q < totXV) { const int j = xdiv(q); vx[m] = ldv<Tin>(xrow(j) + (q - j * PV) * VE); }
-      }
-#pragma unroll
-      for (int m = 0; m < kStageX; ++m) {
-        const int q = q0 + m * kThreads + tid;
-        if (q < totXV) {
-          st_lds_f32(sX + q * VE, vx[m]);
-          const int j = xdiv(q);
-          if (j >= n0)
-            *reinterpret_cast<VT*>(rx + ((size_t)bh * R + ring_slot(head, j, R)) * P +
-                                   (q - j * PV) * VE) = vx[m];
-        }
-      }
-    }
-  } else {
-    for (int e0 = kStageS * kThreads; e0 < L * P; e0 += kStageS * kThreads) {
+    for (int e0 = kStageS * kThreads; e0 < L * P; e0 += kStageS * kThreads) {  // long windows
 #pragma unroll
       for (int m = 0; m < kStageS; ++m) {
         const int e = e0 + m * kThreads + tid;
@@ -266,17 +201,16 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
 #pragma unroll
       for (int m = 0; m < kStageS; ++m) {
         const int e = e0 + m * kThreads + tid;
-        if (e < L * P) {
-          sX[e] = to_f32(sxs[m]);
-          const int j = xdiv(e);
-          if (j >= n0) rx[((size_t)bh * R + ring_slot(head, j, R)) * P + (e - j * P)] = sxs[m];
-        }
+        if (e < L * P) sX[e] = sxs[m];
       }
     }
   }
 
   // Log-decay scan in wavefront 0: lam_i(j) = sum_{j < m <= t_i} l_m, tree-summed.
   if (wave == 0) {
+    const bool fresh = tid >= n0 && tid < L;
+    const float dtj = fresh ? dt_new : dl_ring.x;
+    const float lj = fresh ? dt_new * Ah : dl_ring.y;
 #pragma unroll
     for (int i = 0; i < NTMAX; ++i) {
       if (i >= nt) break;
@@ -287,9 +221,31 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
       if (lane == 0) sDC[i] = expf(lam + u);
     }
     if (lane >= n0 && lane < L)  // the new tokens' (dt, l) into the ring
-      a.ring_dl[(size_t)bh * R + ring_slot(head, lane, R)] = make_float2(dtj, lj);
+      rdl[ring_slot(head, lane, R)] = make_float2(dtj, lj);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads have landed
   __syncthreads();
+
+  // The new tokens' x and B rows go from LDS to the ring.
+  if (xvec) {
+    for (int q = tid; q < nt * PV; q += kThreads) {
+      const int i = q / PV, c = q - i * PV;
+      *reinterpret_cast<VT*>(rx + ring_slot(head, n0 + i, R) * P + c * VE) =
+          *reinterpret_cast<const VT*>(sX + (n0 + i) * P + c * VE);
+    }
+  } else {
+    for (int e = tid; e < nt * P; e += kThreads) {
+      const int i = e / P, p = e - i * P;
+      rx[ring_slot(head, n0 + i, R) * P + p] = sX[(n0 + i) * P + p];
+    }
+  }
+  if (h == g * hpg) {  // the group's first head keeps the group's B
+    for (int q = tid; q < nt * NV; q += kThreads) {
+      const int i = q / NV, c = q - i * NV;
+      *reinterpret_cast<VT*>(rB + ring_slot(head, n0 + i, R) * N + c * VE) =
+          *reinterpret_cast<const VT*>(sB + (n0 + i) * N + c * VE);
+    }
+  }
 
   // 3. Wavefront w takes the window entries j = w (mod 4) of every output i:
   // w_ij = coef_ij (B_j . C_i), and its share of sum_j w_ij x_j, row p on lane p mod 64.
@@ -300,11 +256,14 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     for (int j = wave; j <= ti; j += kWaves) {
       float part = 0.f;
 #pragma unroll
-      for (int n = lane; n < N; n += 64) part = fmaf(sB[j * N + n], sC[i * N + n], part);
+      for (int e = 0; e < EPL; ++e) {
+        const int n = lane * EPL + e;
+        if (n < N) part = fmaf(to_f32(sB[j * N + n]), sC[i * N + n], part);
+      }
       const float w = sCF[i * R + j] * wave_sum(part);
 #pragma unroll
       for (int r = 0; r < kRowsPerLane; ++r)
-        if (r * 64 + lane < P) share[r] = fmaf(w, sX[j * P + r * 64 + lane], share[r]);
+        if (r * 64 + lane < P) share[r] = fmaf(w, to_f32(sX[j * P + r * 64 + lane]), share[r]);
     }
 #pragma unroll
     for (int r = 0; r < kRowsPerLane; ++r)
@@ -340,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
           if (row < P) {
             const float ring = (sRing[i * P + row] + sRing[(NTMAX + i) * P + row]) +
                                (sRing[(2 * NTMAX + i) * P + row] + sRing[(3 * NTMAX + i) * P + row]);
-            a.y[((size_t)(b * nt + i) * H + h) * P + row] = fmaf(sDC[i], part[m], ring);
+            yout[i * xstr + row] = fmaf(sDC[i], part[m], ring);
           }
         }
       }
@@ -352,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
 
 template <int N, typename Tin, bool LOW, int NTMAX>
 static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
-  const size_t lds = (size_t)ReplayLds(a.R, a.P, N, NTMAX).total * sizeof(float);
+  const size_t lds = (size_t)ReplayLds(a.R, a.P, N, NTMAX, (int)sizeof(Tin)).total * sizeof(float);
   auto kern = replay_kernel<N, Tin, LOW, NTMAX>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
