@@ -135,6 +135,155 @@ def cpu_baseline(wl, pool, budget_s: float):
                       f"{steps} decode steps ({el:.1f} s, 1 thread)"}
 
 
+def _timed(torch, fn, n):
+    """Run fn(i) for i < n between two events on the current stream; ms."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def run_dual(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
+    """Dual precision (fp32 master + bf16 read copy), W = 16, same inputs."""
+    wl = workloads.get("mamba2_dual_b256_h128_p64_n128_w16")
+    Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
+    cfg = rss.make_config(Bt, H, P, N, wl.ngroups, W, wl.capacity, 0, rss.RSS_DTYPE_BF16,
+                          rss.RSS_COPY_BF16)
+    layer = rss.ReplayLayer(cfg, A, dev)
+    layer.init_state()
+    y = torch.empty((Bt, H, P), device=dev)
+    T = X.shape[0]
+    ev = {}
+
+    def step(k, rec=False):
+        i = k % T
+        if rec:
+            ev.setdefault("r", []).append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+            ev["r"][-1][0].record()
+        layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
+        if rec:
+            ev["r"][-1][1].record()
+        if (k + 1) % W == 0:
+            if rec:
+                ev.setdefault("f", []).append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                ev["f"][-1][0].record()
+            layer.flush_checkpoint(W)
+            if rec:
+                ev["f"][-1][1].record()
+    for k in range(warmup):
+        step(k)
+    ms = _timed(torch, lambda j: step(warmup + j), steps)
+    base = warmup + steps
+    for j in range(steps):
+        step(base + j, rec=True)
+    torch.cuda.synchronize()
+    r_ms = sum(a.elapsed_time(b) for a, b in ev["r"])
+    f_ms = sum(a.elapsed_time(b) for a, b in ev.get("f", []))
+    rbytes = sum(replay_bytes(wl, (base + j) % W) for j in range(steps)) * Bt * H
+    fbytes = flush_bytes(wl, W) * Bt * H * len(ev.get("f", []))
+    assert layer.device_error() == 0
+    return {"workload": wl.name, "tokens_per_s": Bt * steps / (ms / 1e3),
+            "replay_avg_us": r_ms / steps * 1e3, "replay_GBps": rbytes / (r_ms / 1e3) / 1e9,
+            "flush_avg_us": f_ms / max(len(ev.get("f", [])), 1) * 1e3,
+            "flush_GBps": fbytes / (f_ms / 1e3) / 1e9 if f_ms else None}
+
+
+def _gen_round(args):
+    name, r = args
+    wl = workloads.get(name)
+    d = synth.draft_inputs(wl, r)
+    return r, d["x_bits"], d["B_bits"], d["C_bits"], d["dt"], synth.accepted_drafts(wl, r)
+
+
+def run_spec(torch, rss, dev, rounds, warmup, workers, distinct=6):
+    """Speculative rounds at batch 512, K = 4: replay verify + rollback + flush,
+    against the eager kernel with a state snapshot per draft token."""
+    wl = workloads.get("mamba2_spec_b512_h128_p64_n128_w16_k4")
+    Bt, H, P, N, G, W, K = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window, wl.draft
+    with concurrent.futures.ProcessPoolExecutor(max_workers=min(workers, distinct)) as ex:
+        got = sorted(ex.map(_gen_round, [(wl.name, r) for r in range(distinct)]))
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    RX = [bf(g[1]) for g in got]
+    RB = [bf(g[2]) for g in got]
+    RC = [bf(g[3]) for g in got]
+    RD = [torch.from_numpy(g[4]).to(dev) for g in got]
+    NACC = [g[5] for g in got]
+    NDROP = [torch.from_numpy((K - n).astype(np.int32)).to(dev) for n in NACC]
+    SRC = [torch.from_numpy(n.astype(np.int32)).to(dev) for n in NACC]
+    A = torch.from_numpy(synth.params(wl)["A"]).to(dev)
+    cfg = rss.make_config(Bt, H, P, N, G, W, wl.capacity, K, rss.RSS_DTYPE_BF16, rss.RSS_COPY_NONE)
+    layer = rss.ReplayLayer(cfg, A, dev)
+    layer.init_state()
+    y = torch.empty((Bt, K + 1, H, P), device=dev)
+
+    def rep_round(r):
+        i = r % distinct
+        layer.verify_k_tokens(K, RX[i], RB[i], RC[i], RD[i], y)
+        layer.rollback(NDROP[i])
+        layer.flush_checkpoint(W)
+    for r in range(warmup):
+        rep_round(r)
+    ms_rep = _timed(torch, lambda j: rep_round(warmup + j), rounds)
+    # per-kernel verify duration, and its algorithmic bytes from the window lengths
+    lens = np.zeros(Bt, np.int64)
+    for r in range(warmup + rounds):        # replay the integer pointer rule on the host
+        lens += K + 1 - (K - NACC[r % distinct])
+        lens[lens >= W] = 0
+    vev = []
+    vbytes = 0
+    entry = 2 * P + 2 * N + 8
+    for j in range(rounds):
+        r = warmup + rounds + j
+        i = r % distinct
+        vev.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+        vev[-1][0].record()
+        layer.verify_k_tokens(K, RX[i], RB[i], RC[i], RD[i], y)
+        vev[-1][1].record()
+        vbytes += H * int(np.sum(P * N * 4 + lens * entry + (K + 1) * (2 * P + 4 * N + 4 + 4 * P + entry) + 36))
+        layer.rollback(NDROP[i])
+        layer.flush_checkpoint(W)
+        lens += K + 1 - (K - NACC[i])
+        lens[lens >= W] = 0
+    torch.cuda.synchronize()
+    v_ms = sum(a.elapsed_time(b) for a, b in vev)
+    assert layer.device_error() == 0
+    committed = sum(int(np.sum(NACC[(warmup + j) % distinct] + 1)) for j in range(rounds))
+    del layer
+    # eager baseline: K+1 eager tokens from slot src, snapshot i -> slot i;
+    # rolling back to n_acc accepted drafts = next round reads slot n_acc
+    pool = torch.zeros((Bt, K + 1, H, P, N), device=dev)
+    src = [torch.zeros((Bt,), dtype=torch.int32, device=dev)]
+
+    def eag_round(r):
+        i = r % distinct
+        rss.rss_eager_verify(cfg, pool, src[0], K, RX[i], RB[i], RC[i], RD[i], A, y)
+        src[0] = SRC[i]
+    for r in range(warmup):
+        eag_round(r)
+    ms_eag = _timed(torch, lambda j: eag_round(warmup + j), rounds)
+    eev = []
+    for j in range(rounds):
+        eev.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+        eev[-1][0].record()
+        eag_round(warmup + rounds + j)
+        eev[-1][1].record()
+    torch.cuda.synchronize()
+    e_ms = sum(a.elapsed_time(b) for a, b in eev)
+    ebytes = H * Bt * ((K + 2) * P * N * 4 + (K + 1) * (2 * P + 4 * N + 4 + 4 * P) + 4)
+    del pool
+    return {"workload": wl.name, "rounds": rounds,
+            "replay_committed_tokens_per_s": committed / (ms_rep / 1e3),
+            "eager_snapshot_committed_tokens_per_s": committed / (ms_eag / 1e3),
+            "speedup": ms_eag / ms_rep,
+            "verify_avg_us": v_ms / rounds * 1e3, "verify_GBps": vbytes / (v_ms / 1e3) / 1e9,
+            "eager_verify_avg_us": e_ms / rounds * 1e3,
+            "eager_verify_GBps": ebytes / (e_ms / rounds / 1e3) / 1e9}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +295,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the dual-precision and speculative-verify measurements")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -305,6 +456,9 @@ def main() -> int:
     }
     if out_eager:
         rec["speedup_vs_eager_gpu"] = tok_s / out_eager["tokens_per_s"]
+    if not args.no_extra:
+        rec["dual_precision"] = run_dual(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
+        rec["speculative"] = run_spec(torch, rss, dev, rounds=48, warmup=8, workers=workers)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, pool, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
