@@ -60,6 +60,12 @@ def flush_bytes(wl, n: int) -> int:
     return 2 * P * N * 4 + lo + n * (P * ib + N * ib + 8) + 32
 
 
+def fused_bytes(wl) -> int:
+    """Decode of the token that fills the window, with the fold in the same pass:
+    the replay's bytes plus the new checkpoint written."""
+    return replay_bytes(wl, wl.window - 1) + wl.headdim * wl.dstate * 4
+
+
 def eager_bytes(wl) -> int:
     P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
     return 2 * P * N * 4 + P * ib + 2 * N * ib + 4 + P * 4 + 4
@@ -295,6 +301,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--separate-flush", action="store_true",
+                    help="fold with a separate flush launch instead of the fused decode+fold")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the dual-precision and speculative-verify measurements")
     args = ap.parse_args()
@@ -327,14 +335,20 @@ def main() -> int:
     y = torch.empty((Bt, H, P), device=dev)
     T = args.pool
 
+    fused = not args.separate_flush
+
     def replay_step(k, ev=None):
         i = k % T
+        fold = (k + 1) % W == 0
         if ev is not None:
             ev[0].record()
-        layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
+        if fold and fused:   # this token fills every window: decode and fold in one pass
+            layer.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)
+        else:
+            layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
         if ev is not None:
             ev[1].record()
-        if (k + 1) % W == 0:
+        if fold and not fused:
             if ev is not None:
                 ev[2].record()
             layer.flush_checkpoint(W)
@@ -365,15 +379,24 @@ def main() -> int:
         replay_step(k, ev[j])
         k += 1
     torch.cuda.synchronize()
-    rep_ms, rep_bytes, fl_ms, fl_bytes, n_fl = 0.0, 0, 0.0, 0, 0
+    # "replay decode" = the plain decode launches (window positions 0..W-2, and
+    # W-1 too when the flush runs separately); the fold launches are reported apart.
+    rep_ms, rep_bytes, n_rep, fl_ms, fl_bytes, n_fl = 0.0, 0, 0, 0.0, 0, 0
     for j in range(args.steps):
-        rep_ms += ev[j][0].elapsed_time(ev[j][1])
+        d = ev[j][0].elapsed_time(ev[j][1])
+        if phase[j] == W - 1 and fused:
+            fl_ms += d
+            fl_bytes += fused_bytes(wl) * Bt * H
+            n_fl += 1
+            continue
+        rep_ms += d
         rep_bytes += replay_bytes(wl, phase[j]) * Bt * H
+        n_rep += 1
         if phase[j] == W - 1:
             fl_ms += ev[j][2].elapsed_time(ev[j][3])
             fl_bytes += flush_bytes(wl, W) * Bt * H
             n_fl += 1
-    rep_avg_us = rep_ms / args.steps * 1e3
+    rep_avg_us = rep_ms / n_rep * 1e3
     rep_gbs = rep_bytes / (rep_ms / 1e3) / 1e9
     assert layer.device_error() == 0
 
@@ -418,9 +441,12 @@ def main() -> int:
         del src, dst
 
     # Bytes per decoded token per layer (analytic): state tiles, and everything.
-    st_replay = P * N * 4 * H + 2 * P * N * 4 * H / W
     st_eager = 2 * P * N * 4 * H
-    tot_replay = (sum(replay_bytes(wl, n) for n in range(W)) / W + flush_bytes(wl, W) / W) * H
+    if fused:
+        tot_replay = (sum(replay_bytes(wl, n) for n in range(W - 1)) + fused_bytes(wl)) / W * H
+    else:
+        tot_replay = (sum(replay_bytes(wl, n) for n in range(W)) / W + flush_bytes(wl, W) / W) * H
+    st_replay = P * N * 4 * H + (P * N * 4 * H / W if fused else 2 * P * N * 4 * H / W)
     traffic = counter_traffic()
     rec = {
         "metric": METRIC,
@@ -437,15 +463,17 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "batch": Bt, "heads": H, "headdim": P, "dstate": N,
                    "groups": G, "window": W, "xBC_storage": "bf16", "state": "f32",
+                   "fold": "fused into the window-filling decode" if fused else "separate flush",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": rep_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": rep_gbs / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "replay decode", "avg_launch_us": rep_avg_us,
-                     "algorithmic_bytes_per_launch": rep_bytes / args.steps},
+                     "algorithmic_bytes_per_launch": rep_bytes / n_rep},
         "kernels": {
             "replay_decode": {"avg_us": rep_avg_us, "GBps": rep_gbs},
-            "flush": {"avg_us": fl_ms / max(n_fl, 1) * 1e3,
-                      "GBps": fl_bytes / (fl_ms / 1e3) / 1e9 if n_fl else None, "launches": n_fl},
+            ("fused_decode_fold" if fused else "flush"): {
+                "avg_us": fl_ms / max(n_fl, 1) * 1e3,
+                "GBps": fl_bytes / (fl_ms / 1e3) / 1e9 if n_fl else None, "launches": n_fl},
         },
         "eager_baseline": out_eager,
         "bytes_per_token": {"replay_state": st_replay, "eager_state": st_eager,

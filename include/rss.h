@@ -162,6 +162,19 @@ int32_t rss_init_state(rss_layer* layer, const float* S0, void* stream);
 int32_t rss_decode_step(rss_layer* layer, const void* x, const void* B, const void* C,
                         const float* dt, float* y, void* stream);
 
+/* rss_decode_step followed by rss_flush_checkpoint(min_len), in one pass where
+ * it can be: a sequence whose window reaches min_len entries with this token is
+ * folded while its checkpoint tile is already loaded for the output, and the
+ * new checkpoint is written, so the flush's second read of the tile is saved
+ * (the fold writes the state only once per window, P1 "Tenir le journal plutôt
+ * que le solde"). Results equal the two separate calls bit for bit. With
+ * read_copy = BF16 the replay reads the bf16 copy, so the fold (which needs the
+ * fp32 master) runs as the separate flush launch. min_len >= 1; errors as
+ * rss_decode_step, plus RSS_DEV_UNCOMMITTED if a window to fold still holds
+ * tentative entries (that sequence is then not folded). */
+int32_t rss_decode_flush_step(rss_layer* layer, int32_t min_len, const void* x, const void* B,
+                              const void* C, const float* dt, float* y, void* stream);
+
 /* Fold the ring into the checkpoint for every sequence whose window holds at
  * least min_len >= 1 entries (P1, "Tenir le journal plutôt que le solde":
  * rewritten only when the buffer is full; P3: once per window):

@@ -11,7 +11,7 @@ namespace rss {
 
 // Decode (nt = 1) and speculative verify (nt = K+1) by replay.
 struct ReplayArgs {
-  const float* ckpt;       // [Bt,H,P,N] fp32 master
+  float* ckpt;             // [Bt,H,P,N] fp32 master (written only by the fused fold)
   const void* ckpt_lo;     // [Bt,H,P,N] bf16 read copy (dual mode)
   void* ring_x;            // [Bt,H,R,P]
   void* ring_B;            // [Bt,G,R,N]
@@ -25,6 +25,7 @@ struct ReplayArgs {
   const float* dt;         // [Bt,nt,H]
   float* y;                // [Bt,nt,H,P]
   int H, P, G, R, nt, set_tent;
+  int fold_min_len;        // decode only: also fold windows that reach this length (0: never)
   uint64_t xdiv;           // ceil(2^32 / d): q / d == (q * xdiv) >> 32 for q < 2^16,
                            // d = P/VE (16-byte x vectors per row) or P (element path)
 };

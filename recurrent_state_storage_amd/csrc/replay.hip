@@ -26,6 +26,10 @@
 //      the lanes sharing the row, y = exp(Lam) * dot + the four ring shares.
 // The new tokens' x and B rows are copied from LDS to the ring.
 // The checkpoint tile is read exactly once per call for all nt outputs.
+//
+// Fused fold: a decode launched with a fold threshold also folds, in the same
+// pass, every window the new token fills (the tile is already in registers),
+// and writes the new checkpoint: the flush's extra read of the tile is saved.
 #include <type_traits>
 
 #include "device.h"
@@ -51,7 +55,7 @@ struct ReplayLds {
 
 constexpr int kStageS = 4;  // scalar loads per thread and round (x rows when P % VE != 0)
 
-template <int N, typename Tin, bool LOW, int NTMAX>
+template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD>
 __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   using Geo = TileGeom<N, LOW>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, RPP = Geo::RPP;
@@ -102,6 +106,17 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
       a.y[((size_t)(b * nt + i) * H + h) * P + p] = __builtin_nanf("");
     }
     return;
+  }
+
+  // Fused fold (decode only, fp32 checkpoint): when this token fills the window,
+  // the tile already in registers is folded and written back in this pass,
+  // exactly as a separate flush would (same coefficients, same order).
+  bool do_fold = false;
+  if constexpr (FOLD) {
+    if (L >= a.fold_min_len) {
+      if (pt.z == 0) do_fold = true;
+      else if (tid == 0) atomicOr(a.err, kDevUncommitted);  // never fold tentative entries
+    }
   }
 
   const ReplayLds lay(R, P, N, NTMAX, (int)sizeof(Tin));
@@ -304,15 +319,53 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
         }
       }
     }
+    if constexpr (FOLD) {
+      if (do_fold) {  // S <- exp(Lam) S + sum_j x_j outer (c_j B_j), j ascending
+        const float D = sDC[0];
+#pragma unroll
+        for (int k = 0; k < kMaxPass; ++k) {
+          fr[k].v.x *= D;
+          fr[k].v.y *= D;
+          fr[k].v.z *= D;
+          fr[k].v.w *= D;
+        }
+        for (int j = 0; j < L; ++j) {
+          const float cj = sCF[j];
+          float bv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) bv[v] = cj * to_f32(sB[j * N + col * 4 + v]);
+#pragma unroll
+          for (int k = 0; k < kMaxPass; ++k) {
+            const int r0 = base + k * RPP;
+            if (r0 >= P) break;
+            const int row = r0 + rsub < P ? r0 + rsub : P - 1;   // rows past P: result unused
+            const float xv = to_f32(sX[j * P + row]);
+            fr[k].v.x = fmaf(xv, bv[0], fr[k].v.x);
+            fr[k].v.y = fmaf(xv, bv[1], fr[k].v.y);
+            fr[k].v.z = fmaf(xv, bv[2], fr[k].v.z);
+            fr[k].v.w = fmaf(xv, bv[3], fr[k].v.w);
+          }
+        }
+        float* out = a.ckpt + (size_t)bh * P * N;
+#pragma unroll
+        for (int k = 0; k < kMaxPass; ++k) {
+          const int row = base + k * RPP + rsub;
+          if (row < P) st16(out + row * N + col * 4, fr[k].v);
+        }
+      }
+    }
   }
 
-  if (tid == 0) a.ptr[bh] = make_int4(head, L, a.set_tent ? nt : pt.z, 0);
+  if (tid == 0) {
+    if (do_fold) a.ptr[bh] = make_int4(ring_slot(head, L, R), 0, 0, 0);
+    else a.ptr[bh] = make_int4(head, L, a.set_tent ? nt : pt.z, 0);
+  }
 }
 
-template <int N, typename Tin, bool LOW, int NTMAX>
+template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD>
 static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
   const size_t lds = (size_t)ReplayLds(a.R, a.P, N, NTMAX, (int)sizeof(Tin)).total * sizeof(float);
-  auto kern = replay_kernel<N, Tin, LOW, NTMAX>;
+  auto kern = replay_kernel<N, Tin, LOW, NTMAX, FOLD>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -324,8 +377,11 @@ static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
 
 template <int N, typename Tin, bool LOW>
 static hipError_t launch_nt(const ReplayArgs& a, int batch, hipStream_t s) {
-  return a.nt == 1 ? launch_one<N, Tin, LOW, 1>(a, batch, s)
-                   : launch_one<N, Tin, LOW, kMaxNew>(a, batch, s);
+  if (a.nt != 1) return launch_one<N, Tin, LOW, kMaxNew, false>(a, batch, s);
+  if constexpr (!LOW) {  // the fused fold needs the fp32 checkpoint in registers
+    if (a.fold_min_len > 0) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
+  }
+  return launch_one<N, Tin, LOW, 1, false>(a, batch, s);
 }
 
 template <int N>

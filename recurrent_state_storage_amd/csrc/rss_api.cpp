@@ -131,8 +131,8 @@ int32_t rss_init_state(rss_layer* l, const float* S0, void* stream) {
   return launch_status(rss::launch_init(a, static_cast<hipStream_t>(stream)));
 }
 
-static int32_t replay_call(rss_layer* l, int nt, int set_tent, const void* x, const void* B,
-                           const void* C, const float* dt, float* y, void* stream) {
+static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len, const void* x,
+                           const void* B, const void* C, const float* dt, float* y, void* stream) {
   const rss_config& c = l->cfg;
   if (c.batch == 0) return RSS_OK;
   rss::ReplayArgs a;
@@ -155,6 +155,7 @@ static int32_t replay_call(rss_layer* l, int nt, int set_tent, const void* x, co
   a.R = c.capacity;
   a.nt = nt;
   a.set_tent = set_tent;
+  a.fold_min_len = fold_min_len;
   const int ve = c.in_dtype == RSS_DTYPE_BF16 ? 8 : 4;  // elements per 16-byte vector
   const uint64_t d = c.headdim % ve == 0 ? (uint64_t)(c.headdim / ve) : (uint64_t)c.headdim;
   a.xdiv = ((1ull << 32) + d - 1) / d;
@@ -168,7 +169,20 @@ int32_t rss_decode_step(rss_layer* l, const void* x, const void* B, const void* 
   if (!l) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
   if (l->pending_verify) return RSS_E_ORDER;
-  return replay_call(l, 1, 0, x, B, C, dt, y, stream);
+  return replay_call(l, 1, 0, 0, x, B, C, dt, y, stream);
+}
+
+int32_t rss_decode_flush_step(rss_layer* l, int32_t min_len, const void* x, const void* B,
+                              const void* C, const float* dt, float* y, void* stream) {
+  if (!l) return RSS_E_INVALID;
+  if (min_len < 1) return RSS_E_INVALID;
+  if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
+  if (l->pending_verify) return RSS_E_ORDER;
+  if (l->cfg.read_copy == RSS_COPY_BF16) {  // the fold reads the fp32 master: two launches
+    const int32_t st = replay_call(l, 1, 0, 0, x, B, C, dt, y, stream);
+    return st ? st : rss_flush_checkpoint(l, min_len, stream);
+  }
+  return replay_call(l, 1, 0, min_len, x, B, C, dt, y, stream);
 }
 
 int32_t rss_verify_k_tokens(rss_layer* l, int32_t K, const void* x, const void* B, const void* C,
@@ -178,7 +192,7 @@ int32_t rss_verify_k_tokens(rss_layer* l, int32_t K, const void* x, const void* 
   if (K < 0) return RSS_E_INVALID;
   if (K > l->cfg.max_draft) return RSS_E_CAPACITY;
   if (l->pending_verify) return RSS_E_ORDER;
-  const int32_t st = replay_call(l, K + 1, 1, x, B, C, dt, y, stream);
+  const int32_t st = replay_call(l, K + 1, 1, 0, x, B, C, dt, y, stream);
   if (st == RSS_OK) l->pending_verify = 1;
   return st;
 }

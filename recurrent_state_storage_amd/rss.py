@@ -54,6 +54,7 @@ _SIGS = {
     "rss_init_state": ([_VP, _VP, _VP], _I32),
     "rss_decode_step": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_flush_checkpoint": ([_VP, _I32, _VP], _I32),
+    "rss_decode_flush_step": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_verify_k_tokens": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_rollback": ([_VP, _VP, _VP], _I32),
     "rss_get_device_error": ([_VP, ctypes.POINTER(_I32), _VP], _I32),
@@ -208,6 +209,9 @@ class ReplayLayer:
     def decode_step(self, x, B, C, dt, y, stream=None):
         rss_decode_step(self, x, B, C, dt, y, stream)
 
+    def decode_flush_step(self, min_len, x, B, C, dt, y, stream=None):
+        rss_decode_flush_step(self, min_len, x, B, C, dt, y, stream)
+
     def flush_checkpoint(self, min_len, stream=None):
         rss_flush_checkpoint(self, min_len, stream)
 
@@ -234,6 +238,16 @@ def rss_decode_step(layer: ReplayLayer, x, B, C, dt, y, stream=None) -> None:
     args = (_ptr(x, idt, xs, "x"), _ptr(B, idt, bs, "B"), _ptr(C, idt, bs, "C"),
             _ptr(dt, torch.float32, ds, "dt"), _ptr(y, torch.float32, xs, "y"))
     _check(library().rss_decode_step(layer.handle, *args, _stream(stream)), "rss_decode_step")
+
+
+def rss_decode_flush_step(layer: ReplayLayer, min_len: int, x, B, C, dt, y, stream=None) -> None:
+    c = layer.cfg
+    xs, bs, ds = layer.tok_shapes()
+    idt = _in_dtype(c.in_dtype)
+    args = (_ptr(x, idt, xs, "x"), _ptr(B, idt, bs, "B"), _ptr(C, idt, bs, "C"),
+            _ptr(dt, torch.float32, ds, "dt"), _ptr(y, torch.float32, xs, "y"))
+    _check(library().rss_decode_flush_step(layer.handle, int(min_len), *args, _stream(stream)),
+           "rss_decode_flush_step")
 
 
 def rss_flush_checkpoint(layer: ReplayLayer, min_len: int, stream=None) -> None:

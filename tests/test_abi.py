@@ -39,7 +39,7 @@ def _bind(cfg, bufs):
 def test_library_exports_every_declared_symbol():
     lib = rss.library()
     syms = rss.declared_symbols()
-    assert len(syms) >= 13
+    assert len(syms) >= 14
     for s in syms:
         assert hasattr(lib, s), s
     assert set(syms) == set(rss._SIGS), "binding and header disagree"
@@ -118,6 +118,8 @@ def test_call_order_and_argument_errors_return_before_launch():
         assert lib.rss_verify_k_tokens(h, 5, A, A, A, A, A, None) == rss.RSS_E_CAPACITY
         assert lib.rss_verify_k_tokens(h, -1, A, A, A, A, A, None) == rss.RSS_E_INVALID
         assert lib.rss_flush_checkpoint(h, 0, None) == rss.RSS_E_INVALID
+        assert lib.rss_decode_flush_step(h, 0, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_decode_flush_step(h, 16, A, A, A + 8, A, A, None) == rss.RSS_E_INVALID
         assert lib.rss_rollback(h, None, None) == rss.RSS_E_INVALID
         assert lib.rss_init_state(h, A + 4, None) == rss.RSS_E_INVALID
         v = ctypes.c_int32()

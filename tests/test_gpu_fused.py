@@ -1,0 +1,112 @@
+"""GPU parity of the fused decode + fold entry point: bit for bit the same
+outputs, checkpoint, read copy, ring and pointers as rss_decode_step followed by
+rss_flush_checkpoint, in lockstep decode and with per-sequence windows left
+uneven by speculative rounds; and against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mamba2
+import workloads
+from workloads import synth
+from recurrent_state_storage_amd import rss
+from gpu_util import DEV, cfg_of, dev_inputs, rel_l2, log
+
+pytestmark = pytest.mark.gpu
+
+BASE = workloads.get("tiny_b2_h4_p16_n16_w8")
+
+
+def _pair(wl):
+    cfg = cfg_of(wl)
+    A = torch.from_numpy(synth.params(wl)["A"]).to(DEV)
+    S0 = torch.from_numpy(synth.initial_state(wl)).to(DEV)
+    out = []
+    for _ in range(2):
+        L = rss.ReplayLayer(cfg, A, DEV)
+        L.init_state(S0)
+        out.append(L)
+    return out
+
+
+def _same(L1, L2):
+    torch.cuda.synchronize()
+    assert torch.equal(L1.ckpt, L2.ckpt)
+    assert torch.equal(L1.ptr, L2.ptr)
+    assert torch.equal(L1.ring_x, L2.ring_x) and torch.equal(L1.ring_B, L2.ring_B)
+    assert torch.equal(L1.ring_dl, L2.ring_dl)
+    if L1.ckpt_lo is not None:
+        assert torch.equal(L1.ckpt_lo, L2.ckpt_lo)
+
+
+SHAPES = [
+    # P, N, H, G, W, R, in_dtype, copy
+    (64, 128, 4, 4, 16, 16, "bf16", "none"),
+    (37, 32, 3, 1, 5, 7, "f32", "none"),
+    (100, 256, 2, 2, 4, 4, "f32", "none"),
+    (128, 128, 2, 2, 8, 8, "bf16", "none"),
+    (64, 128, 4, 4, 16, 16, "bf16", "bf16"),
+    (1, 16, 1, 1, 1, 1, "f32", "none"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "P%dN%dH%dG%dW%dR%d-%s-%s" % s)
+def test_fused_equals_separate_and_oracle(shape):
+    P, N, H, G, W, R, idt, copy = shape
+    wl = BASE.replace(name="fused", batch=3, headdim=P, dstate=N, nheads=H, ngroups=G, window=W,
+                      capacity=R, in_dtype=idt, read_copy=copy, s0="normal", seed=5000 + P + N)
+    log(f"[fused] {shape}")
+    sep, fus = _pair(wl)
+    A_np = synth.params(wl)["A"]
+    S_ref = synth.initial_state(wl).astype(np.float64)
+    ys, refs = [], []
+    for t in range(3 * W + 1):
+        s = synth.step_inputs(wl, t)
+        d = dev_inputs(s, idt)
+        y1 = torch.empty((wl.batch, H, P), device=DEV)
+        y2 = torch.empty_like(y1)
+        sep.decode_step(d["x"], d["B"], d["C"], d["dt"], y1)
+        sep.flush_checkpoint(W)
+        fus.decode_flush_step(W, d["x"], d["B"], d["C"], d["dt"], y2)
+        assert torch.equal(y1, y2), t
+        S_ref, y_ref = mamba2.eager_step(S_ref, A_np, s["x"], s["B"], s["C"], s["dt"])
+        ys.append(y2.double().cpu().numpy())
+        refs.append(y_ref)
+        if (t + 1) % W == 0:
+            _same(sep, fus)
+            if copy == "none":
+                assert rel_l2(fus.ckpt.double().cpu().numpy(), S_ref) < 1e-5
+    _same(sep, fus)
+    assert fus.device_error() == 0
+    assert rel_l2(np.stack(ys), np.stack(refs)) < (1e-5 if copy == "none" else 2e-2)
+
+
+def test_fused_folds_only_full_windows():
+    """After speculative rounds the sequences' windows differ; a fused decode
+    folds exactly those that reach the threshold, like decode + flush."""
+    wl = BASE.replace(name="fused-spec", batch=6, headdim=64, dstate=128, nheads=4, ngroups=4,
+                      window=8, capacity=12, max_draft=4, draft=4, in_dtype="bf16", s0="normal",
+                      seed=5100)
+    sep, fus = _pair(wl)
+    K = wl.draft
+    for r in range(9):
+        rin = dev_inputs(synth.draft_inputs(wl, r), "bf16")
+        nd = torch.from_numpy((K - synth.accepted_drafts(wl, r)).astype(np.int32)).to(DEV)
+        y = torch.empty((wl.batch, K + 1, wl.nheads, wl.headdim), device=DEV)
+        for L in (sep, fus):
+            L.verify_k_tokens(K, rin["x"], rin["B"], rin["C"], rin["dt"], y)
+            L.rollback(nd)
+            L.flush_checkpoint(wl.window)
+        lens = fus.ptr[:, 0, 1].cpu().numpy()
+        for t in range(3):
+            d = dev_inputs(synth.step_inputs(wl, 100 * r + t), "bf16")
+            y1 = torch.empty((wl.batch, wl.nheads, wl.headdim), device=DEV)
+            y2 = torch.empty_like(y1)
+            sep.decode_step(d["x"], d["B"], d["C"], d["dt"], y1)
+            sep.flush_checkpoint(wl.window)
+            fus.decode_flush_step(wl.window, d["x"], d["B"], d["C"], d["dt"], y2)
+            assert torch.equal(y1, y2)
+        _same(sep, fus)
+        if r == 0:
+            log(f"  window lengths after round 0: {lens.tolist()}")
+    assert fus.device_error() == 0 and sep.device_error() == 0
