@@ -74,6 +74,12 @@ typedef enum rss_status {
 enum { RSS_DTYPE_F32 = 0, RSS_DTYPE_BF16 = 1 };
 enum { RSS_COPY_NONE = 0, RSS_COPY_BF16 = 1 };
 
+/* Layer types. A Gated DeltaNet layer (P1, "La fiche qu'on réécrit à chaque
+ * token": GDN's delta-rule update has the same form) uses P = d_v, N = d_k,
+ * G = H (one key per head), fp32 inputs, no read copy; its ring holds
+ * (u_t, k_t, (1, log alpha_t)) in ring_x, ring_B and ring_dl, and A is unused. */
+enum { RSS_KIND_MAMBA2 = 0, RSS_KIND_GDN = 1 };
+
 /* Bits of the sticky device error word. */
 enum {
   RSS_DEV_ROLLBACK_RANGE = 1, /* rollback n_drop[b] < 0 or > n_tent           */
@@ -92,6 +98,7 @@ typedef struct rss_config {
   int32_t max_draft; /* K_max                                                */
   int32_t in_dtype;  /* RSS_DTYPE_*: storage of x, B, C and their ring copies */
   int32_t read_copy; /* RSS_COPY_*: RSS_COPY_BF16 = dual precision           */
+  int32_t kind;      /* RSS_KIND_*: layer type                               */
 } rss_config;
 
 /*
@@ -106,7 +113,7 @@ typedef struct rss_config {
  *                                 Every head of a sequence holds the same
  *                                 values; each kernel workgroup owns its own
  *                                 (b, h) copy, so no two workgroups race.
- *   A        fp32 [H]             A_h (negative)
+ *   A        fp32 [H]             A_h (negative); unused (may be NULL) for GDN
  *   dev_err  int32 [1]            sticky device error word
  */
 typedef struct rss_buffers {
@@ -204,6 +211,24 @@ int32_t rss_verify_k_tokens(rss_layer* layer, int32_t K, const void* x, const vo
  * Out-of-range n_drop sets RSS_DEV_ROLLBACK_RANGE and leaves that sequence
  * unchanged. RSS_E_ORDER if no round is pending. Callers then flush(W). */
 int32_t rss_rollback(rss_layer* layer, const int32_t* n_drop, void* stream);
+
+/* Gated DeltaNet decode of one token for every sequence (kind = RSS_KIND_GDN),
+ * by replay: with S_{t-1} = checkpoint + window, and per head
+ *   u_t = beta_t (v_t - alpha_t S_{t-1} k_t),   o_t = alpha_t S_{t-1} q_t + (k_t.q_t) u_t,
+ * which is the gated delta rule S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) +
+ * beta_t v_t k_t^T read out as o_t = S_t q_t, without writing S_t. Appends
+ * (u_t, k_t, (1, log alpha_t)) to the ring; rss_flush_checkpoint folds GDN
+ * windows like Mamba-2 ones. Layouts: q, k [Bt,H,N]; v [Bt,H,P]; beta, alpha
+ * [Bt,H]; o [Bt,H,P]; all fp32. Ring overflow as rss_decode_step. */
+int32_t rss_gdn_decode_step(rss_layer* layer, const float* q, const float* k, const float* v,
+                            const float* beta, const float* alpha, float* o, void* stream);
+
+/* Eager gated delta rule (the GDN baseline): S [Bt,H,P,N] fp32 updated in
+ * place, S <- alpha S + u k^T, o = S q, layouts as rss_gdn_decode_step. Uses
+ * cfg's batch, nheads, headdim (d_v) and dstate (d_k). */
+int32_t rss_gdn_eager_step(const rss_config* cfg, float* S, const float* q, const float* k,
+                           const float* v, const float* beta, const float* alpha, float* o,
+                           void* stream);
 
 /* Copy the sticky device error word to *host_code (synchronises `stream`). */
 int32_t rss_get_device_error(rss_layer* layer, int32_t* host_code, void* stream);

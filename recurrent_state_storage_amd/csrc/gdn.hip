@@ -1,0 +1,385 @@
+// Gated DeltaNet decode: eager baseline and replay from checkpoint + ring.
+//
+// P1 ("La fiche qu'on réécrit à chaque token") says GDN adds a delta-rule
+// correction but writes its update in the same form as Mamba-2; P2 ("Des
+// chiffres qui parlent d'eux-mêmes") says the method runs for Gated DeltaNet.
+// Per head, with a d_v x d_k state S, scalar gate alpha_t and rate beta_t:
+//
+//   u_t = beta_t (v_t - alpha_t S_{t-1} k_t)
+//   S_t = alpha_t S_{t-1} + u_t k_t^T          (the gated delta rule)
+//   o_t = S_t q_t = alpha_t S_{t-1} q_t + (k_t . q_t) u_t
+//
+// i.e. the Mamba-2 step with x -> u, B -> k, dt -> 1 and log-decay log alpha.
+// The ring keeps (k_j, u_j, log alpha_j) (with dt = 1 stored beside it), so the
+// Mamba-2 flush kernel folds a GDN window unchanged. Replay forms
+//   S_{t-1} z = exp(Lam) S_c z + sum_j exp(lam_j) (k_j . z) u_j   for z = k_t, q_t
+// in one pass over the checkpoint tile (two row dots per row), with
+// lam_j = sum of log alpha over the window entries after j, Lam over all of them.
+#include "device.h"
+#include "launch.h"
+
+namespace rss {
+
+// Dynamic LDS of the GDN replay kernel, in floats.
+struct GdnLds {
+  int oK, oU, oQ, oCF, oS, total;
+  __host__ __device__ GdnLds(int R, int P, int N) {
+    oK = 0;                   // window k rows [R][N] (row n0 = k_t)
+    oU = R * N;               // window u rows [R][P]
+    oQ = oU + R * P;          // q_t [N]
+    oCF = oQ + N;             // exp(lam_j) [R], then exp(Lam), k_t . q_t
+    oS = align4(oCF + R + 2); // shares [4 waves][2][P]: sum_j w u_j for z = k_t, q_t
+    total = oS + 8 * P;
+  }
+};
+
+template <int N, int MP>
+__global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
+  using Geo = TileGeom<N, false>;
+  constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
+  constexpr int NV = N / 4;
+  constexpr int EPL = N >= 64 ? N / 64 : 1;
+  using RS = RowScatter<TPR>;
+  static_assert(MP % 8 == 0, "passes come in groups of 8");
+
+  extern __shared__ __align__(16) float lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H, P = a.P, R = a.R;
+  const int bh = blockIdx.x;
+
+  const float* tile = a.ckpt + (size_t)bh * P * N;
+  const int col = tid % TPR, rsub = tid / TPR;
+  const int toff = rsub * N + col * 4;
+  Frag<false> fr[MP];
+  auto load_chunk = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < MP; ++k) {
+      const int r0 = base + k * RPP;
+      if (r0 + RPP <= P) fr[k].v = ld16(tile + r0 * N + toff);
+      else if (r0 + rsub < P) fr[k].v = ld16(tile + r0 * N + toff);
+      else fr[k].v = float4{};
+    }
+  };
+  load_chunk(0);
+  const float alpha = a.alpha[bh], beta = a.beta[bh];
+
+  const int4 pt = a.ptr[bh];
+  const int head = pt.x, n0 = pt.y;
+  const int L = n0 + 1;
+  float* oout = a.o + (size_t)bh * P;
+  if (head < 0 || head >= R || n0 < 0 || L > R) {  // ring full (no flush), or corrupt pointers
+    if (tid == 0) atomicOr(a.err, kDevRingOverflow);
+    for (int p = tid; p < P; p += kThreads) oout[p] = __builtin_nanf("");
+    return;
+  }
+
+  const GdnLds lay(R, P, N);
+  float* sK = lds + lay.oK;
+  float* sU = lds + lay.oU;
+  float* sQ = lds + lay.oQ;
+  float* sCF = lds + lay.oCF;
+  float* sS = lds + lay.oS;
+  float* ru = a.ring_u + (size_t)bh * R * P;
+  float* rk = a.ring_k + (size_t)bh * R * N;
+  float2* rdl = a.ring_dl + (size_t)bh * R;
+  const float* kin = a.k + (size_t)bh * N;
+  const float* qin = a.q + (size_t)bh * N;
+  const float* vin = a.v + (size_t)bh * P;
+
+  // Window k rows (ring, then k_t as row n0) and u rows straight into LDS;
+  // q_t and the log-decays through registers.
+  const int totK = L * NV;
+  for (int q0 = wave * 64; q0 < totK; q0 += kThreads) {
+    const int q = q0 + lane;
+    if (q < totK) {
+      const int j = q / NV;
+      const float* src = j < n0 ? rk + ring_slot(head, j, R) * N : kin;
+      dma16(src + (q - j * NV) * 4, sK + q0 * 4);
+    }
+  }
+  const bool uvec = (P % 4) == 0;
+  if (uvec) {
+    const int PV = P / 4, totU = n0 * PV;
+    for (int q0 = wave * 64; q0 < totU; q0 += kThreads) {
+      const int q = q0 + lane;
+      if (q < totU) {
+        const int j = q / PV;
+        dma16(ru + ring_slot(head, j, R) * P + (q - j * PV) * 4, sU + q0 * 4);
+      }
+    }
+  }
+  float qv = 0.f;
+  if (tid < N) qv = qin[tid];
+  float2 dl = make_float2(0.f, 0.f);
+  if (tid < n0) dl = rdl[ring_slot(head, tid, R)];
+  if (!uvec) {
+    for (int e = tid; e < n0 * P; e += kThreads) {
+      const int j = e / P;
+      sU[e] = ru[ring_slot(head, j, R) * P + (e - j * P)];
+    }
+  }
+  if (tid < N) sQ[tid] = qv;
+  if (wave == 0) {  // exp(lam_j) over the committed entries, and exp(Lam)
+    const float u = lane < n0 ? dl.y : 0.f;
+    const float lam = wave_suffix_excl(u, lane);
+    if (lane < n0) sCF[lane] = expf(lam);
+    if (lane == 0) sCF[R] = expf(lam + u);
+    if (lane == 0) rdl[ring_slot(head, n0, R)] = make_float2(1.f, logf(alpha));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // k_t . q_t, and per wavefront its share of sum_j exp(lam_j)(k_j . z) u_j.
+  if (wave == 0) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int n = lane * EPL + e;
+      if (n < N) part = fmaf(sK[n0 * N + n], sQ[n], part);
+    }
+    part = wave_sum(part);
+    if (lane == 0) sCF[R + 1] = part;
+  }
+  {
+    constexpr int kRowsPerLane = kMaxP / 64;
+    float shk[kRowsPerLane] = {}, shq[kRowsPerLane] = {};
+    for (int j = wave; j < n0; j += kWaves) {
+      float pk = 0.f, pq = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int n = lane * EPL + e;
+        if (n < N) {
+          const float kj = sK[j * N + n];
+          pk = fmaf(kj, sK[n0 * N + n], pk);
+          pq = fmaf(kj, sQ[n], pq);
+        }
+      }
+      const float c = sCF[j];
+      const float wk = c * wave_sum(pk), wq = c * wave_sum(pq);
+#pragma unroll
+      for (int r = 0; r < kRowsPerLane; ++r) {
+        if (r * 64 + lane < P) {
+          const float uj = sU[j * P + r * 64 + lane];
+          shk[r] = fmaf(wk, uj, shk[r]);
+          shq[r] = fmaf(wq, uj, shq[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerLane; ++r) {
+      if (r * 64 + lane < P) {
+        sS[(wave * 2 + 0) * P + r * 64 + lane] = shk[r];
+        sS[(wave * 2 + 1) * P + r * 64 + lane] = shq[r];
+      }
+    }
+  }
+  // k_t into the ring (every head owns its k)
+  for (int q = tid; q < NV; q += kThreads)
+    *reinterpret_cast<float4*>(rk + ring_slot(head, n0, R) * N + q * 4) =
+        *reinterpret_cast<const float4*>(sK + n0 * N + q * 4);
+  __syncthreads();
+
+  const float D = sCF[R], kq = sCF[R + 1];
+  float kc[4], qc[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    kc[v] = sK[n0 * N + col * 4 + v];
+    qc[v] = sQ[col * 4 + v];
+  }
+  float* unew = ru + ring_slot(head, n0, R) * P;
+  for (int base = 0; base < P; base += RPP * MP) {
+    if (base > 0) load_chunk(base);
+#pragma unroll
+    for (int g8 = 0; g8 < MP; g8 += 8) {
+      if (base + g8 * RPP >= P) break;
+      float pk[8], pq[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 s = fr[g8 + k].v;
+        pk[k] = fmaf(s.w, kc[3], fmaf(s.z, kc[2], fmaf(s.y, kc[1], s.x * kc[0])));
+        pq[k] = fmaf(s.w, qc[3], fmaf(s.z, qc[2], fmaf(s.y, qc[1], s.x * qc[0])));
+      }
+      int kb1, kb2;
+      RS::run(pk, col, kb1);
+      RS::run(pq, col, kb2);
+      if ((col & RS::WMASK) == 0) {
+#pragma unroll
+        for (int m = 0; m < RS::NOUT; ++m) {
+          const int row = base + (g8 + kb1 + m) * RPP + rsub;
+          if (row < P) {
+            const float rk_ = (sS[0 * P + row] + sS[2 * P + row]) + (sS[4 * P + row] + sS[6 * P + row]);
+            const float rq_ = (sS[1 * P + row] + sS[3 * P + row]) + (sS[5 * P + row] + sS[7 * P + row]);
+            const float Sk = fmaf(D, pk[m], rk_);
+            const float Sq = fmaf(D, pq[m], rq_);
+            const float u = beta * (vin[row] - alpha * Sk);
+            unew[row] = u;
+            oout[row] = fmaf(alpha, Sq, kq * u);
+          }
+        }
+      }
+    }
+  }
+  if (tid == 0) a.ptr[bh] = make_int4(head, L, 0, 0);
+}
+
+// Eager gated delta rule: S <- alpha S + u k^T with u = beta (v - alpha S k),
+// o = alpha (S q) + (k . q) u, on the state in place.
+template <int N, int MP>
+__global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
+  using Geo = TileGeom<N, false>;
+  constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
+  constexpr int EPL = N >= 64 ? N / 64 : 1;
+  using RS = RowScatter<TPR>;
+
+  extern __shared__ __align__(16) float lds[];  // k [N], q [N], u [P], k.q
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = a.P;
+  const int bh = blockIdx.x;
+  float* tile = a.S + (size_t)bh * P * N;
+  const int col = tid % TPR, rsub = tid / TPR;
+  const int toff = rsub * N + col * 4;
+  Frag<false> fr[MP];
+  auto load_chunk = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < MP; ++k) {
+      const int r0 = base + k * RPP;
+      if (r0 + RPP <= P) fr[k].v = ld16(tile + r0 * N + toff);
+      else if (r0 + rsub < P) fr[k].v = ld16(tile + r0 * N + toff);
+      else fr[k].v = float4{};
+    }
+  };
+  load_chunk(0);
+  const float alpha = a.alpha[bh], beta = a.beta[bh];
+  float* sk = lds;
+  float* sq = lds + N;
+  float* su = lds + 2 * N;
+  float* skq = su + P;
+  for (int n = tid; n < N; n += kThreads) {
+    sk[n] = a.k[(size_t)bh * N + n];
+    sq[n] = a.q[(size_t)bh * N + n];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int n = lane * EPL + e;
+      if (n < N) part = fmaf(sk[n], sq[n], part);
+    }
+    part = wave_sum(part);
+    if (lane == 0) *skq = part;
+  }
+  float kc[4], qc[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    kc[v] = sk[col * 4 + v];
+    qc[v] = sq[col * 4 + v];
+  }
+  const float* vin = a.v + (size_t)bh * P;
+  float* oout = a.o + (size_t)bh * P;
+  for (int base = 0; base < P; base += RPP * MP) {
+    if (base > 0) load_chunk(base);
+    __syncthreads();  // k . q ready; earlier readers of su are done
+    const float kq = *skq;
+#pragma unroll
+    for (int g8 = 0; g8 < MP; g8 += 8) {
+      if (base + g8 * RPP >= P) break;
+      float pk[8], pq[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 s = fr[g8 + k].v;
+        pk[k] = fmaf(s.w, kc[3], fmaf(s.z, kc[2], fmaf(s.y, kc[1], s.x * kc[0])));
+        pq[k] = fmaf(s.w, qc[3], fmaf(s.z, qc[2], fmaf(s.y, qc[1], s.x * qc[0])));
+      }
+      int kb1, kb2;
+      RS::run(pk, col, kb1);
+      RS::run(pq, col, kb2);
+      if ((col & RS::WMASK) == 0) {
+#pragma unroll
+        for (int m = 0; m < RS::NOUT; ++m) {
+          const int row = base + (g8 + kb1 + m) * RPP + rsub;
+          if (row < P) {
+            const float u = beta * (vin[row] - alpha * pk[m]);
+            su[row] = u;
+            oout[row] = fmaf(alpha, pq[m], kq * u);
+          }
+        }
+      }
+    }
+    __syncthreads();  // u of every row in this chunk is in LDS
+#pragma unroll
+    for (int k = 0; k < MP; ++k) {
+      const int row = base + k * RPP + rsub;
+      if (row < P) {
+        const float u = su[row];
+        float4 s = fr[k].v;
+        s.x = fmaf(u, kc[0], alpha * s.x);
+        s.y = fmaf(u, kc[1], alpha * s.y);
+        s.z = fmaf(u, kc[2], alpha * s.z);
+        s.w = fmaf(u, kc[3], alpha * s.w);
+        st16(tile + row * N + col * 4, s);
+      }
+    }
+  }
+}
+
+template <int N, int MP>
+static hipError_t gdn_replay_one(const GdnArgs& a, int batch, hipStream_t s) {
+  const size_t lds = (size_t)GdnLds(a.R, a.P, N).total * sizeof(float);
+  auto kern = gdn_replay_kernel<N, MP>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)batch * a.H)), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int N>
+static hipError_t gdn_replay_n(const GdnArgs& a, int batch, hipStream_t s) {
+  constexpr int RPP = TileGeom<N, false>::RPP;
+  return a.P > 8 * RPP ? gdn_replay_one<N, 16>(a, batch, s) : gdn_replay_one<N, 8>(a, batch, s);
+}
+
+hipError_t launch_gdn_replay(const GdnArgs& a, int batch, int N, hipStream_t s) {
+  switch (N) {
+    case 16: return gdn_replay_n<16>(a, batch, s);
+    case 32: return gdn_replay_n<32>(a, batch, s);
+    case 64: return gdn_replay_n<64>(a, batch, s);
+    case 128: return gdn_replay_n<128>(a, batch, s);
+    case 256: return gdn_replay_n<256>(a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int N, int MP>
+static hipError_t gdn_eager_one(const GdnEagerArgs& a, int batch, hipStream_t s) {
+  const size_t lds = (size_t)(2 * N + a.P + 1) * sizeof(float);
+  hipLaunchKernelGGL((gdn_eager_kernel<N, MP>), dim3((unsigned)((size_t)batch * a.H)),
+                     dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int N>
+static hipError_t gdn_eager_n(const GdnEagerArgs& a, int batch, hipStream_t s) {
+  constexpr int RPP = TileGeom<N, false>::RPP;
+  return a.P > 8 * RPP ? gdn_eager_one<N, 16>(a, batch, s) : gdn_eager_one<N, 8>(a, batch, s);
+}
+
+hipError_t launch_gdn_eager(const GdnEagerArgs& a, int batch, int N, hipStream_t s) {
+  switch (N) {
+    case 16: return gdn_eager_n<16>(a, batch, s);
+    case 32: return gdn_eager_n<32>(a, batch, s);
+    case 64: return gdn_eager_n<64>(a, batch, s);
+    case 128: return gdn_eager_n<128>(a, batch, s);
+    case 256: return gdn_eager_n<256>(a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rss

@@ -83,4 +83,34 @@ struct EagerArgs {
 };
 hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, hipStream_t s);
 
+// Gated DeltaNet replay decode (one token) and its eager baseline.
+struct GdnArgs {
+  float* ckpt;             // [Bt,H,P,N] fp32, P = d_v, N = d_k
+  float* ring_u;           // [Bt,H,R,P]
+  float* ring_k;           // [Bt,H,R,N]
+  float2* ring_dl;         // [Bt,H,R] (1, log alpha)
+  int4* ptr;               // [Bt,H]
+  int* err;
+  const float* q;          // [Bt,H,N]
+  const float* k;          // [Bt,H,N]
+  const float* v;          // [Bt,H,P]
+  const float* beta;       // [Bt,H]
+  const float* alpha;      // [Bt,H]
+  float* o;                // [Bt,H,P]
+  int H, P, R;
+};
+hipError_t launch_gdn_replay(const GdnArgs& a, int batch, int N, hipStream_t s);
+
+struct GdnEagerArgs {
+  float* S;                // [Bt,H,P,N], updated in place
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* beta;
+  const float* alpha;
+  float* o;
+  int H, P;
+};
+hipError_t launch_gdn_eager(const GdnEagerArgs& a, int batch, int N, hipStream_t s);
+
 }  // namespace rss

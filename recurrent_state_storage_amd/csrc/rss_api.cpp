@@ -35,6 +35,12 @@ int32_t check_config(const rss_config* c) {
   int32_t st = check_shape(c);
   if (st) return st;
   if (c->read_copy != RSS_COPY_NONE && c->read_copy != RSS_COPY_BF16) return RSS_E_DTYPE;
+  if (c->kind != RSS_KIND_MAMBA2 && c->kind != RSS_KIND_GDN) return RSS_E_INVALID;
+  if (c->kind == RSS_KIND_GDN) {  // one key per head, fp32, no read copy, no drafts
+    if (c->ngroups != c->nheads) return RSS_E_SHAPE;
+    if (c->in_dtype != RSS_DTYPE_F32 || c->read_copy != RSS_COPY_NONE) return RSS_E_DTYPE;
+    if (c->max_draft != 0) return RSS_E_CAPACITY;
+  }
   if (c->window < 1 || c->capacity < c->window || c->capacity > rss::kMaxRing) return RSS_E_SHAPE;
   if (c->max_draft < 0 || c->max_draft > rss::kMaxNew - 1) return RSS_E_CAPACITY;
   if (c->capacity < c->window + c->max_draft) return RSS_E_CAPACITY;
@@ -54,7 +60,7 @@ bool inputs_ok(const void* x, const void* B, const void* C, const void* dt, cons
 
 extern "C" {
 
-int32_t rss_version(void) { return 10000; }
+int32_t rss_version(void) { return 10100; }
 
 const char* rss_status_string(int32_t s) {
   switch (s) {
@@ -81,7 +87,7 @@ int32_t rss_buffer_sizes(const rss_config* c, rss_sizes* out) {
   out->ring_B = Bt * G * R * N * in_bytes(c);
   out->ring_dl = Bt * H * R * 2 * 4;
   out->ptr = Bt * H * 4 * 4;
-  out->A = H * 4;
+  out->A = c->kind == RSS_KIND_GDN ? 0 : H * 4;
   out->dev_err = 4;
   return RSS_OK;
 }
@@ -92,7 +98,8 @@ int32_t rss_layer_bind(const rss_config* c, const rss_buffers* d, rss_layer** ou
   const int32_t st = check_config(c);
   if (st) return st;
   if (!d) return RSS_E_INVALID;
-  if (!d->A || !aligned16(d->A) || !d->dev_err || !aligned16(d->dev_err)) return RSS_E_INVALID;
+  if (!d->dev_err || !aligned16(d->dev_err)) return RSS_E_INVALID;
+  if (c->kind == RSS_KIND_MAMBA2 && (!d->A || !aligned16(d->A))) return RSS_E_INVALID;
   if (c->batch > 0) {  // with no sequences the per-sequence buffers may be empty (NULL)
     const void* req[] = {d->ckpt, d->ring_x, d->ring_B, d->ring_dl, d->ptr};
     for (const void* p : req)
@@ -166,7 +173,7 @@ static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len,
 
 int32_t rss_decode_step(rss_layer* l, const void* x, const void* B, const void* C, const float* dt,
                         float* y, void* stream) {
-  if (!l) return RSS_E_INVALID;
+  if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
   if (l->pending_verify) return RSS_E_ORDER;
   return replay_call(l, 1, 0, 0, x, B, C, dt, y, stream);
@@ -174,7 +181,7 @@ int32_t rss_decode_step(rss_layer* l, const void* x, const void* B, const void* 
 
 int32_t rss_decode_flush_step(rss_layer* l, int32_t min_len, const void* x, const void* B,
                               const void* C, const float* dt, float* y, void* stream) {
-  if (!l) return RSS_E_INVALID;
+  if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
   if (min_len < 1) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
   if (l->pending_verify) return RSS_E_ORDER;
@@ -187,7 +194,7 @@ int32_t rss_decode_flush_step(rss_layer* l, int32_t min_len, const void* x, cons
 
 int32_t rss_verify_k_tokens(rss_layer* l, int32_t K, const void* x, const void* B, const void* C,
                             const float* dt, float* y, void* stream) {
-  if (!l) return RSS_E_INVALID;
+  if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
   if (K < 0) return RSS_E_INVALID;
   if (K > l->cfg.max_draft) return RSS_E_CAPACITY;
@@ -235,6 +242,56 @@ int32_t rss_flush_checkpoint(rss_layer* l, int32_t min_len, void* stream) {
   return launch_status(rss::launch_flush(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
                                          c.read_copy == RSS_COPY_BF16,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int32_t rss_gdn_decode_step(rss_layer* l, const float* q, const float* k, const float* v,
+                            const float* beta, const float* alpha, float* o, void* stream) {
+  if (!l || l->cfg.kind != RSS_KIND_GDN) return RSS_E_INVALID;
+  const rss_config& c = l->cfg;
+  if (c.batch > 0 && (!inputs_ok(q, k, v, beta, o) || !alpha || !aligned16(alpha)))
+    return RSS_E_INVALID;
+  if (l->pending_verify) return RSS_E_ORDER;
+  if (c.batch == 0) return RSS_OK;
+  rss::GdnArgs a;
+  a.ckpt = l->dev.ckpt;
+  a.ring_u = static_cast<float*>(l->dev.ring_x);
+  a.ring_k = static_cast<float*>(l->dev.ring_B);
+  a.ring_dl = reinterpret_cast<float2*>(l->dev.ring_dl);
+  a.ptr = reinterpret_cast<int4*>(l->dev.ptr);
+  a.err = l->dev.dev_err;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.o = o;
+  a.H = c.nheads;
+  a.P = c.headdim;
+  a.R = c.capacity;
+  return launch_status(rss::launch_gdn_replay(a, c.batch, c.dstate, static_cast<hipStream_t>(stream)));
+}
+
+int32_t rss_gdn_eager_step(const rss_config* c, float* S, const float* q, const float* k,
+                           const float* v, const float* beta, const float* alpha, float* o,
+                           void* stream) {
+  if (!c) return RSS_E_INVALID;
+  if (c->batch < 0 || c->nheads < 1 || c->headdim < 1 || c->headdim > rss::kMaxP) return RSS_E_SHAPE;
+  if (!supported_n(c->dstate)) return RSS_E_SHAPE;
+  if ((int64_t)c->batch * c->nheads > 0x7fffffffLL) return RSS_E_SHAPE;
+  if (c->batch == 0) return RSS_OK;
+  if (!S || !aligned16(S) || !inputs_ok(q, k, v, beta, o) || !alpha || !aligned16(alpha))
+    return RSS_E_INVALID;
+  rss::GdnEagerArgs a;
+  a.S = S;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.o = o;
+  a.H = c->nheads;
+  a.P = c->headdim;
+  return launch_status(rss::launch_gdn_eager(a, c->batch, c->dstate, static_cast<hipStream_t>(stream)));
 }
 
 int32_t rss_get_device_error(rss_layer* l, int32_t* host_code, void* stream) {

@@ -24,6 +24,7 @@ RSS_OK, RSS_E_INVALID, RSS_E_SHAPE, RSS_E_DTYPE, RSS_E_CAPACITY, RSS_E_ORDER, RS
 RSS_DTYPE_F32, RSS_DTYPE_BF16 = 0, 1
 RSS_COPY_NONE, RSS_COPY_BF16 = 0, 1
 RSS_DEV_ROLLBACK_RANGE, RSS_DEV_RING_OVERFLOW, RSS_DEV_UNCOMMITTED = 1, 2, 4
+RSS_KIND_MAMBA2, RSS_KIND_GDN = 0, 1
 
 _I32 = ctypes.c_int32
 _VP = ctypes.c_void_p
@@ -31,7 +32,7 @@ _VP = ctypes.c_void_p
 
 class rss_config(ctypes.Structure):
     _fields_ = [(n, _I32) for n in ("batch", "nheads", "headdim", "dstate", "ngroups", "window",
-                                     "capacity", "max_draft", "in_dtype", "read_copy")]
+                                     "capacity", "max_draft", "in_dtype", "read_copy", "kind")]
 
 
 class rss_buffers(ctypes.Structure):
@@ -58,6 +59,9 @@ _SIGS = {
     "rss_verify_k_tokens": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_rollback": ([_VP, _VP, _VP], _I32),
     "rss_get_device_error": ([_VP, ctypes.POINTER(_I32), _VP], _I32),
+    "rss_gdn_decode_step": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
+    "rss_gdn_eager_step": ([ctypes.POINTER(rss_config), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+                           _I32),
     "rss_eager_step": ([ctypes.POINTER(rss_config), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
                        _I32),
     "rss_eager_verify": ([ctypes.POINTER(rss_config), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
@@ -137,9 +141,9 @@ def _in_dtype(code: int):
 
 
 def make_config(batch, nheads, headdim, dstate, ngroups, window, capacity, max_draft=0,
-                in_dtype=RSS_DTYPE_F32, read_copy=RSS_COPY_NONE) -> rss_config:
+                in_dtype=RSS_DTYPE_F32, read_copy=RSS_COPY_NONE, kind=RSS_KIND_MAMBA2) -> rss_config:
     return rss_config(batch, nheads, headdim, dstate, ngroups, window, capacity, max_draft,
-                      in_dtype, read_copy)
+                      in_dtype, read_copy, kind)
 
 
 # ---- the C calls, one wrapper each -------------------------------------------
@@ -168,7 +172,7 @@ class ReplayLayer:
     """One SSM layer's decode state on a device: checkpoint (+ bf16 read copy),
     input ring and pointers, allocated with torch, bound to a librss handle."""
 
-    def __init__(self, cfg: rss_config, A: torch.Tensor, device="cuda"):
+    def __init__(self, cfg: rss_config, A, device="cuda"):
         self.cfg = cfg
         c = cfg
         dev = torch.device(device)
@@ -183,12 +187,14 @@ class ReplayLayer:
         self.ring_dl = torch.zeros((c.batch, c.nheads, c.capacity, 2), dtype=torch.float32, device=dev)
         self.ptr = torch.zeros((c.batch, c.nheads, 4), dtype=torch.int32, device=dev)
         self.A = A
-        _ptr(A, torch.float32, (c.nheads,), "A")
+        if c.kind == RSS_KIND_MAMBA2 or A is not None:
+            _ptr(A, torch.float32, (c.nheads,), "A")
         self.dev_err = torch.zeros((4,), dtype=torch.int32, device=dev)
         bufs = rss_buffers(self.ckpt.data_ptr(),
                            self.ckpt_lo.data_ptr() if self.ckpt_lo is not None else None,
                            self.ring_x.data_ptr(), self.ring_B.data_ptr(), self.ring_dl.data_ptr(),
-                           self.ptr.data_ptr(), A.data_ptr(), self.dev_err.data_ptr())
+                           self.ptr.data_ptr(), A.data_ptr() if A is not None else None,
+                           self.dev_err.data_ptr())
         self.handle = rss_layer_bind(cfg, bufs)
 
     def __del__(self):
@@ -220,6 +226,9 @@ class ReplayLayer:
 
     def rollback(self, n_drop, stream=None):
         rss_rollback(self, n_drop, stream)
+
+    def gdn_decode_step(self, q, k, v, beta, alpha, o, stream=None):
+        rss_gdn_decode_step(self, q, k, v, beta, alpha, o, stream)
 
     def device_error(self, stream=None) -> int:
         return rss_get_device_error(self, stream)
@@ -308,3 +317,22 @@ def rss_eager_verify(cfg: rss_config, pool, src_slot, K, x, B, C, dt, A, y, stre
             _ptr(y, torch.float32, lead + (c.nheads, c.headdim), "y"))
     _check(library().rss_eager_verify(ctypes.byref(cfg), *args, _stream(stream)),
            "rss_eager_verify")
+
+
+def rss_gdn_decode_step(layer: ReplayLayer, q, k, v, beta, alpha, o, stream=None) -> None:
+    c = layer.cfg
+    kn, vp, bh = (c.batch, c.nheads, c.dstate), (c.batch, c.nheads, c.headdim), (c.batch, c.nheads)
+    f = torch.float32
+    args = (_ptr(q, f, kn, "q"), _ptr(k, f, kn, "k"), _ptr(v, f, vp, "v"), _ptr(beta, f, bh, "beta"),
+            _ptr(alpha, f, bh, "alpha"), _ptr(o, f, vp, "o"))
+    _check(library().rss_gdn_decode_step(layer.handle, *args, _stream(stream)), "rss_gdn_decode_step")
+
+
+def rss_gdn_eager_step(cfg: rss_config, S, q, k, v, beta, alpha, o, stream=None) -> None:
+    c = cfg
+    kn, vp, bh = (c.batch, c.nheads, c.dstate), (c.batch, c.nheads, c.headdim), (c.batch, c.nheads)
+    f = torch.float32
+    args = (_ptr(S, f, (c.batch, c.nheads, c.headdim, c.dstate), "S"), _ptr(q, f, kn, "q"),
+            _ptr(k, f, kn, "k"), _ptr(v, f, vp, "v"), _ptr(beta, f, bh, "beta"),
+            _ptr(alpha, f, bh, "alpha"), _ptr(o, f, vp, "o"))
+    _check(library().rss_gdn_eager_step(ctypes.byref(cfg), *args, _stream(stream)), "rss_gdn_eager_step")

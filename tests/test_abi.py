@@ -12,7 +12,8 @@ from recurrent_state_storage_amd import rss
 
 def _cfg(**kw):
     base = dict(batch=4, nheads=8, headdim=64, dstate=128, ngroups=8, window=16, capacity=20,
-                max_draft=4, in_dtype=rss.RSS_DTYPE_BF16, read_copy=rss.RSS_COPY_NONE)
+                max_draft=4, in_dtype=rss.RSS_DTYPE_BF16, read_copy=rss.RSS_COPY_NONE,
+                kind=rss.RSS_KIND_MAMBA2)
     base.update(kw)
     return rss.rss_config(**base)
 
@@ -39,14 +40,14 @@ def _bind(cfg, bufs):
 def test_library_exports_every_declared_symbol():
     lib = rss.library()
     syms = rss.declared_symbols()
-    assert len(syms) >= 14
+    assert len(syms) >= 16
     for s in syms:
         assert hasattr(lib, s), s
     assert set(syms) == set(rss._SIGS), "binding and header disagree"
 
 
 def test_version_and_status_strings():
-    assert rss.rss_version() == 10000
+    assert rss.rss_version() == 10100
     for s in range(7):
         assert rss.status_string(s)
     assert rss.status_string(99) == "unknown status"
@@ -80,6 +81,12 @@ def test_buffer_sizes():
     (dict(max_draft=-1), rss.RSS_E_CAPACITY),
     (dict(in_dtype=7), rss.RSS_E_DTYPE),
     (dict(read_copy=3), rss.RSS_E_DTYPE),
+    (dict(kind=2), rss.RSS_E_INVALID),
+    (dict(kind=rss.RSS_KIND_GDN, ngroups=4, max_draft=0, in_dtype=rss.RSS_DTYPE_F32), rss.RSS_E_SHAPE),
+    (dict(kind=rss.RSS_KIND_GDN, max_draft=0), rss.RSS_E_DTYPE),
+    (dict(kind=rss.RSS_KIND_GDN, max_draft=0, in_dtype=rss.RSS_DTYPE_F32,
+          read_copy=rss.RSS_COPY_BF16), rss.RSS_E_DTYPE),
+    (dict(kind=rss.RSS_KIND_GDN, in_dtype=rss.RSS_DTYPE_F32), rss.RSS_E_CAPACITY),
 ])
 def test_config_validation(kw, status):
     cfg = _cfg(**kw)
@@ -101,6 +108,28 @@ def test_bind_pointer_checks():
     assert rss.library().rss_layer_free(h) == rss.RSS_OK
     assert rss.library().rss_layer_free(None) == rss.RSS_OK
     assert rss.library().rss_layer_bind(ctypes.byref(cfg), None, None) == rss.RSS_E_INVALID
+
+
+def test_gdn_layer_calls_are_kind_checked():
+    gcfg = _cfg(kind=rss.RSS_KIND_GDN, max_draft=0, in_dtype=rss.RSS_DTYPE_F32)
+    s = rss.rss_buffer_sizes(gcfg)
+    assert s.A == 0 and s.ring_x == 4 * 8 * 20 * 64 * 4 and s.ring_B == 4 * 8 * 20 * 128 * 4
+    st, h = _bind(gcfg, _fake_bufs(gcfg, null="A"))        # A is not needed for GDN
+    assert st == rss.RSS_OK
+    lib = rss.library()
+    A = 0x7000000
+    try:
+        assert lib.rss_decode_step(h, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_verify_k_tokens(h, 0, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_gdn_decode_step(h, None, A, A, A, A, A, None) == rss.RSS_E_INVALID
+    finally:
+        lib.rss_layer_free(h)
+    st, h = _bind(_cfg(), _fake_bufs(_cfg()))
+    try:
+        assert lib.rss_gdn_decode_step(h, A, A, A, A, A, A, None) == rss.RSS_E_INVALID
+    finally:
+        lib.rss_layer_free(h)
+    assert lib.rss_gdn_eager_step(ctypes.byref(gcfg), None, A, A, A, A, A, A, None) == rss.RSS_E_INVALID
 
 
 def test_call_order_and_argument_errors_return_before_launch():
