@@ -290,6 +290,89 @@ def run_spec(torch, rss, dev, rounds, warmup, workers, distinct=6):
             "eager_verify_GBps": ebytes / (e_ms / rounds / 1e3) / 1e9}
 
 
+def gdn_bytes(wl, n0: int) -> dict:
+    """Algorithmic bytes per (sequence, head) of the GDN kernels (fp32)."""
+    P, N = wl.headdim, wl.dstate
+    entry = 4 * N + 4 * P + 8                       # k, u, (1, log alpha)
+    inputs = 4 * N * 2 + 4 * P + 8                  # q, k, v, beta, alpha
+    return {"replay": P * N * 4 + n0 * entry + inputs + 4 * P + entry + 32,
+            "flush": 2 * P * N * 4 + wl.window * entry + 32,
+            "eager": 2 * P * N * 4 + inputs + 4 * P}
+
+
+def _gen_gdn(args):
+    name, t = args
+    s = synth.gdn_step_inputs(workloads.get(name), t)
+    return t, s
+
+
+def run_gdn(torch, rss, dev, steps, warmup, workers, distinct=64):
+    """Gated DeltaNet decode at batch 256, 32 heads, d_k = d_v = 128: replay
+    (+ flush every W) against the eager gated-delta-rule kernel."""
+    wl = workloads.get("gdn_b256_h32_d128_w16")
+    Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
+    with concurrent.futures.ProcessPoolExecutor(max_workers=min(workers, 16)) as ex:
+        got = sorted(ex.map(_gen_gdn, [(wl.name, t) for t in range(distinct)]), key=lambda g: g[0])
+    D = [{k: torch.from_numpy(v).to(dev) for k, v in g[1].items()} for g in got]
+    cfg = rss.make_config(Bt, H, P, N, H, W, wl.capacity, 0, rss.RSS_DTYPE_F32, rss.RSS_COPY_NONE,
+                          rss.RSS_KIND_GDN)
+    layer = rss.ReplayLayer(cfg, None, dev)
+    layer.init_state()
+    o = torch.empty((Bt, H, P), device=dev)
+    evs = []
+
+    def step(k, rec=False):
+        d = D[k % distinct]
+        if rec:
+            evs.append([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+            evs[-1][0].record()
+        layer.gdn_decode_step(d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
+        if rec:
+            evs[-1][1].record()
+        if (k + 1) % W == 0:
+            if rec:
+                evs[-1][2].record()
+            layer.flush_checkpoint(W)
+            if rec:
+                evs[-1][3].record()
+    for k in range(warmup):
+        step(k)
+    ms = _timed(torch, lambda j: step(warmup + j), steps)
+    base = warmup + steps
+    for j in range(steps):
+        step(base + j, rec=True)
+    torch.cuda.synchronize()
+    r_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
+    f_list = [e[2].elapsed_time(e[3]) for j, e in enumerate(evs) if (base + j + 1) % W == 0]
+    rbytes = sum(gdn_bytes(wl, (base + j) % W)["replay"] for j in range(steps)) * Bt * H
+    assert layer.device_error() == 0
+    del layer
+    S = torch.zeros((Bt, H, P, N), device=dev)
+
+    def eager(k):
+        d = D[k % distinct]
+        rss.rss_gdn_eager_step(cfg, S, d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
+    for k in range(warmup):
+        eager(k)
+    ems = _timed(torch, lambda j: eager(warmup + j), steps)
+    eev = []
+    for j in range(steps):
+        eev.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+        eev[-1][0].record()
+        eager(j)
+        eev[-1][1].record()
+    torch.cuda.synchronize()
+    e_ms = sum(a.elapsed_time(b) for a, b in eev)
+    fb = gdn_bytes(wl, W)
+    return {"workload": wl.name, "replay_tokens_per_s": Bt * steps / (ms / 1e3),
+            "eager_tokens_per_s": Bt * steps / (ems / 1e3), "speedup": ems / ms,
+            "replay_avg_us": r_ms / steps * 1e3, "replay_GBps": rbytes / (r_ms / 1e3) / 1e9,
+            "flush_avg_us": sum(f_list) / max(len(f_list), 1) * 1e3,
+            "flush_GBps": fb["flush"] * Bt * H * len(f_list) / (sum(f_list) / 1e3) / 1e9 if f_list else None,
+            "eager_avg_us": e_ms / steps * 1e3,
+            "eager_GBps": fb["eager"] * Bt * H * steps / (e_ms / 1e3) / 1e9}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +570,8 @@ def main() -> int:
     if not args.no_extra:
         rec["dual_precision"] = run_dual(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
         rec["speculative"] = run_spec(torch, rss, dev, rounds=48, warmup=8, workers=workers)
+        rec["gated_deltanet"] = run_gdn(torch, rss, dev, steps=args.steps, warmup=args.warmup,
+                                        workers=workers)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, pool, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
