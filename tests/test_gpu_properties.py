@@ -1,0 +1,133 @@
+"""Property tests on random shapes (hypothesis) and checkpoint/resume.
+
+Random layer shapes within the documented limits, dtypes, read-copy mode,
+window, capacity and draft length: plain decode with the fused fold, a verify
+round with rollback, more decode — every output against the fp64 eager
+recurrence over the committed stream. Resume: the decode state is exactly the
+checkpoint (+ read copy), the ring and the pointers; copying them out to the
+host and into a fresh layer continues bit for bit."""
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, HealthCheck, strategies as st
+
+from oracle import mamba2
+import workloads
+from workloads import synth
+from recurrent_state_storage_amd import rss
+from gpu_util import DEV, cfg_of, dev_inputs, rel_l2, log
+
+pytestmark = pytest.mark.gpu
+
+BASE = workloads.get("tiny_b2_h4_p16_n16_w8")
+
+
+@st.composite
+def layer_shapes(draw):
+    N = draw(st.sampled_from([16, 32, 64, 128, 256]))
+    P = draw(st.integers(1, 160))
+    G = draw(st.sampled_from([1, 2, 3]))
+    H = G * draw(st.integers(1, 3))
+    W = draw(st.integers(1, 12))
+    K = draw(st.integers(0, 4))
+    R = W + K + draw(st.integers(0, 3))
+    idt = draw(st.sampled_from(["f32", "bf16"]))
+    copy = draw(st.sampled_from(["none", "bf16"]))
+    Bt = draw(st.integers(1, 3))
+    seed = draw(st.integers(0, 10**6))
+    return dict(batch=Bt, headdim=P, dstate=N, nheads=H, ngroups=G, window=W, capacity=R,
+                max_draft=K, draft=K, in_dtype=idt, read_copy=copy, seed=seed)
+
+
+@settings(max_examples=30, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(layer_shapes())
+def test_random_layers_match_oracle(shape):
+    wl = BASE.replace(name="prop", s0="normal", **shape)
+    log(f"[prop] {shape}")
+    cfg = cfg_of(wl)
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    S0 = synth.initial_state(wl)
+    L = rss.ReplayLayer(cfg, A, DEV)
+    L.init_state(torch.from_numpy(S0).to(DEV))
+    S = S0.astype(np.float64)
+    Bt, H, P, W, K = wl.batch, wl.nheads, wl.headdim, wl.window, wl.draft
+    tol = 1e-5 if wl.read_copy == "none" else 2e-2
+    ys, refs = [], []
+
+    def decode(t):
+        nonlocal S
+        s = synth.step_inputs(wl, t)
+        d = dev_inputs(s, wl.in_dtype)
+        y = torch.empty((Bt, H, P), device=DEV)
+        L.decode_flush_step(W, d["x"], d["B"], d["C"], d["dt"], y)
+        S, yr = mamba2.eager_step(S, A_np, s["x"], s["B"], s["C"], s["dt"])
+        ys.append(y.double().cpu().numpy().ravel())
+        refs.append(yr.ravel())
+
+    for t in range(W + 2):
+        decode(t)
+    rin = synth.draft_inputs(wl, 0)
+    nacc = synth.accepted_drafts(wl, 0)
+    d = dev_inputs(rin, wl.in_dtype)
+    y = torch.empty((Bt, K + 1, H, P), device=DEV)
+    L.verify_k_tokens(K, d["x"], d["B"], d["C"], d["dt"], y)
+    L.rollback(torch.from_numpy((K - nacc).astype(np.int32)).to(DEV))
+    L.flush_checkpoint(W)
+    states = []
+    Sr = S
+    for i in range(K + 1):
+        Sr, yr = mamba2.eager_step(Sr, A_np, rin["x"][:, i], rin["B"][:, i], rin["C"][:, i], rin["dt"][:, i])
+        states.append(Sr)
+        refs.append(yr.ravel())
+        ys.append(y[:, i].double().cpu().numpy().ravel())
+    S = np.stack([states[nacc[b]][b] for b in range(Bt)])
+    for t in range(W + 1):
+        decode(100 + t)
+    assert L.device_error() == 0
+    err = rel_l2(np.concatenate(ys), np.concatenate(refs))
+    assert err < tol, err
+
+
+def test_checkpoint_resume_is_bit_exact():
+    wl = BASE.replace(name="resume", batch=3, headdim=64, dstate=128, nheads=4, ngroups=2, window=8,
+                      capacity=12, max_draft=4, draft=4, in_dtype="bf16", read_copy="bf16",
+                      s0="normal", seed=7000)
+    cfg = cfg_of(wl)
+    A = torch.from_numpy(synth.params(wl)["A"]).to(DEV)
+    S0 = torch.from_numpy(synth.initial_state(wl)).to(DEV)
+    ref = rss.ReplayLayer(cfg, A, DEV)
+    ref.init_state(S0)
+    run = rss.ReplayLayer(cfg, A, DEV)
+    run.init_state(S0)
+    K = wl.draft
+
+    def drive(L, t0, t1):
+        out = []
+        for t in range(t0, t1):
+            if t % 5 == 3:        # a speculative round now and then
+                rin = dev_inputs(synth.draft_inputs(wl, t), "bf16")
+                y = torch.empty((wl.batch, K + 1, wl.nheads, wl.headdim), device=DEV)
+                L.verify_k_tokens(K, rin["x"], rin["B"], rin["C"], rin["dt"], y)
+                L.rollback(torch.from_numpy((K - synth.accepted_drafts(wl, t)).astype(np.int32)).to(DEV))
+                L.flush_checkpoint(wl.window)
+            else:
+                d = dev_inputs(synth.step_inputs(wl, t), "bf16")
+                y = torch.empty((wl.batch, wl.nheads, wl.headdim), device=DEV)
+                L.decode_flush_step(wl.window, d["x"], d["B"], d["C"], d["dt"], y)
+            out.append(y.cpu())
+        return out
+
+    y_ref = drive(ref, 0, 40)
+    y_a = drive(run, 0, 17)
+    saved = {k: getattr(run, k).cpu().clone() for k in ("ckpt", "ckpt_lo", "ring_x", "ring_B", "ring_dl", "ptr")}
+    del run
+    fresh = rss.ReplayLayer(cfg, A, DEV)
+    for k, v in saved.items():
+        getattr(fresh, k).copy_(v.to(DEV))
+    y_b = drive(fresh, 17, 40)
+    torch.cuda.synchronize()
+    for a, b in zip(y_ref, y_a + y_b):
+        assert torch.equal(a, b)
+    for k in saved:
+        assert torch.equal(getattr(ref, k), getattr(fresh, k)), k
