@@ -72,7 +72,21 @@ typedef enum rss_status {
 } rss_status;
 
 enum { RSS_DTYPE_F32 = 0, RSS_DTYPE_BF16 = 1 };
-enum { RSS_COPY_NONE = 0, RSS_COPY_BF16 = 1 };
+/* Checkpoint precision (rss_config.read_copy):
+ *   RSS_COPY_NONE   fp32 checkpoint, read and folded in fp32;
+ *   RSS_COPY_BF16   dual precision: fp32 master for the fold plus a bf16 copy
+ *                   for reads (P2, "Deux précisions pour le prix d'une");
+ *   RSS_STATE_BF16  a single bf16 checkpoint: read in bf16, folded in fp32
+ *                   from the bf16 values and rounded back to bf16 at every
+ *                   fold. This is the low-precision point the dual mode is
+ *                   measured against: a quantised state accumulates one
+ *                   rounding per rewrite (P1, "Trois ennuis nés de la même
+ *                   fusion"), and ReplaySSM rewrites it once per window
+ *                   instead of once per token (P1, "Tenir le journal plutôt
+ *                   que le solde"). `ckpt` then holds bf16 [Bt,H,P,N] and
+ *                   `ckpt_lo` is unused. For the eager entry points it means
+ *                   an eager state stored in bf16 (rounded every token). */
+enum { RSS_COPY_NONE = 0, RSS_COPY_BF16 = 1, RSS_STATE_BF16 = 2 };
 
 /* Layer types. A Gated DeltaNet layer (P1, "La fiche qu'on réécrit à chaque
  * token": GDN's delta-rule update has the same form) uses P = d_v, N = d_k,
@@ -97,13 +111,14 @@ typedef struct rss_config {
   int32_t capacity;  /* R: ring slots per (sequence, head)                   */
   int32_t max_draft; /* K_max                                                */
   int32_t in_dtype;  /* RSS_DTYPE_*: storage of x, B, C and their ring copies */
-  int32_t read_copy; /* RSS_COPY_*: RSS_COPY_BF16 = dual precision           */
+  int32_t read_copy; /* checkpoint precision: RSS_COPY_NONE / _BF16, RSS_STATE_BF16 */
   int32_t kind;      /* RSS_KIND_*: layer type                               */
 } rss_config;
 
 /*
  * Device buffers of one layer (all device pointers, caller-owned):
- *   ckpt     fp32 [Bt, H, P, N]   checkpoint S_c (the fp32 master)
+ *   ckpt     fp32 [Bt, H, P, N]   checkpoint S_c (the fp32 master); bf16
+ *                                 [Bt, H, P, N] when read_copy = RSS_STATE_BF16
  *   ckpt_lo  bf16 [Bt, H, P, N]   read copy; NULL unless read_copy = BF16
  *   ring_x   in_dtype [Bt, H, R, P]   buffered x_j
  *   ring_B   in_dtype [Bt, G, R, N]   buffered B_j (one copy per group)
@@ -117,7 +132,7 @@ typedef struct rss_config {
  *   dev_err  int32 [1]            sticky device error word
  */
 typedef struct rss_buffers {
-  float* ckpt;
+  void* ckpt;
   void* ckpt_lo;
   void* ring_x;
   void* ring_B;
@@ -152,7 +167,8 @@ int32_t rss_layer_bind(const rss_config* cfg, const rss_buffers* dev, rss_layer*
 int32_t rss_layer_free(rss_layer* layer);
 
 /* Start every sequence from S0 (device fp32 [Bt,H,P,N]; NULL = zeros): the
- * checkpoint becomes S0, the read copy RNE-bf16(S0), the rings empty
+ * checkpoint becomes S0 (RNE-bf16(S0) when read_copy = RSS_STATE_BF16), the
+ * read copy RNE-bf16(S0), the rings empty
  * (head = len = n_tent = 0) and the device error word 0. The prefill that
  * produces S0 is outside this library. */
 int32_t rss_init_state(rss_layer* layer, const float* S0, void* stream);
@@ -175,8 +191,8 @@ int32_t rss_decode_step(rss_layer* layer, const void* x, const void* B, const vo
  * new checkpoint is written, so the flush's second read of the tile is saved
  * (the fold writes the state only once per window, P1 "Tenir le journal plutôt
  * que le solde"). Results equal the two separate calls bit for bit. With
- * read_copy = BF16 the replay reads the bf16 copy, so the fold (which needs the
- * fp32 master) runs as the separate flush launch. min_len >= 1; errors as
+ * read_copy = BF16 or RSS_STATE_BF16 the replay reads a bf16 tile, so the fold
+ * runs as the separate flush launch. min_len >= 1; errors as
  * rss_decode_step, plus RSS_DEV_UNCOMMITTED if a window to fold still holds
  * tentative entries (that sequence is then not folded). */
 int32_t rss_decode_flush_step(rss_layer* layer, int32_t min_len, const void* x, const void* B,
@@ -187,7 +203,9 @@ int32_t rss_decode_flush_step(rss_layer* layer, int32_t min_len, const void* x, 
  * rewritten only when the buffer is full; P3: once per window):
  *   S_c <- exp(Lam_c) S_c + sum_j exp(lam_j) dt_j outer(x_j, B_j)
  * then head <- (head + len) mod R, len <- 0, and in dual mode the read copy
- * becomes RNE-bf16 of the new fp32 master. Other sequences are untouched.
+ * becomes RNE-bf16 of the new fp32 master. With read_copy = RSS_STATE_BF16 the
+ * fold starts from the bf16 checkpoint's values (fp32 arithmetic) and stores
+ * RNE-bf16 of the result. Other sequences are untouched.
  * RSS_E_ORDER while a verify round is uncommitted. */
 int32_t rss_flush_checkpoint(rss_layer* layer, int32_t min_len, void* stream);
 
@@ -235,11 +253,16 @@ int32_t rss_get_device_error(rss_layer* layer, int32_t* host_code, void* stream)
 
 /* Eager baseline (P1, "La fiche qu'on réécrit à chaque token"): for T >= 1
  * tokens per sequence run S <- a S + dt outer(x,B), y = S @ C in order,
- * reading and writing the full state. S fp32 [Bt,H,P,N] is updated in place.
+ * reading and writing the full state. S fp32 [Bt,H,P,N] is updated in place;
+ * with cfg->read_copy = RSS_STATE_BF16, S is bf16 [Bt,H,P,N]: each token
+ * computes in fp32 from the stored bf16 values, takes y from the fp32 result
+ * and stores RNE-bf16 of it (the per-token rounding of a quantised eager
+ * state, P1 "Trois ennuis nés de la même fusion").
  * Layouts: x [Bt,T,H,P], B and C [Bt,T,G,N], dt [Bt,T,H], y [Bt,T,H,P]; A [H].
- * Uses cfg's batch, nheads, headdim, dstate, ngroups and in_dtype only.
+ * Uses cfg's batch, nheads, headdim, dstate, ngroups, in_dtype and read_copy
+ * (RSS_COPY_BF16 is treated as RSS_COPY_NONE: an eager state has no copy).
  * 1 <= T <= 8. */
-int32_t rss_eager_step(const rss_config* cfg, float* S, const void* x, const void* B,
+int32_t rss_eager_step(const rss_config* cfg, void* S, const void* x, const void* B,
                        const void* C, const float* dt, const float* A, float* y,
                        int32_t T, void* stream);
 
@@ -251,7 +274,8 @@ int32_t rss_eager_step(const rss_config* cfg, float* S, const void* x, const voi
  * before any write, so src_slot may be any slot). Rolling back to n_acc
  * accepted drafts is then "next round reads slot n_acc". Layouts as in
  * rss_eager_step with T = K+1; 0 <= K <= 7. An out-of-range src_slot[b]
- * writes NaN outputs for that sequence and leaves its slots unchanged. */
+ * writes NaN outputs for that sequence and leaves its slots unchanged.
+ * The pool is fp32 only: RSS_E_DTYPE if cfg->read_copy = RSS_STATE_BF16. */
 int32_t rss_eager_verify(const rss_config* cfg, float* pool, const int32_t* src_slot,
                          int32_t K, const void* x, const void* B, const void* C,
                          const float* dt, const float* A, float* y, void* stream);

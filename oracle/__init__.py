@@ -24,9 +24,10 @@ are not available). Citations name the page and the section on it:
 Modules:
   mamba2  eager recurrence (the reference result), its unrolled closed form and
           semiseparable matrix, the checkpoint + ring replay model, the
-          dual-precision emulator, the speculative-stream reference
+          dual-precision and bf16-only-checkpoint emulators, the bf16-stored
+          eager state, the speculative-stream reference
   ring    integer model of the per-sequence ring pointers
-  lowp    bf16 round-to-nearest-even used by the dual-precision emulator
+  lowp    bf16 round-to-nearest-even used by the low-precision emulators
   gdn     gated-DeltaNet eager rule and its replay model
 
 Every function is pinned by ``tests/test_oracle_*.py`` to closed forms, exact

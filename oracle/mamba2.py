@@ -69,6 +69,22 @@ def eager_scan(S0, A, xs, Bs, Cs, dts, keep=()):
     return ys, S, kept
 
 
+def eager_scan_bf16_state(S0, A, xs, Bs, Cs, dts):
+    """The eager recurrence with its state *stored* in bf16 (a quantised state
+    rewritten at every token, P1 "Trois ennuis nés de la même fusion": each
+    rewrite adds a rounding). Each step starts from the stored bf16 values, is
+    computed exactly, gives y from that unrounded new state, and stores the new
+    state rounded to nearest (via fp32, ties to even). The initial state is
+    stored the same way. Returns (ys (T,Bt,H,P), stored S_T)."""
+    S = lowp.round_bf16(S0)
+    T = len(xs)
+    ys = np.zeros((T,) + np.shape(xs)[1:], np.float64)
+    for t in range(T):
+        S_new, ys[t] = eager_step(S, A, xs[t], Bs[t], Cs[t], dts[t])
+        S = lowp.round_bf16(S_new)
+    return ys, S
+
+
 # --------------------------------------------------------------------------
 # The recurrence unrolled: closed form and semiseparable matrix.
 # --------------------------------------------------------------------------
@@ -151,6 +167,13 @@ class ReplayModel:
     prix d'une"): outputs read a bf16 copy of the checkpoint, refreshed from the
     high-precision master after each fold; the fold itself only ever reads the
     master, so the copy's rounding never feeds back.
+
+    read_copy="bf16_state" is the single shared low-precision checkpoint that
+    P2 compares the dual mode with: the checkpoint itself is stored in bf16
+    (rounded at init and after every fold), outputs and folds start from those
+    stored values. It rounds once per fold instead of once per token (P1, "Tenir
+    le journal plutôt que le solde": the quantised state is rewritten only at
+    spaced intervals).
     """
 
     def __init__(self, S0, A, ngroups: int, capacity: int, read_copy: str = "none"):
@@ -160,7 +183,9 @@ class ReplayModel:
         self.g = group_index(H, ngroups)
         self.A = _f64(A)
         self.R = capacity
-        self.ckpt = S0.copy()
+        if read_copy not in ("none", "bf16", "bf16_state"):
+            raise ValueError(read_copy)
+        self.ckpt = lowp.round_bf16(S0) if read_copy == "bf16_state" else S0.copy()
         self.read_copy = read_copy
         self.copy = lowp.round_bf16(self.ckpt) if read_copy == "bf16" else None
         self.ptr = PointerModel(Bt, capacity)
@@ -225,6 +250,8 @@ class ReplayModel:
                 raise RingError("flush while a verify round is uncommitted")
             if self.ptr.len[b] >= threshold:
                 self.ckpt[b] = self.implied_state(b)
+                if self.read_copy == "bf16_state":
+                    self.ckpt[b] = lowp.round_bf16(self.ckpt[b])
                 self.ptr.flush(b, threshold)
                 if self.copy is not None:
                     self.copy[b] = lowp.round_bf16(self.ckpt[b])

@@ -159,6 +159,21 @@ __device__ __forceinline__ void st16(float* p, const float4& v) {
   __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
 }
 
+// Four bf16 values of a bf16 checkpoint (8 bytes, non-temporal) widened to
+// fp32, and their RNE-packed store: the tile geometry of the fp32 state (4
+// columns per thread) kept for a bf16-stored state.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 ld8_bf16x4(const bf16_t* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+__device__ __forceinline__ void st8_bf16x4(bf16_t* p, const float4& v) {
+  const u32x2 pk = {(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                    (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+  __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(p));
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }

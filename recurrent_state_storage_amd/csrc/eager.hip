@@ -12,14 +12,18 @@
 // snapshots; P4, "Co się zmieniło?", item 4): the state is read from pool slot
 // src_slot[b], and the state after token i is written to slot i.
 //
+// A bf16-stored state (the quantised eager state of P1, "Trois ennuis nés de
+// la même fusion": rewritten, hence rounded, at every call) is widened to fp32
+// on load, updated and read out in fp32, and stored back RNE-rounded.
+//
 // Same tile geometry as the replay kernels: one 256-thread workgroup per
-// (sequence, head), 16-byte fp32 fragments in registers, row dots by butterfly.
+// (sequence, head), 4-column fragments in registers, row dots by butterfly.
 #include "device.h"
 #include "launch.h"
 
 namespace rss {
 
-template <int N, typename Tin>
+template <int N, typename Tin, bool SB16>
 __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
@@ -36,7 +40,11 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
   const size_t tile_elems = (size_t)P * N;
 
   float* src;
-  if (a.src_slot) {
+  bf16_t* srcb = SB16 ? static_cast<bf16_t*>(a.S) + (size_t)bh * tile_elems : nullptr;
+  float* const S = static_cast<float*>(a.S);
+  if (SB16) {
+    src = nullptr;
+  } else if (a.src_slot) {
     const int s = a.src_slot[b];
     if (s < 0 || s >= a.slots) {
       for (int e = tid; e < T * P; e += kThreads) {
@@ -45,9 +53,9 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
       }
       return;
     }
-    src = a.S + (((size_t)b * a.slots + s) * H + h) * tile_elems;
+    src = S + (((size_t)b * a.slots + s) * H + h) * tile_elems;
   } else {
-    src = a.S + (size_t)bh * tile_elems;
+    src = S + (size_t)bh * tile_elems;
   }
 
   const int col = tid % TPR, rsub = tid / TPR;
@@ -56,8 +64,9 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
       const int row = base + k * RPP + rsub;
-      if (row < P) fr[k].v = ld16(src + (size_t)row * N + col * 4);
-      else fr[k].v = float4{};
+      if (row >= P) fr[k].v = float4{};
+      else if constexpr (SB16) fr[k].v = ld8_bf16x4(srcb + (size_t)row * N + col * 4);
+      else fr[k].v = ld16(src + (size_t)row * N + col * 4);
     }
   };
   load_chunk(0);
@@ -107,8 +116,8 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
         part = fmaf(s.w, cv.w, part);
         part = row_sum<TPR>(part);
         if (col == 0 && row < P) a.y[((size_t)(b * T + i) * H + h) * P + row] = part;
-        if (a.src_slot && row < P) {
-          float* dst = a.S + (((size_t)b * a.slots + i) * H + h) * tile_elems;
+        if (!SB16 && a.src_slot && row < P) {
+          float* dst = S + (((size_t)b * a.slots + i) * H + h) * tile_elems;
           *reinterpret_cast<float4*>(dst + (size_t)row * N + col * 4) = s;
         }
       }
@@ -117,28 +126,37 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
 #pragma unroll
       for (int k = 0; k < kMaxPass; ++k) {
         const int row = base + k * RPP + rsub;
-        if (row < P) *reinterpret_cast<float4*>(src + (size_t)row * N + col * 4) = fr[k].v;
+        if (row >= P) continue;
+        if constexpr (SB16) st8_bf16x4(srcb + (size_t)row * N + col * 4, fr[k].v);
+        else *reinterpret_cast<float4*>(src + (size_t)row * N + col * 4) = fr[k].v;
       }
     }
   }
 }
 
-template <int N>
+template <int N, bool SB16>
 static hipError_t eager_n(const EagerArgs& a, int batch, bool bf16_in, hipStream_t s) {
   const dim3 grid((unsigned)((size_t)batch * a.H)), block(kThreads);
   const size_t lds = (size_t)a.T * (a.P + 2 * N) * sizeof(float);
-  if (bf16_in) hipLaunchKernelGGL((eager_kernel<N, bf16_t>), grid, block, lds, s, a);
-  else hipLaunchKernelGGL((eager_kernel<N, float>), grid, block, lds, s, a);
+  if (bf16_in) hipLaunchKernelGGL((eager_kernel<N, bf16_t, SB16>), grid, block, lds, s, a);
+  else hipLaunchKernelGGL((eager_kernel<N, float, SB16>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, hipStream_t s) {
+template <int N>
+static hipError_t eager_s(const EagerArgs& a, int batch, bool bf16_in, bool bf16_state, hipStream_t s) {
+  return bf16_state ? eager_n<N, true>(a, batch, bf16_in, s) : eager_n<N, false>(a, batch, bf16_in, s);
+}
+
+hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, bool bf16_state,
+                        hipStream_t s) {
+  if (bf16_state && a.src_slot) return hipErrorInvalidValue;  // snapshot pools are fp32
   switch (N) {
-    case 16: return eager_n<16>(a, batch, bf16_in, s);
-    case 32: return eager_n<32>(a, batch, bf16_in, s);
-    case 64: return eager_n<64>(a, batch, bf16_in, s);
-    case 128: return eager_n<128>(a, batch, bf16_in, s);
-    case 256: return eager_n<256>(a, batch, bf16_in, s);
+    case 16: return eager_s<16>(a, batch, bf16_in, bf16_state, s);
+    case 32: return eager_s<32>(a, batch, bf16_in, bf16_state, s);
+    case 64: return eager_s<64>(a, batch, bf16_in, bf16_state, s);
+    case 128: return eager_s<128>(a, batch, bf16_in, bf16_state, s);
+    case 256: return eager_s<256>(a, batch, bf16_in, bf16_state, s);
     default: return hipErrorInvalidValue;
   }
 }

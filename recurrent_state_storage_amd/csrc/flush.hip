@@ -10,7 +10,10 @@
 //
 // This is the only kernel that writes a checkpoint. In dual-precision mode it
 // also refreshes the bf16 read copy from the new fp32 master (P2, "Deux
-// précisions pour le prix d'une"); the fold reads the master only.
+// précisions pour le prix d'une"); the fold reads the master only. With a
+// bf16-only checkpoint (the single low-precision checkpoint the dual mode is
+// compared with) it folds from the bf16 values in fp32 and stores the RNE-bf16
+// result: one rounding per window (P1, "Tenir le journal plutôt que le solde").
 //
 // Rollback (P2, "Un retour en arrière qui devient trivial") touches integers
 // only: len -= n_drop, n_tent = 0.
@@ -35,8 +38,9 @@ struct FlushLds {
   }
 };
 
-template <int N, typename Tin, bool DUAL>
+template <int N, typename Tin, int MODE>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
+  constexpr bool DUAL = MODE == kCkptDual, B16 = MODE == kCkptBf16;
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
   constexpr int VE = V16<Tin>::VE;
@@ -72,16 +76,21 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   auto xrow = [&](int j) { return rx + ((size_t)bh * R + ring_slot(head, j, R)) * P; };
   auto brow = [&](int j) { return rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N; };
 
-  // 1. Tile loads (fp32 master).
+  // 1. Tile loads (the fp32 master, or the bf16 checkpoint widened to fp32).
   const int col = tid % TPR, rsub = tid / TPR;
-  float* tile = a.ckpt + (size_t)bh * P * N;
+  float* tile = B16 ? nullptr : a.ckpt + (size_t)bh * P * N;
+  bf16_t* tileb = B16 ? static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N : nullptr;
   Frag<false> fr[kMaxPass];
+  auto ld_row = [&](int row) {
+    if constexpr (B16) return ld8_bf16x4(tileb + (size_t)row * N + col * 4);
+    else return ld16(tile + (size_t)row * N + col * 4);
+  };
   auto load_chunk = [&](int base) {
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
       const int r0 = base + k * RPP;
-      if (r0 + RPP <= P) fr[k].v = ld16(tile + (size_t)(r0 + rsub) * N + col * 4);
-      else if (r0 + rsub < P) fr[k].v = ld16(tile + (size_t)(r0 + rsub) * N + col * 4);
+      if (r0 + RPP <= P) fr[k].v = ld_row(r0 + rsub);
+      else if (r0 + rsub < P) fr[k].v = ld_row(r0 + rsub);
       else fr[k].v = float4{};
     }
   };
@@ -181,6 +190,10 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     for (int k = 0; k < kMaxPass; ++k) {
       const int row = base + k * RPP + rsub;
       if (row < P) {
+        if constexpr (B16) {
+          st8_bf16x4(tileb + (size_t)row * N + col * 4, fr[k].v);
+          continue;
+        }
         st16(tile + (size_t)row * N + col * 4, fr[k].v);
         if (DUAL) {
           bf16_t* lo = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N + (size_t)row * N + col * 4;
@@ -195,10 +208,10 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   if (tid == 0) a.ptr[bh] = make_int4(ring_slot(head, n, R), 0, 0, 0);
 }
 
-template <int N, typename Tin, bool DUAL>
+template <int N, typename Tin, int MODE>
 static hipError_t flush_one(const FlushArgs& a, int batch, hipStream_t s) {
   const size_t lds = (size_t)FlushLds(a.R, a.P, N).total * sizeof(float);
-  auto kern = flush_kernel<N, Tin, DUAL>;
+  auto kern = flush_kernel<N, Tin, MODE>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -208,20 +221,29 @@ static hipError_t flush_one(const FlushArgs& a, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int N>
-static hipError_t flush_n(const FlushArgs& a, int batch, bool bf16_in, bool low, hipStream_t s) {
-  if (bf16_in) return low ? flush_one<N, bf16_t, true>(a, batch, s) : flush_one<N, bf16_t, false>(a, batch, s);
-  return low ? flush_one<N, float, true>(a, batch, s) : flush_one<N, float, false>(a, batch, s);
+template <int N, typename Tin>
+static hipError_t flush_t(const FlushArgs& a, int batch, int mode, hipStream_t s) {
+  switch (mode) {
+    case kCkptF32: return flush_one<N, Tin, kCkptF32>(a, batch, s);
+    case kCkptDual: return flush_one<N, Tin, kCkptDual>(a, batch, s);
+    case kCkptBf16: return flush_one<N, Tin, kCkptBf16>(a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, bool low_copy,
+template <int N>
+static hipError_t flush_n(const FlushArgs& a, int batch, bool bf16_in, int mode, hipStream_t s) {
+  return bf16_in ? flush_t<N, bf16_t>(a, batch, mode, s) : flush_t<N, float>(a, batch, mode, s);
+}
+
+hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode,
                         hipStream_t s) {
   switch (N) {
-    case 16: return flush_n<16>(a, batch, bf16_in, low_copy, s);
-    case 32: return flush_n<32>(a, batch, bf16_in, low_copy, s);
-    case 64: return flush_n<64>(a, batch, bf16_in, low_copy, s);
-    case 128: return flush_n<128>(a, batch, bf16_in, low_copy, s);
-    case 256: return flush_n<256>(a, batch, bf16_in, low_copy, s);
+    case 16: return flush_n<16>(a, batch, bf16_in, mode, s);
+    case 32: return flush_n<32>(a, batch, bf16_in, mode, s);
+    case 64: return flush_n<64>(a, batch, bf16_in, mode, s);
+    case 128: return flush_n<128>(a, batch, bf16_in, mode, s);
+    case 256: return flush_n<256>(a, batch, bf16_in, mode, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -233,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void init_kernel(InitArgs a) {
   const size_t nvec = a.n_state / 4;
   for (size_t i = i0; i < nvec; i += stride) {
     const float4 v = a.S0 ? reinterpret_cast<const float4*>(a.S0)[i] : float4{};
-    reinterpret_cast<float4*>(a.ckpt)[i] = v;
+    if (a.ckpt) reinterpret_cast<float4*>(a.ckpt)[i] = v;
     if (a.ckpt_lo) {
       uint2 pk;
       pk.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);

@@ -32,10 +32,13 @@ struct ReplayArgs {
 hipError_t launch_replay(const ReplayArgs& a, int batch, int N, bool bf16_in, bool low_copy,
                          hipStream_t s);
 
+// Checkpoint precision modes (the public read_copy codes).
+enum CkptMode { kCkptF32 = 0, kCkptDual = 1, kCkptBf16 = 2 };
+
 // Fold the window into the checkpoint for sequences with len >= min_len.
 struct FlushArgs {
-  float* ckpt;
-  void* ckpt_lo;           // written in dual mode
+  float* ckpt;             // fp32 checkpoint (null in kCkptBf16 mode)
+  void* ckpt_lo;           // bf16 read copy (kCkptDual), or the bf16 checkpoint (kCkptBf16)
   const void* ring_x;
   const void* ring_B;
   const float2* ring_dl;
@@ -43,13 +46,13 @@ struct FlushArgs {
   int* err;
   int H, P, G, R, min_len;
 };
-hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, bool low_copy,
+hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode,
                         hipStream_t s);
 
 // ckpt <- S0 (or 0), read copy <- bf16(ckpt), pointers and error word <- 0.
 struct InitArgs {
-  float* ckpt;
-  void* ckpt_lo;
+  float* ckpt;             // null when the checkpoint is bf16 only
+  void* ckpt_lo;           // bf16 copy or bf16 checkpoint (may be null)
   const float* S0;
   int4* ptr;
   int* err;
@@ -71,7 +74,8 @@ hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
 // Eager baseline: T tokens in place (src_slot == nullptr) or from pool slot
 // src_slot[b] with a snapshot written to slot i after token i.
 struct EagerArgs {
-  float* S;                // in-place state [Bt,H,P,N], or the pool [Bt,slots,H,P,N]
+  void* S;                 // in-place state [Bt,H,P,N] (fp32, or bf16 when bf16_state),
+                           // or the fp32 pool [Bt,slots,H,P,N]
   const int* src_slot;     // nullptr: in place
   const void* x;           // [Bt,T,H,P]
   const void* B;           // [Bt,T,G,N]
@@ -81,7 +85,8 @@ struct EagerArgs {
   float* y;                // [Bt,T,H,P]
   int H, P, G, T, slots;
 };
-hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, hipStream_t s);
+hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, bool bf16_state,
+                        hipStream_t s);
 
 // Gated DeltaNet replay decode (one token) and its eager baseline.
 struct GdnArgs {

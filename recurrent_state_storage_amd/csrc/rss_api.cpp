@@ -31,10 +31,12 @@ int32_t check_shape(const rss_config* c) {
   return RSS_OK;
 }
 
+bool valid_mode(int32_t m) { return m == RSS_COPY_NONE || m == RSS_COPY_BF16 || m == RSS_STATE_BF16; }
+
 int32_t check_config(const rss_config* c) {
   int32_t st = check_shape(c);
   if (st) return st;
-  if (c->read_copy != RSS_COPY_NONE && c->read_copy != RSS_COPY_BF16) return RSS_E_DTYPE;
+  if (!valid_mode(c->read_copy)) return RSS_E_DTYPE;
   if (c->kind != RSS_KIND_MAMBA2 && c->kind != RSS_KIND_GDN) return RSS_E_INVALID;
   if (c->kind == RSS_KIND_GDN) {  // one key per head, fp32, no read copy, no drafts
     if (c->ngroups != c->nheads) return RSS_E_SHAPE;
@@ -51,6 +53,15 @@ size_t in_bytes(const rss_config* c) { return c->in_dtype == RSS_DTYPE_BF16 ? 2 
 
 int32_t launch_status(hipError_t e) { return e == hipSuccess ? RSS_OK : RSS_E_HIP; }
 
+// The fp32 checkpoint (null with a bf16-only checkpoint) and the bf16 tile the
+// kernels read (the read copy, or the bf16-only checkpoint itself).
+float* ckpt_f32(const rss_layer* l) {
+  return l->cfg.read_copy == RSS_STATE_BF16 ? nullptr : static_cast<float*>(l->dev.ckpt);
+}
+void* ckpt_bf16(const rss_layer* l) {
+  return l->cfg.read_copy == RSS_STATE_BF16 ? l->dev.ckpt : l->dev.ckpt_lo;
+}
+
 bool inputs_ok(const void* x, const void* B, const void* C, const void* dt, const void* y) {
   return x && B && C && dt && y && aligned16(x) && aligned16(B) && aligned16(C) &&
          aligned16(dt) && aligned16(y);
@@ -60,7 +71,7 @@ bool inputs_ok(const void* x, const void* B, const void* C, const void* dt, cons
 
 extern "C" {
 
-int32_t rss_version(void) { return 10100; }
+int32_t rss_version(void) { return 10200; }
 
 const char* rss_status_string(int32_t s) {
   switch (s) {
@@ -81,7 +92,7 @@ int32_t rss_buffer_sizes(const rss_config* c, rss_sizes* out) {
   if (st) return st;
   const size_t Bt = c->batch, H = c->nheads, P = c->headdim, N = c->dstate, G = c->ngroups,
                R = c->capacity;
-  out->ckpt = Bt * H * P * N * 4;
+  out->ckpt = Bt * H * P * N * (c->read_copy == RSS_STATE_BF16 ? 2 : 4);
   out->ckpt_lo = c->read_copy == RSS_COPY_BF16 ? Bt * H * P * N * 2 : 0;
   out->ring_x = Bt * H * R * P * in_bytes(c);
   out->ring_B = Bt * G * R * N * in_bytes(c);
@@ -127,8 +138,8 @@ int32_t rss_init_state(rss_layer* l, const float* S0, void* stream) {
   if (S0 && !aligned16(S0)) return RSS_E_INVALID;
   const rss_config& c = l->cfg;
   rss::InitArgs a;
-  a.ckpt = l->dev.ckpt;
-  a.ckpt_lo = l->dev.ckpt_lo;
+  a.ckpt = ckpt_f32(l);
+  a.ckpt_lo = ckpt_bf16(l);
   a.S0 = S0;
   a.ptr = reinterpret_cast<int4*>(l->dev.ptr);
   a.err = l->dev.dev_err;
@@ -143,8 +154,8 @@ static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len,
   const rss_config& c = l->cfg;
   if (c.batch == 0) return RSS_OK;
   rss::ReplayArgs a;
-  a.ckpt = l->dev.ckpt;
-  a.ckpt_lo = l->dev.ckpt_lo;
+  a.ckpt = ckpt_f32(l);
+  a.ckpt_lo = ckpt_bf16(l);
   a.ring_x = l->dev.ring_x;
   a.ring_B = l->dev.ring_B;
   a.ring_dl = reinterpret_cast<float2*>(l->dev.ring_dl);
@@ -167,7 +178,7 @@ static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len,
   const uint64_t d = c.headdim % ve == 0 ? (uint64_t)(c.headdim / ve) : (uint64_t)c.headdim;
   a.xdiv = ((1ull << 32) + d - 1) / d;
   return launch_status(rss::launch_replay(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
-                                          c.read_copy == RSS_COPY_BF16,
+                                          c.read_copy != RSS_COPY_NONE,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -185,7 +196,7 @@ int32_t rss_decode_flush_step(rss_layer* l, int32_t min_len, const void* x, cons
   if (min_len < 1) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
   if (l->pending_verify) return RSS_E_ORDER;
-  if (l->cfg.read_copy == RSS_COPY_BF16) {  // the fold reads the fp32 master: two launches
+  if (l->cfg.read_copy != RSS_COPY_NONE) {  // the replay reads a bf16 tile: two launches
     const int32_t st = replay_call(l, 1, 0, 0, x, B, C, dt, y, stream);
     return st ? st : rss_flush_checkpoint(l, min_len, stream);
   }
@@ -227,8 +238,8 @@ int32_t rss_flush_checkpoint(rss_layer* l, int32_t min_len, void* stream) {
   const rss_config& c = l->cfg;
   if (c.batch == 0) return RSS_OK;
   rss::FlushArgs a;
-  a.ckpt = l->dev.ckpt;
-  a.ckpt_lo = l->dev.ckpt_lo;
+  a.ckpt = ckpt_f32(l);
+  a.ckpt_lo = ckpt_bf16(l);
   a.ring_x = l->dev.ring_x;
   a.ring_B = l->dev.ring_B;
   a.ring_dl = reinterpret_cast<const float2*>(l->dev.ring_dl);
@@ -240,7 +251,7 @@ int32_t rss_flush_checkpoint(rss_layer* l, int32_t min_len, void* stream) {
   a.R = c.capacity;
   a.min_len = min_len;
   return launch_status(rss::launch_flush(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
-                                         c.read_copy == RSS_COPY_BF16,
+                                         c.read_copy,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -253,7 +264,7 @@ int32_t rss_gdn_decode_step(rss_layer* l, const float* q, const float* k, const 
   if (l->pending_verify) return RSS_E_ORDER;
   if (c.batch == 0) return RSS_OK;
   rss::GdnArgs a;
-  a.ckpt = l->dev.ckpt;
+  a.ckpt = static_cast<float*>(l->dev.ckpt);
   a.ring_u = static_cast<float*>(l->dev.ring_x);
   a.ring_k = static_cast<float*>(l->dev.ring_B);
   a.ring_dl = reinterpret_cast<float2*>(l->dev.ring_dl);
@@ -305,11 +316,14 @@ int32_t rss_get_device_error(rss_layer* l, int32_t* host_code, void* stream) {
   return RSS_OK;
 }
 
-static int32_t eager_call(const rss_config* c, float* S, const int32_t* src_slot, int32_t slots,
+static int32_t eager_call(const rss_config* c, void* S, const int32_t* src_slot, int32_t slots,
                           int32_t T, const void* x, const void* B, const void* C, const float* dt,
                           const float* A, float* y, void* stream) {
   const int32_t st = check_shape(c);
   if (st) return st;
+  if (!valid_mode(c->read_copy)) return RSS_E_DTYPE;
+  const bool bf16_state = c->read_copy == RSS_STATE_BF16;
+  if (bf16_state && slots > 0) return RSS_E_DTYPE;  // snapshot pools are fp32
   if (T < 1 || T > rss::kMaxNew) return RSS_E_INVALID;
   if (!A || !aligned16(A)) return RSS_E_INVALID;
   if (c->batch == 0) return RSS_OK;
@@ -329,10 +343,10 @@ static int32_t eager_call(const rss_config* c, float* S, const int32_t* src_slot
   a.T = T;
   a.slots = slots;
   return launch_status(rss::launch_eager(a, c->batch, c->dstate, c->in_dtype == RSS_DTYPE_BF16,
-                                         static_cast<hipStream_t>(stream)));
+                                         bf16_state, static_cast<hipStream_t>(stream)));
 }
 
-int32_t rss_eager_step(const rss_config* c, float* S, const void* x, const void* B, const void* C,
+int32_t rss_eager_step(const rss_config* c, void* S, const void* x, const void* B, const void* C,
                        const float* dt, const float* A, float* y, int32_t T, void* stream) {
   return eager_call(c, S, nullptr, 0, T, x, B, C, dt, A, y, stream);
 }

@@ -22,7 +22,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rss.h")
 
 RSS_OK, RSS_E_INVALID, RSS_E_SHAPE, RSS_E_DTYPE, RSS_E_CAPACITY, RSS_E_ORDER, RSS_E_HIP = range(7)
 RSS_DTYPE_F32, RSS_DTYPE_BF16 = 0, 1
-RSS_COPY_NONE, RSS_COPY_BF16 = 0, 1
+RSS_COPY_NONE, RSS_COPY_BF16, RSS_STATE_BF16 = 0, 1, 2
 RSS_DEV_ROLLBACK_RANGE, RSS_DEV_RING_OVERFLOW, RSS_DEV_UNCOMMITTED = 1, 2, 4
 RSS_KIND_MAMBA2, RSS_KIND_GDN = 0, 1
 
@@ -140,6 +140,11 @@ def _in_dtype(code: int):
     return torch.bfloat16 if code == RSS_DTYPE_BF16 else torch.float32
 
 
+def _state_dtype(cfg):
+    """Storage of the checkpoint / eager state: bf16 only for RSS_STATE_BF16."""
+    return torch.bfloat16 if cfg.read_copy == RSS_STATE_BF16 else torch.float32
+
+
 def make_config(batch, nheads, headdim, dstate, ngroups, window, capacity, max_draft=0,
                 in_dtype=RSS_DTYPE_F32, read_copy=RSS_COPY_NONE, kind=RSS_KIND_MAMBA2) -> rss_config:
     return rss_config(batch, nheads, headdim, dstate, ngroups, window, capacity, max_draft,
@@ -179,7 +184,7 @@ class ReplayLayer:
         sizes = rss_buffer_sizes(cfg)   # validates cfg
         del sizes
         idt = _in_dtype(c.in_dtype)
-        self.ckpt = torch.empty((c.batch, c.nheads, c.headdim, c.dstate), dtype=torch.float32, device=dev)
+        self.ckpt = torch.empty((c.batch, c.nheads, c.headdim, c.dstate), dtype=_state_dtype(c), device=dev)
         self.ckpt_lo = (torch.empty((c.batch, c.nheads, c.headdim, c.dstate), dtype=torch.bfloat16, device=dev)
                         if c.read_copy == RSS_COPY_BF16 else None)
         self.ring_x = torch.zeros((c.batch, c.nheads, c.capacity, c.headdim), dtype=idt, device=dev)
@@ -292,7 +297,7 @@ def rss_eager_step(cfg: rss_config, S, x, B, C, dt, A, y, T=1, stream=None) -> N
 
     def sh(*tail):  # token axis optional when T == 1
         return [(c.batch, T) + tail] + ([(c.batch,) + tail] if T == 1 else [])
-    args = (_ptr(S, torch.float32, (c.batch, c.nheads, c.headdim, c.dstate), "S"),
+    args = (_ptr(S, _state_dtype(c), (c.batch, c.nheads, c.headdim, c.dstate), "S"),
             _ptr(x, idt, sh(c.nheads, c.headdim), "x"),
             _ptr(B, idt, sh(c.ngroups, c.dstate), "B"),
             _ptr(C, idt, sh(c.ngroups, c.dstate), "C"),

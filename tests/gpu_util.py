@@ -24,7 +24,8 @@ def cfg_of(wl, **kw):
     d = dict(batch=wl.batch, nheads=wl.nheads, headdim=wl.headdim, dstate=wl.dstate,
              ngroups=wl.ngroups, window=wl.window, capacity=wl.capacity, max_draft=wl.max_draft,
              in_dtype=rss.RSS_DTYPE_BF16 if wl.in_dtype == "bf16" else rss.RSS_DTYPE_F32,
-             read_copy=rss.RSS_COPY_BF16 if wl.read_copy == "bf16" else rss.RSS_COPY_NONE,
+             read_copy={"none": rss.RSS_COPY_NONE, "bf16": rss.RSS_COPY_BF16,
+                        "bf16_state": rss.RSS_STATE_BF16}[wl.read_copy],
              kind=rss.RSS_KIND_GDN if wl.kind == "gdn" else rss.RSS_KIND_MAMBA2)
     d.update(kw)
     return rss.rss_config(**d)

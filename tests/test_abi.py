@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rss.rss_version() == 10100
+    assert rss.rss_version() == 10200
     for s in range(7):
         assert rss.status_string(s)
     assert rss.status_string(99) == "unknown status"
@@ -64,6 +64,8 @@ def test_buffer_sizes():
     assert s.ptr == 4 * 8 * 16 and s.A == 32 and s.dev_err == 4
     s2 = rss.rss_buffer_sizes(_cfg(read_copy=rss.RSS_COPY_BF16, in_dtype=rss.RSS_DTYPE_F32))
     assert s2.ckpt_lo == 4 * 8 * 64 * 128 * 2 and s2.ring_x == 4 * 8 * 20 * 64 * 4
+    s3 = rss.rss_buffer_sizes(_cfg(read_copy=rss.RSS_STATE_BF16))     # bf16-only checkpoint
+    assert s3.ckpt == 4 * 8 * 64 * 128 * 2 and s3.ckpt_lo == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -87,6 +89,8 @@ def test_buffer_sizes():
     (dict(kind=rss.RSS_KIND_GDN, max_draft=0, in_dtype=rss.RSS_DTYPE_F32,
           read_copy=rss.RSS_COPY_BF16), rss.RSS_E_DTYPE),
     (dict(kind=rss.RSS_KIND_GDN, in_dtype=rss.RSS_DTYPE_F32), rss.RSS_E_CAPACITY),
+    (dict(kind=rss.RSS_KIND_GDN, max_draft=0, in_dtype=rss.RSS_DTYPE_F32,
+          read_copy=rss.RSS_STATE_BF16), rss.RSS_E_DTYPE),
 ])
 def test_config_validation(kw, status):
     cfg = _cfg(**kw)
@@ -163,6 +167,10 @@ def test_call_order_and_argument_errors_return_before_launch():
         assert lib.rss_eager_step(ctypes.byref(bad), A, A, A, A, A, A, A, 1, None) == rss.RSS_E_SHAPE
         assert lib.rss_eager_verify(ctypes.byref(cfg), A, None, 4, A, A, A, A, A, A, None) == rss.RSS_E_INVALID
         assert lib.rss_eager_verify(ctypes.byref(cfg), A, A, 8, A, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        b16 = _cfg(read_copy=rss.RSS_STATE_BF16)          # snapshot pools are fp32 only
+        assert lib.rss_eager_verify(ctypes.byref(b16), A, A, 4, A, A, A, A, A, A, None) == rss.RSS_E_DTYPE
+        bad_mode = _cfg(read_copy=5)
+        assert lib.rss_eager_step(ctypes.byref(bad_mode), A, A, A, A, A, A, A, 1, None) == rss.RSS_E_DTYPE
     finally:
         lib.rss_layer_free(h)
 

@@ -129,3 +129,28 @@ def test_replay_mutant_fails(cls):
 def test_suffix_sum_mutant_fails(monkeypatch):
     monkeypatch.setattr(mamba2, "suffix_decay", _prefix_decay)
     assert _replay_vs_eager(mamba2.ReplayModel) > 1e-6
+
+
+def test_bf16_state_without_per_token_rounding_fails_the_swamping_pin(monkeypatch):
+    """A bf16-stored eager state that forgets to round after each token (only
+    the initial store rounds) is caught by the swamping closed form."""
+    import test_oracle_lowp as tl
+    calls = {"n": 0}
+    real = mamba2.lowp.round_bf16
+
+    def first_only(a):
+        calls["n"] += 1
+        return real(a) if calls["n"] == 1 else np.asarray(a, np.float64)
+    monkeypatch.setattr(mamba2.lowp, "round_bf16", first_only)
+    with pytest.raises(AssertionError):
+        tl.test_eager_bf16_state_swamping_closed_form()
+
+
+def test_bf16_checkpoint_rounding_every_token_fails_the_fold_pin(monkeypatch):
+    """A bf16-only checkpoint that rounds every token (folding after each
+    decode) loses the increments the once-per-window pin requires."""
+    import test_oracle_lowp as tl
+    real_flush = mamba2.ReplayModel.flush
+    monkeypatch.setattr(mamba2.ReplayModel, "flush", lambda self, th: real_flush(self, 1))
+    with pytest.raises(AssertionError):
+        tl.test_bf16_checkpoint_rounds_once_per_fold()

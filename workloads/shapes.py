@@ -33,6 +33,7 @@ class Workload:
     draft: int = 0        # K for speculative rounds
     rounds: int = 0       # speculative rounds
     s0: str = "zeros"     # "zeros" or "normal"
+    a_scale: float = 1.0  # A_h = -a_scale * exp(U(0,1)); < 1 gives long-memory heads
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -54,6 +55,12 @@ def _mk() -> dict:
         n = f"mamba2_dual_b256_h128_p64_n128_w{win}"
         w[n] = Workload(n, "mamba2", 256, 128, 64, 128, 128, win, win, 0, 1024,
                         "bf16", "bf16", 1002)
+    # Long-memory heads (decay per token ~0.997 instead of ~0.8), same shapes:
+    # the regime where per-token rounding of a stored state accumulates.
+    for win in (8, 16, 32):
+        n = f"mamba2_slowdecay_b256_h128_p64_n128_w{win}"
+        w[n] = Workload(n, "mamba2", 256, 128, 64, 128, 128, win, win, 0, 1024,
+                        "bf16", "bf16", 1005, a_scale=0.01)
     w["mamba2_spec_b512_h128_p64_n128_w16_k4"] = Workload(
         "mamba2_spec_b512_h128_p64_n128_w16_k4", "mamba2", 512, 128, 64, 128,
         128, 16, 20, 4, 0, "bf16", "none", 1003, draft=4, rounds=200)

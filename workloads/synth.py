@@ -3,7 +3,8 @@
 Every draw comes from ``numpy.random.default_rng([seed, stream, index])`` so any
 step or round can be regenerated on its own, in any order:
 
-  stream 0            A = -exp(U(0,1)) per head (computed in fp64, stored fp32)
+  stream 0            A = -exp(U(0,1)) per head (computed in fp64, stored fp32),
+                      times a_scale (0.01 for the long-memory workloads)
   stream 1, step t    x (Bt,H,P), B (Bt,G,N), C (Bt,G,N), z (Bt,H): standard
                       normals drawn in that order as float32; dt = softplus(z - 2)
                       computed in fp64 and stored fp32
@@ -63,9 +64,10 @@ def _store(a: np.ndarray, dtype: str) -> dict:
 
 
 def params(wl: Workload) -> dict:
-    """Per-head parameters: A (H,) float32, A = -exp(U(0,1))."""
+    """Per-head parameters: A (H,) float32, A = -a_scale * exp(U(0,1)) (fp64, then
+    rounded to fp32; a_scale = 1 except for the long-memory workloads)."""
     u = _rng(wl.seed, 0).random(wl.nheads)
-    return {"A": (-np.exp(u)).astype(np.float32)}
+    return {"A": (-wl.a_scale * np.exp(u)).astype(np.float32)}
 
 
 def initial_state(wl: Workload) -> np.ndarray:
