@@ -47,7 +47,7 @@ KERNEL_SOURCES = ["replay.hip", "device.h", "limits.h", "launch.h"]
 def replay_bytes(wl, n0: int) -> int:
     """Replay decode of one token with n0 entries already in the window."""
     P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
-    tile = P * N * (2 if wl.read_copy == "bf16" else 4)
+    tile = P * N * (2 if wl.read_copy in ("bf16", "bf16_state") else 4)
     entry = P * ib + N * ib + 8                     # x, B, (dt, dt*A)
     inputs = P * ib + 2 * N * ib + 4                 # x_t, B_t, C_t, dt_t
     return tile + n0 * entry + inputs + P * 4 + entry + 32 + 4   # + y, append, pointers, A
@@ -56,8 +56,11 @@ def replay_bytes(wl, n0: int) -> int:
 def flush_bytes(wl, n: int) -> int:
     """Fold of n window entries into one checkpoint tile (read + write)."""
     P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
+    ring = n * (P * ib + N * ib + 8) + 32
+    if wl.read_copy == "bf16_state":            # bf16 checkpoint read and written
+        return 2 * P * N * 2 + ring
     lo = P * N * 2 if wl.read_copy == "bf16" else 0
-    return 2 * P * N * 4 + lo + n * (P * ib + N * ib + 8) + 32
+    return 2 * P * N * 4 + lo + ring
 
 
 def fused_bytes(wl) -> int:
@@ -66,9 +69,9 @@ def fused_bytes(wl) -> int:
     return replay_bytes(wl, wl.window - 1) + wl.headdim * wl.dstate * 4
 
 
-def eager_bytes(wl) -> int:
+def eager_bytes(wl, state_bytes: int = 4) -> int:
     P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
-    return 2 * P * N * 4 + P * ib + 2 * N * ib + 4 + P * 4 + 4
+    return 2 * P * N * state_bytes + P * ib + 2 * N * ib + 4 + P * 4 + 4
 
 
 def kernel_source_hash() -> str:
@@ -153,12 +156,13 @@ def _timed(torch, fn, n):
     return e0.elapsed_time(e1)
 
 
-def run_dual(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
-    """Dual precision (fp32 master + bf16 read copy), W = 16, same inputs."""
-    wl = workloads.get("mamba2_dual_b256_h128_p64_n128_w16")
+def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16"):
+    """Replay with a bf16 tile read, W = 16, same inputs: dual precision (fp32
+    master + bf16 read copy, mode "bf16") or a single bf16 checkpoint ("bf16_state")."""
+    wl = workloads.get("mamba2_dual_b256_h128_p64_n128_w16").replace(read_copy=mode)
     Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
-    cfg = rss.make_config(Bt, H, P, N, wl.ngroups, W, wl.capacity, 0, rss.RSS_DTYPE_BF16,
-                          rss.RSS_COPY_BF16)
+    code = rss.RSS_COPY_BF16 if mode == "bf16" else rss.RSS_STATE_BF16
+    cfg = rss.make_config(Bt, H, P, N, wl.ngroups, W, wl.capacity, 0, rss.RSS_DTYPE_BF16, code)
     layer = rss.ReplayLayer(cfg, A, dev)
     layer.init_state()
     y = torch.empty((Bt, H, P), device=dev)
@@ -192,7 +196,8 @@ def run_dual(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
     rbytes = sum(replay_bytes(wl, (base + j) % W) for j in range(steps)) * Bt * H
     fbytes = flush_bytes(wl, W) * Bt * H * len(ev.get("f", []))
     assert layer.device_error() == 0
-    return {"workload": wl.name, "tokens_per_s": Bt * steps / (ms / 1e3),
+    return {"workload": wl.name if mode == "bf16" else wl.name + " with a bf16-only checkpoint",
+            "tokens_per_s": Bt * steps / (ms / 1e3),
             "replay_avg_us": r_ms / steps * 1e3, "replay_GBps": rbytes / (r_ms / 1e3) / 1e9,
             "flush_avg_us": f_ms / max(len(ev.get("f", [])), 1) * 1e3,
             "flush_GBps": fbytes / (f_ms / 1e3) / 1e9 if f_ms else None}
@@ -203,6 +208,28 @@ def _gen_round(args):
     wl = workloads.get(name)
     d = synth.draft_inputs(wl, r)
     return r, d["x_bits"], d["B_bits"], d["C_bits"], d["dt"], synth.accepted_drafts(wl, r)
+
+
+def run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
+    """Eager decode with the state stored in bf16 (rounded every token): the
+    low-precision eager point of comparison, same inputs and shape."""
+    wl = workloads.get(WORKLOAD)
+    Bt, H, P, N = wl.batch, wl.nheads, wl.headdim, wl.dstate
+    cfg = rss.make_config(Bt, H, P, N, wl.ngroups, wl.window, wl.capacity, 0, rss.RSS_DTYPE_BF16,
+                          rss.RSS_STATE_BF16)
+    S = torch.zeros((Bt, H, P, N), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((Bt, H, P), device=dev)
+    T = X.shape[0]
+
+    def step(k):
+        i = k % T
+        rss.rss_eager_step(cfg, S, X[i], Bm[i], Cm[i], DT[i], A, y)
+    for k in range(warmup):
+        step(k)
+    ms = _timed(torch, lambda j: step(warmup + j), steps)
+    return {"tokens_per_s": Bt * steps / (ms / 1e3), "kernel_avg_us": ms / steps * 1e3,
+            "kernel_GBps": eager_bytes(wl, 2) * Bt * H * steps / (ms / 1e3) / 1e9,
+            "bytes_per_token": eager_bytes(wl, 2) * H}
 
 
 def run_spec(torch, rss, dev, rounds, warmup, workers, distinct=6):
@@ -568,7 +595,12 @@ def main() -> int:
     if out_eager:
         rec["speedup_vs_eager_gpu"] = tok_s / out_eager["tokens_per_s"]
     if not args.no_extra:
-        rec["dual_precision"] = run_dual(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
+        rec["dual_precision"] = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
+        rec["low_precision"] = {
+            "bf16_checkpoint": run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup,
+                                        mode="bf16_state"),
+            "eager_bf16_state": run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, args.steps,
+                                               args.warmup)}
         rec["speculative"] = run_spec(torch, rss, dev, rounds=48, warmup=8, workers=workers)
         rec["gated_deltanet"] = run_gdn(torch, rss, dev, steps=args.steps, warmup=args.warmup,
                                         workers=workers)
