@@ -29,9 +29,10 @@ Modules:
   ring    integer model of the per-sequence ring pointers
   lowp    bf16 round-to-nearest-even used by the low-precision emulators
   gdn     gated-DeltaNet eager rule and its replay model
+  kda     Kimi Delta Attention (per-channel gated delta rule) and its replay model
 
 Every function is pinned by ``tests/test_oracle_*.py`` to closed forms, exact
 rational or 50-digit arithmetic, textbook special cases and invariants; none is
 "parity unpinned".
 """
-from . import lowp, ring, mamba2, gdn  # noqa: F401
+from . import lowp, ring, mamba2, gdn, kda  # noqa: F401

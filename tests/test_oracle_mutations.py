@@ -154,3 +154,36 @@ def test_bf16_checkpoint_rounding_every_token_fails_the_fold_pin(monkeypatch):
     monkeypatch.setattr(mamba2.ReplayModel, "flush", lambda self, th: real_flush(self, 1))
     with pytest.raises(AssertionError):
         tl.test_bf16_checkpoint_rounds_once_per_fold()
+
+
+def _kda_gate_on_rows(S, q, k, v, beta, alpha):
+    """Mutant: the per-channel gate applied to the value rows instead of the
+    key channels (only meaningful when d_v == d_k)."""
+    S = np.asarray(S, np.float64) * np.asarray(alpha, np.float64)[..., :, None]
+    ones = np.ones_like(np.asarray(alpha, np.float64))
+    return _KDA_STEP(S, q, k, v, beta, ones)
+
+
+def test_kda_gate_on_the_wrong_side_fails_a_pin(monkeypatch):
+    from oracle import kda
+    import test_oracle_kda as tk
+    monkeypatch.setattr(kda, "eager_step", _kda_gate_on_rows)
+    rng = np.random.default_rng(4)
+    S0 = rng.standard_normal((1, 1, 5, 5))
+    inp = tk._rand_inputs(rng, 1, 1, 5, 5)
+    S, _ = kda.eager_step(S0, inp["q"], inp["k"], inp["v"], np.zeros((1, 1)), inp["alpha"])
+    assert pins.rel_err(S, S0 * inp["alpha"][:, :, None, :]) > 1e-3   # the beta = 0 pin's check
+
+
+def test_kda_replay_without_the_new_gate_fails(monkeypatch):
+    from oracle import kda
+    import test_oracle_kda as tk
+    real = kda.KDAReplayModel._apply
+    monkeypatch.setattr(kda.KDAReplayModel, "_apply",
+                        lambda self, b, vec, n, g_next=None: real(self, b, vec, n))
+    with pytest.raises(AssertionError):
+        tk.test_replay_equals_eager_kda(4, 8, 5)
+
+
+from oracle import kda as _kda_mod  # noqa: E402
+_KDA_STEP = _kda_mod.eager_step

@@ -17,7 +17,7 @@ import dataclasses
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str             # "mamba2" or "gdn"
+    kind: str             # "mamba2", "gdn" or "kda"
     batch: int            # Bt
     nheads: int           # H
     headdim: int          # P   (GDN: d_v)
@@ -67,6 +67,10 @@ def _mk() -> dict:
     w["gdn_b256_h32_d128_w16"] = Workload(
         "gdn_b256_h32_d128_w16", "gdn", 256, 32, 128, 128, 32, 16, 16, 0, 256,
         "f32", "none", 1004)
+    # Kimi Delta Attention at the gated-DeltaNet shape (per-channel gates).
+    w["kda_b256_h32_d128_w16"] = Workload(
+        "kda_b256_h32_d128_w16", "kda", 256, 32, 128, 128, 32, 16, 16, 0, 256,
+        "f32", "none", 1006)
     return w
 
 

@@ -13,6 +13,7 @@ step or round can be regenerated on its own, in any order:
   stream 3, round r   accepted drafts n_acc ~ Uniform{0..K}, one per sequence
   stream 4            S0 ~ N(0,1) (Bt,H,P,N) float32, for the "normal" S0 variant
   stream 5, step t    gated-DeltaNet inputs (see ``gdn_step_inputs``)
+  stream 6, step t    Kimi-Delta-Attention inputs (see ``kda_step_inputs``)
 
 Inputs stored as bf16 are rounded from the float32 draw with round-to-nearest-
 even; the returned float32 arrays are the exact values of those bf16 numbers, so
@@ -125,6 +126,29 @@ def gdn_step_inputs(wl: Workload, t: int) -> dict:
     v = rng.standard_normal((Bt, H, dv), dtype=np.float32)
     zb = rng.standard_normal((Bt, H), dtype=np.float32).astype(np.float64)
     za = rng.standard_normal((Bt, H), dtype=np.float32).astype(np.float64)
+    q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True))
+    k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
+    return {
+        "q": q.astype(np.float32),
+        "k": k.astype(np.float32),
+        "v": v,
+        "beta": (1.0 / (1.0 + np.exp(-zb))).astype(np.float32),
+        "alpha": np.exp(-_softplus64(za)).astype(np.float32),
+    }
+
+
+def kda_step_inputs(wl: Workload, t: int) -> dict:
+    """Kimi-Delta-Attention inputs of step t (0-based), all float32: as
+    ``gdn_step_inputs`` but the gate has one value per key channel,
+    alpha = exp(-softplus(N(0,1))) shaped (Bt,H,d_k). Draw order: q, k, v,
+    beta's normal, alpha's normals."""
+    Bt, H, dk, dv = wl.batch, wl.nheads, wl.dstate, wl.headdim
+    rng = _rng(wl.seed, 6, t)
+    q = rng.standard_normal((Bt, H, dk), dtype=np.float32).astype(np.float64)
+    k = rng.standard_normal((Bt, H, dk), dtype=np.float32).astype(np.float64)
+    v = rng.standard_normal((Bt, H, dv), dtype=np.float32)
+    zb = rng.standard_normal((Bt, H), dtype=np.float32).astype(np.float64)
+    za = rng.standard_normal((Bt, H, dk), dtype=np.float32).astype(np.float64)
     q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True))
     k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
     return {
