@@ -91,8 +91,11 @@ enum { RSS_COPY_NONE = 0, RSS_COPY_BF16 = 1, RSS_STATE_BF16 = 2 };
 /* Layer types. A Gated DeltaNet layer (P1, "La fiche qu'on réécrit à chaque
  * token": GDN's delta-rule update has the same form) uses P = d_v, N = d_k,
  * G = H (one key per head), fp32 inputs, no read copy; its ring holds
- * (u_t, k_t, (1, log alpha_t)) in ring_x, ring_B and ring_dl, and A is unused. */
-enum { RSS_KIND_MAMBA2 = 0, RSS_KIND_GDN = 1 };
+ * (u_t, k_t, (1, log alpha_t)) in ring_x, ring_B and ring_dl, and A is unused.
+ * A Kimi Delta Attention layer (KDA, P1 "Des couches rapides sur le papier")
+ * has the same rules and layout except that its gate has one value per key
+ * channel: ring_dl then holds a log-gate row per entry, fp32 [Bt, H, R, N]. */
+enum { RSS_KIND_MAMBA2 = 0, RSS_KIND_GDN = 1, RSS_KIND_KDA = 2 };
 
 /* Bits of the sticky device error word. */
 enum {
@@ -122,13 +125,15 @@ typedef struct rss_config {
  *   ckpt_lo  bf16 [Bt, H, P, N]   read copy; NULL unless read_copy = BF16
  *   ring_x   in_dtype [Bt, H, R, P]   buffered x_j
  *   ring_B   in_dtype [Bt, G, R, N]   buffered B_j (one copy per group)
- *   ring_dl  fp32 [Bt, H, R, 2]   buffered (dt_j, dt_j * A_h)
+ *   ring_dl  fp32 [Bt, H, R, 2]   buffered (dt_j, dt_j * A_h); KDA:
+ *                                 fp32 [Bt, H, R, N] log-gate rows
  *   ptr      int32 [Bt, H, 4]     per (sequence, head): head slot, window
  *                                 length len, tentative count n_tent, 0.
  *                                 Every head of a sequence holds the same
  *                                 values; each kernel workgroup owns its own
  *                                 (b, h) copy, so no two workgroups race.
- *   A        fp32 [H]             A_h (negative); unused (may be NULL) for GDN
+ *   A        fp32 [H]             A_h (negative); unused (may be NULL) for
+ *                                 GDN and KDA
  *   dev_err  int32 [1]            sticky device error word
  */
 typedef struct rss_buffers {
@@ -245,6 +250,26 @@ int32_t rss_gdn_decode_step(rss_layer* layer, const float* q, const float* k, co
  * place, S <- alpha S + u k^T, o = S q, layouts as rss_gdn_decode_step. Uses
  * cfg's batch, nheads, headdim (d_v) and dstate (d_k). */
 int32_t rss_gdn_eager_step(const rss_config* cfg, float* S, const float* q, const float* k,
+                           const float* v, const float* beta, const float* alpha, float* o,
+                           void* stream);
+
+/* Kimi Delta Attention decode of one token for every sequence (kind =
+ * RSS_KIND_KDA), by replay: the gated delta rule with one gate per key channel,
+ *   S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *   u_t = beta_t (v_t - S_{t-1} (alpha_t * k_t)),
+ *   o_t = S_t q_t = S_{t-1} (alpha_t * q_t) + (k_t . q_t) u_t,
+ * with S_{t-1} the checkpoint (each key channel n decayed by the product of its
+ * gates) plus the window, never written. Appends (u_t, k_t, log alpha_t) to the
+ * ring; rss_flush_checkpoint folds KDA windows with per-channel decays.
+ * Layouts: q, k, alpha [Bt,H,N]; v [Bt,H,P]; beta [Bt,H]; o [Bt,H,P]; all
+ * fp32; 0 < alpha < 1. Ring overflow as rss_decode_step. */
+int32_t rss_kda_decode_step(rss_layer* layer, const float* q, const float* k, const float* v,
+                            const float* beta, const float* alpha, float* o, void* stream);
+
+/* Eager KDA step (its baseline): S [Bt,H,P,N] fp32 updated in place by the rule
+ * above, layouts as rss_kda_decode_step; uses cfg's batch, nheads, headdim
+ * (d_v) and dstate (d_k). */
+int32_t rss_kda_eager_step(const rss_config* cfg, float* S, const float* q, const float* k,
                            const float* v, const float* beta, const float* alpha, float* o,
                            void* stream);
 

@@ -15,6 +15,10 @@
 // compared with) it folds from the bf16 values in fp32 and stores the RNE-bf16
 // result: one rounding per window (P1, "Tenir le journal plutôt que le solde").
 //
+// With per-channel decays (Kimi Delta Attention) the scalars become vectors
+// over the key channels n: S_c[:, n] <- exp(Lam[n]) S_c[:, n] + sum_j u_j
+// k_j[n] exp(lam_j[n]), suffix sums taken per channel over the log-gate rows.
+//
 // Rollback (P2, "Un retour en arrière qui devient trivial") touches integers
 // only: len -= n_drop, n_tent = 0.
 #include "device.h"
@@ -28,17 +32,19 @@ constexpr int kFlushStage = 2;  // 16-byte B loads per thread per staging round
 // (row p holds entries j = 0..R-1 contiguously, padded to a multiple of 4) so
 // that one 16-byte read gives a row's x for four consecutive entries.
 struct FlushLds {
-  int RS, oXT, oB, oCF, total;
-  __host__ __device__ FlushLds(int R, int P, int N) {
+  int RS, oXT, oB, oCF, oG, oDc, total;
+  __host__ __device__ FlushLds(int R, int P, int N, bool pcd) {
     RS = align4(R);
     oXT = 0;                 // x transposed  [P][RS]
     oB = P * RS;             // window B rows [R][N]
     oCF = oB + R * N;        // c_j = exp(lam_j) dt_j [R], then exp(Lam)
-    total = oCF + R + 1;
+    oG = align4(oCF + R + 1);        // per-channel log-decay rows [R][N]
+    oDc = oG + (pcd ? R * N : 0);    // per-channel exp(Lam[n]) [N]
+    total = oDc + (pcd ? N : 0);
   }
 };
 
-template <int N, typename Tin, int MODE>
+template <int N, typename Tin, int MODE, bool PCD>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   constexpr bool DUAL = MODE == kCkptDual, B16 = MODE == kCkptBf16;
   using Geo = TileGeom<N, false>;
@@ -66,11 +72,13 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (tid == 0) atomicOr(a.err, kDevUncommitted);
     return;
   }
-  const FlushLds lay(R, P, N);
+  const FlushLds lay(R, P, N, PCD);
   const int RS = lay.RS;
   float* sXT = lds + lay.oXT;
   float* sB = lds + lay.oB;
   float* sCF = lds + lay.oCF;
+  float* sG = lds + lay.oG;
+  float* sDc = lds + lay.oDc;
   const Tin* rx = static_cast<const Tin*>(a.ring_x);
   const Tin* rB = static_cast<const Tin*>(a.ring_B);
   auto xrow = [&](int j) { return rx + ((size_t)bh * R + ring_slot(head, j, R)) * P; };
@@ -98,7 +106,15 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
 
   // 2. Window B rows, x (transposed) and (dt, l), unpacked into LDS.
   float2 dl = make_float2(0.f, 0.f);
-  if (tid < n) dl = a.ring_dl[(size_t)bh * R + ring_slot(head, tid, R)];
+  if (!PCD && tid < n) dl = a.ring_dl[(size_t)bh * R + ring_slot(head, tid, R)];
+  if constexpr (PCD) {  // the window's per-channel log-decay rows
+    const float* rg = a.ring_g + (size_t)bh * R * N;
+    for (int q = tid; q < n * (N / 4); q += kThreads) {
+      const int j = q / (N / 4), c = q - j * (N / 4);
+      *reinterpret_cast<float4*>(sG + j * N + c * 4) =
+          *reinterpret_cast<const float4*>(rg + ring_slot(head, j, R) * N + c * 4);
+    }
+  }
   const int totBV = n * NV;
   for (int q0 = 0; q0 < totBV; q0 += kFlushStage * kThreads) {
     VT vb[kFlushStage];
@@ -138,24 +154,43 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     const int p = e / (n4 - n);
     sXT[p * RS + n + (e - p * (n4 - n))] = 0.f;
   }
-  if (wave == 0) {  // c_j = exp(sum_{j<m<n} l_m) dt_j and exp(Lam), tree-summed
+  if (!PCD && wave == 0) {  // c_j = exp(sum_{j<m<n} l_m) dt_j and exp(Lam), tree-summed
     const float u = lane < n ? dl.y : 0.f;
     const float lam = wave_suffix_excl(u, lane);
     if (lane < n) sCF[lane] = expf(lam) * dl.x;
     if (lane == 0) sCF[R] = expf(lam + u);
   }
   __syncthreads();
-  const float D = sCF[R];
+  if constexpr (PCD) {
+    // Channel c (one thread each): lam_j[c] from the newest entry back; the
+    // decay goes into the staged key rows, exp(Lam[c]) scales tile column c.
+    if (tid < N) {
+      float acc = 0.f;
+      for (int j = n - 1; j >= 0; --j) {
+        sB[j * N + tid] *= expf(acc);
+        acc += sG[j * N + tid];
+      }
+      sDc[tid] = expf(acc);
+    }
+    if (tid < n) sCF[tid] = 1.f;
+    __syncthreads();
+  }
+  const float D = PCD ? 1.f : sCF[R];
+  float Dc[4] = {D, D, D, D};
+  if constexpr (PCD) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Dc[v] = sDc[col * 4 + v];
+  }
 
   // 3. S <- D S + sum_j x_j outer (c_j B_j), four entries per step, in place.
   for (int base = 0; base < P; base += RPP * kMaxPass) {
     if (base > 0) load_chunk(base);
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
-      fr[k].v.x *= D;
-      fr[k].v.y *= D;
-      fr[k].v.z *= D;
-      fr[k].v.w *= D;
+      fr[k].v.x *= Dc[0];
+      fr[k].v.y *= Dc[1];
+      fr[k].v.z *= Dc[2];
+      fr[k].v.w *= Dc[3];
     }
     for (int j4 = 0; j4 < n; j4 += 4) {
       float4 bv[4];
@@ -208,10 +243,10 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   if (tid == 0) a.ptr[bh] = make_int4(ring_slot(head, n, R), 0, 0, 0);
 }
 
-template <int N, typename Tin, int MODE>
+template <int N, typename Tin, int MODE, bool PCD = false>
 static hipError_t flush_one(const FlushArgs& a, int batch, hipStream_t s) {
-  const size_t lds = (size_t)FlushLds(a.R, a.P, N).total * sizeof(float);
-  auto kern = flush_kernel<N, Tin, MODE>;
+  const size_t lds = (size_t)FlushLds(a.R, a.P, N, PCD).total * sizeof(float);
+  auto kern = flush_kernel<N, Tin, MODE, PCD>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -232,18 +267,23 @@ static hipError_t flush_t(const FlushArgs& a, int batch, int mode, hipStream_t s
 }
 
 template <int N>
-static hipError_t flush_n(const FlushArgs& a, int batch, bool bf16_in, int mode, hipStream_t s) {
+static hipError_t flush_n(const FlushArgs& a, int batch, bool bf16_in, int mode, bool pcd,
+                          hipStream_t s) {
+  if (pcd) {  // per-channel decay: fp32 rows and checkpoint only (Kimi Delta Attention)
+    if (bf16_in || mode != kCkptF32) return hipErrorInvalidValue;
+    return flush_one<N, float, kCkptF32, true>(a, batch, s);
+  }
   return bf16_in ? flush_t<N, bf16_t>(a, batch, mode, s) : flush_t<N, float>(a, batch, mode, s);
 }
 
 hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode,
-                        hipStream_t s) {
+                        bool per_channel, hipStream_t s) {
   switch (N) {
-    case 16: return flush_n<16>(a, batch, bf16_in, mode, s);
-    case 32: return flush_n<32>(a, batch, bf16_in, mode, s);
-    case 64: return flush_n<64>(a, batch, bf16_in, mode, s);
-    case 128: return flush_n<128>(a, batch, bf16_in, mode, s);
-    case 256: return flush_n<256>(a, batch, bf16_in, mode, s);
+    case 16: return flush_n<16>(a, batch, bf16_in, mode, per_channel, s);
+    case 32: return flush_n<32>(a, batch, bf16_in, mode, per_channel, s);
+    case 64: return flush_n<64>(a, batch, bf16_in, mode, per_channel, s);
+    case 128: return flush_n<128>(a, batch, bf16_in, mode, per_channel, s);
+    case 256: return flush_n<256>(a, batch, bf16_in, mode, per_channel, s);
     default: return hipErrorInvalidValue;
   }
 }

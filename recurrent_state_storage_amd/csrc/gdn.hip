@@ -15,25 +15,36 @@
 //   S_{t-1} z = exp(Lam) S_c z + sum_j exp(lam_j) (k_j . z) u_j   for z = k_t, q_t
 // in one pass over the checkpoint tile (two row dots per row), with
 // lam_j = sum of log alpha over the window entries after j, Lam over all of them.
+//
+// Kimi Delta Attention (KDA, named beside GDN on P1 "Des couches rapides sur le
+// papier") is the same rule with one gate per key channel:
+//   S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+//   u_t = beta_t (v_t - S_{t-1} (alpha_t * k_t)),  o_t = S_{t-1} (alpha_t * q_t) + (k_t . q_t) u_t
+// The decays become per-channel suffix sums lam_j[n] (entries after j, the new
+// token's gate included) and Lam[n]: replay dots the tile rows with
+// exp(Lam) * k_t and exp(Lam) * q_t, and the ring term uses the channel-scaled
+// keys k_j * exp(lam_j). The ring keeps log alpha_j as a row per entry.
 #include "device.h"
 #include "launch.h"
 
 namespace rss {
 
-// Dynamic LDS of the GDN replay kernel, in floats.
+// Dynamic LDS of the GDN / KDA replay kernel, in floats.
 struct GdnLds {
-  int oK, oU, oQ, oCF, oS, total;
-  __host__ __device__ GdnLds(int R, int P, int N) {
-    oK = 0;                   // window k rows [R][N] (row n0 = k_t)
+  int oK, oU, oQ, oCF, oS, oG, oD, total;
+  __host__ __device__ GdnLds(int R, int P, int N, bool kda) {
+    oK = 0;                   // window k rows [R][N] (row n0 = k_t); KDA: scaled in place
     oU = R * N;               // window u rows [R][P]
     oQ = oU + R * P;          // q_t [N]
     oCF = oQ + N;             // exp(lam_j) [R], then exp(Lam), k_t . q_t
     oS = align4(oCF + R + 2); // shares [4 waves][2][P]: sum_j w u_j for z = k_t, q_t
-    total = oS + 8 * P;
+    oG = oS + 8 * P;          // KDA: committed log-gate rows [R][N]
+    oD = oG + (kda ? R * N : 0);   // KDA: exp(Lam[n]) [N]
+    total = oD + (kda ? N : 0);
   }
 };
 
-template <int N, int MP>
+template <int N, int MP, bool KDA>
 __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
@@ -63,7 +74,9 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     }
   };
   load_chunk(0);
-  const float alpha = a.alpha[bh], beta = a.beta[bh];
+  // KDA: the gates are per channel and enter through the scaled vectors below,
+  // so the scalar gate of the shared formulas is 1.
+  const float alpha = KDA ? 1.f : a.alpha[bh], beta = a.beta[bh];
 
   const int4 pt = a.ptr[bh];
   const int head = pt.x, n0 = pt.y;
@@ -75,12 +88,15 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     return;
   }
 
-  const GdnLds lay(R, P, N);
+  const GdnLds lay(R, P, N, KDA);
   float* sK = lds + lay.oK;
   float* sU = lds + lay.oU;
   float* sQ = lds + lay.oQ;
   float* sCF = lds + lay.oCF;
   float* sS = lds + lay.oS;
+  float* sG = lds + lay.oG;
+  float* sD = lds + lay.oD;
+  float* rg = KDA ? a.ring_g + (size_t)bh * R * N : nullptr;
   float* ru = a.ring_u + (size_t)bh * R * P;
   float* rk = a.ring_k + (size_t)bh * R * N;
   float2* rdl = a.ring_dl + (size_t)bh * R;
@@ -110,10 +126,21 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
       }
     }
   }
-  float qv = 0.f;
+  if constexpr (KDA) {  // the committed entries' log-gate rows
+    const int totG = n0 * NV;
+    for (int q0 = wave * 64; q0 < totG; q0 += kThreads) {
+      const int q = q0 + lane;
+      if (q < totG) {
+        const int j = q / NV;
+        dma16(rg + ring_slot(head, j, R) * N + (q - j * NV) * 4, sG + q0 * 4);
+      }
+    }
+  }
+  float qv = 0.f, av = 1.f;
   if (tid < N) qv = qin[tid];
+  if (KDA && tid < N) av = a.alpha[(size_t)bh * N + tid];
   float2 dl = make_float2(0.f, 0.f);
-  if (tid < n0) dl = rdl[ring_slot(head, tid, R)];
+  if (!KDA && tid < n0) dl = rdl[ring_slot(head, tid, R)];
   if (!uvec) {
     for (int e = tid; e < n0 * P; e += kThreads) {
       const int j = e / P;
@@ -121,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     }
   }
   if (tid < N) sQ[tid] = qv;
-  if (wave == 0) {  // exp(lam_j) over the committed entries, and exp(Lam)
+  if (!KDA && wave == 0) {  // exp(lam_j) over the committed entries, and exp(Lam)
     const float u = lane < n0 ? dl.y : 0.f;
     const float lam = wave_suffix_excl(u, lane);
     if (lane < n0) sCF[lane] = expf(lam);
@@ -130,6 +157,23 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (KDA) {
+    // Channel n (one thread each): lam_j[n] from the newest entry back, the new
+    // token's gate included; scale the committed keys in place; exp(Lam[n]).
+    if (tid < N) {
+      const float gt = logf(av);
+      rg[ring_slot(head, n0, R) * N + tid] = gt;
+      float acc = gt;
+      for (int j = n0 - 1; j >= 0; --j) {
+        sK[j * N + tid] *= expf(acc);
+        acc += sG[j * N + tid];
+      }
+      sD[tid] = expf(acc);
+    }
+    if (tid < n0) sCF[tid] = 1.f;
+    if (tid == 0) sCF[R] = 1.f;
+    __syncthreads();
+  }
 
   // k_t . q_t, and per wavefront its share of sum_j exp(lam_j)(k_j . z) u_j.
   if (wave == 0) {
@@ -185,8 +229,9 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   float kc[4], qc[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    kc[v] = sK[n0 * N + col * 4 + v];
-    qc[v] = sQ[col * 4 + v];
+    const float dn = KDA ? sD[col * 4 + v] : 1.f;
+    kc[v] = dn * sK[n0 * N + col * 4 + v];
+    qc[v] = dn * sQ[col * 4 + v];
   }
   float* unew = ru + ring_slot(head, n0, R) * P;
   for (int base = 0; base < P; base += RPP * MP) {
@@ -226,14 +271,14 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
 
 // Eager gated delta rule: S <- alpha S + u k^T with u = beta (v - alpha S k),
 // o = alpha (S q) + (k . q) u, on the state in place.
-template <int N, int MP>
+template <int N, int MP, bool KDA>
 __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
   constexpr int EPL = N >= 64 ? N / 64 : 1;
   using RS = RowScatter<TPR>;
 
-  extern __shared__ __align__(16) float lds[];  // k [N], q [N], u [P], k.q
+  extern __shared__ __align__(16) float lds[];  // k [N], q [N], u [P], k.q, KDA gates [N]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -253,14 +298,16 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
     }
   };
   load_chunk(0);
-  const float alpha = a.alpha[bh], beta = a.beta[bh];
+  const float alpha = KDA ? 1.f : a.alpha[bh], beta = a.beta[bh];
   float* sk = lds;
   float* sq = lds + N;
   float* su = lds + 2 * N;
   float* skq = su + P;
+  float* sa = skq + 1;
   for (int n = tid; n < N; n += kThreads) {
     sk[n] = a.k[(size_t)bh * N + n];
     sq[n] = a.q[(size_t)bh * N + n];
+    if (KDA) sa[n] = a.alpha[(size_t)bh * N + n];
   }
   __syncthreads();
   if (wave == 0) {
@@ -273,11 +320,16 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
     part = wave_sum(part);
     if (lane == 0) *skq = part;
   }
-  float kc[4], qc[4];
+  // Row dots use S (alpha * k) and S (alpha * q); the update decays column c by
+  // its gate ac[c] (KDA) or every column by alpha (GDN: the gate is folded below).
+  float kc[4], qc[4], kr[4], ac[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    kc[v] = sk[col * 4 + v];
-    qc[v] = sq[col * 4 + v];
+    const float g = KDA ? sa[col * 4 + v] : 1.f;
+    kr[v] = sk[col * 4 + v];
+    kc[v] = g * kr[v];
+    qc[v] = g * sq[col * 4 + v];
+    ac[v] = KDA ? g : alpha;
   }
   const float* vin = a.v + (size_t)bh * P;
   float* oout = a.o + (size_t)bh * P;
@@ -317,20 +369,20 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
       if (row < P) {
         const float u = su[row];
         float4 s = fr[k].v;
-        s.x = fmaf(u, kc[0], alpha * s.x);
-        s.y = fmaf(u, kc[1], alpha * s.y);
-        s.z = fmaf(u, kc[2], alpha * s.z);
-        s.w = fmaf(u, kc[3], alpha * s.w);
+        s.x = fmaf(u, kr[0], ac[0] * s.x);
+        s.y = fmaf(u, kr[1], ac[1] * s.y);
+        s.z = fmaf(u, kr[2], ac[2] * s.z);
+        s.w = fmaf(u, kr[3], ac[3] * s.w);
         st16(tile + row * N + col * 4, s);
       }
     }
   }
 }
 
-template <int N, int MP>
+template <int N, int MP, bool KDA>
 static hipError_t gdn_replay_one(const GdnArgs& a, int batch, hipStream_t s) {
-  const size_t lds = (size_t)GdnLds(a.R, a.P, N).total * sizeof(float);
-  auto kern = gdn_replay_kernel<N, MP>;
+  const size_t lds = (size_t)GdnLds(a.R, a.P, N, KDA).total * sizeof(float);
+  auto kern = gdn_replay_kernel<N, MP, KDA>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -340,44 +392,54 @@ static hipError_t gdn_replay_one(const GdnArgs& a, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int N>
+template <int N, bool KDA>
 static hipError_t gdn_replay_n(const GdnArgs& a, int batch, hipStream_t s) {
   constexpr int RPP = TileGeom<N, false>::RPP;
-  return a.P > 8 * RPP ? gdn_replay_one<N, 16>(a, batch, s) : gdn_replay_one<N, 8>(a, batch, s);
+  return a.P > 8 * RPP ? gdn_replay_one<N, 16, KDA>(a, batch, s) : gdn_replay_one<N, 8, KDA>(a, batch, s);
 }
 
-hipError_t launch_gdn_replay(const GdnArgs& a, int batch, int N, hipStream_t s) {
+template <int N>
+static hipError_t gdn_replay_k(const GdnArgs& a, int batch, bool kda, hipStream_t s) {
+  return kda ? gdn_replay_n<N, true>(a, batch, s) : gdn_replay_n<N, false>(a, batch, s);
+}
+
+hipError_t launch_gdn_replay(const GdnArgs& a, int batch, int N, bool kda, hipStream_t s) {
   switch (N) {
-    case 16: return gdn_replay_n<16>(a, batch, s);
-    case 32: return gdn_replay_n<32>(a, batch, s);
-    case 64: return gdn_replay_n<64>(a, batch, s);
-    case 128: return gdn_replay_n<128>(a, batch, s);
-    case 256: return gdn_replay_n<256>(a, batch, s);
+    case 16: return gdn_replay_k<16>(a, batch, kda, s);
+    case 32: return gdn_replay_k<32>(a, batch, kda, s);
+    case 64: return gdn_replay_k<64>(a, batch, kda, s);
+    case 128: return gdn_replay_k<128>(a, batch, kda, s);
+    case 256: return gdn_replay_k<256>(a, batch, kda, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int N, int MP>
+template <int N, int MP, bool KDA>
 static hipError_t gdn_eager_one(const GdnEagerArgs& a, int batch, hipStream_t s) {
-  const size_t lds = (size_t)(2 * N + a.P + 1) * sizeof(float);
-  hipLaunchKernelGGL((gdn_eager_kernel<N, MP>), dim3((unsigned)((size_t)batch * a.H)),
+  const size_t lds = (size_t)(2 * N + a.P + 1 + (KDA ? N : 0)) * sizeof(float);
+  hipLaunchKernelGGL((gdn_eager_kernel<N, MP, KDA>), dim3((unsigned)((size_t)batch * a.H)),
                      dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
-template <int N>
+template <int N, bool KDA>
 static hipError_t gdn_eager_n(const GdnEagerArgs& a, int batch, hipStream_t s) {
   constexpr int RPP = TileGeom<N, false>::RPP;
-  return a.P > 8 * RPP ? gdn_eager_one<N, 16>(a, batch, s) : gdn_eager_one<N, 8>(a, batch, s);
+  return a.P > 8 * RPP ? gdn_eager_one<N, 16, KDA>(a, batch, s) : gdn_eager_one<N, 8, KDA>(a, batch, s);
 }
 
-hipError_t launch_gdn_eager(const GdnEagerArgs& a, int batch, int N, hipStream_t s) {
+template <int N>
+static hipError_t gdn_eager_k(const GdnEagerArgs& a, int batch, bool kda, hipStream_t s) {
+  return kda ? gdn_eager_n<N, true>(a, batch, s) : gdn_eager_n<N, false>(a, batch, s);
+}
+
+hipError_t launch_gdn_eager(const GdnEagerArgs& a, int batch, int N, bool kda, hipStream_t s) {
   switch (N) {
-    case 16: return gdn_eager_n<16>(a, batch, s);
-    case 32: return gdn_eager_n<32>(a, batch, s);
-    case 64: return gdn_eager_n<64>(a, batch, s);
-    case 128: return gdn_eager_n<128>(a, batch, s);
-    case 256: return gdn_eager_n<256>(a, batch, s);
+    case 16: return gdn_eager_k<16>(a, batch, kda, s);
+    case 32: return gdn_eager_k<32>(a, batch, kda, s);
+    case 64: return gdn_eager_k<64>(a, batch, kda, s);
+    case 128: return gdn_eager_k<128>(a, batch, kda, s);
+    case 256: return gdn_eager_k<256>(a, batch, kda, s);
     default: return hipErrorInvalidValue;
   }
 }

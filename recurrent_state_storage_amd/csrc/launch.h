@@ -42,12 +42,13 @@ struct FlushArgs {
   const void* ring_x;
   const void* ring_B;
   const float2* ring_dl;
+  const float* ring_g;     // per-channel log-decay rows [Bt,H,R,N] (KDA), else unused
   int4* ptr;
   int* err;
   int H, P, G, R, min_len;
 };
 hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode,
-                        hipStream_t s);
+                        bool per_channel, hipStream_t s);
 
 // ckpt <- S0 (or 0), read copy <- bf16(ckpt), pointers and error word <- 0.
 struct InitArgs {
@@ -88,23 +89,24 @@ struct EagerArgs {
 hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, bool bf16_state,
                         hipStream_t s);
 
-// Gated DeltaNet replay decode (one token) and its eager baseline.
+// Gated DeltaNet / KDA replay decode (one token) and the eager baselines.
 struct GdnArgs {
   float* ckpt;             // [Bt,H,P,N] fp32, P = d_v, N = d_k
   float* ring_u;           // [Bt,H,R,P]
   float* ring_k;           // [Bt,H,R,N]
-  float2* ring_dl;         // [Bt,H,R] (1, log alpha)
+  float2* ring_dl;         // GDN: [Bt,H,R] (1, log alpha)
+  float* ring_g;           // KDA: [Bt,H,R,N] log alpha per channel
   int4* ptr;               // [Bt,H]
   int* err;
   const float* q;          // [Bt,H,N]
   const float* k;          // [Bt,H,N]
   const float* v;          // [Bt,H,P]
   const float* beta;       // [Bt,H]
-  const float* alpha;      // [Bt,H]
+  const float* alpha;      // GDN [Bt,H]; KDA [Bt,H,N]
   float* o;                // [Bt,H,P]
   int H, P, R;
 };
-hipError_t launch_gdn_replay(const GdnArgs& a, int batch, int N, hipStream_t s);
+hipError_t launch_gdn_replay(const GdnArgs& a, int batch, int N, bool kda, hipStream_t s);
 
 struct GdnEagerArgs {
   float* S;                // [Bt,H,P,N], updated in place
@@ -116,6 +118,6 @@ struct GdnEagerArgs {
   float* o;
   int H, P;
 };
-hipError_t launch_gdn_eager(const GdnEagerArgs& a, int batch, int N, hipStream_t s);
+hipError_t launch_gdn_eager(const GdnEagerArgs& a, int batch, int N, bool kda, hipStream_t s);
 
 }  // namespace rss

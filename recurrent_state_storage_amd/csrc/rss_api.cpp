@@ -37,8 +37,9 @@ int32_t check_config(const rss_config* c) {
   int32_t st = check_shape(c);
   if (st) return st;
   if (!valid_mode(c->read_copy)) return RSS_E_DTYPE;
-  if (c->kind != RSS_KIND_MAMBA2 && c->kind != RSS_KIND_GDN) return RSS_E_INVALID;
-  if (c->kind == RSS_KIND_GDN) {  // one key per head, fp32, no read copy, no drafts
+  if (c->kind != RSS_KIND_MAMBA2 && c->kind != RSS_KIND_GDN && c->kind != RSS_KIND_KDA)
+    return RSS_E_INVALID;
+  if (c->kind != RSS_KIND_MAMBA2) {  // delta rules: one key per head, fp32, no read copy, no drafts
     if (c->ngroups != c->nheads) return RSS_E_SHAPE;
     if (c->in_dtype != RSS_DTYPE_F32 || c->read_copy != RSS_COPY_NONE) return RSS_E_DTYPE;
     if (c->max_draft != 0) return RSS_E_CAPACITY;
@@ -71,7 +72,7 @@ bool inputs_ok(const void* x, const void* B, const void* C, const void* dt, cons
 
 extern "C" {
 
-int32_t rss_version(void) { return 10200; }
+int32_t rss_version(void) { return 10300; }
 
 const char* rss_status_string(int32_t s) {
   switch (s) {
@@ -96,9 +97,9 @@ int32_t rss_buffer_sizes(const rss_config* c, rss_sizes* out) {
   out->ckpt_lo = c->read_copy == RSS_COPY_BF16 ? Bt * H * P * N * 2 : 0;
   out->ring_x = Bt * H * R * P * in_bytes(c);
   out->ring_B = Bt * G * R * N * in_bytes(c);
-  out->ring_dl = Bt * H * R * 2 * 4;
+  out->ring_dl = Bt * H * R * (c->kind == RSS_KIND_KDA ? N : 2) * 4;
   out->ptr = Bt * H * 4 * 4;
-  out->A = c->kind == RSS_KIND_GDN ? 0 : H * 4;
+  out->A = c->kind == RSS_KIND_MAMBA2 ? H * 4 : 0;
   out->dev_err = 4;
   return RSS_OK;
 }
@@ -110,7 +111,7 @@ int32_t rss_layer_bind(const rss_config* c, const rss_buffers* d, rss_layer** ou
   if (st) return st;
   if (!d) return RSS_E_INVALID;
   if (!d->dev_err || !aligned16(d->dev_err)) return RSS_E_INVALID;
-  if (c->kind == RSS_KIND_MAMBA2 && (!d->A || !aligned16(d->A))) return RSS_E_INVALID;
+  if (c->kind == RSS_KIND_MAMBA2 && (!d->A || !aligned16(d->A))) return RSS_E_INVALID;  // delta rules: unused
   if (c->batch > 0) {  // with no sequences the per-sequence buffers may be empty (NULL)
     const void* req[] = {d->ckpt, d->ring_x, d->ring_B, d->ring_dl, d->ptr};
     for (const void* p : req)
@@ -250,14 +251,16 @@ int32_t rss_flush_checkpoint(rss_layer* l, int32_t min_len, void* stream) {
   a.G = c.ngroups;
   a.R = c.capacity;
   a.min_len = min_len;
+  a.ring_g = c.kind == RSS_KIND_KDA ? l->dev.ring_dl : nullptr;
   return launch_status(rss::launch_flush(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
-                                         c.read_copy,
+                                         c.read_copy, c.kind == RSS_KIND_KDA,
                                          static_cast<hipStream_t>(stream)));
 }
 
-int32_t rss_gdn_decode_step(rss_layer* l, const float* q, const float* k, const float* v,
-                            const float* beta, const float* alpha, float* o, void* stream) {
-  if (!l || l->cfg.kind != RSS_KIND_GDN) return RSS_E_INVALID;
+static int32_t delta_decode(rss_layer* l, int32_t kind, const float* q, const float* k,
+                            const float* v, const float* beta, const float* alpha, float* o,
+                            void* stream) {
+  if (!l || l->cfg.kind != kind) return RSS_E_INVALID;
   const rss_config& c = l->cfg;
   if (c.batch > 0 && (!inputs_ok(q, k, v, beta, o) || !alpha || !aligned16(alpha)))
     return RSS_E_INVALID;
@@ -268,6 +271,7 @@ int32_t rss_gdn_decode_step(rss_layer* l, const float* q, const float* k, const 
   a.ring_u = static_cast<float*>(l->dev.ring_x);
   a.ring_k = static_cast<float*>(l->dev.ring_B);
   a.ring_dl = reinterpret_cast<float2*>(l->dev.ring_dl);
+  a.ring_g = l->dev.ring_dl;
   a.ptr = reinterpret_cast<int4*>(l->dev.ptr);
   a.err = l->dev.dev_err;
   a.q = q;
@@ -279,10 +283,21 @@ int32_t rss_gdn_decode_step(rss_layer* l, const float* q, const float* k, const 
   a.H = c.nheads;
   a.P = c.headdim;
   a.R = c.capacity;
-  return launch_status(rss::launch_gdn_replay(a, c.batch, c.dstate, static_cast<hipStream_t>(stream)));
+  return launch_status(rss::launch_gdn_replay(a, c.batch, c.dstate, kind == RSS_KIND_KDA,
+                                              static_cast<hipStream_t>(stream)));
 }
 
-int32_t rss_gdn_eager_step(const rss_config* c, float* S, const float* q, const float* k,
+int32_t rss_gdn_decode_step(rss_layer* l, const float* q, const float* k, const float* v,
+                            const float* beta, const float* alpha, float* o, void* stream) {
+  return delta_decode(l, RSS_KIND_GDN, q, k, v, beta, alpha, o, stream);
+}
+
+int32_t rss_kda_decode_step(rss_layer* l, const float* q, const float* k, const float* v,
+                            const float* beta, const float* alpha, float* o, void* stream) {
+  return delta_decode(l, RSS_KIND_KDA, q, k, v, beta, alpha, o, stream);
+}
+
+static int32_t delta_eager(const rss_config* c, bool kda, float* S, const float* q, const float* k,
                            const float* v, const float* beta, const float* alpha, float* o,
                            void* stream) {
   if (!c) return RSS_E_INVALID;
@@ -302,7 +317,20 @@ int32_t rss_gdn_eager_step(const rss_config* c, float* S, const float* q, const 
   a.o = o;
   a.H = c->nheads;
   a.P = c->headdim;
-  return launch_status(rss::launch_gdn_eager(a, c->batch, c->dstate, static_cast<hipStream_t>(stream)));
+  return launch_status(rss::launch_gdn_eager(a, c->batch, c->dstate, kda,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int32_t rss_gdn_eager_step(const rss_config* c, float* S, const float* q, const float* k,
+                           const float* v, const float* beta, const float* alpha, float* o,
+                           void* stream) {
+  return delta_eager(c, false, S, q, k, v, beta, alpha, o, stream);
+}
+
+int32_t rss_kda_eager_step(const rss_config* c, float* S, const float* q, const float* k,
+                           const float* v, const float* beta, const float* alpha, float* o,
+                           void* stream) {
+  return delta_eager(c, true, S, q, k, v, beta, alpha, o, stream);
 }
 
 int32_t rss_get_device_error(rss_layer* l, int32_t* host_code, void* stream) {

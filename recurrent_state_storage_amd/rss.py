@@ -24,7 +24,7 @@ RSS_OK, RSS_E_INVALID, RSS_E_SHAPE, RSS_E_DTYPE, RSS_E_CAPACITY, RSS_E_ORDER, RS
 RSS_DTYPE_F32, RSS_DTYPE_BF16 = 0, 1
 RSS_COPY_NONE, RSS_COPY_BF16, RSS_STATE_BF16 = 0, 1, 2
 RSS_DEV_ROLLBACK_RANGE, RSS_DEV_RING_OVERFLOW, RSS_DEV_UNCOMMITTED = 1, 2, 4
-RSS_KIND_MAMBA2, RSS_KIND_GDN = 0, 1
+RSS_KIND_MAMBA2, RSS_KIND_GDN, RSS_KIND_KDA = 0, 1, 2
 
 _I32 = ctypes.c_int32
 _VP = ctypes.c_void_p
@@ -61,6 +61,9 @@ _SIGS = {
     "rss_get_device_error": ([_VP, ctypes.POINTER(_I32), _VP], _I32),
     "rss_gdn_decode_step": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_gdn_eager_step": ([ctypes.POINTER(rss_config), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+                           _I32),
+    "rss_kda_decode_step": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
+    "rss_kda_eager_step": ([ctypes.POINTER(rss_config), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
                            _I32),
     "rss_eager_step": ([ctypes.POINTER(rss_config), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
                        _I32),
@@ -189,7 +192,8 @@ class ReplayLayer:
                         if c.read_copy == RSS_COPY_BF16 else None)
         self.ring_x = torch.zeros((c.batch, c.nheads, c.capacity, c.headdim), dtype=idt, device=dev)
         self.ring_B = torch.zeros((c.batch, c.ngroups, c.capacity, c.dstate), dtype=idt, device=dev)
-        self.ring_dl = torch.zeros((c.batch, c.nheads, c.capacity, 2), dtype=torch.float32, device=dev)
+        self.ring_dl = torch.zeros((c.batch, c.nheads, c.capacity, c.dstate if c.kind == RSS_KIND_KDA else 2),
+                                   dtype=torch.float32, device=dev)
         self.ptr = torch.zeros((c.batch, c.nheads, 4), dtype=torch.int32, device=dev)
         self.A = A
         if c.kind == RSS_KIND_MAMBA2 or A is not None:
@@ -234,6 +238,9 @@ class ReplayLayer:
 
     def gdn_decode_step(self, q, k, v, beta, alpha, o, stream=None):
         rss_gdn_decode_step(self, q, k, v, beta, alpha, o, stream)
+
+    def kda_decode_step(self, q, k, v, beta, alpha, o, stream=None):
+        rss_kda_decode_step(self, q, k, v, beta, alpha, o, stream)
 
     def device_error(self, stream=None) -> int:
         return rss_get_device_error(self, stream)
@@ -341,3 +348,22 @@ def rss_gdn_eager_step(cfg: rss_config, S, q, k, v, beta, alpha, o, stream=None)
             _ptr(k, f, kn, "k"), _ptr(v, f, vp, "v"), _ptr(beta, f, bh, "beta"),
             _ptr(alpha, f, bh, "alpha"), _ptr(o, f, vp, "o"))
     _check(library().rss_gdn_eager_step(ctypes.byref(cfg), *args, _stream(stream)), "rss_gdn_eager_step")
+
+
+def rss_kda_decode_step(layer: ReplayLayer, q, k, v, beta, alpha, o, stream=None) -> None:
+    c = layer.cfg
+    kn, vp, bh = (c.batch, c.nheads, c.dstate), (c.batch, c.nheads, c.headdim), (c.batch, c.nheads)
+    f = torch.float32
+    args = (_ptr(q, f, kn, "q"), _ptr(k, f, kn, "k"), _ptr(v, f, vp, "v"), _ptr(beta, f, bh, "beta"),
+            _ptr(alpha, f, kn, "alpha"), _ptr(o, f, vp, "o"))
+    _check(library().rss_kda_decode_step(layer.handle, *args, _stream(stream)), "rss_kda_decode_step")
+
+
+def rss_kda_eager_step(cfg: rss_config, S, q, k, v, beta, alpha, o, stream=None) -> None:
+    c = cfg
+    kn, vp, bh = (c.batch, c.nheads, c.dstate), (c.batch, c.nheads, c.headdim), (c.batch, c.nheads)
+    f = torch.float32
+    args = (_ptr(S, f, (c.batch, c.nheads, c.headdim, c.dstate), "S"), _ptr(q, f, kn, "q"),
+            _ptr(k, f, kn, "k"), _ptr(v, f, vp, "v"), _ptr(beta, f, bh, "beta"),
+            _ptr(alpha, f, kn, "alpha"), _ptr(o, f, vp, "o"))
+    _check(library().rss_kda_eager_step(ctypes.byref(cfg), *args, _stream(stream)), "rss_kda_eager_step")

@@ -26,7 +26,8 @@ def cfg_of(wl, **kw):
              in_dtype=rss.RSS_DTYPE_BF16 if wl.in_dtype == "bf16" else rss.RSS_DTYPE_F32,
              read_copy={"none": rss.RSS_COPY_NONE, "bf16": rss.RSS_COPY_BF16,
                         "bf16_state": rss.RSS_STATE_BF16}[wl.read_copy],
-             kind=rss.RSS_KIND_GDN if wl.kind == "gdn" else rss.RSS_KIND_MAMBA2)
+             kind={"mamba2": rss.RSS_KIND_MAMBA2, "gdn": rss.RSS_KIND_GDN,
+                   "kda": rss.RSS_KIND_KDA}[wl.kind])
     d.update(kw)
     return rss.rss_config(**d)
 

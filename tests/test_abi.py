@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rss.rss_version() == 10200
+    assert rss.rss_version() == 10300
     for s in range(7):
         assert rss.status_string(s)
     assert rss.status_string(99) == "unknown status"
@@ -83,7 +83,7 @@ def test_buffer_sizes():
     (dict(max_draft=-1), rss.RSS_E_CAPACITY),
     (dict(in_dtype=7), rss.RSS_E_DTYPE),
     (dict(read_copy=3), rss.RSS_E_DTYPE),
-    (dict(kind=2), rss.RSS_E_INVALID),
+    (dict(kind=3), rss.RSS_E_INVALID),
     (dict(kind=rss.RSS_KIND_GDN, ngroups=4, max_draft=0, in_dtype=rss.RSS_DTYPE_F32), rss.RSS_E_SHAPE),
     (dict(kind=rss.RSS_KIND_GDN, max_draft=0), rss.RSS_E_DTYPE),
     (dict(kind=rss.RSS_KIND_GDN, max_draft=0, in_dtype=rss.RSS_DTYPE_F32,
@@ -134,6 +134,30 @@ def test_gdn_layer_calls_are_kind_checked():
     finally:
         lib.rss_layer_free(h)
     assert lib.rss_gdn_eager_step(ctypes.byref(gcfg), None, A, A, A, A, A, A, None) == rss.RSS_E_INVALID
+
+
+def test_kda_layer_sizes_and_kind_checks():
+    kcfg = _cfg(kind=rss.RSS_KIND_KDA, max_draft=0, in_dtype=rss.RSS_DTYPE_F32)
+    s = rss.rss_buffer_sizes(kcfg)
+    assert s.A == 0 and s.ring_dl == 4 * 8 * 20 * 128 * 4       # one log-gate row per entry
+    st, h = _bind(kcfg, _fake_bufs(kcfg, null="A"))
+    assert st == rss.RSS_OK
+    lib = rss.library()
+    A = 0x7000000
+    try:
+        assert lib.rss_gdn_decode_step(h, A, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_decode_step(h, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_kda_decode_step(h, A, None, A, A, A, A, None) == rss.RSS_E_INVALID
+    finally:
+        lib.rss_layer_free(h)
+    st, h = _bind(_cfg(), _fake_bufs(_cfg()))
+    try:
+        assert lib.rss_kda_decode_step(h, A, A, A, A, A, A, None) == rss.RSS_E_INVALID
+    finally:
+        lib.rss_layer_free(h)
+    assert lib.rss_kda_eager_step(ctypes.byref(kcfg), None, A, A, A, A, A, A, None) == rss.RSS_E_INVALID
+    bad = _cfg(kind=rss.RSS_KIND_KDA, max_draft=0, in_dtype=rss.RSS_DTYPE_F32, ngroups=4)
+    assert _bind(bad, _fake_bufs(kcfg))[0] == rss.RSS_E_SHAPE
 
 
 def test_call_order_and_argument_errors_return_before_launch():
