@@ -210,6 +210,41 @@ def _gen_round(args):
     return r, d["x_bits"], d["B_bits"], d["C_bits"], d["dt"], synth.accepted_drafts(wl, r)
 
 
+def run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
+    """The benchmark workload with staggered folds: sequence b's first window is
+    1 + (b mod W) tokens long (per-sequence fold thresholds), W after that, so
+    every step folds ~Bt/W sequences inside the fused decode instead of all of
+    them on one step in W. Same inputs, same bytes per token."""
+    wl = workloads.get(WORKLOAD)
+    Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
+    cfg = rss.make_config(Bt, H, P, N, wl.ngroups, W, wl.capacity, 0, rss.RSS_DTYPE_BF16,
+                          rss.RSS_COPY_NONE)
+    layer = rss.ReplayLayer(cfg, A, dev)
+    layer.init_state()
+    y = torch.empty((Bt, H, P), device=dev)
+    T = X.shape[0]
+    first = 1 + np.arange(Bt) % W
+    th = [torch.from_numpy(np.where(t < first, first, W).astype(np.int32)).to(dev) for t in range(W + 1)]
+
+    def step(k):
+        i = k % T
+        layer.decode_flush_step_each(th[min(k, W)], X[i], Bm[i], Cm[i], DT[i], y)
+    for k in range(max(warmup, W)):
+        step(k)
+    k0 = max(warmup, W)
+    ms = _timed(torch, lambda j: step(k0 + j), steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for j in range(steps):
+        ev[j][0].record()
+        step(k0 + steps + j)
+        ev[j][1].record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    assert layer.device_error() == 0
+    return {"tokens_per_s": Bt * steps / (ms / 1e3), "step_us_median": float(np.median(d)),
+            "step_us_max": float(d.max()), "step_us_min": float(d.min())}
+
+
 def run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
     """Eager decode with the state stored in bf16 (rounded every token): the
     low-precision eager point of comparison, same inputs and shape."""
@@ -318,10 +353,14 @@ def run_spec(torch, rss, dev, rounds, warmup, workers, distinct=6):
 
 
 def gdn_bytes(wl, n0: int) -> dict:
-    """Algorithmic bytes per (sequence, head) of the GDN kernels (fp32)."""
+    """Algorithmic bytes per (sequence, head) of the GDN / KDA kernels (fp32)."""
     P, N = wl.headdim, wl.dstate
-    entry = 4 * N + 4 * P + 8                       # k, u, (1, log alpha)
-    inputs = 4 * N * 2 + 4 * P + 8                  # q, k, v, beta, alpha
+    if wl.kind == "kda":
+        entry = 8 * N + 4 * P                       # k, u, log-gate row
+        inputs = 4 * N * 3 + 4 * P + 4              # q, k, alpha row, v, beta
+    else:
+        entry = 4 * N + 4 * P + 8                   # k, u, (1, log alpha)
+        inputs = 4 * N * 2 + 4 * P + 8              # q, k, v, beta, alpha
     return {"replay": P * N * 4 + n0 * entry + inputs + 4 * P + entry + 32,
             "flush": 2 * P * N * 4 + wl.window * entry + 32,
             "eager": 2 * P * N * 4 + inputs + 4 * P}
@@ -329,21 +368,26 @@ def gdn_bytes(wl, n0: int) -> dict:
 
 def _gen_gdn(args):
     name, t = args
-    s = synth.gdn_step_inputs(workloads.get(name), t)
+    wl = workloads.get(name)
+    s = (synth.kda_step_inputs if wl.kind == "kda" else synth.gdn_step_inputs)(wl, t)
     return t, s
 
 
-def run_gdn(torch, rss, dev, steps, warmup, workers, distinct=64):
-    """Gated DeltaNet decode at batch 256, 32 heads, d_k = d_v = 128: replay
-    (+ flush every W) against the eager gated-delta-rule kernel."""
-    wl = workloads.get("gdn_b256_h32_d128_w16")
+def run_gdn(torch, rss, dev, steps, warmup, workers, distinct=64, name="gdn_b256_h32_d128_w16"):
+    """Gated DeltaNet (or, with the KDA workload, Kimi Delta Attention) decode at
+    batch 256, 32 heads, d_k = d_v = 128: replay (+ flush every W) against the
+    eager delta-rule kernel."""
+    wl = workloads.get(name)
+    kda = wl.kind == "kda"
     Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
     with concurrent.futures.ProcessPoolExecutor(max_workers=min(workers, 16)) as ex:
         got = sorted(ex.map(_gen_gdn, [(wl.name, t) for t in range(distinct)]), key=lambda g: g[0])
     D = [{k: torch.from_numpy(v).to(dev) for k, v in g[1].items()} for g in got]
     cfg = rss.make_config(Bt, H, P, N, H, W, wl.capacity, 0, rss.RSS_DTYPE_F32, rss.RSS_COPY_NONE,
-                          rss.RSS_KIND_GDN)
+                          rss.RSS_KIND_KDA if kda else rss.RSS_KIND_GDN)
     layer = rss.ReplayLayer(cfg, None, dev)
+    decode = layer.kda_decode_step if kda else layer.gdn_decode_step
+    eager_step = rss.rss_kda_eager_step if kda else rss.rss_gdn_eager_step
     layer.init_state()
     o = torch.empty((Bt, H, P), device=dev)
     evs = []
@@ -353,7 +397,7 @@ def run_gdn(torch, rss, dev, steps, warmup, workers, distinct=64):
         if rec:
             evs.append([torch.cuda.Event(enable_timing=True) for _ in range(4)])
             evs[-1][0].record()
-        layer.gdn_decode_step(d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
+        decode(d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
         if rec:
             evs[-1][1].record()
         if (k + 1) % W == 0:
@@ -373,12 +417,12 @@ def run_gdn(torch, rss, dev, steps, warmup, workers, distinct=64):
     f_list = [e[2].elapsed_time(e[3]) for j, e in enumerate(evs) if (base + j + 1) % W == 0]
     rbytes = sum(gdn_bytes(wl, (base + j) % W)["replay"] for j in range(steps)) * Bt * H
     assert layer.device_error() == 0
-    del layer
+    del layer, decode
     S = torch.zeros((Bt, H, P, N), device=dev)
 
     def eager(k):
         d = D[k % distinct]
-        rss.rss_gdn_eager_step(cfg, S, d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
+        eager_step(cfg, S, d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
     for k in range(warmup):
         eager(k)
     ems = _timed(torch, lambda j: eager(warmup + j), steps)
@@ -506,6 +550,8 @@ def main() -> int:
             fl_ms += ev[j][2].elapsed_time(ev[j][3])
             fl_bytes += flush_bytes(wl, W) * Bt * H
             n_fl += 1
+    step_us = [ev[j][0].elapsed_time(ev[j][1]) * 1e3 + (ev[j][2].elapsed_time(ev[j][3]) * 1e3
+               if phase[j] == W - 1 and not fused else 0.0) for j in range(args.steps)]
     rep_avg_us = rep_ms / n_rep * 1e3
     rep_gbs = rep_bytes / (rep_ms / 1e3) / 1e9
     assert layer.device_error() == 0
@@ -585,6 +631,7 @@ def main() -> int:
                 "avg_us": fl_ms / max(n_fl, 1) * 1e3,
                 "GBps": fl_bytes / (fl_ms / 1e3) / 1e9 if n_fl else None, "launches": n_fl},
         },
+        "step_us": {"median": float(np.median(step_us)), "max": float(np.max(step_us))},
         "eager_baseline": out_eager,
         "bytes_per_token": {"replay_state": st_replay, "eager_state": st_eager,
                             "state_ratio": st_replay / st_eager, "replay_total": tot_replay,
@@ -595,6 +642,8 @@ def main() -> int:
     if out_eager:
         rec["speedup_vs_eager_gpu"] = tok_s / out_eager["tokens_per_s"]
     if not args.no_extra:
+        rec["staggered_folds"] = run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, args.steps,
+                                             args.warmup)
         rec["dual_precision"] = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
         rec["low_precision"] = {
             "bf16_checkpoint": run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup,
@@ -604,6 +653,8 @@ def main() -> int:
         rec["speculative"] = run_spec(torch, rss, dev, rounds=48, warmup=8, workers=workers)
         rec["gated_deltanet"] = run_gdn(torch, rss, dev, steps=args.steps, warmup=args.warmup,
                                         workers=workers)
+        rec["kimi_delta_attention"] = run_gdn(torch, rss, dev, steps=args.steps, warmup=args.warmup,
+                                              workers=workers, name="kda_b256_h32_d128_w16")
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, pool, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -203,6 +203,18 @@ int32_t rss_decode_step(rss_layer* layer, const void* x, const void* B, const vo
 int32_t rss_decode_flush_step(rss_layer* layer, int32_t min_len, const void* x, const void* B,
                               const void* C, const float* dt, float* y, void* stream);
 
+/* rss_decode_flush_step with a threshold per sequence: min_len is device int32
+ * [Bt] (values below 1 act as 1), read by the launch, so sequences whose
+ * windows are out of phase fold on different steps. Setting min_len[b] =
+ * 1 + (b mod W) for the first window and W afterwards staggers the folds: every
+ * step then writes about Bt/W checkpoints instead of all Bt on one step in W,
+ * which flattens the per-step time (the fold still happens once per window per
+ * sequence, P1 "Tenir le journal plutôt que le solde"). Errors as
+ * rss_decode_flush_step; RSS_E_INVALID if min_len is null or misaligned. */
+int32_t rss_decode_flush_step_each(rss_layer* layer, const int32_t* min_len, const void* x,
+                                   const void* B, const void* C, const float* dt, float* y,
+                                   void* stream);
+
 /* Fold the ring into the checkpoint for every sequence whose window holds at
  * least min_len >= 1 entries (P1, "Tenir le journal plutôt que le solde":
  * rewritten only when the buffer is full; P3: once per window):
@@ -213,6 +225,11 @@ int32_t rss_decode_flush_step(rss_layer* layer, int32_t min_len, const void* x, 
  * RNE-bf16 of the result. Other sequences are untouched.
  * RSS_E_ORDER while a verify round is uncommitted. */
 int32_t rss_flush_checkpoint(rss_layer* layer, int32_t min_len, void* stream);
+
+/* rss_flush_checkpoint with a threshold per sequence (device int32 [Bt], values
+ * below 1 act as 1): sequence b is folded if its window holds >= min_len[b]
+ * entries. RSS_E_INVALID if min_len is null or misaligned. */
+int32_t rss_flush_checkpoint_each(rss_layer* layer, const int32_t* min_len, void* stream);
 
 /* Speculative verify of K+1 tokens per sequence (the last sampled token and K
  * drafts; 0 <= K <= K_max): append all K+1 as tentative entries (n_tent =

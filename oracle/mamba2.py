@@ -242,17 +242,19 @@ class ReplayModel:
             y[b] = self._output(b, C[b], int(self.ptr.len[b]))
         return y
 
-    def flush(self, threshold: int):
-        """Fold every sequence whose window holds >= threshold entries."""
+    def flush(self, threshold):
+        """Fold every sequence whose window holds >= threshold entries; the
+        threshold may be one value or one per sequence (values below 1 act as 1)."""
         folded = []
         for b in range(self.Bt):
             if self.ptr.n_tent[b]:
                 raise RingError("flush while a verify round is uncommitted")
-            if self.ptr.len[b] >= threshold:
+            th = max(1, int(threshold[b] if np.ndim(threshold) else threshold))
+            if self.ptr.len[b] >= th:
                 self.ckpt[b] = self.implied_state(b)
                 if self.read_copy == "bf16_state":
                     self.ckpt[b] = lowp.round_bf16(self.ckpt[b])
-                self.ptr.flush(b, threshold)
+                self.ptr.flush(b, th)
                 if self.copy is not None:
                     self.copy[b] = lowp.round_bf16(self.ckpt[b])
                 folded.append(b)

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   const int g = h / (H / G);
   const int4 pt = a.ptr[bh];
   const int head = pt.x, n = pt.y;
-  if (n == 0 || n < a.min_len) return;
+  const int th = a.min_len_dev ? a.min_len_dev[b] : a.min_len;
+  if (n == 0 || n < th) return;
   if (head < 0 || head >= R || n < 0 || n > R) {  // corrupt pointers: never index with them
     if (tid == 0) atomicOr(a.err, kDevRingOverflow);
     return;

@@ -26,6 +26,7 @@ struct ReplayArgs {
   float* y;                // [Bt,nt,H,P]
   int H, P, G, R, nt, set_tent;
   int fold_min_len;        // decode only: also fold windows that reach this length (0: never)
+  const int* fold_min_len_dev;  // [Bt] per-sequence fold thresholds (overrides fold_min_len), or null
   uint64_t xdiv;           // ceil(2^32 / d): q / d == (q * xdiv) >> 32 for q < 2^16,
                            // d = P/VE (16-byte x vectors per row) or P (element path)
 };
@@ -46,6 +47,7 @@ struct FlushArgs {
   int4* ptr;
   int* err;
   int H, P, G, R, min_len;
+  const int* min_len_dev;  // [Bt] per-sequence thresholds (overrides min_len), or null
 };
 hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode,
                         bool per_channel, hipStream_t s);

@@ -30,6 +30,8 @@
 // Fused fold: a decode launched with a fold threshold also folds, in the same
 // pass, every window the new token fills (the tile is already in registers),
 // and writes the new checkpoint: the flush's extra read of the tile is saved.
+// The threshold may differ per sequence, so that sequences whose windows are
+// out of phase fold on different steps (a staggered schedule).
 #include <type_traits>
 
 #include "device.h"
@@ -113,7 +115,8 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   // exactly as a separate flush would (same coefficients, same order).
   bool do_fold = false;
   if constexpr (FOLD) {
-    if (L >= a.fold_min_len) {
+    const int th = a.fold_min_len_dev ? a.fold_min_len_dev[b] : a.fold_min_len;
+    if (L >= th) {
       if (pt.z == 0) do_fold = true;
       else if (tid == 0) atomicOr(a.err, kDevUncommitted);  // never fold tentative entries
     }
@@ -379,7 +382,7 @@ template <int N, typename Tin, bool LOW>
 static hipError_t launch_nt(const ReplayArgs& a, int batch, hipStream_t s) {
   if (a.nt != 1) return launch_one<N, Tin, LOW, kMaxNew, false>(a, batch, s);
   if constexpr (!LOW) {  // the fused fold needs the fp32 checkpoint in registers
-    if (a.fold_min_len > 0) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
+    if (a.fold_min_len > 0 || a.fold_min_len_dev) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
   }
   return launch_one<N, Tin, LOW, 1, false>(a, batch, s);
 }

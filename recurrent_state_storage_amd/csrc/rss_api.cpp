@@ -150,8 +150,9 @@ int32_t rss_init_state(rss_layer* l, const float* S0, void* stream) {
   return launch_status(rss::launch_init(a, static_cast<hipStream_t>(stream)));
 }
 
-static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len, const void* x,
-                           const void* B, const void* C, const float* dt, float* y, void* stream) {
+static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len,
+                           const int32_t* fold_each, const void* x, const void* B, const void* C,
+                           const float* dt, float* y, void* stream) {
   const rss_config& c = l->cfg;
   if (c.batch == 0) return RSS_OK;
   rss::ReplayArgs a;
@@ -175,6 +176,7 @@ static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len,
   a.nt = nt;
   a.set_tent = set_tent;
   a.fold_min_len = fold_min_len;
+  a.fold_min_len_dev = fold_each;
   const int ve = c.in_dtype == RSS_DTYPE_BF16 ? 8 : 4;  // elements per 16-byte vector
   const uint64_t d = c.headdim % ve == 0 ? (uint64_t)(c.headdim / ve) : (uint64_t)c.headdim;
   a.xdiv = ((1ull << 32) + d - 1) / d;
@@ -188,20 +190,35 @@ int32_t rss_decode_step(rss_layer* l, const void* x, const void* B, const void* 
   if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
   if (l->pending_verify) return RSS_E_ORDER;
-  return replay_call(l, 1, 0, 0, x, B, C, dt, y, stream);
+  return replay_call(l, 1, 0, 0, nullptr, x, B, C, dt, y, stream);
+}
+
+static int32_t flush_call(rss_layer* l, int32_t min_len, const int32_t* each, void* stream);
+
+static int32_t decode_fold(rss_layer* l, int32_t min_len, const int32_t* each, const void* x,
+                           const void* B, const void* C, const float* dt, float* y, void* stream) {
+  if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
+  if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
+  if (l->pending_verify) return RSS_E_ORDER;
+  if (l->cfg.read_copy != RSS_COPY_NONE) {  // the replay reads a bf16 tile: two launches
+    const int32_t st = replay_call(l, 1, 0, 0, nullptr, x, B, C, dt, y, stream);
+    return st ? st : flush_call(l, min_len, each, stream);
+  }
+  return replay_call(l, 1, 0, min_len, each, x, B, C, dt, y, stream);
 }
 
 int32_t rss_decode_flush_step(rss_layer* l, int32_t min_len, const void* x, const void* B,
                               const void* C, const float* dt, float* y, void* stream) {
-  if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
   if (min_len < 1) return RSS_E_INVALID;
-  if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
-  if (l->pending_verify) return RSS_E_ORDER;
-  if (l->cfg.read_copy != RSS_COPY_NONE) {  // the replay reads a bf16 tile: two launches
-    const int32_t st = replay_call(l, 1, 0, 0, x, B, C, dt, y, stream);
-    return st ? st : rss_flush_checkpoint(l, min_len, stream);
-  }
-  return replay_call(l, 1, 0, min_len, x, B, C, dt, y, stream);
+  return decode_fold(l, min_len, nullptr, x, B, C, dt, y, stream);
+}
+
+int32_t rss_decode_flush_step_each(rss_layer* l, const int32_t* min_len, const void* x,
+                                   const void* B, const void* C, const float* dt, float* y,
+                                   void* stream) {
+  if (!l) return RSS_E_INVALID;
+  if (l->cfg.batch > 0 && (!min_len || !aligned16(min_len))) return RSS_E_INVALID;
+  return decode_fold(l, 1, min_len, x, B, C, dt, y, stream);
 }
 
 int32_t rss_verify_k_tokens(rss_layer* l, int32_t K, const void* x, const void* B, const void* C,
@@ -211,7 +228,7 @@ int32_t rss_verify_k_tokens(rss_layer* l, int32_t K, const void* x, const void* 
   if (K < 0) return RSS_E_INVALID;
   if (K > l->cfg.max_draft) return RSS_E_CAPACITY;
   if (l->pending_verify) return RSS_E_ORDER;
-  const int32_t st = replay_call(l, K + 1, 1, 0, x, B, C, dt, y, stream);
+  const int32_t st = replay_call(l, K + 1, 1, 0, nullptr, x, B, C, dt, y, stream);
   if (st == RSS_OK) l->pending_verify = 1;
   return st;
 }
@@ -235,6 +252,16 @@ int32_t rss_rollback(rss_layer* l, const int32_t* n_drop, void* stream) {
 int32_t rss_flush_checkpoint(rss_layer* l, int32_t min_len, void* stream) {
   if (!l) return RSS_E_INVALID;
   if (min_len < 1) return RSS_E_INVALID;
+  return flush_call(l, min_len, nullptr, stream);
+}
+
+int32_t rss_flush_checkpoint_each(rss_layer* l, const int32_t* min_len, void* stream) {
+  if (!l) return RSS_E_INVALID;
+  if (l->cfg.batch > 0 && (!min_len || !aligned16(min_len))) return RSS_E_INVALID;
+  return flush_call(l, 1, min_len, stream);
+}
+
+static int32_t flush_call(rss_layer* l, int32_t min_len, const int32_t* each, void* stream) {
   if (l->pending_verify) return RSS_E_ORDER;
   const rss_config& c = l->cfg;
   if (c.batch == 0) return RSS_OK;
@@ -251,6 +278,7 @@ int32_t rss_flush_checkpoint(rss_layer* l, int32_t min_len, void* stream) {
   a.G = c.ngroups;
   a.R = c.capacity;
   a.min_len = min_len;
+  a.min_len_dev = each;
   a.ring_g = c.kind == RSS_KIND_KDA ? l->dev.ring_dl : nullptr;
   return launch_status(rss::launch_flush(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
                                          c.read_copy, c.kind == RSS_KIND_KDA,

@@ -56,6 +56,8 @@ _SIGS = {
     "rss_decode_step": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_flush_checkpoint": ([_VP, _I32, _VP], _I32),
     "rss_decode_flush_step": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
+    "rss_decode_flush_step_each": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
+    "rss_flush_checkpoint_each": ([_VP, _VP, _VP], _I32),
     "rss_verify_k_tokens": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_rollback": ([_VP, _VP, _VP], _I32),
     "rss_get_device_error": ([_VP, ctypes.POINTER(_I32), _VP], _I32),
@@ -230,6 +232,12 @@ class ReplayLayer:
     def flush_checkpoint(self, min_len, stream=None):
         rss_flush_checkpoint(self, min_len, stream)
 
+    def decode_flush_step_each(self, min_len, x, B, C, dt, y, stream=None):
+        rss_decode_flush_step_each(self, min_len, x, B, C, dt, y, stream)
+
+    def flush_checkpoint_each(self, min_len, stream=None):
+        rss_flush_checkpoint_each(self, min_len, stream)
+
     def verify_k_tokens(self, K, x, B, C, dt, y, stream=None):
         rss_verify_k_tokens(self, K, x, B, C, dt, y, stream)
 
@@ -269,6 +277,23 @@ def rss_decode_flush_step(layer: ReplayLayer, min_len: int, x, B, C, dt, y, stre
             _ptr(dt, torch.float32, ds, "dt"), _ptr(y, torch.float32, xs, "y"))
     _check(library().rss_decode_flush_step(layer.handle, int(min_len), *args, _stream(stream)),
            "rss_decode_flush_step")
+
+
+def rss_decode_flush_step_each(layer: ReplayLayer, min_len, x, B, C, dt, y, stream=None) -> None:
+    c = layer.cfg
+    xs, bs, ds = layer.tok_shapes()
+    idt = _in_dtype(c.in_dtype)
+    args = (_ptr(x, idt, xs, "x"), _ptr(B, idt, bs, "B"), _ptr(C, idt, bs, "C"),
+            _ptr(dt, torch.float32, ds, "dt"), _ptr(y, torch.float32, xs, "y"))
+    th = _ptr(min_len, torch.int32, (c.batch,), "min_len")
+    _check(library().rss_decode_flush_step_each(layer.handle, th, *args, _stream(stream)),
+           "rss_decode_flush_step_each")
+
+
+def rss_flush_checkpoint_each(layer: ReplayLayer, min_len, stream=None) -> None:
+    th = _ptr(min_len, torch.int32, (layer.cfg.batch,), "min_len")
+    _check(library().rss_flush_checkpoint_each(layer.handle, th, _stream(stream)),
+           "rss_flush_checkpoint_each")
 
 
 def rss_flush_checkpoint(layer: ReplayLayer, min_len: int, stream=None) -> None:

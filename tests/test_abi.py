@@ -177,6 +177,9 @@ def test_call_order_and_argument_errors_return_before_launch():
         assert lib.rss_flush_checkpoint(h, 0, None) == rss.RSS_E_INVALID
         assert lib.rss_decode_flush_step(h, 0, A, A, A, A, A, None) == rss.RSS_E_INVALID
         assert lib.rss_decode_flush_step(h, 16, A, A, A + 8, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_decode_flush_step_each(h, None, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_decode_flush_step_each(h, A + 4, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_flush_checkpoint_each(h, None, None) == rss.RSS_E_INVALID
         assert lib.rss_rollback(h, None, None) == rss.RSS_E_INVALID
         assert lib.rss_init_state(h, A + 4, None) == rss.RSS_E_INVALID
         v = ctypes.c_int32()

@@ -110,3 +110,43 @@ def test_fused_folds_only_full_windows():
         if r == 0:
             log(f"  window lengths after round 0: {lens.tolist()}")
     assert fus.device_error() == 0 and sep.device_error() == 0
+
+
+@pytest.mark.parametrize("copy", ["none", "bf16", "bf16_state"])
+def test_staggered_folds(copy):
+    """Per-sequence thresholds 1 + (b mod W) until a sequence's first fold, W
+    after: each step folds only the sequences at their phase. The fused entry
+    point with per-sequence thresholds equals decode + per-sequence flush bit
+    for bit, folds exactly the sequences the integer schedule names, and matches
+    the oracle (driven with the same thresholds) at every step."""
+    W = 4
+    wl = BASE.replace(name="stagger", batch=7, headdim=64, dstate=128, nheads=3, ngroups=3,
+                      window=W, capacity=W, in_dtype="bf16", read_copy=copy, s0="normal", seed=5200)
+    log(f"[fused] staggered folds, Bt=7, W=4, copy={copy}")
+    sep, fus = _pair(wl)
+    A_np = synth.params(wl)["A"]
+    model = mamba2.ReplayModel(synth.initial_state(wl), A_np, wl.ngroups, wl.capacity, read_copy=copy)
+    first = 1 + np.arange(wl.batch) % W
+    worst = 0.0
+    for t in range(4 * W + 3):
+        th_np = np.where(t < first, first, W).astype(np.int32)
+        th = torch.from_numpy(th_np).to(DEV)
+        s = synth.step_inputs(wl, t)
+        d = dev_inputs(s, "bf16")
+        y1 = torch.empty((wl.batch, wl.nheads, wl.headdim), device=DEV)
+        y2 = torch.empty_like(y1)
+        sep.decode_step(d["x"], d["B"], d["C"], d["dt"], y1)
+        sep.flush_checkpoint_each(th)
+        fus.decode_flush_step_each(th, d["x"], d["B"], d["C"], d["dt"], y2)
+        assert torch.equal(y1, y2), t
+        y_m = model.decode(s["x"], s["B"], s["C"], s["dt"])
+        folded = model.flush(th_np)
+        want = [b for b in range(wl.batch) if t + 1 >= first[b] and (t + 1 - first[b]) % W == 0]
+        assert folded == want, t
+        lens = fus.ptr[:, :, 1].cpu().numpy()
+        assert np.array_equal(lens, np.repeat(model.ptr.len[:, None], wl.nheads, axis=1)), t
+        worst = max(worst, rel_l2(y2.double().cpu().numpy(), y_m))
+    _same(sep, fus)
+    log(f"  worst vs oracle {worst:.2e}")
+    assert worst < (1e-5 if copy == "none" else 1e-3)
+    assert fus.device_error() == 0 and sep.device_error() == 0

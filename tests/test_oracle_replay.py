@@ -159,3 +159,34 @@ def test_decode_refuses_uncommitted_round():
         model.decode(s["x"], s["B"], s["C"], s["dt"])
     with pytest.raises(RingError):
         model.flush(1)
+
+
+def test_staggered_thresholds_fold_each_sequence_on_its_own_phase():
+    """Per-sequence fold thresholds: 1 + (b mod W) until sequence b's first fold,
+    W after it, so sequence b folds after tokens 1 + (b mod W) + k W; every
+    output still equals the eager one, and every fold leaves that sequence's
+    checkpoint at its eager state."""
+    wl = workloads.get(TINY).replace(batch=6, ngroups=2, s0="normal")
+    W = 4
+    A, st = _tiny_inputs(wl)
+    S0 = synth.initial_state(wl)
+    model = mamba2.ReplayModel(S0, A, wl.ngroups, W)
+    S = S0.astype(np.float64)
+    first = 1 + np.arange(wl.batch) % W
+    for t, s in enumerate(st[:20]):
+        S, y_e = mamba2.eager_step(S, A, s["x"], s["B"], s["C"], s["dt"])
+        assert pins.rel_err(model.decode(s["x"], s["B"], s["C"], s["dt"]), y_e) < 1e-12, t
+        th = np.where(t < first, first, W)
+        folded = model.flush(th)
+        want = [b for b in range(wl.batch) if (t + 1 - first[b]) % W == 0 and t + 1 >= first[b]]
+        assert folded == want, t
+        for b in folded:
+            assert pins.rel_err(model.ckpt[b], S[b]) < 1e-12
+    # one value per sequence, all equal, is the scalar threshold
+    m1 = mamba2.ReplayModel(S0, A, wl.ngroups, W)
+    m2 = mamba2.ReplayModel(S0, A, wl.ngroups, W)
+    for s in st[:9]:
+        m1.decode(s["x"], s["B"], s["C"], s["dt"])
+        m2.decode(s["x"], s["B"], s["C"], s["dt"])
+        assert m1.flush(W) == m2.flush(np.full(wl.batch, W))
+    assert np.array_equal(m1.ckpt, m2.ckpt)
