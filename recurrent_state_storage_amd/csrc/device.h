@@ -41,11 +41,11 @@ template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
 
-template <int N, bool LOW>
+template <int N, bool LOW, int NT = kThreads>
 struct TileGeom {
   static constexpr int VEC = LOW ? 8 : 4;       // elements per 16-byte load
   static constexpr int TPR = N / VEC;            // threads per row
-  static constexpr int RPP = kThreads / TPR;     // rows per pass
+  static constexpr int RPP = NT / TPR;           // rows per pass (NT threads per workgroup)
   static_assert(N % VEC == 0 && TPR >= 1 && TPR <= 64, "unsupported N");
   static_assert((TPR & (TPR - 1)) == 0, "N/VEC must be a power of two");
 };

@@ -44,26 +44,27 @@ namespace rss {
 // deliver them; everything else is fp32.
 struct ReplayLds {
   int oX, oB, oC, oCF, oDC, oRing, total;
-  __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes) {
+  __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes, int nw) {
     oX = 0;                                            // raw window x [R][P]
     oB = align4((R * P * tin_bytes + 3) / 4);          // raw window B [R][N]
     oC = oB + align4((R * N * tin_bytes + 3) / 4);     // new tokens' C [ntmax][N]
     oCF = oC + ntmax * N;                              // exp(lam) * dt [ntmax][R]
     oDC = oCF + ntmax * R;                             // exp(Lam) [ntmax]
-    oRing = align4(oDC + ntmax);                       // ring shares [4][ntmax][P]
-    total = oRing + 4 * ntmax * P;
+    oRing = align4(oDC + ntmax);                       // ring shares [nw][ntmax][P]
+    total = oRing + nw * ntmax * P;
   }
 };
 
 constexpr int kStageS = 4;  // scalar loads per thread and round (x rows when P % VE != 0)
 
-template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD>
-__global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
-  using Geo = TileGeom<N, LOW>;
+template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD, int NT>
+__global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
+  constexpr int NW = NT / 64;                                  // wavefronts per workgroup
+  using Geo = TileGeom<N, LOW, NT>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, RPP = Geo::RPP;
   constexpr int VE = V16<Tin>::VE;
   constexpr int NV = N / VE;                                   // 16-byte vectors per B or C row
-  constexpr int kStageC = (NTMAX * NV + kThreads - 1) / kThreads;
+  constexpr int kStageC = (NTMAX * NV + NT - 1) / NT;
   constexpr int EPL = N >= 64 ? N / 64 : 1;                    // B elements per lane in a dot
   using TileT = typename std::conditional<LOW, bf16_t, float>::type;
   using VT = typename V16<Tin>::T;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   const int L = n0 + nt;
   if (head < 0 || head >= R || n0 < 0 || L > R) {  // ring full (no flush), or corrupt pointers
     if (tid == 0) atomicOr(a.err, kDevRingOverflow);
-    for (int e = tid; e < nt * P; e += kThreads) {
+    for (int e = tid; e < nt * P; e += NT) {
       const int i = e / P, p = e - i * P;
       a.y[((size_t)(b * nt + i) * H + h) * P + p] = __builtin_nanf("");
     }
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     }
   }
 
-  const ReplayLds lay(R, P, N, NTMAX, (int)sizeof(Tin));
+  const ReplayLds lay(R, P, N, NTMAX, (int)sizeof(Tin), NW);
   Tin* sX = reinterpret_cast<Tin*>(lds + lay.oX);
   Tin* sB = reinterpret_cast<Tin*>(lds + lay.oB);
   float* sC = lds + lay.oC;
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   const int PV = xvec ? P / VE : 0;
   auto xdiv = [&](int q) { return (int)(((uint64_t)(uint32_t)q * a.xdiv) >> 32); };
   const int totXV = L * PV, totBV = L * NV, totCV = nt * NV;
-  for (int q0 = wave * 64; q0 < totBV; q0 += kThreads) {
+  for (int q0 = wave * 64; q0 < totBV; q0 += NT) {
     const int q = q0 + lane;
     if (q < totBV) {
       const int j = q / NV;
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   }
   Tin sxs[kStageS];
   if (xvec) {
-    for (int q0 = wave * 64; q0 < totXV; q0 += kThreads) {
+    for (int q0 = wave * 64; q0 < totXV; q0 += NT) {
       const int q = q0 + lane;
       if (q < totXV) {
         const int j = xdiv(q);
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   } else {
 #pragma unroll
     for (int m = 0; m < kStageS; ++m) {
-      const int e = m * kThreads + tid;
+      const int e = m * NT + tid;
       if (e < L * P) {
         const int j = xdiv(e);
         sxs[m] = xrow(j)[e - j * P];
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   VT vc[kStageC];
 #pragma unroll
   for (int m = 0; m < kStageC; ++m) {
-    const int q = m * kThreads + tid;
+    const int q = m * NT + tid;
     if (q < totCV) {
       const int i = q / NV, c = q - i * NV;
       vc[m] = ldv<Tin>(Cin + i * bstr + c * VE);
@@ -201,24 +202,24 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   if (tid >= n0 && tid < L) dt_new = dtin[(tid - n0) * H];
 #pragma unroll
   for (int m = 0; m < kStageC; ++m) {
-    const int q = m * kThreads + tid;
+    const int q = m * NT + tid;
     if (q < totCV) st_lds_f32(sC + q * VE, vc[m]);
   }
   if (!xvec) {
 #pragma unroll
     for (int m = 0; m < kStageS; ++m) {
-      const int e = m * kThreads + tid;
+      const int e = m * NT + tid;
       if (e < L * P) sX[e] = sxs[m];
     }
-    for (int e0 = kStageS * kThreads; e0 < L * P; e0 += kStageS * kThreads) {  // long windows
+    for (int e0 = kStageS * NT; e0 < L * P; e0 += kStageS * NT) {  // long windows
 #pragma unroll
       for (int m = 0; m < kStageS; ++m) {
-        const int e = e0 + m * kThreads + tid;
+        const int e = e0 + m * NT + tid;
         if (e < L * P) { const int j = xdiv(e); sxs[m] = xrow(j)[e - j * P]; }
       }
 #pragma unroll
       for (int m = 0; m < kStageS; ++m) {
-        const int e = e0 + m * kThreads + tid;
+        const int e = e0 + m * NT + tid;
         if (e < L * P) sX[e] = sxs[m];
       }
     }
@@ -246,19 +247,19 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
 
   // The new tokens' x and B rows go from LDS to the ring.
   if (xvec) {
-    for (int q = tid; q < nt * PV; q += kThreads) {
+    for (int q = tid; q < nt * PV; q += NT) {
       const int i = q / PV, c = q - i * PV;
       *reinterpret_cast<VT*>(rx + ring_slot(head, n0 + i, R) * P + c * VE) =
           *reinterpret_cast<const VT*>(sX + (n0 + i) * P + c * VE);
     }
   } else {
-    for (int e = tid; e < nt * P; e += kThreads) {
+    for (int e = tid; e < nt * P; e += NT) {
       const int i = e / P, p = e - i * P;
       rx[ring_slot(head, n0 + i, R) * P + p] = sX[(n0 + i) * P + p];
     }
   }
   if (h == g * hpg) {  // the group's first head keeps the group's B
-    for (int q = tid; q < nt * NV; q += kThreads) {
+    for (int q = tid; q < nt * NV; q += NT) {
       const int i = q / NV, c = q - i * NV;
       *reinterpret_cast<VT*>(rB + ring_slot(head, n0 + i, R) * N + c * VE) =
           *reinterpret_cast<const VT*>(sB + (n0 + i) * N + c * VE);
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   for (int i = 0; i < nt; ++i) {
     const int ti = n0 + i;
     float share[kRowsPerLane] = {};
-    for (int j = wave; j <= ti; j += kWaves) {
+    for (int j = wave; j <= ti; j += NW) {
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
@@ -315,8 +316,12 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
         for (int m = 0; m < RS::NOUT; ++m) {
           const int row = base + (kbase + m) * RPP + rsub;
           if (row < P) {
-            const float ring = (sRing[i * P + row] + sRing[(NTMAX + i) * P + row]) +
-                               (sRing[(2 * NTMAX + i) * P + row] + sRing[(3 * NTMAX + i) * P + row]);
+            float ring;
+            if constexpr (NW == 4)
+              ring = (sRing[i * P + row] + sRing[(NTMAX + i) * P + row]) +
+                     (sRing[(2 * NTMAX + i) * P + row] + sRing[(3 * NTMAX + i) * P + row]);
+            else
+              ring = sRing[i * P + row] + sRing[(NTMAX + i) * P + row];
             yout[i * xstr + row] = fmaf(sDC[i], part[m], ring);
           }
         }
@@ -365,16 +370,17 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
   }
 }
 
-template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD>
+template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD, int NT = kThreads>
 static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
-  const size_t lds = (size_t)ReplayLds(a.R, a.P, N, NTMAX, (int)sizeof(Tin)).total * sizeof(float);
-  auto kern = replay_kernel<N, Tin, LOW, NTMAX, FOLD>;
+  const size_t lds =
+      (size_t)ReplayLds(a.R, a.P, N, NTMAX, (int)sizeof(Tin), NT / 64).total * sizeof(float);
+  auto kern = replay_kernel<N, Tin, LOW, NTMAX, FOLD, NT>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)batch * a.H)), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)batch * a.H)), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -383,6 +389,11 @@ static hipError_t launch_nt(const ReplayArgs& a, int batch, hipStream_t s) {
   if (a.nt != 1) return launch_one<N, Tin, LOW, kMaxNew, false>(a, batch, s);
   if constexpr (!LOW) {  // the fused fold needs the fp32 checkpoint in registers
     if (a.fold_min_len > 0 || a.fold_min_len_dev) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
+  } else {
+    // A bf16 tile is half the bytes: two wavefronts per (sequence, head) hold
+    // it in the same 8 fragments per lane, and twice as many workgroups fit on
+    // a CU, so twice the bytes are in flight.
+    return launch_one<N, Tin, LOW, 1, false, 128>(a, batch, s);
   }
   return launch_one<N, Tin, LOW, 1, false>(a, batch, s);
 }
