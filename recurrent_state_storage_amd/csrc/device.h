@@ -89,7 +89,22 @@ template <> struct Log2<1> { static constexpr int v = 0; };
 template <int TPR>
 __device__ __forceinline__ float row_sum(float v) { return lanes_sum<Log2<TPR>::v>(v); }
 
-__device__ __forceinline__ float wave_sum(float v) { return lanes_sum<6>(v); }
+// Sum over the 64 lanes, returned as a wavefront-uniform value: the 16-lane
+// row butterfly above, then the GFX9 row broadcasts (lane 15 of row r into row
+// r + 1 for rows 1 and 3, lane 31 into rows 2 and 3) leave the total in lane
+// 63, which is read into a scalar register. No LDS round trip (the lane ^ 16 and
+// lane ^ 32 exchanges of a full butterfly go through the LDS crossbar), fixed
+// order, so deterministic.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = lanes_sum<4>(v);
+  v += dpp_rows<0x142, 0xa>(v);   // row_bcast:15
+  v += dpp_rows<0x143, 0xc>(v);   // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 
 // Reduce-scatter of the 8 tile passes over a row group of TPR = 2^T lanes.
 // On entry a[k] is this lane's partial dot for the row of pass k. Each step

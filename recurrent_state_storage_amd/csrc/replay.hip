@@ -268,7 +268,10 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
 
   // 3. Wavefront w takes the window entries j = w (mod 4) of every output i:
   // w_ij = coef_ij (B_j . C_i), and its share of sum_j w_ij x_j, row p on lane p mod 64.
+  // Rows are visited in blocks of 64 up to P only (a uniform bound), so short
+  // heads spend no instructions on the rows they do not have.
   constexpr int kRowsPerLane = kMaxP / 64;
+  const int nrb = (P + 63) >> 6;
   for (int i = 0; i < nt; ++i) {
     const int ti = n0 + i;
     float share[kRowsPerLane] = {};
@@ -281,12 +284,16 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       }
       const float w = sCF[i * R + j] * wave_sum(part);
 #pragma unroll
-      for (int r = 0; r < kRowsPerLane; ++r)
+      for (int r = 0; r < kRowsPerLane; ++r) {
+        if (r >= nrb) break;
         if (r * 64 + lane < P) share[r] = fmaf(w, to_f32(sX[j * P + r * 64 + lane]), share[r]);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < kRowsPerLane; ++r)
+    for (int r = 0; r < kRowsPerLane; ++r) {
+      if (r >= nrb) break;
       if (r * 64 + lane < P) sRing[(wave * NTMAX + i) * P + r * 64 + lane] = share[r];
+    }
   }
   __syncthreads();
 
