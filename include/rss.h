@@ -48,7 +48,11 @@
  *    config says.
  *  - Supported sizes: N in {16, 32, 64, 128, 256}; 1 <= P <= 256; Bt, H >= 1
  *    (Bt = 0 is accepted and launches nothing); 1 <= W <= R <= 64;
- *    0 <= K_max <= 7 and R >= W + K_max.
+ *    0 <= K_max <= 7 and R >= W + K_max. The window's rows are staged in LDS,
+ *    of which one gfx950 workgroup may hold 160 KiB: a configuration whose
+ *    kernels would need more is refused with RSS_E_SHAPE. Only
+ *    the largest shapes reach it: at P = N = 256, fp32 x/B/C with K_max > 0
+ *    allow R <= 59 and a KDA layer R <= 49; bf16 x/B/C and GDN allow R = 64.
  */
 #ifndef RSS_H_
 #define RSS_H_

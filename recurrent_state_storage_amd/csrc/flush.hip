@@ -23,26 +23,12 @@
 // only: len -= n_drop, n_tent = 0.
 #include "device.h"
 #include "launch.h"
+#include "lds.h"
 
 namespace rss {
 
 constexpr int kFlushStage = 2;  // 16-byte B loads per thread per staging round
 
-// Dynamic LDS layout of the flush kernel, in floats. x is stored transposed
-// (row p holds entries j = 0..R-1 contiguously, padded to a multiple of 4) so
-// that one 16-byte read gives a row's x for four consecutive entries.
-struct FlushLds {
-  int RS, oXT, oB, oCF, oG, oDc, total;
-  __host__ __device__ FlushLds(int R, int P, int N, bool pcd) {
-    RS = align4(R);
-    oXT = 0;                 // x transposed  [P][RS]
-    oB = P * RS;             // window B rows [R][N]
-    oCF = oB + R * N;        // c_j = exp(lam_j) dt_j [R], then exp(Lam)
-    oG = align4(oCF + R + 1);        // per-channel log-decay rows [R][N]
-    oDc = oG + (pcd ? R * N : 0);    // per-channel exp(Lam[n]) [N]
-    total = oDc + (pcd ? N : 0);
-  }
-};
 
 template <int N, typename Tin, int MODE, bool PCD>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {

@@ -26,23 +26,10 @@
 // keys k_j * exp(lam_j). The ring keeps log alpha_j as a row per entry.
 #include "device.h"
 #include "launch.h"
+#include "lds.h"
 
 namespace rss {
 
-// Dynamic LDS of the GDN / KDA replay kernel, in floats.
-struct GdnLds {
-  int oK, oU, oQ, oCF, oS, oG, oD, total;
-  __host__ __device__ GdnLds(int R, int P, int N, bool kda) {
-    oK = 0;                   // window k rows [R][N] (row n0 = k_t); KDA: scaled in place
-    oU = R * N;               // window u rows [R][P]
-    oQ = oU + R * P;          // q_t [N]
-    oCF = oQ + N;             // exp(lam_j) [R], then exp(Lam), k_t . q_t
-    oS = align4(oCF + R + 2); // shares [4 waves][2][P]: sum_j w u_j for z = k_t, q_t
-    oG = oS + 8 * P;          // KDA: committed log-gate rows [R][N]
-    oD = oG + (kda ? R * N : 0);   // KDA: exp(Lam[n]) [N]
-    total = oD + (kda ? N : 0);
-  }
-};
 
 template <int N, int MP, bool KDA>
 __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {

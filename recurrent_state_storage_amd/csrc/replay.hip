@@ -36,24 +36,10 @@
 
 #include "device.h"
 #include "launch.h"
+#include "lds.h"
 
 namespace rss {
 
-// Dynamic LDS layout of the replay kernel, in 4-byte words. The window's x and
-// B rows are kept raw (input dtype), exactly as the direct global->LDS loads
-// deliver them; everything else is fp32.
-struct ReplayLds {
-  int oX, oB, oC, oCF, oDC, oRing, total;
-  __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes, int nw) {
-    oX = 0;                                            // raw window x [R][P]
-    oB = align4((R * P * tin_bytes + 3) / 4);          // raw window B [R][N]
-    oC = oB + align4((R * N * tin_bytes + 3) / 4);     // new tokens' C [ntmax][N]
-    oCF = oC + ntmax * N;                              // exp(lam) * dt [ntmax][R]
-    oDC = oCF + ntmax * R;                             // exp(Lam) [ntmax]
-    oRing = align4(oDC + ntmax);                       // ring shares [nw][ntmax][P]
-    total = oRing + nw * ntmax * P;
-  }
-};
 
 constexpr int kStageS = 4;  // scalar loads per thread and round (x rows when P % VE != 0)
 

@@ -7,6 +7,7 @@
 
 #include "../../include/rss.h"
 #include "launch.h"
+#include "lds.h"
 
 struct rss_layer {
   rss_config cfg;
@@ -31,6 +32,24 @@ int32_t check_shape(const rss_config* c) {
   return RSS_OK;
 }
 
+// Largest dynamic LDS any kernel of this layer allocates per workgroup.
+size_t layer_lds_bytes(const rss_config* c) {
+  const int R = c->capacity, P = c->headdim, N = c->dstate;
+  size_t m = 0;
+  auto upd = [&m](int words) { if ((size_t)words * 4 > m) m = (size_t)words * 4; };
+  if (c->kind == RSS_KIND_MAMBA2) {
+    const int tin = c->in_dtype == RSS_DTYPE_BF16 ? 2 : 4;
+    upd(rss::ReplayLds(R, P, N, 1, tin, c->read_copy == RSS_COPY_NONE ? 4 : 2).total);
+    if (c->max_draft > 0) upd(rss::ReplayLds(R, P, N, rss::kMaxNew, tin, 4).total);
+    upd(rss::FlushLds(R, P, N, false).total);
+  } else {
+    const bool kda = c->kind == RSS_KIND_KDA;
+    upd(rss::GdnLds(R, P, N, kda).total);
+    upd(rss::FlushLds(R, P, N, kda).total);
+  }
+  return m;
+}
+
 bool valid_mode(int32_t m) { return m == RSS_COPY_NONE || m == RSS_COPY_BF16 || m == RSS_STATE_BF16; }
 
 int32_t check_config(const rss_config* c) {
@@ -47,6 +66,7 @@ int32_t check_config(const rss_config* c) {
   if (c->window < 1 || c->capacity < c->window || c->capacity > rss::kMaxRing) return RSS_E_SHAPE;
   if (c->max_draft < 0 || c->max_draft > rss::kMaxNew - 1) return RSS_E_CAPACITY;
   if (c->capacity < c->window + c->max_draft) return RSS_E_CAPACITY;
+  if (layer_lds_bytes(c) > (size_t)rss::kMaxLdsBytes) return RSS_E_SHAPE;
   return RSS_OK;
 }
 

@@ -53,6 +53,21 @@ def test_version_and_status_strings():
     assert rss.status_string(99) == "unknown status"
 
 
+def test_largest_shapes_within_the_lds_budget_are_accepted():
+    ok = [dict(headdim=256, dstate=256, window=57, capacity=64, max_draft=7),
+          dict(headdim=256, dstate=256, window=52, capacity=59, max_draft=7, in_dtype=rss.RSS_DTYPE_F32),
+          dict(headdim=256, dstate=256, window=64, capacity=64, max_draft=0, in_dtype=rss.RSS_DTYPE_F32),
+          dict(headdim=256, dstate=256, window=57, capacity=64, max_draft=7,
+               read_copy=rss.RSS_COPY_BF16),
+          dict(kind=rss.RSS_KIND_GDN, headdim=256, dstate=256, window=64, capacity=64, max_draft=0,
+               in_dtype=rss.RSS_DTYPE_F32),
+          dict(kind=rss.RSS_KIND_KDA, headdim=256, dstate=256, window=49, capacity=49, max_draft=0,
+               in_dtype=rss.RSS_DTYPE_F32)]
+    for kw in ok:
+        out = rss.rss_sizes()
+        assert rss.library().rss_buffer_sizes(ctypes.byref(_cfg(**kw)), ctypes.byref(out)) == rss.RSS_OK, kw
+
+
 def test_buffer_sizes():
     cfg = _cfg()
     s = rss.rss_buffer_sizes(cfg)
@@ -91,6 +106,11 @@ def test_buffer_sizes():
     (dict(kind=rss.RSS_KIND_GDN, in_dtype=rss.RSS_DTYPE_F32), rss.RSS_E_CAPACITY),
     (dict(kind=rss.RSS_KIND_GDN, max_draft=0, in_dtype=rss.RSS_DTYPE_F32,
           read_copy=rss.RSS_STATE_BF16), rss.RSS_E_DTYPE),
+    # LDS budget (160 KiB per workgroup) at the largest shapes
+    (dict(headdim=256, dstate=256, window=57, capacity=64, max_draft=7, in_dtype=rss.RSS_DTYPE_F32),
+     rss.RSS_E_SHAPE),
+    (dict(kind=rss.RSS_KIND_KDA, headdim=256, dstate=256, window=50, capacity=50, max_draft=0,
+          in_dtype=rss.RSS_DTYPE_F32), rss.RSS_E_SHAPE),
 ])
 def test_config_validation(kw, status):
     cfg = _cfg(**kw)
