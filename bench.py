@@ -120,28 +120,58 @@ def gen_pool(wl, T: int, workers: int):
 
 
 # ---- CPU baseline: the fp64 oracle as it stands ----------------------------------
-def cpu_baseline(wl, pool, budget_s: float):
+_CPU_POOL = None       # (x, B, C, dt bits, A), inherited by forked workers
+
+
+def _cpu_worker(args):
+    """fp64 eager recurrence of the oracle on sequences [w*nseq, (w+1)*nseq),
+    one BLAS thread, until the time budget or the pool's steps run out."""
+    w, nseq, budget_s = args
     from threadpoolctl import threadpool_limits
     from oracle import mamba2
-    nseq = 16
-    xs, Bs, Cs, dts = pool
-    A = synth.params(wl)["A"]
-    S = np.zeros((nseq, wl.nheads, wl.headdim, wl.dstate))
+    xs, Bs, Cs, dts, A = _CPU_POOL
+    lo, hi = w * nseq, (w + 1) * nseq
+    S = np.zeros((nseq,) + xs.shape[2:] + (Bs.shape[-1],))
     bf = synth.bf16_value
     steps = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while True:
             i = steps % xs.shape[0]
-            S, _ = mamba2.eager_step(S, A, bf(xs[i, :nseq]), bf(Bs[i, :nseq]), bf(Cs[i, :nseq]),
-                                     dts[i, :nseq])
+            S, _ = mamba2.eager_step(S, A, bf(xs[i, lo:hi]), bf(Bs[i, lo:hi]), bf(Cs[i, lo:hi]),
+                                     dts[i, lo:hi])
             steps += 1
             el = time.perf_counter() - t0
-            if el >= budget_s or steps >= 256:
+            if el >= budget_s or steps >= xs.shape[0]:
                 break
-    return {"value": nseq * steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 eager recurrence, {nseq} of {wl.batch} sequences x {wl.nheads} heads, "
-                      f"{steps} decode steps ({el:.1f} s, 1 thread)"}
+    return nseq * steps, el, steps
+
+
+def cpu_baseline(wl, pool, budget_s: float, workers: int):
+    """The oracle timed on the host: once on one core, then sharded over
+    `workers` processes (sequences are independent), each with one thread."""
+    import multiprocessing
+    global _CPU_POOL
+    _CPU_POOL = tuple(pool) + (synth.params(wl)["A"],)
+    nseq = 16
+    workers = max(1, min(workers, wl.batch // nseq))
+    tok1, el1, st1 = _cpu_worker((0, nseq, budget_s / 3))
+    with multiprocessing.get_context("fork").Pool(workers) as p:
+        res = p.map(_cpu_worker, [(w, nseq, budget_s) for w in range(workers)])
+    tokens = sum(r[0] for r in res)
+    el = max(r[1] for r in res)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": tokens / el, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "one_core_tokens_per_s": tok1 / el1, "cpu_model": model,
+            "sample": f"fp64 eager recurrence of the oracle, {workers} processes x 1 thread, each "
+                      f"{nseq} sequences x {wl.nheads} heads ({workers * nseq} of {wl.batch} sequences), "
+                      f"{min(r[2] for r in res)}-{max(r[2] for r in res)} decode steps in {el:.1f} s; "
+                      f"one core alone: {st1} steps of {nseq} sequences in {el1:.1f} s"}
 
 
 def _timed(torch, fn, n):
@@ -454,7 +484,7 @@ def main() -> int:
     ap.add_argument("--no-eager", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--separate-flush", action="store_true",
                     help="fold with a separate flush launch instead of the fused decode+fold")
     ap.add_argument("--no-extra", action="store_true",
@@ -478,6 +508,8 @@ def main() -> int:
     t0 = time.perf_counter()
     pool = gen_pool(wl, args.pool, workers)
     gen_s = time.perf_counter() - t0
+    # The host baseline runs before the device is touched (its workers are forked).
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, pool, args.cpu_seconds, workers)
     X = torch.from_numpy(pool[0].view(np.int16)).view(torch.bfloat16).to(dev)
     Bm = torch.from_numpy(pool[1].view(np.int16)).view(torch.bfloat16).to(dev)
     Cm = torch.from_numpy(pool[2].view(np.int16)).view(torch.bfloat16).to(dev)
@@ -655,8 +687,8 @@ def main() -> int:
                                         workers=workers)
         rec["kimi_delta_attention"] = run_gdn(torch, rss, dev, steps=args.steps, warmup=args.warmup,
                                               workers=workers, name="kda_b256_h32_d128_w16")
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, pool, args.cpu_seconds)
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
     return 0
 
