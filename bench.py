@@ -485,6 +485,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed repeats of --steps steps (each after a fresh init); median reported")
     ap.add_argument("--separate-flush", action="store_true",
                     help="fold with a separate flush launch instead of the fused decode+fold")
     ap.add_argument("--no-extra", action="store_true",
@@ -541,19 +543,25 @@ def main() -> int:
             if ev is not None:
                 ev[3].record()
 
-    k = 0
-    for _ in range(args.warmup):
-        replay_step(k)
-        k += 1
-    torch.cuda.synchronize()
+    # Repeats: each starts from a fresh init_state and W warm-up steps (untimed),
+    # then exactly `steps` steps between two events; the median repeat is reported.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        replay_step(k)
-        k += 1
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
+    reps_ms = []
+    for _ in range(max(1, args.repeats)):
+        layer.init_state()
+        k = 0
+        for _ in range(args.warmup):
+            replay_step(k)
+            k += 1
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            replay_step(k)
+            k += 1
+        e1.record()
+        torch.cuda.synchronize()
+        reps_ms.append(e0.elapsed_time(e1))
+    ms = float(np.median(reps_ms))
     tok_s = Bt * args.steps / (ms / 1e3)
 
     # Per-kernel durations: HIP events around every launch on the launch stream,
@@ -620,6 +628,14 @@ def main() -> int:
         }
         del S
 
+    # Context: a plain device copy (torch copy_, 1 GiB read + 1 GiB written).
+    csrc = torch.ones((1 << 28,), device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    copy_ms = _timed(torch, lambda j: cdst.copy_(csrc), 10) / 10
+    copy_gbs = 2 * (1 << 30) / (copy_ms / 1e3) / 1e9
+    del csrc, cdst
+
     if args.calibrate_copy:
         src = torch.ones((1 << 28,), device=dev)      # 1 GiB fp32
         dst = torch.empty_like(src)
@@ -664,11 +680,15 @@ def main() -> int:
                 "GBps": fl_bytes / (fl_ms / 1e3) / 1e9 if n_fl else None, "launches": n_fl},
         },
         "step_us": {"median": float(np.median(step_us)), "max": float(np.max(step_us))},
+        "repeats_ms": reps_ms,
+        "context": {"device_copy_GBps": copy_gbs, "replay_frac_of_copy": rep_gbs / copy_gbs},
         "eager_baseline": out_eager,
         "bytes_per_token": {"replay_state": st_replay, "eager_state": st_eager,
                             "state_ratio": st_replay / st_eager, "replay_total": tot_replay,
                             "eager_total": eager_bytes(wl) * H,
-                            "total_ratio": tot_replay / (eager_bytes(wl) * H)},
+                            "total_ratio": tot_replay / (eager_bytes(wl) * H),
+                            "replay_decode_launch_analytic": rep_bytes / n_rep / Bt,
+                            "replay_decode_launch_counters": traffic / Bt if traffic else None},
         "input_generation_s": gen_s,
     }
     if out_eager:
