@@ -140,10 +140,11 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     const float lam = wave_suffix_excl(u, lane);
     if (lane < n0) sCF[lane] = expf(lam);
     if (lane == 0) sCF[R] = expf(lam + u);
-    if (lane == 0) rdl[ring_slot(head, n0, R)] = make_float2(1.f, logf(alpha));
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // the new entry's (1, log alpha) after the wait: a store before it would be waited for too
+  if (!KDA && tid == 0) rdl[ring_slot(head, n0, R)] = make_float2(1.f, logf(alpha));
   if constexpr (KDA) {
     // Channel n (one thread each): lam_j[n] from the newest entry back, the new
     // token's gate included; scale the committed keys in place; exp(Lam[n]).

@@ -212,6 +212,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   }
 
   // Log-decay scan in wavefront 0: lam_i(j) = sum_{j < m <= t_i} l_m, tree-summed.
+  float2 dl_new = make_float2(0.f, 0.f);
   if (wave == 0) {
     const bool fresh = tid >= n0 && tid < L;
     const float dtj = fresh ? dt_new : dl_ring.x;
@@ -225,11 +226,14 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       if (lane < L) sCF[i * R + lane] = lane <= ti ? expf(lam) * dtj : 0.f;
       if (lane == 0) sDC[i] = expf(lam + u);
     }
-    if (lane >= n0 && lane < L)  // the new tokens' (dt, l) into the ring
-      rdl[ring_slot(head, lane, R)] = make_float2(dtj, lj);
+    dl_new = make_float2(dtj, lj);
   }
   __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads have landed
   __syncthreads();
+  // The new tokens' (dt, l) into the ring, only now: on this target a store
+  // counts in the same counter as the loads, so a store issued before the wait
+  // above would have been waited for too.
+  if (wave == 0 && lane >= n0 && lane < L) rdl[ring_slot(head, lane, R)] = dl_new;
 
   // The new tokens' x and B rows go from LDS to the ring.
   if (xvec) {
