@@ -52,7 +52,7 @@
  *    of which one gfx950 workgroup may hold 160 KiB: a configuration whose
  *    kernels would need more is refused with RSS_E_SHAPE. Only
  *    the largest shapes reach it: at P = N = 256, fp32 x/B/C with K_max > 0
- *    allow R <= 59 and a KDA layer R <= 49; bf16 x/B/C and GDN allow R = 64.
+ *    allow R <= 58 and a KDA layer R <= 49; bf16 x/B/C and GDN allow R = 64.
  */
 #ifndef RSS_H_
 #define RSS_H_
@@ -245,6 +245,28 @@ int32_t rss_flush_checkpoint_each(rss_layer* layer, const int32_t* min_len, void
  * RSS_E_ORDER if a previous round is still uncommitted. */
 int32_t rss_verify_k_tokens(rss_layer* layer, int32_t K, const void* x, const void* B,
                             const void* C, const float* dt, float* y, void* stream);
+
+/* rss_flush_checkpoint(min_len) followed by rss_verify_k_tokens(K), in one pass
+ * where it can be: a sequence whose committed window holds >= min_len entries
+ * (min_len >= 1) has that window folded into its checkpoint while the tile is
+ * loaded for the K+1 outputs, and the new checkpoint is written; the K+1 new
+ * entries then start the next window. The checkpoint, ring and pointers equal
+ * the two separate calls' bit for bit; the outputs are computed from the
+ * unfolded checkpoint and the whole window, equal up to rounding. A speculative
+ * loop of this call and rss_rollback needs no separate flush: a window the
+ * accepted drafts fill is folded by the next round (R >= W + K_max still
+ * bounds the ring between rounds; during the call a folding sequence stages up
+ * to R + K + 1 positions, the committed ones read before their slots are
+ * reused). With read_copy = BF16 or RSS_STATE_BF16 the fold runs as a separate
+ * flush launch first. Errors as rss_verify_k_tokens and rss_flush_checkpoint,
+ * plus RSS_E_CAPACITY if R + K + 1 > 64, or if G < H and R < min_len + 2K + 1
+ * (heads of a group share B rows, so no slot is reused within the call: a
+ * grouped layer needs room for a full window plus two rounds), and
+ * RSS_E_SHAPE if the staged window would exceed the LDS budget (fp32
+ * checkpoint only). */
+int32_t rss_verify_k_tokens_fold(rss_layer* layer, int32_t min_len, int32_t K, const void* x,
+                                 const void* B, const void* C, const float* dt, float* y,
+                                 void* stream);
 
 /* Commit a verify round: per sequence drop the n_drop[b] newest tentative
  * entries (0 <= n_drop[b] <= n_tent; n_drop = K - accepted drafts) and keep

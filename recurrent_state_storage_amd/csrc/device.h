@@ -254,4 +254,12 @@ __device__ __forceinline__ int ring_slot(int head, int j, int R) {
   return s >= R ? s - R : s;
 }
 
+// Ring slot of window position j for 0 <= j < 2R (a verify that folds its
+// committed window in the same pass stages up to R + K + 1 positions).
+__device__ __forceinline__ int ring_slot2(int head, int j, int R) {
+  int s = head + j;
+  if (s >= R) s -= R;
+  return s >= R ? s - R : s;
+}
+
 }  // namespace rss

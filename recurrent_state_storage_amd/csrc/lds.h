@@ -13,7 +13,7 @@ constexpr int kMaxLdsBytes = 160 * 1024;  // LDS one gfx950 workgroup may alloca
 // B rows are kept raw (input dtype), exactly as the direct global->LDS loads
 // deliver them; everything else is fp32.
 struct ReplayLds {
-  int oX, oB, oC, oCF, oDC, oRing, total;
+  int oX, oB, oC, oCF, oDC, oRing, oFC, total;
   __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes, int nw) {
     oX = 0;                                            // raw window x [R][P]
     oB = align4((R * P * tin_bytes + 3) / 4);          // raw window B [R][N]
@@ -21,7 +21,8 @@ struct ReplayLds {
     oCF = oC + ntmax * N;                              // exp(lam) * dt [ntmax][R]
     oDC = oCF + ntmax * R;                             // exp(Lam) [ntmax]
     oRing = align4(oDC + ntmax);                       // ring shares [nw][ntmax][P]
-    total = oRing + nw * ntmax * P;
+    oFC = oRing + nw * ntmax * P;                      // fused fold: c_j [R], then exp(Lam)
+    total = oFC + R + 1;
   }
 };
 

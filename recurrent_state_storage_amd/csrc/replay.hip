@@ -88,7 +88,30 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   const int4 pt = a.ptr[bh];
   const int head = pt.x, n0 = pt.y;
   const int L = n0 + nt;
-  if (head < 0 || head >= R || n0 < 0 || L > R) {  // ring full (no flush), or corrupt pointers
+
+  // Fused fold (fp32 checkpoint): the tile already in registers is folded and
+  // written back in this pass, exactly as a separate flush would (same
+  // coefficients, same order). A decode folds its whole window, the new token
+  // included, once that reaches the threshold; a verify folds the committed
+  // window it starts from (never the tentative tokens it appends), as a flush
+  // just before it would. Such a verify frees the committed slots for the new
+  // entries, so its window may span up to R + K + 1 positions (all staged in
+  // LDS before any slot is overwritten).
+  constexpr int XR = (FOLD && NTMAX > 1) ? NTMAX : 0;   // extra staged rows
+  const int RL = R + XR;                                 // staged rows (LDS layout)
+  bool do_fold = false, tent = false;
+  const int F = a.set_tent ? n0 : L;   // entries a fold takes
+  if constexpr (FOLD) {
+    const int th = a.fold_min_len_dev ? a.fold_min_len_dev[b] : a.fold_min_len;
+    if (F >= th && F > 0 && n0 <= R) {
+      if (pt.z == 0) do_fold = true;
+      else tent = true;
+    }
+  }
+  // (Only with one B row set per head: a group's B ring is written by its first
+  // head while the other heads read it, so grouped layers never reuse a slot here.)
+  const int cap = do_fold && XR && G == H ? (RL < 64 ? RL : 64) : R;
+  if (head < 0 || head >= R || n0 < 0 || n0 > R || L > cap) {  // ring full (no flush), or corrupt pointers
     if (tid == 0) atomicOr(a.err, kDevRingOverflow);
     for (int e = tid; e < nt * P; e += NT) {
       const int i = e / P, p = e - i * P;
@@ -96,25 +119,15 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
     }
     return;
   }
+  if (tent && tid == 0) atomicOr(a.err, kDevUncommitted);  // never fold tentative entries
 
-  // Fused fold (decode only, fp32 checkpoint): when this token fills the window,
-  // the tile already in registers is folded and written back in this pass,
-  // exactly as a separate flush would (same coefficients, same order).
-  bool do_fold = false;
-  if constexpr (FOLD) {
-    const int th = a.fold_min_len_dev ? a.fold_min_len_dev[b] : a.fold_min_len;
-    if (L >= th) {
-      if (pt.z == 0) do_fold = true;
-      else if (tid == 0) atomicOr(a.err, kDevUncommitted);  // never fold tentative entries
-    }
-  }
-
-  const ReplayLds lay(R, P, N, NTMAX, (int)sizeof(Tin), NW);
+  const ReplayLds lay(RL, P, N, NTMAX, (int)sizeof(Tin), NW);
   Tin* sX = reinterpret_cast<Tin*>(lds + lay.oX);
   Tin* sB = reinterpret_cast<Tin*>(lds + lay.oB);
   float* sC = lds + lay.oC;
   float* sCF = lds + lay.oCF;
   float* sDC = lds + lay.oDC;
+  float* sFC = lds + lay.oFC;
   float* sRing = lds + lay.oRing;
 
   // Per-workgroup base pointers (uniform, held in scalar registers); every
@@ -223,8 +236,14 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       const int ti = n0 + i;
       const float u = lane <= ti ? lj : 0.f;
       const float lam = wave_suffix_excl(u, lane);
-      if (lane < L) sCF[i * R + lane] = lane <= ti ? expf(lam) * dtj : 0.f;
+      if (lane < L) sCF[i * RL + lane] = lane <= ti ? expf(lam) * dtj : 0.f;
       if (lane == 0) sDC[i] = expf(lam + u);
+    }
+    if constexpr (FOLD) {  // the fold's coefficients: window entries 0..F-1
+      const float u = lane < F ? lj : 0.f;
+      const float lam = wave_suffix_excl(u, lane);
+      if (lane < RL) sFC[lane] = lane < F ? expf(lam) * dtj : 0.f;
+      if (lane == 0) sFC[RL] = expf(lam + u);
     }
     dl_new = make_float2(dtj, lj);
   }
@@ -233,25 +252,25 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   // The new tokens' (dt, l) into the ring, only now: on this target a store
   // counts in the same counter as the loads, so a store issued before the wait
   // above would have been waited for too.
-  if (wave == 0 && lane >= n0 && lane < L) rdl[ring_slot(head, lane, R)] = dl_new;
+  if (wave == 0 && lane >= n0 && lane < L) rdl[ring_slot2(head, lane, R)] = dl_new;
 
   // The new tokens' x and B rows go from LDS to the ring.
   if (xvec) {
     for (int q = tid; q < nt * PV; q += NT) {
       const int i = q / PV, c = q - i * PV;
-      *reinterpret_cast<VT*>(rx + ring_slot(head, n0 + i, R) * P + c * VE) =
+      *reinterpret_cast<VT*>(rx + ring_slot2(head, n0 + i, R) * P + c * VE) =
           *reinterpret_cast<const VT*>(sX + (n0 + i) * P + c * VE);
     }
   } else {
     for (int e = tid; e < nt * P; e += NT) {
       const int i = e / P, p = e - i * P;
-      rx[ring_slot(head, n0 + i, R) * P + p] = sX[(n0 + i) * P + p];
+      rx[ring_slot2(head, n0 + i, R) * P + p] = sX[(n0 + i) * P + p];
     }
   }
   if (h == g * hpg) {  // the group's first head keeps the group's B
     for (int q = tid; q < nt * NV; q += NT) {
       const int i = q / NV, c = q - i * NV;
-      *reinterpret_cast<VT*>(rB + ring_slot(head, n0 + i, R) * N + c * VE) =
+      *reinterpret_cast<VT*>(rB + ring_slot2(head, n0 + i, R) * N + c * VE) =
           *reinterpret_cast<const VT*>(sB + (n0 + i) * N + c * VE);
     }
   }
@@ -272,7 +291,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
         const int n = lane * EPL + e;
         if (n < N) part = fmaf(to_f32(sB[j * N + n]), sC[i * N + n], part);
       }
-      const float w = sCF[i * R + j] * wave_sum(part);
+      const float w = sCF[i * RL + j] * wave_sum(part);
 #pragma unroll
       for (int r = 0; r < kRowsPerLane; ++r) {
         if (r >= nrb) break;
@@ -326,7 +345,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
     }
     if constexpr (FOLD) {
       if (do_fold) {  // S <- exp(Lam) S + sum_j x_j outer (c_j B_j), j ascending
-        const float D = sDC[0];
+        const float D = sFC[RL];
 #pragma unroll
         for (int k = 0; k < kMaxPass; ++k) {
           fr[k].v.x *= D;
@@ -334,8 +353,8 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
           fr[k].v.z *= D;
           fr[k].v.w *= D;
         }
-        for (int j = 0; j < L; ++j) {
-          const float cj = sCF[j];
+        for (int j = 0; j < F; ++j) {
+          const float cj = sFC[j];
           float bv[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) bv[v] = cj * to_f32(sB[j * N + col * 4 + v]);
@@ -362,7 +381,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   }
 
   if (tid == 0) {
-    if (do_fold) a.ptr[bh] = make_int4(ring_slot(head, L, R), 0, 0, 0);
+    if (do_fold) a.ptr[bh] = make_int4(ring_slot(head, F, R), L - F, a.set_tent ? nt : 0, 0);
     else a.ptr[bh] = make_int4(head, L, a.set_tent ? nt : pt.z, 0);
   }
 }
@@ -370,7 +389,8 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
 template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD, int NT = kThreads>
 static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
   const size_t lds =
-      (size_t)ReplayLds(a.R, a.P, N, NTMAX, (int)sizeof(Tin), NT / 64).total * sizeof(float);
+      (size_t)ReplayLds(a.R + ((FOLD && NTMAX > 1) ? NTMAX : 0), a.P, N, NTMAX, (int)sizeof(Tin), NT / 64)
+          .total * sizeof(float);
   auto kern = replay_kernel<N, Tin, LOW, NTMAX, FOLD, NT>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -383,9 +403,15 @@ static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
 
 template <int N, typename Tin, bool LOW>
 static hipError_t launch_nt(const ReplayArgs& a, int batch, hipStream_t s) {
-  if (a.nt != 1) return launch_one<N, Tin, LOW, kMaxNew, false>(a, batch, s);
+  const bool fold = a.fold_min_len > 0 || a.fold_min_len_dev;
+  if (a.nt != 1 || (fold && a.set_tent)) {   // verify (a folding verify of one token too)
+    if constexpr (!LOW) {
+      if (fold) return launch_one<N, Tin, LOW, kMaxNew, true>(a, batch, s);
+    }
+    return launch_one<N, Tin, LOW, kMaxNew, false>(a, batch, s);
+  }
   if constexpr (!LOW) {  // the fused fold needs the fp32 checkpoint in registers
-    if (a.fold_min_len > 0 || a.fold_min_len_dev) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
+    if (fold) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
   } else {
     // A bf16 tile is half the bytes: two wavefronts per (sequence, head) hold
     // it in the same 8 fragments per lane, and twice as many workgroups fit on

@@ -92,7 +92,7 @@ bool inputs_ok(const void* x, const void* B, const void* C, const void* dt, cons
 
 extern "C" {
 
-int32_t rss_version(void) { return 10300; }
+int32_t rss_version(void) { return 10400; }
 
 const char* rss_status_string(int32_t s) {
   switch (s) {
@@ -249,6 +249,40 @@ int32_t rss_verify_k_tokens(rss_layer* l, int32_t K, const void* x, const void* 
   if (K > l->cfg.max_draft) return RSS_E_CAPACITY;
   if (l->pending_verify) return RSS_E_ORDER;
   const int32_t st = replay_call(l, K + 1, 1, 0, nullptr, x, B, C, dt, y, stream);
+  if (st == RSS_OK) l->pending_verify = 1;
+  return st;
+}
+
+int32_t rss_verify_k_tokens_fold(rss_layer* l, int32_t min_len, int32_t K, const void* x,
+                                 const void* B, const void* C, const float* dt, float* y,
+                                 void* stream) {
+  if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
+  if (min_len < 1) return RSS_E_INVALID;
+  if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
+  if (K < 0) return RSS_E_INVALID;
+  if (K > l->cfg.max_draft) return RSS_E_CAPACITY;
+  if (l->pending_verify) return RSS_E_ORDER;
+  const rss_config& c = l->cfg;
+  if (c.read_copy == RSS_COPY_NONE) {
+    // The fold frees the committed slots in the same pass, so a window of up to
+    // R + K + 1 positions is staged at once: it must fit one wavefront's scan
+    // (64 lanes) and the LDS budget.
+    if (c.capacity + K + 1 > 64) return RSS_E_CAPACITY;
+    // Grouped B rows are shared by the group's heads, so no slot may be reused
+    // within the call: the window must fit R even before its fold.
+    if (c.ngroups != c.nheads && c.capacity < min_len + 2 * K + 1) return RSS_E_CAPACITY;
+    const int tin = c.in_dtype == RSS_DTYPE_BF16 ? 2 : 4;
+    const size_t lds = (size_t)rss::ReplayLds(c.capacity + rss::kMaxNew, c.headdim, c.dstate,
+                                              rss::kMaxNew, tin, 4).total * 4;
+    if (lds > (size_t)rss::kMaxLdsBytes) return RSS_E_SHAPE;
+  }
+  int32_t st;
+  if (c.read_copy != RSS_COPY_NONE) {  // the replay reads a bf16 tile: fold first, separately
+    st = flush_call(l, min_len, nullptr, stream);
+    if (st == RSS_OK) st = replay_call(l, K + 1, 1, 0, nullptr, x, B, C, dt, y, stream);
+  } else {
+    st = replay_call(l, K + 1, 1, min_len, nullptr, x, B, C, dt, y, stream);
+  }
   if (st == RSS_OK) l->pending_verify = 1;
   return st;
 }

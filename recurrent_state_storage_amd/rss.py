@@ -59,6 +59,7 @@ _SIGS = {
     "rss_decode_flush_step_each": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_flush_checkpoint_each": ([_VP, _VP, _VP], _I32),
     "rss_verify_k_tokens": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
+    "rss_verify_k_tokens_fold": ([_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_rollback": ([_VP, _VP, _VP], _I32),
     "rss_get_device_error": ([_VP, ctypes.POINTER(_I32), _VP], _I32),
     "rss_gdn_decode_step": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
@@ -241,6 +242,9 @@ class ReplayLayer:
     def verify_k_tokens(self, K, x, B, C, dt, y, stream=None):
         rss_verify_k_tokens(self, K, x, B, C, dt, y, stream)
 
+    def verify_k_tokens_fold(self, min_len, K, x, B, C, dt, y, stream=None):
+        rss_verify_k_tokens_fold(self, min_len, K, x, B, C, dt, y, stream)
+
     def rollback(self, n_drop, stream=None):
         rss_rollback(self, n_drop, stream)
 
@@ -309,6 +313,17 @@ def rss_verify_k_tokens(layer: ReplayLayer, K: int, x, B, C, dt, y, stream=None)
             _ptr(dt, torch.float32, ds, "dt"), _ptr(y, torch.float32, xs, "y"))
     _check(library().rss_verify_k_tokens(layer.handle, int(K), *args, _stream(stream)),
            "rss_verify_k_tokens")
+
+
+def rss_verify_k_tokens_fold(layer: ReplayLayer, min_len: int, K: int, x, B, C, dt, y,
+                             stream=None) -> None:
+    c = layer.cfg
+    xs, bs, ds = layer.tok_shapes(K + 1)
+    idt = _in_dtype(c.in_dtype)
+    args = (_ptr(x, idt, xs, "x"), _ptr(B, idt, bs, "B"), _ptr(C, idt, bs, "C"),
+            _ptr(dt, torch.float32, ds, "dt"), _ptr(y, torch.float32, xs, "y"))
+    _check(library().rss_verify_k_tokens_fold(layer.handle, int(min_len), int(K), *args,
+                                              _stream(stream)), "rss_verify_k_tokens_fold")
 
 
 def rss_rollback(layer: ReplayLayer, n_drop, stream=None) -> None:

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rss.rss_version() == 10300
+    assert rss.rss_version() == 10400
     for s in range(7):
         assert rss.status_string(s)
     assert rss.status_string(99) == "unknown status"
@@ -55,7 +55,7 @@ def test_version_and_status_strings():
 
 def test_largest_shapes_within_the_lds_budget_are_accepted():
     ok = [dict(headdim=256, dstate=256, window=57, capacity=64, max_draft=7),
-          dict(headdim=256, dstate=256, window=52, capacity=59, max_draft=7, in_dtype=rss.RSS_DTYPE_F32),
+          dict(headdim=256, dstate=256, window=51, capacity=58, max_draft=7, in_dtype=rss.RSS_DTYPE_F32),
           dict(headdim=256, dstate=256, window=64, capacity=64, max_draft=0, in_dtype=rss.RSS_DTYPE_F32),
           dict(headdim=256, dstate=256, window=57, capacity=64, max_draft=7,
                read_copy=rss.RSS_COPY_BF16),
@@ -180,6 +180,25 @@ def test_kda_layer_sizes_and_kind_checks():
     assert _bind(bad, _fake_bufs(kcfg))[0] == rss.RSS_E_SHAPE
 
 
+def test_verify_fold_capacity_rules_return_before_launch():
+    """R + K + 1 > 64, and grouped B rows without room for a window plus two
+    rounds, are refused on the host (the fake pointers are never launched on)."""
+    A = 0x7000000
+    lib = rss.library()
+    big = _cfg(window=50, capacity=60, max_draft=4)                   # 60 + 4 + 1 > 64
+    st, h = _bind(big, _fake_bufs(big))
+    try:
+        assert lib.rss_verify_k_tokens_fold(h, 50, 4, A, A, A, A, A, None) == rss.RSS_E_CAPACITY
+    finally:
+        lib.rss_layer_free(h)
+    grp = _cfg(ngroups=4, window=8, capacity=12, max_draft=4)          # needs 8 + 9 = 17
+    st, h = _bind(grp, _fake_bufs(grp))
+    try:
+        assert lib.rss_verify_k_tokens_fold(h, 8, 4, A, A, A, A, A, None) == rss.RSS_E_CAPACITY
+    finally:
+        lib.rss_layer_free(h)
+
+
 def test_call_order_and_argument_errors_return_before_launch():
     cfg = _cfg()
     st, h = _bind(cfg, _fake_bufs(cfg))
@@ -194,6 +213,8 @@ def test_call_order_and_argument_errors_return_before_launch():
         assert lib.rss_decode_step(h, A + 2, A, A, A, A, None) == rss.RSS_E_INVALID
         assert lib.rss_verify_k_tokens(h, 5, A, A, A, A, A, None) == rss.RSS_E_CAPACITY
         assert lib.rss_verify_k_tokens(h, -1, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_verify_k_tokens_fold(h, 0, 2, A, A, A, A, A, None) == rss.RSS_E_INVALID
+        assert lib.rss_verify_k_tokens_fold(h, 16, 5, A, A, A, A, A, None) == rss.RSS_E_CAPACITY
         assert lib.rss_flush_checkpoint(h, 0, None) == rss.RSS_E_INVALID
         assert lib.rss_decode_flush_step(h, 0, A, A, A, A, A, None) == rss.RSS_E_INVALID
         assert lib.rss_decode_flush_step(h, 16, A, A, A + 8, A, A, None) == rss.RSS_E_INVALID

@@ -211,3 +211,60 @@ def test_empty_batch_is_a_no_op():
     L.decode_step(e.to(torch.bfloat16), eB, eB, torch.empty((0, wl.nheads), device=DEV), e)
     L.flush_checkpoint(1)
     assert L.device_error() == 0
+
+
+@pytest.mark.parametrize("copy,K,G", [("none", 4, 4), ("bf16", 4, 4), ("none", 0, 4), ("none", 7, 4),
+                                     ("none", 4, 2), ("bf16", 4, 2)])
+def test_verify_with_fold_equals_flush_then_verify(copy, K, G):
+    """rss_verify_k_tokens_fold(W) against rss_flush_checkpoint(W) followed by
+    rss_verify_k_tokens: checkpoint, read copy, ring and pointers bit for bit
+    after every round; outputs equal up to rounding and match the eager
+    recurrence on the committed stream; no flush call in the fused loop."""
+    # one B row set per head: R = W + K_max (the fold frees slots in the same
+    # pass); grouped B rows: R = W + 2K + 1, no slot reuse within a call
+    R = 8 + max(K, 1) if G == 4 else 8 + 2 * K + 1
+    wl = _spec_wl(read_copy=copy, ngroups=G, max_draft=max(K, 1), draft=K, capacity=R, rounds=12,
+                  seed=4100 + K + G)
+    log(f"[spec] verify+fold vs flush+verify, copy={copy}, K={K}, G={G}, R={R}")
+    cfg = cfg_of(wl)
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    S0 = torch.from_numpy(synth.initial_state(wl)).to(DEV)
+    sep, fus = rss.ReplayLayer(cfg, A, DEV), rss.ReplayLayer(cfg, A, DEV)
+    sep.init_state(S0)
+    fus.init_state(S0)
+    S_ref = synth.initial_state(wl).astype(np.float64)
+    Bt, H, P, W = wl.batch, wl.nheads, wl.headdim, wl.window
+    tol = 1e-5 if copy == "none" else 2e-2
+    worst = worst_pair = 0.0
+    folds = 0
+    for r in range(wl.rounds):
+        rin = synth.draft_inputs(wl, r)
+        nacc = synth.accepted_drafts(wl, r) if K > 0 else np.zeros(Bt, np.int32)
+        d = dev_inputs(rin, wl.in_dtype)
+        y1 = torch.empty((Bt, K + 1, H, P), device=DEV)
+        y2 = torch.empty_like(y1)
+        lens = sep.ptr[:, 0, 1].cpu().numpy()
+        folds += int(np.sum(lens >= W))
+        sep.flush_checkpoint(W)
+        sep.verify_k_tokens(K, d["x"], d["B"], d["C"], d["dt"], y1)
+        fus.verify_k_tokens_fold(W, K, d["x"], d["B"], d["C"], d["dt"], y2)
+        torch.cuda.synchronize()
+        assert torch.equal(sep.ckpt, fus.ckpt), r
+        if copy == "bf16":
+            assert torch.equal(sep.ckpt_lo, fus.ckpt_lo), r
+            assert torch.equal(y1, y2), r          # same launches in this mode
+        assert torch.equal(sep.ptr, fus.ptr), r
+        assert torch.equal(sep.ring_x, fus.ring_x) and torch.equal(sep.ring_B, fus.ring_B), r
+        assert torch.equal(sep.ring_dl, fus.ring_dl), r
+        worst_pair = max(worst_pair, float(torch.linalg.vector_norm(y1 - y2) / torch.linalg.vector_norm(y1)))
+        y_ref, states = _eager_round(S_ref, A_np, rin)
+        worst = max(worst, rel_l2(y2.double().cpu().numpy(), y_ref))
+        nd = torch.from_numpy((K - nacc).astype(np.int32)).to(DEV)
+        sep.rollback(nd)
+        fus.rollback(nd)
+        S_ref = np.stack([states[nacc[b]][b] for b in range(Bt)])
+    log(f"  folds {folds}, fused vs separate {worst_pair:.2e}, vs oracle {worst:.2e}")
+    assert folds > 0
+    assert worst_pair < 1e-5 and worst < tol
+    assert sep.device_error() == 0 and fus.device_error() == 0
