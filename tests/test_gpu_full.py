@@ -172,3 +172,63 @@ def test_dual_precision_drift(window):
     assert torch.equal(dual.ckpt, ref32.ckpt)
     assert drift < 2e-2 and run < 2e-2
     assert master < 1e-5
+
+
+def test_spec_b512_fold_verify_full_size():
+    """The benchmark's speculative schedule at full size: verify with the
+    committed-window fold in the same pass, then rollback, no flush call.
+    Outputs on sampled pairs against the committed-stream recurrence, every
+    (sequence, head) pointer against the integer model, and every folded
+    checkpoint (sampled pairs) against the recurrence's state."""
+    wl = workloads.get("mamba2_spec_b512_h128_p64_n128_w16_k4")
+    rounds = 12
+    log(f"[full] {wl.name} with fold in verify: {rounds} rounds")
+    cfg = cfg_of(wl)
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    Bt, H, P, N, K, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.draft, wl.window
+    layer = rss.ReplayLayer(cfg, A, DEV)
+    layer.init_state()
+    pm = PointerModel(Bt, wl.capacity)
+    pg = PairGather(wl, sample_pairs(wl, 24, seed=14))
+    S_ref = np.zeros((1, len(pg.pairs), P, N))
+    A_pair = pg.A(A_np)
+    y = torch.empty((Bt, K + 1, H, P), device=DEV)
+    bidx, hidx = torch.as_tensor(pg.b, device=DEV), torch.as_tensor(pg.h, device=DEV)
+    folds = 0
+    for r in range(rounds):
+        rin = synth.draft_inputs(wl, r)
+        nacc = synth.accepted_drafts(wl, r)
+        d = dev_inputs(rin, wl.in_dtype)
+        folded = np.array([pm.len[b] >= W for b in range(Bt)])
+        for b in range(Bt):
+            pm.flush(b, W)
+        layer.verify_k_tokens_fold(W, K, d["x"], d["B"], d["C"], d["dt"], y)
+        folds += int(folded.sum())
+        fp = folded[pg.b]
+        if fp.any():
+            ck = layer.ckpt[bidx, hidx].double().cpu().numpy()
+            assert rel_l2(ck[fp], S_ref[0][fp]) < 1e-5, r
+        pr = pg.draft(rin)
+        states, refs = [], []
+        S_run = S_ref
+        for i in range(K + 1):
+            S_run, yi = mamba2.eager_step(S_run, A_pair, pr["x"][:, i], pr["B"][:, i], pr["C"][:, i], pr["dt"][:, i])
+            states.append(S_run)
+            refs.append(yi)
+        y_ref = np.stack(refs, axis=1)
+        got = y[bidx, :, hidx].permute(1, 0, 2).double().cpu().numpy()[None]
+        e1 = rel_l2(got, y_ref)
+        assert e1 < 1e-5, r
+        layer.rollback(torch.from_numpy((K - nacc).astype(np.int32)).to(DEV))
+        for b in range(Bt):
+            pm.append(b, K + 1)
+            pm.mark_tentative(b, K + 1)
+            pm.rollback(b, int(K - nacc[b]))
+        ptr = layer.ptr.cpu().numpy()
+        assert all(np.array_equal(ptr[:, h, :3], pm.as_array()) for h in range(H)), r
+        keep = nacc[pg.b]
+        S_ref = np.stack([states[keep[i]][0, i] for i in range(len(pg.pairs))])[None]
+    log(f"  {folds} sequence folds over {rounds} rounds")
+    assert folds > Bt        # most sequences folded at least once
+    assert layer.device_error() == 0
