@@ -289,6 +289,14 @@ int32_t rss_rollback(rss_layer* layer, const int32_t* n_drop, void* stream);
 int32_t rss_gdn_decode_step(rss_layer* layer, const float* q, const float* k, const float* v,
                             const float* beta, const float* alpha, float* o, void* stream);
 
+/* rss_gdn_decode_step followed by rss_flush_checkpoint(min_len), in one pass:
+ * a sequence whose window reaches min_len >= 1 entries with this token has it
+ * folded (the new entry included) into the tile already loaded for the output,
+ * and the new checkpoint written. Results equal the two calls bit for bit. */
+int32_t rss_gdn_decode_flush_step(rss_layer* layer, int32_t min_len, const float* q,
+                                  const float* k, const float* v, const float* beta,
+                                  const float* alpha, float* o, void* stream);
+
 /* Eager gated delta rule (the GDN baseline): S [Bt,H,P,N] fp32 updated in
  * place, S <- alpha S + u k^T, o = S q, layouts as rss_gdn_decode_step. Uses
  * cfg's batch, nheads, headdim (d_v) and dstate (d_k). */
@@ -308,6 +316,12 @@ int32_t rss_gdn_eager_step(const rss_config* cfg, float* S, const float* q, cons
  * fp32; 0 < alpha < 1. Ring overflow as rss_decode_step. */
 int32_t rss_kda_decode_step(rss_layer* layer, const float* q, const float* k, const float* v,
                             const float* beta, const float* alpha, float* o, void* stream);
+
+/* rss_kda_decode_step followed by rss_flush_checkpoint(min_len), in one pass,
+ * as rss_gdn_decode_flush_step; results equal the two calls bit for bit. */
+int32_t rss_kda_decode_flush_step(rss_layer* layer, int32_t min_len, const float* q,
+                                  const float* k, const float* v, const float* beta,
+                                  const float* alpha, float* o, void* stream);
 
 /* Eager KDA step (its baseline): S [Bt,H,P,N] fp32 updated in place by the rule
  * above, layouts as rss_kda_decode_step; uses cfg's batch, nheads, headdim

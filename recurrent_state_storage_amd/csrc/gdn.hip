@@ -31,7 +31,7 @@
 namespace rss {
 
 
-template <int N, int MP, bool KDA>
+template <int N, int MP, bool KDA, bool FOLD>
 __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   const int H = a.H, P = a.P, R = a.R;
   const int bh = blockIdx.x;
 
-  const float* tile = a.ckpt + (size_t)bh * P * N;
+  float* tile = a.ckpt + (size_t)bh * P * N;
   const int col = tid % TPR, rsub = tid / TPR;
   const int toff = rsub * N + col * 4;
   Frag<false> fr[MP];
@@ -74,6 +74,11 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     for (int p = tid; p < P; p += kThreads) oout[p] = __builtin_nanf("");
     return;
   }
+  // Fused fold: the token that fills the window also folds it (the new entry
+  // included) into the tile already in registers and writes the tile, with the
+  // flush's coefficients in the flush's order, so the result is bitwise the
+  // separate flush's.
+  const bool do_fold = FOLD && L >= a.fold_min_len && pt.z == 0;
 
   const GdnLds lay(R, P, N, KDA);
   float* sK = lds + lay.oK;
@@ -83,6 +88,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   float* sS = lds + lay.oS;
   float* sG = lds + lay.oG;
   float* sD = lds + lay.oD;
+  float* sFC = lds + lay.oFC;
   float* rg = KDA ? a.ring_g + (size_t)bh * R * N : nullptr;
   float* ru = a.ring_u + (size_t)bh * R * P;
   float* rk = a.ring_k + (size_t)bh * R * N;
@@ -140,6 +146,13 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     const float lam = wave_suffix_excl(u, lane);
     if (lane < n0) sCF[lane] = expf(lam);
     if (lane == 0) sCF[R] = expf(lam + u);
+    if (FOLD) {  // the fold's coefficients over all L entries, as the flush forms them
+      const float g = lane < n0 ? dl.y : logf(alpha);
+      const float u2 = lane < L ? g : 0.f;
+      const float lam2 = wave_suffix_excl(u2, lane);
+      if (lane < L) sFC[lane] = expf(lam2) * 1.f;
+      if (lane == 0) sFC[R] = expf(lam2 + u2);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -248,13 +261,56 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
             const float Sq = fmaf(D, pq[m], rq_);
             const float u = beta * (vin[row] - alpha * Sk);
             unew[row] = u;
+            if (FOLD) sU[n0 * P + row] = u;
             oout[row] = fmaf(alpha, Sq, kq * u);
           }
         }
       }
     }
+    if constexpr (FOLD) {
+      __syncthreads();   // this chunk's new u rows are in LDS (do_fold is uniform)
+      if (do_fold) {
+        // S <- D S + sum_j u_j outer (c_j k_j), j ascending; KDA: D and the
+        // decays per key channel (the keys in LDS are already scaled, c_j = 1).
+        float Dc[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Dc[v] = KDA ? sD[col * 4 + v] : sFC[R];
+#pragma unroll
+        for (int k = 0; k < MP; ++k) {
+          fr[k].v.x *= Dc[0];
+          fr[k].v.y *= Dc[1];
+          fr[k].v.z *= Dc[2];
+          fr[k].v.w *= Dc[3];
+        }
+        for (int j = 0; j < L; ++j) {
+          const float cj = KDA ? 1.f : sFC[j];
+          float bv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) bv[v] = cj * sK[j * N + col * 4 + v];
+#pragma unroll
+          for (int k = 0; k < MP; ++k) {
+            const int r0 = base + k * RPP;
+            if (r0 >= P) break;
+            const int row = r0 + rsub < P ? r0 + rsub : P - 1;   // rows past P: result unused
+            const float xv = sU[j * P + row];
+            fr[k].v.x = fmaf(xv, bv[0], fr[k].v.x);
+            fr[k].v.y = fmaf(xv, bv[1], fr[k].v.y);
+            fr[k].v.z = fmaf(xv, bv[2], fr[k].v.z);
+            fr[k].v.w = fmaf(xv, bv[3], fr[k].v.w);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < MP; ++k) {
+          const int row = base + k * RPP + rsub;
+          if (row < P) st16(tile + row * N + col * 4, fr[k].v);
+        }
+      }
+    }
   }
-  if (tid == 0) a.ptr[bh] = make_int4(head, L, 0, 0);
+  if (tid == 0) {
+    if (do_fold) a.ptr[bh] = make_int4(ring_slot(head, L, R), 0, 0, 0);
+    else a.ptr[bh] = make_int4(head, L, 0, 0);
+  }
 }
 
 // Eager gated delta rule: S <- alpha S + u k^T with u = beta (v - alpha S k),
@@ -367,10 +423,10 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
   }
 }
 
-template <int N, int MP, bool KDA>
+template <int N, int MP, bool KDA, bool FOLD>
 static hipError_t gdn_replay_one(const GdnArgs& a, int batch, hipStream_t s) {
   const size_t lds = (size_t)GdnLds(a.R, a.P, N, KDA).total * sizeof(float);
-  auto kern = gdn_replay_kernel<N, MP, KDA>;
+  auto kern = gdn_replay_kernel<N, MP, KDA, FOLD>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -380,10 +436,16 @@ static hipError_t gdn_replay_one(const GdnArgs& a, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int N, bool KDA, bool FOLD>
+static hipError_t gdn_replay_f(const GdnArgs& a, int batch, hipStream_t s) {
+  constexpr int RPP = TileGeom<N, false>::RPP;
+  return a.P > 8 * RPP ? gdn_replay_one<N, 16, KDA, FOLD>(a, batch, s)
+                       : gdn_replay_one<N, 8, KDA, FOLD>(a, batch, s);
+}
+
 template <int N, bool KDA>
 static hipError_t gdn_replay_n(const GdnArgs& a, int batch, hipStream_t s) {
-  constexpr int RPP = TileGeom<N, false>::RPP;
-  return a.P > 8 * RPP ? gdn_replay_one<N, 16, KDA>(a, batch, s) : gdn_replay_one<N, 8, KDA>(a, batch, s);
+  return a.fold_min_len > 0 ? gdn_replay_f<N, KDA, true>(a, batch, s) : gdn_replay_f<N, KDA, false>(a, batch, s);
 }
 
 template <int N>

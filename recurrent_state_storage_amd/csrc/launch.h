@@ -107,6 +107,7 @@ struct GdnArgs {
   const float* alpha;      // GDN [Bt,H]; KDA [Bt,H,N]
   float* o;                // [Bt,H,P]
   int H, P, R;
+  int fold_min_len;        // also fold windows that reach this length (0: never)
 };
 hipError_t launch_gdn_replay(const GdnArgs& a, int batch, int N, bool kda, hipStream_t s);
 

@@ -44,7 +44,7 @@ struct FlushLds {
 
 // Dynamic LDS of the GDN / KDA replay kernel, in floats.
 struct GdnLds {
-  int oK, oU, oQ, oCF, oS, oG, oD, total;
+  int oK, oU, oQ, oCF, oS, oG, oD, oFC, total;
   __host__ __device__ GdnLds(int R, int P, int N, bool kda) {
     oK = 0;                   // window k rows [R][N] (row n0 = k_t); KDA: scaled in place
     oU = R * N;               // window u rows [R][P]
@@ -53,7 +53,8 @@ struct GdnLds {
     oS = align4(oCF + R + 2); // shares [4 waves][2][P]: sum_j w u_j for z = k_t, q_t
     oG = oS + 8 * P;          // KDA: committed log-gate rows [R][N]
     oD = oG + (kda ? R * N : 0);   // KDA: exp(Lam[n]) [N]
-    total = oD + (kda ? N : 0);
+    oFC = oD + (kda ? N : 0);      // fused fold (GDN): c_j [R], then exp(Lam)
+    total = oFC + R + 1;
   }
 };
 

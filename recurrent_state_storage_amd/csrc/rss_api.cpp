@@ -92,7 +92,7 @@ bool inputs_ok(const void* x, const void* B, const void* C, const void* dt, cons
 
 extern "C" {
 
-int32_t rss_version(void) { return 10400; }
+int32_t rss_version(void) { return 10500; }
 
 const char* rss_status_string(int32_t s) {
   switch (s) {
@@ -339,9 +339,9 @@ static int32_t flush_call(rss_layer* l, int32_t min_len, const int32_t* each, vo
                                          static_cast<hipStream_t>(stream)));
 }
 
-static int32_t delta_decode(rss_layer* l, int32_t kind, const float* q, const float* k,
-                            const float* v, const float* beta, const float* alpha, float* o,
-                            void* stream) {
+static int32_t delta_decode(rss_layer* l, int32_t kind, int32_t fold_min_len, const float* q,
+                            const float* k, const float* v, const float* beta, const float* alpha,
+                            float* o, void* stream) {
   if (!l || l->cfg.kind != kind) return RSS_E_INVALID;
   const rss_config& c = l->cfg;
   if (c.batch > 0 && (!inputs_ok(q, k, v, beta, o) || !alpha || !aligned16(alpha)))
@@ -365,18 +365,33 @@ static int32_t delta_decode(rss_layer* l, int32_t kind, const float* q, const fl
   a.H = c.nheads;
   a.P = c.headdim;
   a.R = c.capacity;
+  a.fold_min_len = fold_min_len;
   return launch_status(rss::launch_gdn_replay(a, c.batch, c.dstate, kind == RSS_KIND_KDA,
                                               static_cast<hipStream_t>(stream)));
 }
 
 int32_t rss_gdn_decode_step(rss_layer* l, const float* q, const float* k, const float* v,
                             const float* beta, const float* alpha, float* o, void* stream) {
-  return delta_decode(l, RSS_KIND_GDN, q, k, v, beta, alpha, o, stream);
+  return delta_decode(l, RSS_KIND_GDN, 0, q, k, v, beta, alpha, o, stream);
+}
+
+int32_t rss_gdn_decode_flush_step(rss_layer* l, int32_t min_len, const float* q, const float* k,
+                                  const float* v, const float* beta, const float* alpha, float* o,
+                                  void* stream) {
+  if (min_len < 1) return RSS_E_INVALID;
+  return delta_decode(l, RSS_KIND_GDN, min_len, q, k, v, beta, alpha, o, stream);
 }
 
 int32_t rss_kda_decode_step(rss_layer* l, const float* q, const float* k, const float* v,
                             const float* beta, const float* alpha, float* o, void* stream) {
-  return delta_decode(l, RSS_KIND_KDA, q, k, v, beta, alpha, o, stream);
+  return delta_decode(l, RSS_KIND_KDA, 0, q, k, v, beta, alpha, o, stream);
+}
+
+int32_t rss_kda_decode_flush_step(rss_layer* l, int32_t min_len, const float* q, const float* k,
+                                  const float* v, const float* beta, const float* alpha, float* o,
+                                  void* stream) {
+  if (min_len < 1) return RSS_E_INVALID;
+  return delta_decode(l, RSS_KIND_KDA, min_len, q, k, v, beta, alpha, o, stream);
 }
 
 static int32_t delta_eager(const rss_config* c, bool kda, float* S, const float* q, const float* k,

@@ -63,6 +63,8 @@ _SIGS = {
     "rss_rollback": ([_VP, _VP, _VP], _I32),
     "rss_get_device_error": ([_VP, ctypes.POINTER(_I32), _VP], _I32),
     "rss_gdn_decode_step": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
+    "rss_gdn_decode_flush_step": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
+    "rss_kda_decode_flush_step": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "rss_gdn_eager_step": ([ctypes.POINTER(rss_config), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
                            _I32),
     "rss_kda_decode_step": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
@@ -254,6 +256,12 @@ class ReplayLayer:
     def kda_decode_step(self, q, k, v, beta, alpha, o, stream=None):
         rss_kda_decode_step(self, q, k, v, beta, alpha, o, stream)
 
+    def gdn_decode_flush_step(self, min_len, q, k, v, beta, alpha, o, stream=None):
+        rss_gdn_decode_flush_step(self, min_len, q, k, v, beta, alpha, o, stream)
+
+    def kda_decode_flush_step(self, min_len, q, k, v, beta, alpha, o, stream=None):
+        rss_kda_decode_flush_step(self, min_len, q, k, v, beta, alpha, o, stream)
+
     def device_error(self, stream=None) -> int:
         return rss_get_device_error(self, stream)
 
@@ -407,3 +415,23 @@ def rss_kda_eager_step(cfg: rss_config, S, q, k, v, beta, alpha, o, stream=None)
             _ptr(k, f, kn, "k"), _ptr(v, f, vp, "v"), _ptr(beta, f, bh, "beta"),
             _ptr(alpha, f, kn, "alpha"), _ptr(o, f, vp, "o"))
     _check(library().rss_kda_eager_step(ctypes.byref(cfg), *args, _stream(stream)), "rss_kda_eager_step")
+
+
+def _delta_args(layer, q, k, v, beta, alpha, o, kda):
+    c = layer.cfg
+    kn, vp, bh = (c.batch, c.nheads, c.dstate), (c.batch, c.nheads, c.headdim), (c.batch, c.nheads)
+    f = torch.float32
+    return (_ptr(q, f, kn, "q"), _ptr(k, f, kn, "k"), _ptr(v, f, vp, "v"), _ptr(beta, f, bh, "beta"),
+            _ptr(alpha, f, kn if kda else bh, "alpha"), _ptr(o, f, vp, "o"))
+
+
+def rss_gdn_decode_flush_step(layer: ReplayLayer, min_len: int, q, k, v, beta, alpha, o, stream=None) -> None:
+    args = _delta_args(layer, q, k, v, beta, alpha, o, False)
+    _check(library().rss_gdn_decode_flush_step(layer.handle, int(min_len), *args, _stream(stream)),
+           "rss_gdn_decode_flush_step")
+
+
+def rss_kda_decode_flush_step(layer: ReplayLayer, min_len: int, q, k, v, beta, alpha, o, stream=None) -> None:
+    args = _delta_args(layer, q, k, v, beta, alpha, o, True)
+    _check(library().rss_kda_decode_flush_step(layer.handle, int(min_len), *args, _stream(stream)),
+           "rss_kda_decode_flush_step")

@@ -183,3 +183,33 @@ def test_kda_b256_full_size():
     assert worst_pair < 1e-5 and run < 1e-5 and worst_eager < 1e-5
     ck = layer.ckpt[bi, hi].double().cpu().numpy()[None]
     assert rel_l2(ck, S_ref) < 1e-5
+
+
+@pytest.mark.parametrize("shape", [(128, 128, 2, 8, 8), (37, 16, 2, 3, 3), (256, 256, 1, 4, 5),
+                                   (64, 32, 3, 1, 1)], ids=lambda s: "dv%ddk%dH%dW%dR%d" % s)
+def test_kda_fused_fold_equals_separate(shape):
+    """rss_kda_decode_flush_step against rss_kda_decode_step + rss_flush_checkpoint:
+    outputs, checkpoint, ring and pointers bit for bit at every step."""
+    dv, dk, H, W, R = shape
+    wl = KDA.replace(name="kda-fused", batch=3, nheads=H, ngroups=H, headdim=dv, dstate=dk, window=W,
+                     capacity=R, s0="normal", seed=7300 + dv + dk)
+    log(f"[kda] fused fold {shape}")
+    cfg = cfg_of(wl)
+    sep, fus = rss.ReplayLayer(cfg, None, DEV), rss.ReplayLayer(cfg, None, DEV)
+    S0 = torch.from_numpy(synth.initial_state(wl)).to(DEV)
+    sep.init_state(S0)
+    fus.init_state(S0)
+    o1 = torch.empty((wl.batch, H, dv), device=DEV)
+    o2 = torch.empty_like(o1)
+    for t in range(3 * W + 2):
+        d = _dev(synth.kda_step_inputs(wl, t))
+        sep.kda_decode_step(d["q"], d["k"], d["v"], d["beta"], d["alpha"], o1)
+        sep.flush_checkpoint(W)
+        fus.kda_decode_flush_step(W, d["q"], d["k"], d["v"], d["beta"], d["alpha"], o2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), t
+        assert torch.equal(sep.ckpt, fus.ckpt), t
+        assert torch.equal(sep.ptr, fus.ptr), t
+        assert torch.equal(sep.ring_x, fus.ring_x) and torch.equal(sep.ring_B, fus.ring_B), t
+        assert torch.equal(sep.ring_dl, fus.ring_dl), t
+    assert sep.device_error() == 0 and fus.device_error() == 0
