@@ -40,7 +40,7 @@ WORKLOAD = "mamba2_b256_h128_p64_n128_w16"
 METRIC = "SSM decode tokens/s per layer + achieved HBM GB/s (% of peak), batch 256"
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "replay_decode_b256_hbm_counters.txt")
-KERNEL_SOURCES = ["replay.hip", "device.h", "limits.h", "launch.h"]
+KERNEL_SOURCES = ["replay.hip", "device.h", "limits.h", "launch.h", "lds.h"]
 
 
 # ---- algorithmic bytes (what the method must move, per (sequence, head)) ----
