@@ -20,9 +20,12 @@ from gpu_util import DEV, PairGather, cfg_of, dev_inputs, rel_l2, sample_pairs, 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def test_decode_b256_full_size():
+@pytest.mark.parametrize("schedule", ["separate", "fused", "staggered"])
+def test_decode_b256_full_size(schedule):
+    """The benchmark workload in each fold schedule the benchmark times: decode +
+    flush every W steps, the fused decode + fold, and staggered per-sequence folds."""
     wl = workloads.get("mamba2_b256_h128_p64_n128_w16")
-    log(f"[full] {wl.name}: {wl.steps} steps, flush every {wl.window}")
+    log(f"[full] {wl.name}: {wl.steps} steps, {schedule} folds every {wl.window}")
     cfg = cfg_of(wl)
     A_np = synth.params(wl)["A"]
     A = torch.from_numpy(A_np).to(DEV)
@@ -36,10 +39,22 @@ def test_decode_b256_full_size():
     ye = torch.empty_like(y)
     worst_pair = worst_eager = worst_ckpt = 0.0
     ys, refs = [], []
+    W = wl.window
+    first = 1 + np.arange(wl.batch) % W
+    lens = np.zeros(wl.batch, np.int64)
     for t in range(wl.steps):
         s = synth.step_inputs(wl, t)
         d = dev_inputs(s, wl.in_dtype)
-        layer.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+        if schedule == "separate" or (schedule == "fused" and (t + 1) % W != 0):
+            layer.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+        elif schedule == "fused":
+            layer.decode_flush_step(W, d["x"], d["B"], d["C"], d["dt"], y)
+        else:
+            th = np.where(t < first, first, W).astype(np.int32)
+            layer.decode_flush_step_each(torch.from_numpy(th).to(DEV), d["x"], d["B"], d["C"], d["dt"], y)
+            lens += 1
+            lens[lens >= th] = 0
+            assert np.array_equal(layer.ptr[:, :, 1].cpu().numpy(), np.repeat(lens[:, None], wl.nheads, 1)), t
         rss.rss_eager_step(cfg, S_eag, d["x"], d["B"], d["C"], d["dt"], A, ye)
         ps = pg.step(s)
         S_ref, y_ref = mamba2.eager_step(S_ref, A_pair, ps["x"], ps["B"], ps["C"], ps["dt"])
@@ -48,8 +63,9 @@ def test_decode_b256_full_size():
         ys.append(got)
         refs.append(y_ref)
         worst_eager = max(worst_eager, float(torch.linalg.vector_norm(y - ye) / torch.linalg.vector_norm(ye)))
-        if (t + 1) % wl.window == 0:
-            layer.flush_checkpoint(wl.window)
+        if (t + 1) % wl.window == 0 and schedule != "staggered":
+            if schedule == "separate":
+                layer.flush_checkpoint(wl.window)
             ck = layer.ckpt[torch.as_tensor(pg.b, device=DEV), torch.as_tensor(pg.h, device=DEV)]
             worst_ckpt = max(worst_ckpt, rel_l2(ck.double().cpu().numpy()[None], S_ref))
             st = layer.ptr.cpu()
