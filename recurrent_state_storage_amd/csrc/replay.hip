@@ -21,17 +21,21 @@
 //      kept raw), the new tokens' C and the window's (dt, l) pairs; scan the
 //      log-decays in one wavefront (a reverse tree sum: no prefix differences);
 //   3. per (i, j) pair, one wavefront: w_ij = exp(lam) dt (B_j . C_i), and the
-//      wavefront's share of sum_j w_ij x_j (wavefront w takes j = w mod 4);
-//   4. consume the tile: per row a 16-byte fragment dot C_i, a butterfly over
-//      the lanes sharing the row, y = exp(Lam) * dot + the four ring shares.
-// The new tokens' x and B rows are copied from LDS to the ring.
-// The checkpoint tile is read exactly once per call for all nt outputs.
+//      wavefront's share of sum_j w_ij x_j (wavefront w takes j = w mod the
+//      number of wavefronts);
+//   4. consume the tile: per pass a 16-byte fragment dot C_i, reduce-scattered
+//      over the lanes sharing the row, y = exp(Lam) * dot + the ring shares.
+// The new tokens' x and B rows are copied from LDS to the ring, and their
+// (dt, l) pairs stored, after the loads have landed (a store issued before that
+// wait would be waited for too). The checkpoint tile is read exactly once per
+// call for all nt outputs. A bf16 tile is read by two-wavefront workgroups.
 //
 // Fused fold: a decode launched with a fold threshold also folds, in the same
 // pass, every window the new token fills (the tile is already in registers),
 // and writes the new checkpoint: the flush's extra read of the tile is saved.
 // The threshold may differ per sequence, so that sequences whose windows are
-// out of phase fold on different steps (a staggered schedule).
+// out of phase fold on different steps (a staggered schedule). A verify
+// launched with a threshold folds the committed window it starts from instead.
 #include <type_traits>
 
 #include "device.h"
@@ -39,7 +43,6 @@
 #include "lds.h"
 
 namespace rss {
-
 
 constexpr int kStageS = 4;  // scalar loads per thread and round (x rows when P % VE != 0)
 
