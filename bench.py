@@ -75,10 +75,15 @@ def eager_bytes(wl, state_bytes: int = 4) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the replay kernel's code (comments and blank space removed, so a
+    comment edit does not retire the committed counter measurements)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "recurrent_state_storage_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "recurrent_state_storage_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
