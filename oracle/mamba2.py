@@ -92,10 +92,10 @@ def semiseparable_matrix(A_h, B_seq, C_seq, dt_seq) -> np.ndarray:
     """M (T,T) of one (sequence, head): Y = M @ X + (initial-state term).
 
     M[t, j] = exp(sum_{i=j+1..t} dt_i*A_h) * dt_j * (C_t . B_j) for j <= t, else 0.
-    This is the unrolled recurrence ("ReplaySSM déroule la récurrence", P2,
-    section "L'astuce du checkpoint et du tampon"); the same lower-triangular
-    matrix is the structured-SSM / linear-attention duality P5 mentions
-    ("De Mamba à Mamba-3"). B_seq, C_seq (T,N), dt_seq (T,)."""
+    This is the recurrence unrolled, which is what ReplaySSM does (P2, section
+    "L'astuce du checkpoint et du tampon"); the same lower-triangular matrix is
+    the structured-SSM / linear-attention duality P5 mentions (section "De Mamba
+    à Mamba-3"). B_seq, C_seq (T,N), dt_seq (T,)."""
     A_h = float(A_h)
     B_seq, C_seq, dt_seq = map(_f64, (B_seq, C_seq, dt_seq))
     T = len(dt_seq)
