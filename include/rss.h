@@ -255,7 +255,8 @@ int32_t rss_verify_k_tokens(rss_layer* layer, int32_t K, const void* x, const vo
  * unfolded checkpoint and the whole window, equal up to rounding. A speculative
  * loop of this call and rss_rollback needs no separate flush: a window the
  * accepted drafts fill is folded by the next round (R >= W + K_max still
- * bounds the ring between rounds; during the call a folding sequence stages up
+ * bounds the ring between rounds, where a window may hold up to W + K entries,
+ * so call rss_flush_checkpoint(W) before returning to plain decode; during the call a folding sequence stages up
  * to R + K + 1 positions, the committed ones read before their slots are
  * reused). With read_copy = BF16 or RSS_STATE_BF16 the fold runs as a separate
  * flush launch first. Errors as rss_verify_k_tokens and rss_flush_checkpoint,

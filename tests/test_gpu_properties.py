@@ -35,15 +35,19 @@ def layer_shapes(draw):
     copy = draw(st.sampled_from(["none", "bf16"]))
     Bt = draw(st.integers(1, 3))
     seed = draw(st.integers(0, 10**6))
+    fold_verify = draw(st.booleans())
+    if fold_verify and G < H:   # grouped B rows: no slot reuse within a call
+        R = max(R, W + 2 * K + 1)
     return dict(batch=Bt, headdim=P, dstate=N, nheads=H, ngroups=G, window=W, capacity=R,
-                max_draft=K, draft=K, in_dtype=idt, read_copy=copy, seed=seed)
+                max_draft=K, draft=K, in_dtype=idt, read_copy=copy, seed=seed), fold_verify
 
 
 @settings(max_examples=30, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 @given(layer_shapes())
 def test_random_layers_match_oracle(shape):
+    shape, fold_verify = shape
     wl = BASE.replace(name="prop", s0="normal", **shape)
-    log(f"[prop] {shape}")
+    log(f"[prop] {shape} fold_verify={fold_verify}")
     cfg = cfg_of(wl)
     A_np = synth.params(wl)["A"]
     A = torch.from_numpy(A_np).to(DEV)
@@ -67,21 +71,28 @@ def test_random_layers_match_oracle(shape):
 
     for t in range(W + 2):
         decode(t)
-    rin = synth.draft_inputs(wl, 0)
-    nacc = synth.accepted_drafts(wl, 0)
-    d = dev_inputs(rin, wl.in_dtype)
-    y = torch.empty((Bt, K + 1, H, P), device=DEV)
-    L.verify_k_tokens(K, d["x"], d["B"], d["C"], d["dt"], y)
-    L.rollback(torch.from_numpy((K - nacc).astype(np.int32)).to(DEV))
-    L.flush_checkpoint(W)
-    states = []
-    Sr = S
-    for i in range(K + 1):
-        Sr, yr = mamba2.eager_step(Sr, A_np, rin["x"][:, i], rin["B"][:, i], rin["C"][:, i], rin["dt"][:, i])
-        states.append(Sr)
-        refs.append(yr.ravel())
-        ys.append(y[:, i].double().cpu().numpy().ravel())
-    S = np.stack([states[nacc[b]][b] for b in range(Bt)])
+    for r in range(3):   # speculative rounds; the fused variant folds inside the verify
+        rin = synth.draft_inputs(wl, r)
+        nacc = synth.accepted_drafts(wl, r)
+        d = dev_inputs(rin, wl.in_dtype)
+        y = torch.empty((Bt, K + 1, H, P), device=DEV)
+        if fold_verify:
+            L.verify_k_tokens_fold(W, K, d["x"], d["B"], d["C"], d["dt"], y)
+            L.rollback(torch.from_numpy((K - nacc).astype(np.int32)).to(DEV))
+        else:
+            L.verify_k_tokens(K, d["x"], d["B"], d["C"], d["dt"], y)
+            L.rollback(torch.from_numpy((K - nacc).astype(np.int32)).to(DEV))
+            L.flush_checkpoint(W)
+        states = []
+        Sr = S
+        for i in range(K + 1):
+            Sr, yr = mamba2.eager_step(Sr, A_np, rin["x"][:, i], rin["B"][:, i], rin["C"][:, i],
+                                       rin["dt"][:, i])
+            states.append(Sr)
+            refs.append(yr.ravel())
+            ys.append(y[:, i].double().cpu().numpy().ravel())
+        S = np.stack([states[nacc[b]][b] for b in range(Bt)])
+    L.flush_checkpoint(W)   # back to plain decode: fold a full window first
     for t in range(W + 1):
         decode(100 + t)
     assert L.device_error() == 0
