@@ -248,3 +248,50 @@ def test_spec_b512_fold_verify_full_size():
     log(f"  {folds} sequence folds over {rounds} rounds")
     assert folds > Bt        # most sequences folded at least once
     assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("copy", ["bf16", "bf16_state"])
+def test_bf16_tile_modes_b256_full_size(copy):
+    """The bf16-tile modes the benchmark times at batch 256 (dual precision and
+    the bf16-only checkpoint, W = 16, the two-wavefront replay launch): 48 steps,
+    sampled pairs against their fp64 emulators (1e-3) and the exact recurrence
+    (2e-2); the eager bf16-stored state beside them, against its emulator."""
+    wl = workloads.get("mamba2_dual_b256_h128_p64_n128_w16").replace(read_copy=copy)
+    steps = 48
+    log(f"[full] {wl.name} read_copy={copy}: {steps} steps")
+    cfg = cfg_of(wl)
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    layer = rss.ReplayLayer(cfg, A, DEV)
+    layer.init_state()
+    pg = PairGather(wl, sample_pairs(wl, 24, seed=15))
+    A_pair = pg.A(A_np)
+    Z = np.zeros((1, len(pg.pairs), wl.headdim, wl.dstate))
+    emu = mamba2.ReplayModel(Z, A_pair, len(pg.pairs), wl.capacity, read_copy=copy)
+    S_ref, S_eb = Z.copy(), Z.copy()
+    Se = torch.zeros((wl.batch, wl.nheads, wl.headdim, wl.dstate), dtype=torch.bfloat16, device=DEV)
+    ecfg = cfg_of(wl, read_copy=rss.RSS_STATE_BF16)
+    y = torch.empty((wl.batch, wl.nheads, wl.headdim), device=DEV)
+    ye = torch.empty_like(y)
+    got, emus, refs, egot, eemu = [], [], [], [], []
+    for t in range(steps):
+        s = synth.step_inputs(wl, t)
+        d = dev_inputs(s, wl.in_dtype)
+        layer.decode_flush_step(wl.window, d["x"], d["B"], d["C"], d["dt"], y)
+        rss.rss_eager_step(ecfg, Se, d["x"], d["B"], d["C"], d["dt"], A, ye)
+        ps = pg.step(s)
+        S_ref, y_ref = mamba2.eager_step(S_ref, A_pair, ps["x"], ps["B"], ps["C"], ps["dt"])
+        emus.append(emu.decode(ps["x"], ps["B"], ps["C"], ps["dt"]))
+        emu.flush(wl.window)
+        S_new, y_eb = mamba2.eager_step(S_eb, A_pair, ps["x"], ps["B"], ps["C"], ps["dt"])
+        S_eb = mamba2.lowp.round_bf16(S_new)
+        got.append(pg.out(y))
+        egot.append(pg.out(ye))
+        eemu.append(y_eb)
+        refs.append(y_ref)
+    vs_emu = rel_l2(np.stack(got), np.stack(emus))
+    vs_exact = rel_l2(np.stack(got), np.stack(refs))
+    eager_vs_emu = rel_l2(np.stack(egot), np.stack(eemu))
+    log(f"  replay vs emulator {vs_emu:.2e}, vs exact {vs_exact:.2e}; eager bf16 vs emulator {eager_vs_emu:.2e}")
+    assert vs_emu < 1e-3 and vs_exact < 2e-2 and eager_vs_emu < 1e-3
+    assert layer.device_error() == 0
