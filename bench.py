@@ -66,7 +66,8 @@ def flush_bytes(wl, n: int) -> int:
 def fused_bytes(wl) -> int:
     """Decode of the token that fills the window, with the fold in the same pass:
     the replay's bytes plus the new checkpoint written."""
-    return replay_bytes(wl, wl.window - 1) + wl.headdim * wl.dstate * 4
+    sb = 2 if wl.read_copy == "bf16_state" else 4
+    return replay_bytes(wl, wl.window - 1) + wl.headdim * wl.dstate * sb
 
 
 def eager_bytes(wl, state_bytes: int = 4) -> int:
@@ -193,7 +194,9 @@ def _timed(torch, fn, n):
 
 def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16"):
     """Replay with a bf16 tile read, W = 16, same inputs: dual precision (fp32
-    master + bf16 read copy, mode "bf16") or a single bf16 checkpoint ("bf16_state")."""
+    master + bf16 read copy, mode "bf16"; the fold of the master is a separate
+    flush launch) or a single bf16 checkpoint ("bf16_state"; folded inside the
+    decode that fills the window)."""
     wl = workloads.get("mamba2_dual_b256_h128_p64_n128_w16").replace(read_copy=mode)
     Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
     code = rss.RSS_COPY_BF16 if mode == "bf16" else rss.RSS_STATE_BF16
@@ -202,20 +205,28 @@ def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16"):
     layer.init_state()
     y = torch.empty((Bt, H, P), device=dev)
     T = X.shape[0]
-    ev = {}
+    fused = mode == "bf16_state"
+    ev = {"r": [], "f": []}
+
+    def mark(key):
+        ev[key].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+        ev[key][-1][0].record()
 
     def step(k, rec=False):
         i = k % T
+        fold = (k + 1) % W == 0
+        key = "f" if fold and fused else "r"
         if rec:
-            ev.setdefault("r", []).append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-            ev["r"][-1][0].record()
-        layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
+            mark(key)
+        if fold and fused:
+            layer.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)
+        else:
+            layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
         if rec:
-            ev["r"][-1][1].record()
-        if (k + 1) % W == 0:
+            ev[key][-1][1].record()
+        if fold and not fused:
             if rec:
-                ev.setdefault("f", []).append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-                ev["f"][-1][0].record()
+                mark("f")
             layer.flush_checkpoint(W)
             if rec:
                 ev["f"][-1][1].record()
@@ -227,15 +238,19 @@ def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16"):
         step(base + j, rec=True)
     torch.cuda.synchronize()
     r_ms = sum(a.elapsed_time(b) for a, b in ev["r"])
-    f_ms = sum(a.elapsed_time(b) for a, b in ev.get("f", []))
-    rbytes = sum(replay_bytes(wl, (base + j) % W) for j in range(steps)) * Bt * H
-    fbytes = flush_bytes(wl, W) * Bt * H * len(ev.get("f", []))
+    f_ms = sum(a.elapsed_time(b) for a, b in ev["f"])
+    phases = [(base + j) % W for j in range(steps)]
+    rbytes = sum(replay_bytes(wl, n0) for n0 in phases if not (fused and n0 == W - 1)) * Bt * H
+    per_fold = fused_bytes(wl) if fused else flush_bytes(wl, W)
+    fbytes = per_fold * Bt * H * len(ev["f"])
     assert layer.device_error() == 0
     return {"workload": wl.name if mode == "bf16" else wl.name + " with a bf16-only checkpoint",
             "tokens_per_s": Bt * steps / (ms / 1e3),
-            "replay_avg_us": r_ms / steps * 1e3, "replay_GBps": rbytes / (r_ms / 1e3) / 1e9,
-            "flush_avg_us": f_ms / max(len(ev.get("f", [])), 1) * 1e3,
-            "flush_GBps": fbytes / (f_ms / 1e3) / 1e9 if f_ms else None}
+            "replay_avg_us": r_ms / max(len(ev["r"]), 1) * 1e3,
+            "replay_GBps": rbytes / (r_ms / 1e3) / 1e9,
+            "fold": "fused into the decode that fills the window" if fused else "separate flush launch",
+            "fold_avg_us": f_ms / max(len(ev["f"]), 1) * 1e3,
+            "fold_GBps": fbytes / (f_ms / 1e3) / 1e9 if f_ms else None}
 
 
 def _gen_round(args):

@@ -29,12 +29,19 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest, ties to even; NaN stays a (quiet) NaN.
+// fp32 -> bf16, round to nearest, ties to even; a NaN stays NaN (quiet bit set,
+// sign and top payload bits kept); denormals are rounded, not flushed. gfx950's
+// packed conversion (v_cvt_pk_bf16_f32, two values per instruction) does
+// exactly this: it agrees with the bit-level definition (add 0x7fff plus the
+// lowest kept bit, truncate; NaN -> (bits >> 16) | 0x40) on all 2^32 inputs.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return static_cast<bf16_t>(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
@@ -173,6 +180,14 @@ __device__ __forceinline__ uint4 ld16(const bf16_t* p) {
 __device__ __forceinline__ void st16(float* p, const float4& v) {
   __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
 }
+// Eight fp32 values stored as RNE bf16 (16 bytes, non-temporal).
+__device__ __forceinline__ void st16_bf16x8(bf16_t* p, const float (&v)[8]) {
+  u32x4 pk;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    pk[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(p));
+}
 
 // Four bf16 values of a bf16 checkpoint (8 bytes, non-temporal) widened to
 // fp32, and their RNE-packed store: the tile geometry of the fp32 state (4
@@ -184,8 +199,7 @@ __device__ __forceinline__ float4 ld8_bf16x4(const bf16_t* p) {
                      __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
 }
 __device__ __forceinline__ void st8_bf16x4(bf16_t* p, const float4& v) {
-  const u32x2 pk = {(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
-                    (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+  const u32x2 pk = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
   __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(p));
 }
 

@@ -220,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
         if (DUAL) {
           bf16_t* lo = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N + (size_t)row * N + col * 4;
           uint2 pk;
-          pk.x = (uint32_t)f32_to_bf16(fr[k].v.x) | ((uint32_t)f32_to_bf16(fr[k].v.y) << 16);
-          pk.y = (uint32_t)f32_to_bf16(fr[k].v.z) | ((uint32_t)f32_to_bf16(fr[k].v.w) << 16);
+          pk.x = pack_bf16x2(fr[k].v.x, fr[k].v.y);
+          pk.y = pack_bf16x2(fr[k].v.z, fr[k].v.w);
           *reinterpret_cast<uint2*>(lo) = pk;
         }
       }
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(kThreads) void init_kernel(InitArgs a) {
     if (a.ckpt) reinterpret_cast<float4*>(a.ckpt)[i] = v;
     if (a.ckpt_lo) {
       uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-      pk.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+      pk.x = pack_bf16x2(v.x, v.y);
+      pk.y = pack_bf16x2(v.z, v.w);
       reinterpret_cast<uint2*>(a.ckpt_lo)[i] = pk;
     }
   }

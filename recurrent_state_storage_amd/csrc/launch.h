@@ -12,7 +12,8 @@ namespace rss {
 // Decode (nt = 1) and speculative verify (nt = K+1) by replay.
 struct ReplayArgs {
   float* ckpt;             // [Bt,H,P,N] fp32 master (written only by the fused fold)
-  const void* ckpt_lo;     // [Bt,H,P,N] bf16 read copy (dual mode)
+  void* ckpt_lo;           // [Bt,H,P,N] bf16 read copy (dual mode), or the bf16-stored
+                           // checkpoint (written only by its fused fold)
   void* ring_x;            // [Bt,H,R,P]
   void* ring_B;            // [Bt,G,R,N]
   float2* ring_dl;         // [Bt,H,R] (dt, dt*A)

@@ -13,8 +13,11 @@ constexpr int kMaxLdsBytes = 160 * 1024;  // LDS one gfx950 workgroup may alloca
 // B rows are kept raw (input dtype), exactly as the direct global->LDS loads
 // deliver them; everything else is fp32.
 struct ReplayLds {
-  int oX, oB, oC, oCF, oDC, oRing, oFC, total;
-  __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes, int nw) {
+  int oX, oB, oC, oCF, oDC, oRing, oFC, RS, oXT, oCB, total;
+  // fold_f32: room for the fused fold of a bf16-stored checkpoint, whose
+  // operands are widened once: x transposed [P][RS] and c_j B_j [RS][N].
+  __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes, int nw,
+                                bool fold_f32 = false) {
     oX = 0;                                            // raw window x [R][P]
     oB = align4((R * P * tin_bytes + 3) / 4);          // raw window B [R][N]
     oC = oB + align4((R * N * tin_bytes + 3) / 4);     // new tokens' C [ntmax][N]
@@ -22,7 +25,10 @@ struct ReplayLds {
     oDC = oCF + ntmax * R;                             // exp(Lam) [ntmax]
     oRing = align4(oDC + ntmax);                       // ring shares [nw][ntmax][P]
     oFC = oRing + nw * ntmax * P;                      // fused fold: c_j [R], then exp(Lam)
-    total = oFC + R + 1;
+    RS = align4(R);
+    oXT = align4(oFC + R + 1);
+    oCB = oXT + (fold_f32 ? P * RS : 0);
+    total = fold_f32 ? oCB + RS * N : oFC + R + 1;
   }
 };
 

@@ -36,6 +36,8 @@
 // The threshold may differ per sequence, so that sequences whose windows are
 // out of phase fold on different steps (a staggered schedule). A verify
 // launched with a threshold folds the committed window it starts from instead.
+// A bf16-stored checkpoint is folded the same way by the two-wavefront decode
+// (widened to fp32, folded, stored RNE-bf16, as its separate flush does).
 #include <type_traits>
 
 #include "device.h"
@@ -92,9 +94,9 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   const int head = pt.x, n0 = pt.y;
   const int L = n0 + nt;
 
-  // Fused fold (fp32 checkpoint): the tile already in registers is folded and
-  // written back in this pass, exactly as a separate flush would (same
-  // coefficients, same order). A decode folds its whole window, the new token
+  // Fused fold (fp32 checkpoint, or a bf16-stored one in a decode): the tile
+  // already in registers is folded and written back in this pass, exactly as a
+  // separate flush would (same coefficients, same order). A decode folds its whole window, the new token
   // included, once that reaches the threshold; a verify folds the committed
   // window it starts from (never the tentative tokens it appends), as a flush
   // just before it would. Such a verify frees the committed slots for the new
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   }
   if (tent && tid == 0) atomicOr(a.err, kDevUncommitted);  // never fold tentative entries
 
-  const ReplayLds lay(RL, P, N, NTMAX, (int)sizeof(Tin), NW);
+  const ReplayLds lay(RL, P, N, NTMAX, (int)sizeof(Tin), NW, FOLD && LOW);
   Tin* sX = reinterpret_cast<Tin*>(lds + lay.oX);
   Tin* sB = reinterpret_cast<Tin*>(lds + lay.oB);
   float* sC = lds + lay.oC;
@@ -307,6 +309,19 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       if (r * 64 + lane < P) sRing[(wave * NTMAX + i) * P + r * 64 + lane] = share[r];
     }
   }
+  if constexpr (FOLD && LOW) {
+    if (do_fold) {  // the fold's operands widened once: x transposed, and c_j B_j
+      const int F4 = align4(F);                  // entries F..F4-1 are zero padding
+      float* sXT = lds + lay.oXT;
+      float* sCB = lds + lay.oCB;
+      for (int j = 0; j < F4; ++j)
+        for (int p = tid; p < P; p += NT) sXT[p * lay.RS + j] = j < F ? to_f32(sX[j * P + p]) : 0.f;
+      for (int e = tid; e < F4 * N; e += NT) {
+        const int j = e / N;
+        sCB[e] = j < F ? sFC[j] * to_f32(sB[e]) : 0.f;
+      }
+    }
+  }
   __syncthreads();
 
   // 4. Consume the tile: per pass a 16-byte fragment dot C_i, reduce-scattered
@@ -346,7 +361,45 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
         }
       }
     }
-    if constexpr (FOLD) {
+    if constexpr (FOLD && LOW) {
+      if (do_fold) {  // bf16-stored checkpoint: the same fold in fp32 (the flush's
+                      // order, four entries per step), stored RNE-bf16
+        const float D = sFC[RL];
+        const float* sXT = lds + lay.oXT;
+        const float* sCB = lds + lay.oCB;
+        float sv[kMaxPass][8];
+        const float* xr[kMaxPass];
+        // Every pass is computed (rows past P read a valid row; their results
+        // are never stored), so the entry loop has no branches.
+#pragma unroll
+        for (int k = 0; k < kMaxPass; ++k) {
+#pragma unroll
+          for (int v = 0; v < 8; ++v) sv[k][v] = fr[k].get(v) * D;
+          const int row = base + k * RPP + rsub;
+          xr[k] = sXT + (row < P ? row : P - 1) * lay.RS;
+        }
+        for (int j4 = 0; j4 < F; j4 += 4) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float4 b0 = *reinterpret_cast<const float4*>(&sCB[(j4 + jj) * N + col * 8]);
+            const float4 b1 = *reinterpret_cast<const float4*>(&sCB[(j4 + jj) * N + col * 8 + 4]);
+            const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int k = 0; k < kMaxPass; ++k) {
+              const float x = xr[k][j4 + jj];
+#pragma unroll
+              for (int v = 0; v < 8; ++v) sv[k][v] = fmaf(x, bv[v], sv[k][v]);
+            }
+          }
+        }
+        bf16_t* out = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N;
+#pragma unroll
+        for (int k = 0; k < kMaxPass; ++k) {
+          const int row = base + k * RPP + rsub;
+          if (row < P) st16_bf16x8(out + row * N + col * 8, sv[k]);
+        }
+      }
+    } else if constexpr (FOLD) {
       if (do_fold) {  // S <- exp(Lam) S + sum_j x_j outer (c_j B_j), j ascending
         const float D = sFC[RL];
 #pragma unroll
@@ -392,7 +445,8 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
 template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD, int NT = kThreads>
 static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
   const size_t lds =
-      (size_t)ReplayLds(a.R + ((FOLD && NTMAX > 1) ? NTMAX : 0), a.P, N, NTMAX, (int)sizeof(Tin), NT / 64)
+      (size_t)ReplayLds(a.R + ((FOLD && NTMAX > 1) ? NTMAX : 0), a.P, N, NTMAX, (int)sizeof(Tin), NT / 64,
+                        FOLD && LOW)
           .total * sizeof(float);
   auto kern = replay_kernel<N, Tin, LOW, NTMAX, FOLD, NT>;
   if (lds > 64 * 1024) {
@@ -410,18 +464,23 @@ static hipError_t launch_nt(const ReplayArgs& a, int batch, hipStream_t s) {
   if (a.nt != 1 || (fold && a.set_tent)) {   // verify (a folding verify of one token too)
     if constexpr (!LOW) {
       if (fold) return launch_one<N, Tin, LOW, kMaxNew, true>(a, batch, s);
+    } else {
+      if (fold) return hipErrorInvalidValue;
     }
     return launch_one<N, Tin, LOW, kMaxNew, false>(a, batch, s);
   }
-  if constexpr (!LOW) {  // the fused fold needs the fp32 checkpoint in registers
-    if (fold) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
-  } else {
+  if constexpr (LOW) {
     // A bf16 tile is half the bytes: two wavefronts per (sequence, head) hold
     // it in the same 8 fragments per lane, and twice as many workgroups fit on
-    // a CU, so twice the bytes are in flight.
+    // a CU, so twice the bytes are in flight. A fold writes the bf16 tile back:
+    // only for a bf16-stored checkpoint (a dual-precision layer folds its fp32
+    // master, which this kernel never reads).
+    if (fold) return launch_one<N, Tin, LOW, 1, true, 128>(a, batch, s);
     return launch_one<N, Tin, LOW, 1, false, 128>(a, batch, s);
+  } else {
+    if (fold) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
+    return launch_one<N, Tin, LOW, 1, false>(a, batch, s);
   }
-  return launch_one<N, Tin, LOW, 1, false>(a, batch, s);
 }
 
 template <int N>

@@ -92,7 +92,7 @@ bool inputs_ok(const void* x, const void* B, const void* C, const void* dt, cons
 
 extern "C" {
 
-int32_t rss_version(void) { return 10500; }
+int32_t rss_version(void) { return 10600; }
 
 const char* rss_status_string(int32_t s) {
   switch (s) {
@@ -220,7 +220,17 @@ static int32_t decode_fold(rss_layer* l, int32_t min_len, const int32_t* each, c
   if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
   if (l->pending_verify) return RSS_E_ORDER;
-  if (l->cfg.read_copy != RSS_COPY_NONE) {  // the replay reads a bf16 tile: two launches
+  const rss_config& c = l->cfg;
+  // Two launches where the fold cannot ride on the replay: dual precision (the
+  // replay reads the copy, the fold the fp32 master), or a bf16-stored
+  // checkpoint whose widened fold operands would not fit the LDS budget.
+  bool separate = c.read_copy == RSS_COPY_BF16;
+  if (c.read_copy == RSS_STATE_BF16) {
+    const int tin = c.in_dtype == RSS_DTYPE_BF16 ? 2 : 4;
+    const size_t lds = (size_t)rss::ReplayLds(c.capacity, c.headdim, c.dstate, 1, tin, 2, true).total * 4;
+    separate = lds > (size_t)rss::kMaxLdsBytes;
+  }
+  if (separate) {
     const int32_t st = replay_call(l, 1, 0, 0, nullptr, x, B, C, dt, y, stream);
     return st ? st : flush_call(l, min_len, each, stream);
   }

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rss.rss_version() == 10500
+    assert rss.rss_version() == 10600
     for s in range(7):
         assert rss.status_string(s)
     assert rss.status_string(99) == "unknown status"

@@ -47,6 +47,13 @@ SHAPES = [
     (128, 128, 2, 2, 8, 8, "bf16", "none"),
     (64, 128, 4, 4, 16, 16, "bf16", "bf16"),
     (1, 16, 1, 1, 1, 1, "f32", "none"),
+    # a bf16-stored checkpoint, folded inside the two-wavefront decode
+    (64, 128, 4, 4, 16, 16, "bf16", "bf16_state"),
+    (37, 32, 3, 1, 5, 7, "f32", "bf16_state"),
+    (100, 256, 2, 2, 4, 4, "f32", "bf16_state"),
+    (128, 128, 2, 2, 8, 8, "bf16", "bf16_state"),
+    (256, 64, 1, 1, 3, 3, "bf16", "bf16_state"),
+    (1, 16, 1, 1, 1, 1, "f32", "bf16_state"),
 ]
 
 
@@ -81,12 +88,13 @@ def test_fused_equals_separate_and_oracle(shape):
     assert rel_l2(np.stack(ys), np.stack(refs)) < (1e-5 if copy == "none" else 2e-2)
 
 
-def test_fused_folds_only_full_windows():
+@pytest.mark.parametrize("copy", ["none", "bf16_state"])
+def test_fused_folds_only_full_windows(copy):
     """After speculative rounds the sequences' windows differ; a fused decode
     folds exactly those that reach the threshold, like decode + flush."""
     wl = BASE.replace(name="fused-spec", batch=6, headdim=64, dstate=128, nheads=4, ngroups=4,
                       window=8, capacity=12, max_draft=4, draft=4, in_dtype="bf16", s0="normal",
-                      seed=5100)
+                      read_copy=copy, seed=5100)
     sep, fus = _pair(wl)
     K = wl.draft
     for r in range(9):
