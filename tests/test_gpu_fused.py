@@ -47,6 +47,11 @@ SHAPES = [
     (128, 128, 2, 2, 8, 8, "bf16", "none"),
     (64, 128, 4, 4, 16, 16, "bf16", "bf16"),
     (1, 16, 1, 1, 1, 1, "f32", "none"),
+    # dual precision: the bf16 copy is read, the fp32 master folded in the same launch
+    (37, 32, 3, 1, 5, 7, "f32", "bf16"),
+    (100, 256, 2, 2, 4, 4, "f32", "bf16"),
+    (128, 128, 2, 2, 8, 8, "bf16", "bf16"),
+    (1, 16, 1, 1, 1, 1, "f32", "bf16"),
     # a bf16-stored checkpoint, folded inside the two-wavefront decode
     (64, 128, 4, 4, 16, 16, "bf16", "bf16_state"),
     (37, 32, 3, 1, 5, 7, "f32", "bf16_state"),
@@ -88,7 +93,7 @@ def test_fused_equals_separate_and_oracle(shape):
     assert rel_l2(np.stack(ys), np.stack(refs)) < (1e-5 if copy == "none" else 2e-2)
 
 
-@pytest.mark.parametrize("copy", ["none", "bf16_state"])
+@pytest.mark.parametrize("copy", ["none", "bf16", "bf16_state"])
 def test_fused_folds_only_full_windows(copy):
     """After speculative rounds the sequences' windows differ; a fused decode
     folds exactly those that reach the threshold, like decode + flush."""

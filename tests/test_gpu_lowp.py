@@ -246,3 +246,58 @@ def test_low_precision_drift_curves(family):
         assert res[("bf16_state", 8)]["run"] > res[("bf16_state", 16)]["run"] > res[("bf16_state", 32)]["run"]
     for layer in layers.values():
         assert layer.device_error() == 0
+
+
+# ---- the bf16 rounding itself ---------------------------------------------------
+def _edge_patterns(n, seed=77):
+    """fp32 bit patterns that stress a round-to-nearest-even conversion: exact
+    ties with even and odd kept parts (both signs), values just above and below
+    a tie, denormals (smallest, largest, ties), the largest finite values (which
+    round up to infinity), infinities, signed zeros, NaNs with a quiet bit and
+    with only low payload bits, then random patterns to fill n."""
+    edges = []
+    for hi in (0x3F80, 0x3F81, 0x0001, 0x007F, 0x0080, 0x7F7E, 0x7F7F, 0x4B00, 0x3400):
+        for lo in (0x8000, 0x7FFF, 0x8001, 0x0000, 0xFFFF, 0x0001):
+            for sign in (0, 0x80000000):
+                edges.append(((hi << 16) | lo) | sign)
+    edges += [0x00000001, 0x007FFFFF, 0x00400000, 0x00008000, 0x00018000, 0x7F800000, 0xFF800000,
+              0x00000000, 0x80000000, 0x7FC00000, 0xFFC00001, 0x7F800001, 0x7FBFFFFF, 0xFF80FFFF,
+              0x7FFFFFFF, 0x7F808000]
+    rng = np.random.default_rng(seed)
+    rest = rng.integers(0, 2 ** 32, size=n - len(edges), dtype=np.uint64).astype(np.uint32)
+    return np.concatenate([np.array(edges, dtype=np.uint32), rest])
+
+
+def _rne_bits(u):
+    """Expected bf16 bits, written from the definition: NaN -> top half with the
+    quiet bit set; otherwise the oracle's round-to-nearest-even."""
+    from oracle import lowp
+    u = np.asarray(u, dtype=np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    f = u.copy()
+    f[nan] = 0                                   # the oracle rounds finite values and infinities
+    r = lowp.round_bf16_from_f32(f.view(np.float32)).astype(np.float32).view(np.uint32) >> 16
+    return np.where(nan, (u >> 16) | 0x40, r).astype(np.uint16)
+
+
+@pytest.mark.parametrize("copy", ["bf16", "bf16_state"])
+def test_bf16_rounding_bit_exact_on_edge_patterns(copy):
+    """init_state stores the bf16 image of S0 (the read copy in dual mode, the
+    checkpoint itself with a bf16-only checkpoint) through the same packed
+    conversion every bf16 store uses; its bits must be round-to-nearest-even of
+    the fp32 input, ties, denormals, overflow to infinity and NaNs included."""
+    P, N = 64, 128
+    code = rss.RSS_COPY_BF16 if copy == "bf16" else rss.RSS_STATE_BF16
+    cfg = rss.make_config(2, 3, P, N, 3, 4, 4, 0, rss.RSS_DTYPE_F32, code)
+    u = _edge_patterns(2 * 3 * P * N)
+    S0 = torch.from_numpy(u.view(np.float32).reshape(2, 3, P, N).copy()).to(DEV)
+    layer = rss.ReplayLayer(cfg, torch.zeros(3, device=DEV), DEV)
+    layer.init_state(S0)
+    lo = layer.ckpt_lo if copy == "bf16" else layer.ckpt
+    got = lo.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    want = _rne_bits(u)
+    bad = np.nonzero(got != want)[0]
+    log(f"[lowp] {copy}: {len(u)} patterns, {len(bad)} mismatches")
+    assert len(bad) == 0, [(hex(u[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+    if copy == "bf16":   # the fp32 master keeps the input bits
+        assert np.array_equal(layer.ckpt.cpu().numpy().view(np.uint32).reshape(-1), u)
