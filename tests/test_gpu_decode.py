@@ -188,3 +188,57 @@ def test_deterministic():
             ys.append(y)
         outs.append((torch.stack(ys).cpu(), L.ckpt.cpu()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("copy", ["none", "bf16", "bf16_state"])
+def test_empty_batch_every_entry_point(copy):
+    """Zero sequences: every Mamba-2 entry point (init, decode, the fused and
+    per-sequence folds, flush, verify with and without the fold, rollback, the
+    eager baselines) returns OK on empty tensors and launches nothing that could
+    touch memory; the device error word stays clear."""
+    code = {"none": rss.RSS_COPY_NONE, "bf16": rss.RSS_COPY_BF16, "bf16_state": rss.RSS_STATE_BF16}[copy]
+    H, P, N, K = 4, 16, 16, 2
+    cfg = rss.make_config(0, H, P, N, H, 4, 6, K, rss.RSS_DTYPE_F32, code)
+    A = torch.full((H,), -0.5, device=DEV)
+    layer = rss.ReplayLayer(cfg, A, DEV)
+    layer.init_state()
+    e = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device=DEV)
+    x, B, C, dt, y = e(0, H, P), e(0, H, N), e(0, H, N), e(0, H), e(0, H, P)
+    th = e(0, dt=torch.int32)
+    layer.decode_step(x, B, C, dt, y)
+    layer.decode_flush_step(4, x, B, C, dt, y)
+    layer.decode_flush_step_each(th, x, B, C, dt, y)
+    layer.flush_checkpoint(4)
+    layer.flush_checkpoint_each(th)
+    xs, Bs, Cs, dts, ys = e(0, K + 1, H, P), e(0, K + 1, H, N), e(0, K + 1, H, N), e(0, K + 1, H), e(0, K + 1, H, P)
+    layer.verify_k_tokens(K, xs, Bs, Cs, dts, ys)
+    layer.rollback(th)
+    layer.verify_k_tokens_fold(4, K, xs, Bs, Cs, dts, ys)
+    layer.rollback(th)
+    S = e(0, H, P, N, dt=torch.bfloat16 if copy == "bf16_state" else torch.float32)
+    rss.rss_eager_step(cfg, S, x, B, C, dt, A, y)
+    if copy != "bf16_state":
+        rss.rss_eager_verify(cfg, e(0, K + 1, H, P, N), th, K, xs, Bs, Cs, dts, A, ys)
+    assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_empty_batch_delta_rules(kind):
+    """Zero sequences for the delta-rule layers: decode, fused fold, flush and the
+    eager baseline return OK on empty tensors."""
+    code = rss.RSS_KIND_GDN if kind == "gdn" else rss.RSS_KIND_KDA
+    H, P, N = 2, 16, 16
+    cfg = rss.make_config(0, H, P, N, H, 4, 4, 0, rss.RSS_DTYPE_F32, rss.RSS_COPY_NONE, code)
+    layer = rss.ReplayLayer(cfg, None, DEV)
+    layer.init_state()
+    e = lambda *s: torch.empty(s, device=DEV)
+    q, k, v, beta, o = e(0, H, N), e(0, H, N), e(0, H, P), e(0, H), e(0, H, P)
+    alpha = e(0, H, N) if kind == "kda" else e(0, H)
+    dec = layer.kda_decode_step if kind == "kda" else layer.gdn_decode_step
+    fused = layer.kda_decode_flush_step if kind == "kda" else layer.gdn_decode_flush_step
+    dec(q, k, v, beta, alpha, o)
+    fused(4, q, k, v, beta, alpha, o)
+    layer.flush_checkpoint(4)
+    eager = rss.rss_kda_eager_step if kind == "kda" else rss.rss_gdn_eager_step
+    eager(cfg, e(0, H, P, N), q, k, v, beta, alpha, o)
+    assert layer.device_error() == 0
