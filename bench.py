@@ -192,12 +192,12 @@ def _timed(torch, fn, n):
     return e0.elapsed_time(e1)
 
 
-def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16"):
-    """Replay with a bf16 tile read, W = 16, same inputs: dual precision (fp32
+def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16", window=16):
+    """Replay with a bf16 tile read, W = window (16 by default), same inputs: dual precision (fp32
     master + bf16 read copy, mode "bf16"; the fold of the master is a separate
     flush launch) or a single bf16 checkpoint ("bf16_state"; folded inside the
     decode that fills the window)."""
-    wl = workloads.get("mamba2_dual_b256_h128_p64_n128_w16").replace(read_copy=mode)
+    wl = workloads.get(f"mamba2_dual_b256_h128_p64_n128_w{window}").replace(read_copy=mode)
     Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
     code = rss.RSS_COPY_BF16 if mode == "bf16" else rss.RSS_STATE_BF16
     cfg = rss.make_config(Bt, H, P, N, wl.ngroups, W, wl.capacity, 0, rss.RSS_DTYPE_BF16, code)
@@ -746,6 +746,11 @@ def main() -> int:
         rec["staggered_folds"] = run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, args.steps,
                                              args.warmup)
         rec["dual_precision"] = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
+        # the dual-precision window sweep (W = 8, 16, 32; R = W), same inputs
+        rec["dual_precision"]["by_window"] = {
+            w: {k: v for k, v in run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup,
+                                          window=w).items() if k != "workload"}
+            for w in (8, 16, 32)}
         rec["low_precision"] = {
             "bf16_checkpoint": run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup,
                                         mode="bf16_state"),
