@@ -55,5 +55,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi", "rss_c_driver.cpp")
+DRIVER = os.path.join(ROOT, "tests", "c_abi", "rss_c_driver")
+
+
+def build_c_driver(verbose: bool = False) -> str:
+    """Compile the plain C++ test caller of the C ABI (host code only), linked
+    against librss.so with a relative run path, so it finds the in-tree library
+    wherever the repository is copied."""
+    tmp = DRIVER + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-Wall",
+           f"-I{os.path.join(ROOT, 'include')}", DRIVER_SRC, f"-L{PKG}", "-lrss",
+           "-Wl,-rpath,$ORIGIN/../../recurrent_state_storage_amd", "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {DRIVER_SRC}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, DRIVER)
+    if verbose:
+        print(f"built {DRIVER}")
+    return DRIVER
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_driver(verbose=True)
