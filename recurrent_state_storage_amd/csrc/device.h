@@ -207,17 +207,27 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
-// Reverse exclusive scan over the 64 lanes of a wavefront:
-// returns sum_{m > lane} v_m, summed as a fixed tree (deterministic).
+// Reverse exclusive scan over the 64 lanes of a wavefront: returns
+// sum_{m > lane} v_m as a fixed tree, with no LDS traffic: the wavefront shift
+// (lane i takes v_{i+1}, lane 63 takes 0), the inclusive suffix within each
+// 16-lane row by row shifts of 1, 2, 4 and 8 (lanes past the row's end read 0),
+// then the totals of the higher rows, read into scalar registers, added per row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
 __device__ __forceinline__ float wave_suffix_excl(float v, int lane) {
-  float s = __shfl_down(v, 1, 64);
-  if (lane == 63) s = 0.f;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float t = __shfl_down(s, off, 64);
-    if (lane + off < 64) s += t;
-  }
-  return s;
+  float x = dpp_or_zero<0x130>(v);   // wave_shl:1
+  x += dpp_or_zero<0x101>(x);        // row_shl:1
+  x += dpp_or_zero<0x102>(x);        // row_shl:2
+  x += dpp_or_zero<0x104>(x);        // row_shl:4
+  x += dpp_or_zero<0x108>(x);        // row_shl:8
+  const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float t3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  const float s23 = t2 + t3, s123 = t1 + s23;
+  const int row = lane >> 4;
+  return x + (row == 0 ? s123 : row == 1 ? s23 : row == 2 ? t3 : 0.f);
 }
 
 // 16-byte vectors of input elements (8 bf16 or 4 fp32) and their fp32 unpacking
