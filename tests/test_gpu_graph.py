@@ -2,8 +2,10 @@
 (plain replay launches and the fused decode + fold) captured once and replayed
 with fresh inputs copied into the captured buffers, eager work and
 synchronisations between the replays; every replay's outputs, checkpoint and
-pointers equal those of the same calls made without a graph, bit for bit.
-No entry point on these paths issues a memset or a host synchronisation."""
+pointers equal those of the same calls made without a graph, bit for bit; and
+one speculative round (verify with the fold, rollback) captured and replayed
+round after round. No entry point on these paths issues a memset or a host
+synchronisation."""
 import numpy as np
 import pytest
 import torch
@@ -69,4 +71,65 @@ def test_captured_window_replays_match_eager_calls():
         assert torch.equal(cap.ptr, ref.ptr), rep
         assert torch.equal(cap.ring_x, ref.ring_x) and torch.equal(cap.ring_B, ref.ring_B), rep
         _ = torch.ones(1000, device=DEV).sum().item()   # eager work between replays
+    assert cap.device_error() == 0 and ref.device_error() == 0
+
+
+def test_captured_speculative_round_replays_match_eager_calls():
+    """One speculative round (verify K+1 tokens with the committed-window fold,
+    then rollback by a device n_drop array) captured once and replayed for eight
+    rounds with fresh drafts and acceptance counts copied into the captured
+    buffers: outputs, checkpoint, ring and pointers equal the uncaptured calls
+    bit for bit after every round, folds included."""
+    wl = workloads.get("mamba2_spec_b512_h128_p64_n128_w16_k4").replace(
+        name="graph-spec", batch=4, nheads=4, ngroups=4, s0="normal", seed=9200)
+    K, W = wl.draft, wl.window
+    log(f"[graph] capture one speculative round (K={K}, W={W}, R={wl.capacity}), replay 8 rounds")
+    cfg = cfg_of(wl)
+    A = torch.from_numpy(synth.params(wl)["A"]).to(DEV)
+    S0 = torch.from_numpy(synth.initial_state(wl)).to(DEV)
+    ref, cap = rss.ReplayLayer(cfg, A, DEV), rss.ReplayLayer(cfg, A, DEV)
+    ref.init_state(S0)
+    cap.init_state(S0)
+    Bt, H, P = wl.batch, wl.nheads, wl.headdim
+    d = dev_inputs(synth.draft_inputs(wl, 0), "bf16")
+    y = torch.empty((Bt, K + 1, H, P), device=DEV)
+    nd = torch.zeros((Bt,), dtype=torch.int32, device=DEV)
+
+    def round_(layer, inp, out, n_drop):
+        layer.verify_k_tokens_fold(W, K, inp["x"], inp["B"], inp["C"], inp["dt"], out)
+        layer.rollback(n_drop)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        round_(cap, d, y, nd)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    cap.init_state(S0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        round_(cap, d, y, nd)
+    torch.cuda.synchronize()
+    folded = 0
+    for r in range(8):
+        fresh = dev_inputs(synth.draft_inputs(wl, r), "bf16")
+        nd_r = torch.from_numpy((K - synth.accepted_drafts(wl, r)).astype(np.int32)).to(DEV)
+        for k in d:
+            d[k].copy_(fresh[k])
+        nd.copy_(nd_r)
+        g.replay()
+        y_ref = torch.empty_like(y)
+        before = ref.ptr[:, 0, 1].clone()
+        round_(ref, fresh, y_ref, nd_r)
+        torch.cuda.synchronize()
+        folded += int((ref.ptr[:, 0, 1] < before).sum())
+        assert torch.equal(y, y_ref), r
+        assert torch.equal(cap.ckpt, ref.ckpt), r
+        assert torch.equal(cap.ptr, ref.ptr), r
+        assert torch.equal(cap.ring_x, ref.ring_x) and torch.equal(cap.ring_B, ref.ring_B), r
+        assert torch.equal(cap.ring_dl, ref.ring_dl), r
+        _ = torch.ones(1000, device=DEV).sum().item()   # eager work between replays
+    log(f"  sequence folds over the 8 rounds: {folded}")
+    assert folded > 0
     assert cap.device_error() == 0 and ref.device_error() == 0
