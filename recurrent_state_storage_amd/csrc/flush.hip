@@ -136,11 +136,6 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     for (int p = tid >> lgJP; p < P; p += kThreads >> lgJP)
       if (jx < n) sXT[p * RS + jx] = to_f32(xrow(jx)[p]);
   }
-  const int n4 = align4(n);  // zero the padding entries n..n4-1 read by the last group of 4
-  for (int e = tid; e < P * (n4 - n); e += kThreads) {
-    const int p = e / (n4 - n);
-    sXT[p * RS + n + (e - p * (n4 - n))] = 0.f;
-  }
   if (!PCD && wave == 0) {  // c_j = exp(sum_{j<m<n} l_m) dt_j and exp(Lam), tree-summed
     const float u = lane < n ? dl.y : 0.f;
     const float lam = wave_suffix_excl(u, lane);
@@ -169,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     for (int v = 0; v < 4; ++v) Dc[v] = sDc[col * 4 + v];
   }
 
-  // 3. S <- D S + sum_j x_j outer (c_j B_j), four entries per step, in place.
+  // 3. S <- D S + sum_j x_j outer (c_j B_j), j ascending, in place.
   for (int base = 0; base < P; base += RPP * kMaxPass) {
     if (base > 0) load_chunk(base);
 #pragma unroll
@@ -179,33 +174,23 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
       fr[k].v.z *= Dc[2];
       fr[k].v.w *= Dc[3];
     }
-    for (int j4 = 0; j4 < n; j4 += 4) {
-      float4 bv[4];
+    // Rows past P read a valid row (results unused): every pass without a branch.
+    const float* xr[kMaxPass];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        if (j4 + jj < n) {
-          const float cj = sCF[j4 + jj];
-          const float4 t = *reinterpret_cast<const float4*>(&sB[(j4 + jj) * N + col * 4]);
-          bv[jj] = make_float4(cj * t.x, cj * t.y, cj * t.z, cj * t.w);
-        } else {
-          bv[jj] = float4{};
-        }
-      }
+    for (int k = 0; k < kMaxPass; ++k) {
+      const int row = base + k * RPP + rsub;
+      xr[k] = sXT + (row < P ? row : P - 1) * RS;
+    }
+    for (int j = 0; j < n; ++j) {
+      const float cj = sCF[j];
+      const float4 t = *reinterpret_cast<const float4*>(&sB[j * N + col * 4]);
+      const float b0 = cj * t.x, b1 = cj * t.y, b2 = cj * t.z, b3 = cj * t.w;
 #pragma unroll
       for (int k = 0; k < kMaxPass; ++k) {
-        const int r0 = base + k * RPP;
-        if (r0 >= P) break;
-        const int row = r0 + rsub < P ? r0 + rsub : P - 1;   // rows past P: any valid row, result unused
-        const float4 xv = *reinterpret_cast<const float4*>(&sXT[row * RS + j4]);
+        const float xv = xr[k][j];
         float4& s = fr[k].v;
-        s.x = fmaf(xv.x, bv[0].x, s.x); s.y = fmaf(xv.x, bv[0].y, s.y);
-        s.z = fmaf(xv.x, bv[0].z, s.z); s.w = fmaf(xv.x, bv[0].w, s.w);
-        s.x = fmaf(xv.y, bv[1].x, s.x); s.y = fmaf(xv.y, bv[1].y, s.y);
-        s.z = fmaf(xv.y, bv[1].z, s.z); s.w = fmaf(xv.y, bv[1].w, s.w);
-        s.x = fmaf(xv.z, bv[2].x, s.x); s.y = fmaf(xv.z, bv[2].y, s.y);
-        s.z = fmaf(xv.z, bv[2].z, s.z); s.w = fmaf(xv.z, bv[2].w, s.w);
-        s.x = fmaf(xv.w, bv[3].x, s.x); s.y = fmaf(xv.w, bv[3].y, s.y);
-        s.z = fmaf(xv.w, bv[3].z, s.z); s.w = fmaf(xv.w, bv[3].w, s.w);
+        s.x = fmaf(xv, b0, s.x); s.y = fmaf(xv, b1, s.y);
+        s.z = fmaf(xv, b2, s.z); s.w = fmaf(xv, b3, s.w);
       }
     }
 #pragma unroll

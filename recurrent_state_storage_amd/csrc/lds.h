@@ -33,8 +33,8 @@ struct ReplayLds {
 };
 
 // Dynamic LDS layout of the flush kernel, in floats. x is stored transposed
-// (row p holds entries j = 0..R-1 contiguously, padded to a multiple of 4) so
-// that one 16-byte read gives a row's x for four consecutive entries.
+// (row p holds entries j = 0..R-1 contiguously, rows padded to a multiple of 4
+// words), so the window's x values of one row sit together.
 struct FlushLds {
   int RS, oXT, oB, oCF, oG, oDc, total;
   __host__ __device__ FlushLds(int R, int P, int N, bool pcd) {
