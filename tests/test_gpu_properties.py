@@ -1,7 +1,8 @@
 """Property tests on random shapes (hypothesis) and checkpoint/resume.
 
-Random layer shapes within the documented limits, dtypes, read-copy mode,
-window, capacity and draft length: plain decode with the fused fold, a verify
+Random layer shapes within the documented limits, dtypes, checkpoint precision
+(fp32, dual, bf16-only), window, capacity and draft length: plain decode with
+the fused fold, a verify
 round with rollback, more decode — every output against the fp64 eager
 recurrence over the committed stream. Resume: the decode state is exactly the
 checkpoint (+ read copy), the ring and the pointers; copying them out to the
@@ -32,7 +33,7 @@ def layer_shapes(draw):
     K = draw(st.integers(0, 4))
     R = W + K + draw(st.integers(0, 3))
     idt = draw(st.sampled_from(["f32", "bf16"]))
-    copy = draw(st.sampled_from(["none", "bf16"]))
+    copy = draw(st.sampled_from(["none", "bf16", "bf16_state"]))
     Bt = draw(st.integers(1, 3))
     seed = draw(st.integers(0, 10**6))
     fold_verify = draw(st.booleans())
