@@ -43,7 +43,7 @@ def layer_shapes(draw):
                 max_draft=K, draft=K, in_dtype=idt, read_copy=copy, seed=seed), fold_verify
 
 
-@settings(max_examples=30, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 @given(layer_shapes())
 def test_random_layers_match_oracle(shape):
     shape, fold_verify = shape
@@ -99,6 +99,66 @@ def test_random_layers_match_oracle(shape):
     assert L.device_error() == 0
     err = rel_l2(np.concatenate(ys), np.concatenate(refs))
     assert err < tol, err
+
+
+@st.composite
+def delta_shapes(draw):
+    N = draw(st.sampled_from([16, 32, 64, 128, 256]))
+    P = draw(st.integers(1, 256))
+    H = draw(st.integers(1, 3))
+    W = draw(st.integers(1, 12))
+    R = W + draw(st.integers(0, 3))
+    return dict(batch=draw(st.integers(1, 3)), headdim=P, dstate=N, nheads=H, ngroups=H, window=W,
+                capacity=R, seed=draw(st.integers(0, 10**6))), draw(st.sampled_from(["gdn", "kda"])), \
+        draw(st.booleans())
+
+
+@settings(max_examples=40, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(delta_shapes())
+def test_random_delta_rule_layers_match_oracle(shape):
+    """Gated DeltaNet and Kimi Delta Attention layers of random shapes (d_v = P
+    up to 256, d_k = N, windows and capacities within the limits), decoded with
+    the fused fold or with decode + flush: every output and the checkpoint after
+    every fold against the fp64 delta rule."""
+    from oracle import gdn, kda
+    from oracle.ring import PointerModel
+    shape, kind, fused = shape
+    base = workloads.get("gdn_b256_h32_d128_w16" if kind == "gdn" else "kda_b256_h32_d128_w16")
+    wl = base.replace(name="prop-delta", s0="normal", **shape)
+    log(f"[prop] {kind} {shape} fused={fused}")
+    orc = gdn if kind == "gdn" else kda
+    gen = synth.gdn_step_inputs if kind == "gdn" else synth.kda_step_inputs
+    cfg = cfg_of(wl)
+    L = rss.ReplayLayer(cfg, None, DEV)
+    S0 = synth.initial_state(wl)
+    L.init_state(torch.from_numpy(S0).to(DEV))
+    S = S0.astype(np.float64)
+    pm = PointerModel(wl.batch, wl.capacity)
+    dec = L.kda_decode_step if kind == "kda" else L.gdn_decode_step
+    dec_fold = L.kda_decode_flush_step if kind == "kda" else L.gdn_decode_flush_step
+    ys, refs, worst_ck = [], [], 0.0
+    for t in range(2 * wl.window + 3):
+        s = gen(wl, t)
+        d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in s.items()}
+        o = torch.empty((wl.batch, wl.nheads, wl.headdim), device=DEV)
+        if fused:
+            dec_fold(wl.window, d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
+        else:
+            dec(d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
+            L.flush_checkpoint(wl.window)
+        S, o_ref = orc.eager_step(S, s["q"], s["k"], s["v"], s["beta"], s["alpha"])
+        ys.append(o.double().cpu().numpy())
+        refs.append(o_ref)
+        folded = False
+        for b in range(wl.batch):
+            pm.append(b, 1)
+            folded |= pm.flush(b, wl.window)
+        if folded:
+            worst_ck = max(worst_ck, rel_l2(L.ckpt.double().cpu().numpy(), S))
+    assert L.device_error() == 0
+    assert np.array_equal(L.ptr[:, 0, :3].cpu().numpy(), pm.as_array())
+    err = rel_l2(np.stack(ys), np.stack(refs))
+    assert err < 1e-5 and worst_ck < 1e-5, (err, worst_ck)
 
 
 def test_checkpoint_resume_is_bit_exact():
