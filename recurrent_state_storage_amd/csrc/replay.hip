@@ -56,7 +56,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   constexpr int VE = V16<Tin>::VE;
   constexpr int NV = N / VE;                                   // 16-byte vectors per B or C row
   constexpr int kStageC = (NTMAX * NV + NT - 1) / NT;
-  constexpr int EPL = N >= 64 ? N / 64 : 1;                    // B elements per lane in a dot
+  constexpr int EPL = N >= 64 ? N / 64 : 1;                    // B elements per lane in a 64-lane dot
   using TileT = typename std::conditional<LOW, bf16_t, float>::type;
   using VT = typename V16<Tin>::T;
 
@@ -280,34 +280,66 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
     }
   }
 
-  // 3. Wavefront w takes the window entries j = w (mod 4) of every output i:
-  // w_ij = coef_ij (B_j . C_i), and its share of sum_j w_ij x_j, row p on lane p mod 64.
-  // Rows are visited in blocks of 64 up to P only (a uniform bound), so short
-  // heads spend no instructions on the rows they do not have.
+  // 3. w_ij = coef_ij (B_j . C_i) for every output i and window entry j <= t_i,
+  // and each wavefront's share of sum_j w_ij x_j (wavefront w takes j = w mod
+  // the number of wavefronts; row p on lane p mod 64). Rows are visited in
+  // blocks of 64 up to P only (a uniform bound), so short heads spend no
+  // instructions on the rows they do not have.
   constexpr int kRowsPerLane = kMaxP / 64;
   const int nrb = (P + 63) >> 6;
-  for (int i = 0; i < nt; ++i) {
-    const int ti = n0 + i;
-    float share[kRowsPerLane] = {};
-    for (int j = wave; j <= ti; j += NW) {
+  auto ring_shares = [&](auto&& weight) {
+    for (int i = 0; i < nt; ++i) {
+      const int ti = n0 + i;
+      float share[kRowsPerLane] = {};
+      for (int j = wave; j <= ti; j += NW) {
+        const float w = weight(i, j);
+#pragma unroll
+        for (int r = 0; r < kRowsPerLane; ++r) {
+          if (r >= nrb) break;
+          if (r * 64 + lane < P) share[r] = fmaf(w, to_f32(sX[j * P + r * 64 + lane]), share[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRowsPerLane; ++r) {
+        if (r >= nrb) break;
+        if (r * 64 + lane < P) sRing[(wave * NTMAX + i) * P + r * 64 + lane] = share[r];
+      }
+    }
+  };
+  if (NTMAX == 1 || nt == 1) {
+    // One output: its wavefront computes each dot over 64 lanes (wave_sum), in
+    // the loop that accumulates the shares.
+    ring_shares([&](int i, int j) {
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int n = lane * EPL + e;
         if (n < N) part = fmaf(to_f32(sB[j * N + n]), sC[i * N + n], part);
       }
-      const float w = sCF[i * RL + j] * wave_sum(part);
+      return sCF[i * RL + j] * wave_sum(part);
+    });
+  } else {
+    // Several outputs: all (i, j) dots first, one 16-lane group per pair (16
+    // pairs in flight per workgroup pass, each lane a contiguous slice of N,
+    // a 4-step butterfly inside the group); the group's first lane overwrites
+    // coef_ij with w_ij. Then the shares read w_ij back.
+    constexpr int GL = 16, EPG = N / GL;
+    const int gl = tid & (GL - 1);
+    const int npairs = nt * n0 + nt * (nt + 1) / 2;
+    for (int q = tid / GL; q < npairs; q += NT / GL) {
+      int i = 0, j = q;
+      while (j > n0 + i) { j -= n0 + i + 1; ++i; }
+      float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < kRowsPerLane; ++r) {
-        if (r >= nrb) break;
-        if (r * 64 + lane < P) share[r] = fmaf(w, to_f32(sX[j * P + r * 64 + lane]), share[r]);
+      for (int e = 0; e < EPG; ++e) {
+        const int n = gl * EPG + e;
+        part = fmaf(to_f32(sB[j * N + n]), sC[i * N + n], part);
       }
+      part = lanes_sum<4>(part);
+      if (gl == 0) sCF[i * RL + j] *= part;
     }
-#pragma unroll
-    for (int r = 0; r < kRowsPerLane; ++r) {
-      if (r >= nrb) break;
-      if (r * 64 + lane < P) sRing[(wave * NTMAX + i) * P + r * 64 + lane] = share[r];
-    }
+    __syncthreads();
+    ring_shares([&](int i, int j) { return sCF[i * RL + j]; });
   }
   if constexpr (FOLD && LOW) {
     if (do_fold) {  // the fold's operands widened once: x transposed, and c_j B_j
