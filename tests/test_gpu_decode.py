@@ -190,6 +190,61 @@ def test_deterministic():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+def test_explicit_streams():
+    """Every call enqueues on the stream it is given: two layers driven on two
+    side streams (passed explicitly, default priority), their inputs produced on
+    the default stream and handed over with events, equal one layer driven on the
+    default stream, bit for bit."""
+    wl = TINY.replace(name="streams", batch=3, headdim=64, dstate=128, nheads=4, ngroups=4,
+                      window=8, capacity=12, max_draft=4, draft=4, in_dtype="bf16", s0="normal",
+                      seed=3003)
+    cfg = cfg_of(wl)
+    A = torch.from_numpy(synth.params(wl)["A"]).to(DEV)
+    S0 = torch.from_numpy(synth.initial_state(wl)).to(DEV)
+    ref, a, b = (rss.ReplayLayer(cfg, A, DEV) for _ in range(3))
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ref.init_state(S0)
+    torch.cuda.synchronize()
+    a.init_state(S0, stream=sa)
+    b.init_state(S0, stream=sb)
+    K = wl.draft
+    outs = {0: [], 1: [], 2: []}
+    keep = []      # inputs stay referenced until the side streams are done with them
+    for t in range(20):
+        ready = torch.cuda.Event()
+        if t % 6 == 5:
+            rin = dev_inputs(synth.draft_inputs(wl, t), "bf16")
+            nd = torch.from_numpy((K - synth.accepted_drafts(wl, t)).astype(np.int32)).to(DEV)
+            keep.append((rin, nd))
+            ready.record()
+            for idx, (L, s) in enumerate(((ref, None), (a, sa), (b, sb))):
+                y = torch.empty((wl.batch, K + 1, wl.nheads, wl.headdim), device=DEV)
+                if s is not None:
+                    s.wait_event(ready)
+                L.verify_k_tokens_fold(wl.window, K, rin["x"], rin["B"], rin["C"], rin["dt"], y, stream=s)
+                L.rollback(nd, stream=s)
+                outs[idx].append(y)
+        else:
+            d = dev_inputs(synth.step_inputs(wl, t), "bf16")
+            keep.append(d)
+            ready.record()
+            for idx, (L, s) in enumerate(((ref, None), (a, sa), (b, sb))):
+                y = torch.empty((wl.batch, wl.nheads, wl.headdim), device=DEV)
+                if s is not None:
+                    s.wait_event(ready)
+                L.decode_flush_step(wl.window, d["x"], d["B"], d["C"], d["dt"], y, stream=s)
+                outs[idx].append(y)
+    torch.cuda.synchronize()
+    for idx in (1, 2):
+        for y0, y1 in zip(outs[0], outs[idx]):
+            assert torch.equal(y0, y1)
+    for L in (a, b):
+        assert torch.equal(L.ckpt, ref.ckpt) and torch.equal(L.ptr, ref.ptr)
+        assert torch.equal(L.ring_x, ref.ring_x) and torch.equal(L.ring_B, ref.ring_B)
+        assert L.device_error(stream=sa) == 0
+    assert ref.device_error() == 0
+
+
 @pytest.mark.parametrize("copy", ["none", "bf16", "bf16_state"])
 def test_empty_batch_every_entry_point(copy):
     """Zero sequences: every Mamba-2 entry point (init, decode, the fused and
