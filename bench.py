@@ -88,9 +88,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
-    """HBM bytes per replay launch from the committed rocprofv3 counter summary,
-    or None when the summary is absent or the kernel changed since."""
+def counter_traffic(key: str = "replay"):
+    """HBM bytes per launch of the replay decode kernel ("replay"), the fused
+    decode + fold ("fused") or the eager step ("eager") from the committed
+    rocprofv3 counter summary, or None when the summary is absent, lacks the
+    figure, or the replay kernel's code changed since."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     vals = {}
@@ -102,7 +104,7 @@ def counter_traffic():
     if vals.get("kernel_source_hash") != kernel_source_hash():
         return None
     try:
-        return float(vals["replay_hbm_bytes_per_launch"])
+        return float(vals[f"{key}_hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -701,6 +703,11 @@ def main() -> int:
         tot_replay = (sum(replay_bytes(wl, n) for n in range(W)) / W + flush_bytes(wl, W) / W) * H
     st_replay = P * N * 4 * H + (P * N * 4 * H / W if fused else 2 * P * N * 4 * H / W)
     traffic = counter_traffic()
+    # Measured bytes per token over one window (W - 1 replay launches and the
+    # fused one) against the eager launch, both from the HBM counters.
+    c_fused, c_eager = counter_traffic("fused"), counter_traffic("eager")
+    meas_replay = ((W - 1) * traffic + c_fused) / W / Bt if traffic and c_fused and fused else None
+    meas_eager = c_eager / Bt if c_eager else None
     rec = {
         "metric": METRIC,
         "value": tok_s,
@@ -737,7 +744,11 @@ def main() -> int:
                             "eager_total": eager_bytes(wl) * H,
                             "total_ratio": tot_replay / (eager_bytes(wl) * H),
                             "replay_decode_launch_analytic": rep_bytes / n_rep / Bt,
-                            "replay_decode_launch_counters": traffic / Bt if traffic else None},
+                            "replay_decode_launch_counters": traffic / Bt if traffic else None,
+                            "replay_window_counters": meas_replay,
+                            "eager_counters": meas_eager,
+                            "total_ratio_counters": (meas_replay / meas_eager
+                                                     if meas_replay and meas_eager else None)},
         "input_generation_s": gen_s,
     }
     if out_eager:
