@@ -239,8 +239,8 @@ int32_t rss_flush_checkpoint_each(rss_layer* layer, const int32_t* min_len, void
 /* Speculative verify of K+1 tokens per sequence (the last sampled token and K
  * drafts; 0 <= K <= K_max): append all K+1 as tentative entries (n_tent =
  * K+1) and write the K+1 outputs, output i being the decode output of token i
- * over the committed window plus tokens 0..i (P3, "Почему это важно": drafts
- * are added to the buffer). One pass over S_c serves all K+1 outputs.
+ * over the committed window plus tokens 0..i (P3, "Почему это важно для
+ * индустрии": drafts are added to the buffer). One pass over S_c serves all K+1 outputs.
  * Layouts: x [Bt,K+1,H,P], B and C [Bt,K+1,G,N], dt [Bt,K+1,H], y
  * [Bt,K+1,H,P]. Device error RSS_DEV_RING_OVERFLOW if len + K + 1 > R.
  * RSS_E_ORDER if a previous round is still uncommitted. */
@@ -255,11 +255,12 @@ int32_t rss_verify_k_tokens(rss_layer* layer, int32_t K, const void* x, const vo
  * the two separate calls' bit for bit; the outputs are computed from the
  * unfolded checkpoint and the whole window, equal up to rounding. A speculative
  * loop of this call and rss_rollback needs no separate flush: a window the
- * accepted drafts fill is folded by the next round (R >= W + K_max still
+ * accepted drafts fill is folded by the next round. R >= W + K_max still
  * bounds the ring between rounds, where a window may hold up to W + K entries,
- * so call rss_flush_checkpoint(W) before returning to plain decode; during the call a folding sequence stages up
- * to R + K + 1 positions, the committed ones read before their slots are
- * reused). With read_copy = BF16 or RSS_STATE_BF16 the fold runs as a separate
+ * so call rss_flush_checkpoint(W) before returning to plain decode. During the
+ * call a folding sequence stages up to R + K + 1 positions, the committed ones
+ * read before their slots are reused. With read_copy = BF16 or RSS_STATE_BF16
+ * the fold runs as a separate
  * flush launch first. Errors as rss_verify_k_tokens and rss_flush_checkpoint,
  * plus RSS_E_CAPACITY if R + K + 1 > 64, or if G < H and R < min_len + 2K + 1
  * (heads of a group share B rows, so no slot is reused within the call: a
@@ -351,8 +352,8 @@ int32_t rss_eager_step(const rss_config* cfg, void* S, const void* x, const void
                        int32_t T, void* stream);
 
 /* Eager speculative baseline with per-token state snapshots, the rollback
- * scheme ReplaySSM removes (P3, "Почему это важно"; P4, "Co się zmieniło?",
- * item 4): pool fp32 [Bt, K+1, H, P, N]. Sequence b starts from slot
+ * scheme ReplaySSM removes (P3, "Почему это важно для индустрии"; P4, "Co się
+ * zmieniło?", item 4): pool fp32 [Bt, K+1, H, P, N]. Sequence b starts from slot
  * src_slot[b] (device int32 [Bt], 0 <= src_slot[b] <= K), runs K+1 eager
  * tokens and writes the state after token i to slot i (the read completes
  * before any write, so src_slot may be any slot). Rolling back to n_acc

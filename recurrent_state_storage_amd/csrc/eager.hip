@@ -8,9 +8,9 @@
 //   a = exp(dt A_h);  S <- a S + dt outer(x, B);  y = S @ C
 //
 // In-place mode runs T tokens on S. Snapshot mode is the pre-ReplaySSM
-// speculative rollback scheme (P3, "Почему это важно": rollback needed state
-// snapshots; P4, "Co się zmieniło?", item 4): the state is read from pool slot
-// src_slot[b], and the state after token i is written to slot i.
+// speculative rollback scheme (P3, "Почему это важно для индустрии": rollback
+// needed state snapshots; P4, "Co się zmieniło?", item 4): the state is read
+// from pool slot src_slot[b], and the state after token i is written to slot i.
 //
 // A bf16-stored state (the quantised eager state of P1, "Trois ennuis nés de
 // la même fusion": rewritten, hence rounded, at every call) is widened to fp32
