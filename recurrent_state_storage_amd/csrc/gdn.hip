@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = a.H, P = a.P, R = a.R;
+  const int P = a.P, R = a.R;
   const int bh = blockIdx.x;
 
   float* tile = a.ckpt + (size_t)bh * P * N;
