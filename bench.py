@@ -297,6 +297,46 @@ def run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
             "step_us_max": float(d.max()), "step_us_min": float(d.min())}
 
 
+def run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, groups=1):
+    """The benchmark workload with B and C shared by groups of heads (G = 1: one
+    B, C row per sequence, as in Mamba-2 models with a single group): the same x
+    and dt, B and C taken from the first group of the same inputs. The ring's B
+    rows shrink by H/G, so fewer bytes per token; replay + fused fold schedule,
+    and the eager kernel on the same inputs."""
+    wl = workloads.get(WORKLOAD)
+    Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
+    B1 = Bm[:, :, :groups, :].contiguous()
+    C1 = Cm[:, :, :groups, :].contiguous()
+    cfg = rss.make_config(Bt, H, P, N, groups, W, wl.capacity, 0, rss.RSS_DTYPE_BF16,
+                          rss.RSS_COPY_NONE)
+    layer = rss.ReplayLayer(cfg, A, dev)
+    layer.init_state()
+    y = torch.empty((Bt, H, P), device=dev)
+    T = X.shape[0]
+
+    def step(k):
+        i = k % T
+        if (k + 1) % W == 0:
+            layer.decode_flush_step(W, X[i], B1[i], C1[i], DT[i], y)
+        else:
+            layer.decode_step(X[i], B1[i], C1[i], DT[i], y)
+    for k in range(warmup):
+        step(k)
+    ms = _timed(torch, lambda j: step(warmup + j), steps)
+    S = torch.zeros((Bt, H, P, N), device=dev)
+    ye = torch.empty_like(y)
+
+    def eager(k):
+        i = k % T
+        rss.rss_eager_step(cfg, S, X[i], B1[i], C1[i], DT[i], A, ye)
+    for k in range(warmup):
+        eager(k)
+    ms_e = _timed(torch, lambda j: eager(warmup + j), steps)
+    assert layer.device_error() == 0
+    return {"groups": groups, "tokens_per_s": Bt * steps / (ms / 1e3),
+            "eager_tokens_per_s": Bt * steps / (ms_e / 1e3), "speedup": ms_e / ms}
+
+
 def run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
     """Eager decode with the state stored in bf16 (rounded every token): the
     low-precision eager point of comparison, same inputs and shape."""
@@ -756,6 +796,7 @@ def main() -> int:
     if not args.no_extra:
         rec["staggered_folds"] = run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, args.steps,
                                              args.warmup)
+        rec["grouped_bc"] = run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
         rec["dual_precision"] = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
         # the dual-precision window sweep (W = 8, 16, 32; R = W), same inputs
         rec["dual_precision"]["by_window"] = {

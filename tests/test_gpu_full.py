@@ -20,11 +20,14 @@ from gpu_util import DEV, PairGather, cfg_of, dev_inputs, rel_l2, sample_pairs, 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-@pytest.mark.parametrize("schedule", ["separate", "fused", "staggered"])
+@pytest.mark.parametrize("schedule", ["separate", "fused", "staggered", "fused-G1"])
 def test_decode_b256_full_size(schedule):
     """The benchmark workload in each fold schedule the benchmark times: decode +
-    flush every W steps, the fused decode + fold, and staggered per-sequence folds."""
+    flush every W steps, the fused decode + fold, and staggered per-sequence folds;
+    and the fused schedule with B and C shared by all heads (G = 1)."""
     wl = workloads.get("mamba2_b256_h128_p64_n128_w16")
+    if schedule == "fused-G1":
+        wl, schedule = wl.replace(ngroups=1), "fused"
     log(f"[full] {wl.name}: {wl.steps} steps, {schedule} folds every {wl.window}")
     cfg = cfg_of(wl)
     A_np = synth.params(wl)["A"]
