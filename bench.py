@@ -716,7 +716,30 @@ def main() -> int:
             "kernel_GBps": eager_bytes(wl) * Bt * H * args.steps / (eag_ms / 1e3) / 1e9,
             "bytes_per_token": eager_bytes(wl) * H,
         }
-        del S
+        # Parity of the timed path on the whole batch: a fresh replay layer (the
+        # benchmark's schedule) and a fresh eager state run 2W steps side by side.
+        S.zero_()
+        chk = rss.ReplayLayer(cfg, A, dev)
+        chk.init_state()
+        num = den = 0.0
+        worst = 0.0
+        for k in range(2 * W):
+            i = k % T
+            if (k + 1) % W == 0 and fused:
+                chk.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)
+            else:
+                chk.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
+                if (k + 1) % W == 0:
+                    chk.flush_checkpoint(W)
+            rss.rss_eager_step(cfg, S, X[i], Bm[i], Cm[i], DT[i], A, ye)
+            d2 = float(torch.sum((y - ye).double() ** 2))
+            r2 = float(torch.sum(ye.double() ** 2))
+            num, den = num + d2, den + r2
+            worst = max(worst, (d2 / r2) ** 0.5)
+        assert chk.device_error() == 0
+        out_eager["parity_replay_vs_eager"] = {"steps": 2 * W, "run_rel_l2": (num / den) ** 0.5,
+                                               "worst_step_rel_l2": worst}
+        del S, chk
 
     # Context: a plain device copy, 1 GiB read + 1 GiB written (torch's vectorised
     # elementwise kernel multiplying by 1, the faster of torch's copy paths here).
