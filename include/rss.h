@@ -200,9 +200,13 @@ int32_t rss_decode_step(rss_layer* layer, const void* x, const void* B, const vo
  * new checkpoint is written, so the flush's second read of the tile is saved
  * (the fold writes the state only once per window, P1 "Tenir le journal plutôt
  * que le solde"). Results equal the two separate calls bit for bit. A
- * bf16-stored checkpoint (RSS_STATE_BF16) is folded in the same pass too. With
- * read_copy = BF16 the replay reads the bf16 copy while the fold needs the fp32
- * master, so the fold runs as the separate flush launch. min_len >= 1; errors as
+ * bf16-stored checkpoint (RSS_STATE_BF16) is folded in the same pass too,
+ * unless its fold operands, widened to fp32 in LDS, would not fit the budget
+ * (P = N = 256 with a long window): then, as always with read_copy = BF16
+ * (the replay reads the bf16 copy while the fold needs the fp32 master), the
+ * fold runs as the separate flush launch, with the same results. On steps
+ * where no sequence folds the call costs what rss_decode_step does, so a
+ * caller may simply use it for every token. min_len >= 1; errors as
  * rss_decode_step, plus RSS_DEV_UNCOMMITTED if a window to fold still holds
  * tentative entries (that sequence is then not folded). */
 int32_t rss_decode_flush_step(rss_layer* layer, int32_t min_len, const void* x, const void* B,
