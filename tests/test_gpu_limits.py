@@ -20,7 +20,11 @@ BASE = workloads.get("tiny_b2_h4_p16_n16_w8")
 
 
 @pytest.mark.parametrize("in_dtype,copy,R", [("bf16", "none", 64), ("f32", "none", 58),
-                                              ("bf16", "bf16", 64)])
+                                              ("bf16", "bf16", 64),
+                                              # bf16-stored checkpoint: the fold inside the decode
+                                              # (R = 16), and the separate fold its LDS budget
+                                              # forces at R = 64
+                                              ("bf16", "bf16_state", 16), ("bf16", "bf16_state", 64)])
 def test_mamba2_largest_shape(in_dtype, copy, R):
     K = 7
     W = R - K
