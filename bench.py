@@ -7,14 +7,19 @@ W=16, synthetic seeded inputs (workloads.synth; 256 distinct decode steps
 resident in HBM before timing, cycled when more steps are timed).
 
 A step is one decode token for the whole batch through the replay path: the
-replay decode kernel every step, plus the checkpoint fold every W steps (the
-fold's cost is part of the timed region). The eager-rewrite kernel on the same
-inputs is timed too, so the state-traffic cut is measured.
+replay decode kernel every step, and the checkpoint fold every W steps inside
+the decode that fills the window (the fold's cost is part of the timed region).
+`value` times exactly --steps steps; `steady_state` times whole windows, so
+that it holds exactly one fold per W tokens whatever --steps is.
 
 Output: one JSON line with tokens/s per layer (whole-job throughput, inputs
 already in HBM), the dominant kernel's roofline (algorithmic bytes per launch
-over the HIP-event-measured launch duration, against 8 TB/s), and the fp64 CPU
-oracle timed on a bounded sample on this host's cores.
+over the HIP-event-measured launch duration, against 8 TB/s), the HBM read
+and copy rates this GPU achieves (the library's calibration kernels), the eager
+GPU baseline, the further workloads (staggered folds, dual precision and its
+window sweep, the low-precision comparison, speculative rounds at batch 512,
+Gated DeltaNet, Kimi Delta Attention, a single B/C group), each timed over
+whole windows, and the fp64 CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -40,7 +45,8 @@ WORKLOAD = "mamba2_b256_h128_p64_n128_w16"
 METRIC = "SSM decode tokens/s per layer + achieved HBM GB/s (% of peak), batch 256"
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "replay_decode_b256_hbm_counters.txt")
-KERNEL_SOURCES = ["replay.hip", "device.h", "limits.h", "launch.h", "lds.h"]
+KERNEL_SOURCES = ["replay.hip", "device.h", "limits.h", "launch.h", "lds.h", "fold.h"]
+SWEEP_WINDOWS = (8, 16, 32)
 
 
 # ---- algorithmic bytes (what the method must move, per (sequence, head)) ----
@@ -73,6 +79,38 @@ def fused_bytes(wl) -> int:
 def eager_bytes(wl, state_bytes: int = 4) -> int:
     P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
     return 2 * P * N * state_bytes + P * ib + 2 * N * ib + 4 + P * 4 + 4
+
+
+def verify_bytes(wl, n0: np.ndarray, fold: np.ndarray) -> int:
+    """Verify of K+1 tokens per (sequence, head) with n0[b] committed entries in
+    the window, summed over the batch and the heads; fold[b]: the committed
+    window is folded in the same pass (its tile written back)."""
+    P, N, K = wl.headdim, wl.dstate, wl.draft
+    entry = 2 * P + 2 * N + 8
+    per = (P * N * 4 + n0 * entry + (K + 1) * (2 * P + 4 * N + 4 + 4 * P + entry) + 36
+           + fold.astype(np.int64) * P * N * 4)
+    return int(np.sum(per)) * wl.nheads
+
+
+def gdn_bytes(wl, n0: int) -> dict:
+    """Algorithmic bytes per (sequence, head) of the GDN / KDA kernels (fp32)."""
+    P, N = wl.headdim, wl.dstate
+    if wl.kind == "kda":
+        entry = 8 * N + 4 * P                       # k, u, log-gate row
+        inputs = 4 * N * 3 + 4 * P + 4              # q, k, alpha row, v, beta
+    else:
+        entry = 4 * N + 4 * P + 8                   # k, u, (1, log alpha)
+        inputs = 4 * N * 2 + 4 * P + 8              # q, k, v, beta, alpha
+    replay = P * N * 4 + n0 * entry + inputs + 4 * P + entry + 32
+    return {"replay": replay,
+            "fused": P * N * 4 * 2 + (wl.window - 1) * entry + inputs + 4 * P + entry + 32,
+            "flush": 2 * P * N * 4 + wl.window * entry + 32,
+            "eager": 2 * P * N * 4 + inputs + 4 * P}
+
+
+def whole(steps: int, multiple: int, minimum: int) -> int:
+    """`steps` rounded up to a whole number of windows, at least `minimum`."""
+    return max(minimum, -(-steps // multiple) * multiple)
 
 
 def kernel_source_hash() -> str:
@@ -109,7 +147,7 @@ def counter_traffic(key: str = "replay"):
         return None
 
 
-# ---- inputs -------------------------------------------------------------------
+# ---- inputs (host generators; run before the device is touched) ----------------
 def _gen_step(args):
     name, t = args
     s = synth.step_inputs(workloads.get(name), t)
@@ -182,86 +220,212 @@ def cpu_baseline(wl, pool, budget_s: float, workers: int):
                       f"one core alone: {st1} steps of {nseq} sequences in {el1:.1f} s"}
 
 
-def _timed(torch, fn, n):
-    """Run fn(i) for i < n between two events on the current stream; ms."""
+# ---- timing helpers --------------------------------------------------------------
+def _timed(torch, fn, n, start=0):
+    """Run fn(start + i) for i < n between two events on the current stream; ms."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for i in range(n):
-        fn(i)
+        fn(start + i)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1)
 
 
-def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16", window=16):
-    """Replay with a bf16 tile read, W = window (16 by default), same inputs: dual precision (fp32
-    master + bf16 read copy, mode "bf16"; the fold of the master is a separate
-    flush launch) or a single bf16 checkpoint ("bf16_state"; folded inside the
-    decode that fills the window)."""
-    wl = workloads.get(f"mamba2_dual_b256_h128_p64_n128_w{window}").replace(read_copy=mode)
-    Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
-    code = rss.RSS_COPY_BF16 if mode == "bf16" else rss.RSS_STATE_BF16
-    cfg = rss.make_config(Bt, H, P, N, wl.ngroups, W, wl.capacity, 0, rss.RSS_DTYPE_BF16, code)
+class Launches:
+    """HIP events around individual launches on the current (launch) stream,
+    grouped by a key; durations in microseconds."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def around(self, key, fn):
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.ev.setdefault(key, []).append((a, b))
+
+    def us(self, key):
+        return [a.elapsed_time(b) * 1e3 for a, b in self.ev.get(key, [])]
+
+
+def rate(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9 if us else None
+
+
+# ---- calibration: what HBM delivers ---------------------------------------------
+def run_calibration(torch, rss, dev):
+    """Best of three grid sizes of the library's streaming-read and copy kernels
+    over 1 GiB (16-byte non-temporal accesses, as the decode kernels use), and
+    torch's elementwise copy for comparison."""
+    n = 1 << 28                                        # 1 GiB of fp32
+    src = torch.ones((n,), device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros((4,), device=dev)
+    nbytes = n * 4
+    read = {}
+    for g in (2048, 4096, 8192):
+        rss.rss_calib_read(src, sink, g)
+        ms = _timed(torch, lambda i: rss.rss_calib_read(src, sink, g), 10) / 10
+        read[g] = rate(nbytes, ms * 1e3)
+    copy = {}
+    for g in (4096, 8192, 16384):
+        rss.rss_calib_copy(src, dst, g)
+        ms = _timed(torch, lambda i: rss.rss_calib_copy(src, dst, g), 10) / 10
+        copy[g] = rate(2 * nbytes, ms * 1e3)
+    torch.mul(src, 1.0, out=dst)
+    ms = _timed(torch, lambda i: torch.mul(src, 1.0, out=dst), 10) / 10
+    out = {"read_ceiling_GBps": max(read.values()), "copy_ceiling_GBps": max(copy.values()),
+           "read_by_grid": read, "copy_by_grid": copy, "torch_elementwise_copy_GBps": rate(2 * nbytes, ms * 1e3),
+           "how": "rss_calib_read / rss_calib_copy over 1 GiB, best of grids of 256-thread workgroups"}
+    del src, dst, sink
+    return out
+
+
+def calibrate_counters(torch, rss, dev):
+    """A plain 1 GiB -> 1 GiB copy by the library's copy kernel, run three
+    times: the reference a profiler's HBM byte counters are scaled by."""
+    src = torch.ones((1 << 28,), device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        rss.rss_calib_copy(src, dst, 8192)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+# ---- the benchmark workload ------------------------------------------------------
+def run_main(torch, rss, dev, X, Bm, Cm, DT, A, args):
+    wl = workloads.get(WORKLOAD)
+    Bt, H, P, N, G, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window
+    cfg = rss.make_config(Bt, H, P, N, G, W, wl.capacity, 0, rss.RSS_DTYPE_BF16, rss.RSS_COPY_NONE)
     layer = rss.ReplayLayer(cfg, A, dev)
-    layer.init_state()
     y = torch.empty((Bt, H, P), device=dev)
     T = X.shape[0]
-    fused = mode == "bf16_state"
-    ev = {"r": [], "f": []}
+    fused = not args.separate_flush
 
-    def mark(key):
-        ev[key].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-        ev[key][-1][0].record()
-
-    def step(k, rec=False):
+    def step(k, lt=None):
         i = k % T
         fold = (k + 1) % W == 0
-        key = "f" if fold and fused else "r"
-        if rec:
-            mark(key)
-        if fold and fused:
-            layer.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)
+        if fused and fold:   # this token fills every window: decode and fold in one pass
+            f = lambda: layer.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)  # noqa: E731
+            key = "fused"
         else:
-            layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
-        if rec:
-            ev[key][-1][1].record()
+            f = lambda: layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)  # noqa: E731
+            key = f"replay{k % W}"
+        if lt is None:
+            f()
+        else:
+            lt.around(key, f)
         if fold and not fused:
-            if rec:
-                mark("f")
-            layer.flush_checkpoint(W)
-            if rec:
-                ev["f"][-1][1].record()
-    for k in range(warmup):
+            g = lambda: layer.flush_checkpoint(W)  # noqa: E731
+            if lt is None:
+                g()
+            else:
+                lt.around("flush", g)
+
+    def repeats(nsteps, warm, reps):
+        out = []
+        for _ in range(reps):
+            layer.init_state()
+            for k in range(warm):
+                step(k)
+            out.append(_timed(torch, step, nsteps, start=warm))
+        return out
+
+    # value: exactly --steps steps after --warmup steps, median of the repeats
+    reps_ms = repeats(args.steps, args.warmup, max(1, args.repeats))
+    ms = float(np.median(reps_ms))
+    # steady state: whole windows, starting at a window boundary
+    ss_steps = whole(args.steps, W, 4 * W)
+    ss_warm = whole(args.warmup, W, W)
+    ss_ms = float(np.median(repeats(ss_steps, ss_warm, 3)))
+    # per-launch durations (HIP events on the launch stream), in a further pass
+    lt = Launches(torch)
+    layer.init_state()
+    for k in range(ss_warm):
         step(k)
-    ms = _timed(torch, lambda j: step(warmup + j), steps)
-    base = warmup + steps
-    for j in range(steps):
-        step(base + j, rec=True)
+    for k in range(ss_warm, ss_warm + ss_steps):
+        step(k, lt)
     torch.cuda.synchronize()
-    r_ms = sum(a.elapsed_time(b) for a, b in ev["r"])
-    f_ms = sum(a.elapsed_time(b) for a, b in ev["f"])
-    phases = [(base + j) % W for j in range(steps)]
-    rbytes = sum(replay_bytes(wl, n0) for n0 in phases if not (fused and n0 == W - 1)) * Bt * H
-    per_fold = fused_bytes(wl) if fused else flush_bytes(wl, W)
-    fbytes = per_fold * Bt * H * len(ev["f"])
     assert layer.device_error() == 0
-    return {"workload": wl.name if mode == "bf16" else wl.name + " with a bf16-only checkpoint",
-            "tokens_per_s": Bt * steps / (ms / 1e3),
-            "replay_avg_us": r_ms / max(len(ev["r"]), 1) * 1e3,
-            "replay_GBps": rbytes / (r_ms / 1e3) / 1e9,
-            "fold": "fused into the decode that fills the window" if fused else "separate flush launch",
-            "fold_avg_us": f_ms / max(len(ev["f"]), 1) * 1e3,
-            "fold_GBps": fbytes / (f_ms / 1e3) / 1e9 if f_ms else None}
+    rep_us, rep_bytes = 0.0, 0
+    n_rep = 0
+    for n0 in range(W):
+        d = lt.us(f"replay{n0}")
+        rep_us += sum(d)
+        rep_bytes += len(d) * replay_bytes(wl, n0) * Bt * H
+        n_rep += len(d)
+    fold_key, fold_b = ("fused", fused_bytes(wl)) if fused else ("flush", flush_bytes(wl, W))
+    f_us = lt.us(fold_key)
+    step_us = []
+    kernels = {"replay_decode": {"avg_us": rep_us / n_rep, "GBps": rate(rep_bytes, rep_us),
+                                 "frac_of_peak": rate(rep_bytes, rep_us) / PEAK_HBM_GBS,
+                                 "launches": n_rep, "algorithmic_bytes_per_launch": rep_bytes / n_rep},
+               ("fused_decode_fold" if fused else "flush"): {
+                   "avg_us": float(np.mean(f_us)), "GBps": rate(fold_b * Bt * H * len(f_us), sum(f_us)),
+                   "frac_of_peak": rate(fold_b * Bt * H * len(f_us), sum(f_us)) / PEAK_HBM_GBS,
+                   "launches": len(f_us), "algorithmic_bytes_per_launch": fold_b * Bt * H}}
+    for n0 in range(W):
+        step_us += lt.us(f"replay{n0}")
+    step_us += f_us
+    return {"tokens_per_s": Bt * args.steps / (ms / 1e3), "ms": ms, "reps_ms": reps_ms,
+            "steady": {"tokens_per_s": Bt * ss_steps / (ss_ms / 1e3), "steps": ss_steps,
+                       "folds_timed": ss_steps // W, "ms_per_step": ss_ms / ss_steps},
+            "kernels": kernels, "rep_us": rep_us / n_rep, "rep_gbs": rate(rep_bytes, rep_us),
+            "rep_bytes": rep_bytes / n_rep, "step_us": step_us, "cfg": cfg, "fused": fused}
 
 
-def _gen_round(args):
-    name, r = args
-    wl = workloads.get(name)
-    d = synth.draft_inputs(wl, r)
-    return r, d["x_bits"], d["B_bits"], d["C_bits"], d["dt"], synth.accepted_drafts(wl, r)
+def run_eager(torch, rss, dev, X, Bm, Cm, DT, A, cfg, steps, warmup):
+    wl = workloads.get(WORKLOAD)
+    Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
+    T = X.shape[0]
+    S = torch.zeros((Bt, H, P, N), device=dev)
+    ye = torch.empty((Bt, H, P), device=dev)
+
+    def eager_step(k):
+        i = k % T
+        rss.rss_eager_step(cfg, S, X[i], Bm[i], Cm[i], DT[i], A, ye)
+    for k in range(warmup):
+        eager_step(k)
+    ems = _timed(torch, eager_step, steps, start=warmup)
+    lt = Launches(torch)
+    for k in range(steps):
+        lt.around("e", lambda k=k: eager_step(k))
+    torch.cuda.synchronize()
+    e_us = lt.us("e")
+    out = {"tokens_per_s": Bt * steps / (ems / 1e3), "ms_per_step": ems / steps,
+           "kernel_avg_us": float(np.mean(e_us)),
+           "kernel_GBps": rate(eager_bytes(wl) * Bt * H * len(e_us), sum(e_us)),
+           "bytes_per_token": eager_bytes(wl) * H}
+    # Parity of the timed path on the whole batch: a fresh replay layer (the
+    # benchmark's schedule) and a fresh eager state run 2W steps side by side.
+    S.zero_()
+    y = torch.empty_like(ye)
+    chk = rss.ReplayLayer(cfg, A, dev)
+    chk.init_state()
+    num = den = worst = 0.0
+    for k in range(2 * W):
+        i = k % T
+        if (k + 1) % W == 0:
+            chk.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)
+        else:
+            chk.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
+        rss.rss_eager_step(cfg, S, X[i], Bm[i], Cm[i], DT[i], A, ye)
+        d2 = float(torch.sum((y - ye).double() ** 2))
+        r2 = float(torch.sum(ye.double() ** 2))
+        num, den = num + d2, den + r2
+        worst = max(worst, (d2 / r2) ** 0.5)
+    assert chk.device_error() == 0
+    out["parity_replay_vs_eager"] = {"steps": 2 * W, "run_rel_l2": (num / den) ** 0.5,
+                                     "worst_step_rel_l2": worst}
+    return out
 
 
+# ---- further workloads, each over whole windows -----------------------------------
 def run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
     """The benchmark workload with staggered folds: sequence b's first window is
     1 + (b mod W) tokens long (per-sequence fold thresholds), W after that, so
@@ -281,20 +445,19 @@ def run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
     def step(k):
         i = k % T
         layer.decode_flush_step_each(th[min(k, W)], X[i], Bm[i], Cm[i], DT[i], y)
-    for k in range(max(warmup, W)):
+    k0 = whole(warmup, W, W)
+    for k in range(k0):
         step(k)
-    k0 = max(warmup, W)
-    ms = _timed(torch, lambda j: step(k0 + j), steps)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for j in range(steps):
-        ev[j][0].record()
-        step(k0 + steps + j)
-        ev[j][1].record()
+    ms = _timed(torch, step, steps, start=k0)
+    lt = Launches(torch)
+    for k in range(k0 + steps, k0 + 2 * steps):
+        lt.around("s", lambda k=k: step(k))
     torch.cuda.synchronize()
-    d = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    d = np.array(lt.us("s"))
     assert layer.device_error() == 0
-    return {"tokens_per_s": Bt * steps / (ms / 1e3), "step_us_median": float(np.median(d)),
-            "step_us_max": float(d.max()), "step_us_min": float(d.min())}
+    return {"tokens_per_s": Bt * steps / (ms / 1e3), "steps": steps,
+            "step_us_median": float(np.median(d)), "step_us_max": float(d.max()),
+            "step_us_min": float(d.min())}
 
 
 def run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, groups=1):
@@ -320,21 +483,84 @@ def run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, groups=1):
             layer.decode_flush_step(W, X[i], B1[i], C1[i], DT[i], y)
         else:
             layer.decode_step(X[i], B1[i], C1[i], DT[i], y)
-    for k in range(warmup):
+    k0 = whole(warmup, W, W)
+    for k in range(k0):
         step(k)
-    ms = _timed(torch, lambda j: step(warmup + j), steps)
+    ms = _timed(torch, step, steps, start=k0)
     S = torch.zeros((Bt, H, P, N), device=dev)
     ye = torch.empty_like(y)
 
     def eager(k):
         i = k % T
         rss.rss_eager_step(cfg, S, X[i], B1[i], C1[i], DT[i], A, ye)
-    for k in range(warmup):
+    for k in range(k0):
         eager(k)
-    ms_e = _timed(torch, lambda j: eager(warmup + j), steps)
+    ms_e = _timed(torch, eager, steps, start=k0)
     assert layer.device_error() == 0
-    return {"groups": groups, "tokens_per_s": Bt * steps / (ms / 1e3),
+    return {"groups": groups, "steps": steps, "tokens_per_s": Bt * steps / (ms / 1e3),
             "eager_tokens_per_s": Bt * steps / (ms_e / 1e3), "speedup": ms_e / ms}
+
+
+def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16", window=16):
+    """Replay with a bf16 tile read, W = window, same inputs: dual precision
+    (fp32 master + bf16 read copy, mode "bf16"; the fold of the master is a
+    separate flush launch) or a single bf16 checkpoint ("bf16_state"; folded
+    inside the decode that fills the window). `steps` is a whole number of
+    windows, and the timed region starts at a window boundary."""
+    wl = workloads.get(f"mamba2_dual_b256_h128_p64_n128_w{window}").replace(read_copy=mode)
+    Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
+    assert steps % W == 0
+    code = rss.RSS_COPY_BF16 if mode == "bf16" else rss.RSS_STATE_BF16
+    cfg = rss.make_config(Bt, H, P, N, wl.ngroups, W, wl.capacity, 0, rss.RSS_DTYPE_BF16, code)
+    layer = rss.ReplayLayer(cfg, A, dev)
+    layer.init_state()
+    y = torch.empty((Bt, H, P), device=dev)
+    T = X.shape[0]
+    fused = mode == "bf16_state"
+
+    def step(k, lt=None):
+        i = k % T
+        fold = (k + 1) % W == 0
+        if fold and fused:
+            f, key = (lambda: layer.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)), "f"  # noqa: E731
+        else:
+            f, key = (lambda: layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)), f"r{k % W}"  # noqa: E731
+        if lt is None:
+            f()
+        else:
+            lt.around(key, f)
+        if fold and not fused:
+            g = lambda: layer.flush_checkpoint(W)  # noqa: E731
+            if lt is None:
+                g()
+            else:
+                lt.around("f", g)
+    k0 = whole(warmup, W, W)
+    for k in range(k0):
+        step(k)
+    ms = _timed(torch, step, steps, start=k0)
+    lt = Launches(torch)
+    for k in range(k0 + steps, k0 + 2 * steps):
+        step(k, lt)
+    torch.cuda.synchronize()
+    r_us = r_b = 0
+    n_r = 0
+    for n0 in range(W):
+        d = lt.us(f"r{n0}")
+        r_us += sum(d)
+        r_b += len(d) * replay_bytes(wl, n0) * Bt * H
+        n_r += len(d)
+    f_us = lt.us("f")
+    per_fold = fused_bytes(wl) if fused else flush_bytes(wl, W)
+    assert layer.device_error() == 0
+    return {"workload": wl.name if mode == "bf16" else wl.name + " with a bf16-only checkpoint",
+            "steps": steps, "folds_timed": steps // W,
+            "tokens_per_s": Bt * steps / (ms / 1e3),
+            "replay_avg_us": r_us / n_r, "replay_GBps": rate(r_b, r_us),
+            "fold": "fused into the decode that fills the window" if fused else "separate flush launch",
+            "fold_avg_us": float(np.mean(f_us)),
+            "fold_GBps": rate(per_fold * Bt * H * len(f_us), sum(f_us)),
+            "fold_frac_of_peak": rate(per_fold * Bt * H * len(f_us), sum(f_us)) / PEAK_HBM_GBS}
 
 
 def run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
@@ -353,215 +579,201 @@ def run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
         rss.rss_eager_step(cfg, S, X[i], Bm[i], Cm[i], DT[i], A, y)
     for k in range(warmup):
         step(k)
-    ms = _timed(torch, lambda j: step(warmup + j), steps)
+    ms = _timed(torch, step, steps, start=warmup)
     return {"tokens_per_s": Bt * steps / (ms / 1e3), "kernel_avg_us": ms / steps * 1e3,
             "kernel_GBps": eager_bytes(wl, 2) * Bt * H * steps / (ms / 1e3) / 1e9,
             "bytes_per_token": eager_bytes(wl, 2) * H}
 
 
-def run_spec(torch, rss, dev, rounds, warmup, workers, distinct=6):
-    """Speculative rounds at batch 512, K = 4: replay verify + rollback + flush,
-    against the eager kernel with a state snapshot per draft token."""
+def run_spec(torch, rss, dev, warmup=8):
+    """Speculative rounds at batch 512, K = 4, over the workload's 200 rounds,
+    each with its own draft inputs (drawn on the device) and accepted lengths:
+    verify with the committed window's fold in the same pass + rollback, the
+    same with a separate flush launch, and the eager kernel with a state
+    snapshot per draft token."""
     wl = workloads.get("mamba2_spec_b512_h128_p64_n128_w16_k4")
     Bt, H, P, N, G, W, K = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window, wl.draft
-    with concurrent.futures.ProcessPoolExecutor(max_workers=min(workers, distinct)) as ex:
-        got = sorted(ex.map(_gen_round, [(wl.name, r) for r in range(distinct)]))
-    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
-    RX = [bf(g[1]) for g in got]
-    RB = [bf(g[2]) for g in got]
-    RC = [bf(g[3]) for g in got]
-    RD = [torch.from_numpy(g[4]).to(dev) for g in got]
-    NACC = [g[5] for g in got]
+    R = wl.rounds
+    D = [synth.device_draft_inputs(wl, r, dev) for r in range(R)]
+    NACC = [synth.accepted_drafts(wl, r) for r in range(R)]
     NDROP = [torch.from_numpy((K - n).astype(np.int32)).to(dev) for n in NACC]
     SRC = [torch.from_numpy(n.astype(np.int32)).to(dev) for n in NACC]
     A = torch.from_numpy(synth.params(wl)["A"]).to(dev)
     cfg = rss.make_config(Bt, H, P, N, G, W, wl.capacity, K, rss.RSS_DTYPE_BF16, rss.RSS_COPY_NONE)
     layer = rss.ReplayLayer(cfg, A, dev)
-    layer.init_state()
     y = torch.empty((Bt, K + 1, H, P), device=dev)
 
-    def sep_round(r):   # verify, rollback, then a flush of the windows the accepted tokens filled
-        i = r % distinct
-        layer.verify_k_tokens(K, RX[i], RB[i], RC[i], RD[i], y)
-        layer.rollback(NDROP[i])
+    def sep_round(r, lt=None):   # verify, rollback, then a flush of the windows the accepted tokens filled
+        d = D[r % R]
+        f = lambda: layer.verify_k_tokens(K, d["x"], d["B"], d["C"], d["dt"], y)  # noqa: E731
+        f() if lt is None else lt.around("v", f)
+        layer.rollback(NDROP[r % R])
         layer.flush_checkpoint(W)
 
-    def rep_round(r):   # the fold of a full committed window rides on the next verify
-        i = r % distinct
-        layer.verify_k_tokens_fold(W, K, RX[i], RB[i], RC[i], RD[i], y)
-        layer.rollback(NDROP[i])
-    for r in range(warmup):
-        sep_round(r)
-    ms_sep = _timed(torch, lambda j: sep_round(warmup + j), rounds)
-    layer.init_state()
-    for r in range(warmup):
-        rep_round(r)
-    ms_rep = _timed(torch, lambda j: rep_round(warmup + j), rounds)
-    # per-kernel duration of the plain verify (separate-flush schedule), and its
-    # algorithmic bytes from the window lengths
-    layer.init_state()
-    for r in range(warmup + rounds):
-        sep_round(r)
+    def rep_round(r, lt=None):   # the fold of a full committed window rides on the next verify
+        d = D[r % R]
+        f = lambda: layer.verify_k_tokens_fold(W, K, d["x"], d["B"], d["C"], d["dt"], y)  # noqa: E731
+        f() if lt is None else lt.around("vf", f)
+        layer.rollback(NDROP[r % R])
+
+    def timed_schedule(fn):
+        layer.init_state()
+        for r in range(warmup):
+            fn(r)
+        layer.init_state()
+        return _timed(torch, fn, R)
+    ms_rep = timed_schedule(rep_round)
+    ms_sep = timed_schedule(sep_round)
+    # per-launch durations and algorithmic bytes (window lengths replayed on the host)
+    committed = sum(int(np.sum(n + 1)) for n in NACC)
+    lt = Launches(torch)
     lens = np.zeros(Bt, np.int64)
-    for r in range(warmup + rounds):        # replay the integer pointer rule on the host
-        lens += K + 1 - (K - NACC[r % distinct])
-        lens[lens >= W] = 0
-    vev = []
     vbytes = 0
-    entry = 2 * P + 2 * N + 8
-    for j in range(rounds):
-        r = warmup + rounds + j
-        i = r % distinct
-        vev.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-        vev[-1][0].record()
-        layer.verify_k_tokens(K, RX[i], RB[i], RC[i], RD[i], y)
-        vev[-1][1].record()
-        vbytes += H * int(np.sum(P * N * 4 + lens * entry + (K + 1) * (2 * P + 4 * N + 4 + 4 * P + entry) + 36))
-        layer.rollback(NDROP[i])
-        layer.flush_checkpoint(W)
-        lens += K + 1 - (K - NACC[i])
+    layer.init_state()
+    for r in range(R):
+        sep_round(r, lt)
+        vbytes += verify_bytes(wl, lens, np.zeros(Bt, bool))
+        lens += NACC[r] + 1
         lens[lens >= W] = 0
+    lens[:] = 0
+    vfbytes = 0
+    layer.init_state()
+    for r in range(R):
+        fold = lens >= W
+        rep_round(r, lt)
+        vfbytes += verify_bytes(wl, lens, fold)
+        lens[fold] = 0
+        lens += NACC[r] + 1
     torch.cuda.synchronize()
-    v_ms = sum(a.elapsed_time(b) for a, b in vev)
     assert layer.device_error() == 0
-    committed = sum(int(np.sum(NACC[(warmup + j) % distinct] + 1)) for j in range(rounds))
+    v_us, vf_us = lt.us("v"), lt.us("vf")
     del layer
     # eager baseline: K+1 eager tokens from slot src, snapshot i -> slot i;
     # rolling back to n_acc accepted drafts = next round reads slot n_acc
     pool = torch.zeros((Bt, K + 1, H, P, N), device=dev)
     src = [torch.zeros((Bt,), dtype=torch.int32, device=dev)]
 
-    def eag_round(r):
-        i = r % distinct
-        rss.rss_eager_verify(cfg, pool, src[0], K, RX[i], RB[i], RC[i], RD[i], A, y)
-        src[0] = SRC[i]
+    def eag_round(r, lt=None):
+        d = D[r % R]
+        f = lambda: rss.rss_eager_verify(cfg, pool, src[0], K, d["x"], d["B"], d["C"], d["dt"], A, y)  # noqa: E731
+        f() if lt is None else lt.around("e", f)
+        src[0] = SRC[r % R]
     for r in range(warmup):
         eag_round(r)
-    ms_eag = _timed(torch, lambda j: eag_round(warmup + j), rounds)
-    eev = []
-    for j in range(rounds):
-        eev.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-        eev[-1][0].record()
-        eag_round(warmup + rounds + j)
-        eev[-1][1].record()
+    pool.zero_()
+    src[0] = torch.zeros((Bt,), dtype=torch.int32, device=dev)
+    ms_eag = _timed(torch, eag_round, R)
+    lt2 = Launches(torch)
+    for r in range(R):
+        eag_round(r, lt2)
     torch.cuda.synchronize()
-    e_ms = sum(a.elapsed_time(b) for a, b in eev)
+    e_us = lt2.us("e")
     ebytes = H * Bt * ((K + 2) * P * N * 4 + (K + 1) * (2 * P + 4 * N + 4 + 4 * P) + 4)
-    del pool
-    return {"workload": wl.name, "rounds": rounds,
+    del pool, D
+    return {"workload": wl.name, "rounds": R, "inputs": "fresh draws every round (device generator)",
+            "committed_tokens": committed,
             "replay_committed_tokens_per_s": committed / (ms_rep / 1e3),
             "schedule": "verify with the committed-window fold in the same pass, then rollback",
             "replay_separate_flush_committed_tokens_per_s": committed / (ms_sep / 1e3),
             "eager_snapshot_committed_tokens_per_s": committed / (ms_eag / 1e3),
             "speedup": ms_eag / ms_rep,
-            "verify_avg_us": v_ms / rounds * 1e3, "verify_GBps": vbytes / (v_ms / 1e3) / 1e9,
-            "eager_verify_avg_us": e_ms / rounds * 1e3,
-            "eager_verify_GBps": ebytes / (e_ms / rounds / 1e3) / 1e9}
+            "verify_avg_us": float(np.mean(v_us)), "verify_GBps": rate(vbytes, sum(v_us)),
+            "verify_frac_of_peak": rate(vbytes, sum(v_us)) / PEAK_HBM_GBS,
+            "verify_fold_avg_us": float(np.mean(vf_us)), "verify_fold_GBps": rate(vfbytes, sum(vf_us)),
+            "verify_fold_frac_of_peak": rate(vfbytes, sum(vf_us)) / PEAK_HBM_GBS,
+            "eager_verify_avg_us": float(np.mean(e_us)),
+            "eager_verify_GBps": rate(ebytes * len(e_us), sum(e_us))}
 
 
-def gdn_bytes(wl, n0: int) -> dict:
-    """Algorithmic bytes per (sequence, head) of the GDN / KDA kernels (fp32)."""
-    P, N = wl.headdim, wl.dstate
-    if wl.kind == "kda":
-        entry = 8 * N + 4 * P                       # k, u, log-gate row
-        inputs = 4 * N * 3 + 4 * P + 4              # q, k, alpha row, v, beta
-    else:
-        entry = 4 * N + 4 * P + 8                   # k, u, (1, log alpha)
-        inputs = 4 * N * 2 + 4 * P + 8              # q, k, v, beta, alpha
-    return {"replay": P * N * 4 + n0 * entry + inputs + 4 * P + entry + 32,
-            "flush": 2 * P * N * 4 + wl.window * entry + 32,
-            "eager": 2 * P * N * 4 + inputs + 4 * P}
-
-
-def _gen_gdn(args):
-    name, t = args
-    wl = workloads.get(name)
-    s = (synth.kda_step_inputs if wl.kind == "kda" else synth.gdn_step_inputs)(wl, t)
-    return t, s
-
-
-def run_gdn(torch, rss, dev, steps, warmup, workers, distinct=64, name="gdn_b256_h32_d128_w16"):
+def run_gdn(torch, rss, dev, steps, warmup, name="gdn_b256_h32_d128_w16"):
     """Gated DeltaNet (or, with the KDA workload, Kimi Delta Attention) decode at
-    batch 256, 32 heads, d_k = d_v = 128: replay (+ flush every W) against the
-    eager delta-rule kernel."""
+    batch 256, 32 heads, d_k = d_v = 128: replay with the fold inside the decode
+    that fills the window (and with a separate flush launch), against the eager
+    delta-rule kernel. `steps` distinct inputs, drawn on the device."""
     wl = workloads.get(name)
     kda = wl.kind == "kda"
     Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
-    with concurrent.futures.ProcessPoolExecutor(max_workers=min(workers, 16)) as ex:
-        got = sorted(ex.map(_gen_gdn, [(wl.name, t) for t in range(distinct)]), key=lambda g: g[0])
-    D = [{k: torch.from_numpy(v).to(dev) for k, v in g[1].items()} for g in got]
+    assert steps % W == 0
+    D = [synth.device_delta_inputs(wl, t, dev) for t in range(steps)]
     cfg = rss.make_config(Bt, H, P, N, H, W, wl.capacity, 0, rss.RSS_DTYPE_F32, rss.RSS_COPY_NONE,
                           rss.RSS_KIND_KDA if kda else rss.RSS_KIND_GDN)
     layer = rss.ReplayLayer(cfg, None, dev)
     decode = layer.kda_decode_step if kda else layer.gdn_decode_step
     decode_fold = layer.kda_decode_flush_step if kda else layer.gdn_decode_flush_step
     eager_step = rss.rss_kda_eager_step if kda else rss.rss_gdn_eager_step
-    layer.init_state()
     o = torch.empty((Bt, H, P), device=dev)
-    evs = []
 
-    def step(k, rec=False):
-        d = D[k % distinct]
-        if rec:
-            evs.append([torch.cuda.Event(enable_timing=True) for _ in range(4)])
-            evs[-1][0].record()
-        decode(d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
-        if rec:
-            evs[-1][1].record()
+    def args(k):
+        d = D[k % steps]
+        return d["q"], d["k"], d["v"], d["beta"], d["alpha"], o
+
+    def fused_step(k, lt=None):  # the window-filling token folds in the same pass
         if (k + 1) % W == 0:
-            if rec:
-                evs[-1][2].record()
-            layer.flush_checkpoint(W)
-            if rec:
-                evs[-1][3].record()
-    def fused_step(k):  # the window-filling token folds in the same pass
-        d = D[k % distinct]
-        if (k + 1) % W == 0:
-            decode_fold(W, d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
+            f, key = (lambda: decode_fold(W, *args(k))), "fused"  # noqa: E731
         else:
-            decode(d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
-    for k in range(warmup):
-        fused_step(k)
-    ms_fused = _timed(torch, lambda j: fused_step(warmup + j), steps)
+            f, key = (lambda: decode(*args(k))), f"r{k % W}"  # noqa: E731
+        f() if lt is None else lt.around(key, f)
+
+    def sep_step(k, lt=None):
+        f = lambda: decode(*args(k))  # noqa: E731
+        f() if lt is None else lt.around(f"r{k % W}", f)
+        if (k + 1) % W == 0:
+            g = lambda: layer.flush_checkpoint(W)  # noqa: E731
+            g() if lt is None else lt.around("flush", g)
+
+    k0 = whole(warmup, W, W)
+
+    def timed(fn):
+        layer.init_state()
+        for k in range(k0):
+            fn(k)
+        return _timed(torch, fn, steps, start=k0)
+    ms_fused = timed(fused_step)
+    ms_sep = timed(sep_step)
+    lt = Launches(torch)
     layer.init_state()
-    for k in range(warmup):
-        step(k)
-    ms = _timed(torch, lambda j: step(warmup + j), steps)
-    base = warmup + steps
-    for j in range(steps):
-        step(base + j, rec=True)
+    for k in range(steps):
+        fused_step(k, lt)
+    layer.init_state()
+    for k in range(steps):
+        sep_step(k, lt)
     torch.cuda.synchronize()
-    r_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
-    f_list = [e[2].elapsed_time(e[3]) for j, e in enumerate(evs) if (base + j + 1) % W == 0]
-    rbytes = sum(gdn_bytes(wl, (base + j) % W)["replay"] for j in range(steps)) * Bt * H
     assert layer.device_error() == 0
+    r_us = r_b = n_r = 0
+    for n0 in range(W):
+        d = lt.us(f"r{n0}")
+        r_us += sum(d)
+        r_b += len(d) * gdn_bytes(wl, n0)["replay"] * Bt * H
+        n_r += len(d)
+    fb = gdn_bytes(wl, W)
+    fu_us, fl_us = lt.us("fused"), lt.us("flush")
     del layer, decode, decode_fold
     S = torch.zeros((Bt, H, P, N), device=dev)
 
     def eager(k):
-        d = D[k % distinct]
-        eager_step(cfg, S, d["q"], d["k"], d["v"], d["beta"], d["alpha"], o)
-    for k in range(warmup):
+        eager_step(cfg, S, *args(k))
+    for k in range(k0):
         eager(k)
-    ems = _timed(torch, lambda j: eager(warmup + j), steps)
-    eev = []
-    for j in range(steps):
-        eev.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-        eev[-1][0].record()
-        eager(j)
-        eev[-1][1].record()
+    ems = _timed(torch, eager, steps, start=k0)
+    lt2 = Launches(torch)
+    for k in range(steps):
+        lt2.around("e", lambda k=k: eager(k))
     torch.cuda.synchronize()
-    e_ms = sum(a.elapsed_time(b) for a, b in eev)
-    fb = gdn_bytes(wl, W)
-    return {"workload": wl.name, "replay_tokens_per_s": Bt * steps / (ms_fused / 1e3),
+    e_us = lt2.us("e")
+    del D
+    return {"workload": wl.name, "steps": steps, "folds_timed": steps // W,
+            "replay_tokens_per_s": Bt * steps / (ms_fused / 1e3),
             "schedule": "replay, the window-filling token folds in the same pass",
-            "replay_separate_flush_tokens_per_s": Bt * steps / (ms / 1e3),
+            "replay_separate_flush_tokens_per_s": Bt * steps / (ms_sep / 1e3),
             "eager_tokens_per_s": Bt * steps / (ems / 1e3), "speedup": ems / ms_fused,
-            "replay_avg_us": r_ms / steps * 1e3, "replay_GBps": rbytes / (r_ms / 1e3) / 1e9,
-            "flush_avg_us": sum(f_list) / max(len(f_list), 1) * 1e3,
-            "flush_GBps": fb["flush"] * Bt * H * len(f_list) / (sum(f_list) / 1e3) / 1e9 if f_list else None,
-            "eager_avg_us": e_ms / steps * 1e3,
-            "eager_GBps": fb["eager"] * Bt * H * steps / (e_ms / 1e3) / 1e9}
+            "replay_avg_us": r_us / n_r, "replay_GBps": rate(r_b, r_us),
+            "fused_avg_us": float(np.mean(fu_us)),
+            "fused_GBps": rate(fb["fused"] * Bt * H * len(fu_us), sum(fu_us)),
+            "fused_frac_of_peak": rate(fb["fused"] * Bt * H * len(fu_us), sum(fu_us)) / PEAK_HBM_GBS,
+            "flush_avg_us": float(np.mean(fl_us)),
+            "flush_GBps": rate(fb["flush"] * Bt * H * len(fl_us), sum(fl_us)),
+            "eager_avg_us": float(np.mean(e_us)),
+            "eager_GBps": rate(fb["eager"] * Bt * H * len(e_us), sum(e_us))}
 
 
 def main() -> int:
@@ -573,14 +785,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
+                    help="also run a 1 GiB -> 1 GiB copy with the library's copy kernel (counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed repeats of --steps steps (each after a fresh init); median reported")
     ap.add_argument("--separate-flush", action="store_true",
                     help="fold with a separate flush launch instead of the fused decode+fold")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the dual-precision and speculative-verify measurements")
+                    help="skip the further workloads (dual precision, speculative, GDN, ...)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -590,173 +802,33 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import torch
-    from recurrent_state_storage_amd import rss
-
     wl = workloads.get(WORKLOAD)
     Bt, H, P, N, G, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window
-    dev = torch.device("cuda:0")
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    # Host-side work that forks (input pool, CPU baseline) runs before the device
+    # is touched.
     t0 = time.perf_counter()
     pool = gen_pool(wl, args.pool, workers)
     gen_s = time.perf_counter() - t0
-    # The host baseline runs before the device is touched (its workers are forked).
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, pool, args.cpu_seconds, workers)
+
+    import torch
+    from recurrent_state_storage_amd import rss
+
+    dev = torch.device("cuda:0")
     X = torch.from_numpy(pool[0].view(np.int16)).view(torch.bfloat16).to(dev)
     Bm = torch.from_numpy(pool[1].view(np.int16)).view(torch.bfloat16).to(dev)
     Cm = torch.from_numpy(pool[2].view(np.int16)).view(torch.bfloat16).to(dev)
     DT = torch.from_numpy(pool[3]).to(dev)
     A = torch.from_numpy(synth.params(wl)["A"]).to(dev)
-    cfg = rss.make_config(Bt, H, P, N, G, W, wl.capacity, 0, rss.RSS_DTYPE_BF16, rss.RSS_COPY_NONE)
-    layer = rss.ReplayLayer(cfg, A, dev)
-    layer.init_state()
-    y = torch.empty((Bt, H, P), device=dev)
-    T = args.pool
 
-    fused = not args.separate_flush
-
-    def replay_step(k, ev=None):
-        i = k % T
-        fold = (k + 1) % W == 0
-        if ev is not None:
-            ev[0].record()
-        if fold and fused:   # this token fills every window: decode and fold in one pass
-            layer.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)
-        else:
-            layer.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
-        if ev is not None:
-            ev[1].record()
-        if fold and not fused:
-            if ev is not None:
-                ev[2].record()
-            layer.flush_checkpoint(W)
-            if ev is not None:
-                ev[3].record()
-
-    # Repeats: each starts from a fresh init_state and W warm-up steps (untimed),
-    # then exactly `steps` steps between two events; the median repeat is reported.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps_ms = []
-    for _ in range(max(1, args.repeats)):
-        layer.init_state()
-        k = 0
-        for _ in range(args.warmup):
-            replay_step(k)
-            k += 1
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            replay_step(k)
-            k += 1
-        e1.record()
-        torch.cuda.synchronize()
-        reps_ms.append(e0.elapsed_time(e1))
-    ms = float(np.median(reps_ms))
-    tok_s = Bt * args.steps / (ms / 1e3)
-
-    # Per-kernel durations: HIP events around every launch on the launch stream,
-    # in a second pass of the same length (so the timed pass above is unperturbed).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    phase = []
-    for j in range(args.steps):
-        phase.append(k % W)
-        replay_step(k, ev[j])
-        k += 1
-    torch.cuda.synchronize()
-    # "replay decode" = the plain decode launches (window positions 0..W-2, and
-    # W-1 too when the flush runs separately); the fold launches are reported apart.
-    rep_ms, rep_bytes, n_rep, fl_ms, fl_bytes, n_fl = 0.0, 0, 0, 0.0, 0, 0
-    for j in range(args.steps):
-        d = ev[j][0].elapsed_time(ev[j][1])
-        if phase[j] == W - 1 and fused:
-            fl_ms += d
-            fl_bytes += fused_bytes(wl) * Bt * H
-            n_fl += 1
-            continue
-        rep_ms += d
-        rep_bytes += replay_bytes(wl, phase[j]) * Bt * H
-        n_rep += 1
-        if phase[j] == W - 1:
-            fl_ms += ev[j][2].elapsed_time(ev[j][3])
-            fl_bytes += flush_bytes(wl, W) * Bt * H
-            n_fl += 1
-    step_us = [ev[j][0].elapsed_time(ev[j][1]) * 1e3 + (ev[j][2].elapsed_time(ev[j][3]) * 1e3
-               if phase[j] == W - 1 and not fused else 0.0) for j in range(args.steps)]
-    rep_avg_us = rep_ms / n_rep * 1e3
-    rep_gbs = rep_bytes / (rep_ms / 1e3) / 1e9
-    assert layer.device_error() == 0
-
-    out_eager = None
-    if not args.no_eager:
-        S = torch.zeros((Bt, H, P, N), device=dev)
-        ye = torch.empty_like(y)
-
-        def eager_step(k):
-            i = k % T
-            rss.rss_eager_step(cfg, S, X[i], Bm[i], Cm[i], DT[i], A, ye)
-        for j in range(args.warmup):
-            eager_step(j)
-        torch.cuda.synchronize()
-        e0.record()
-        for j in range(args.steps):
-            eager_step(j)
-        e1.record()
-        torch.cuda.synchronize()
-        ems = e0.elapsed_time(e1)
-        eev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for j in range(args.steps):
-            eev[j][0].record()
-            eager_step(j)
-            eev[j][1].record()
-        torch.cuda.synchronize()
-        eag_ms = sum(a.elapsed_time(b) for a, b in eev)
-        out_eager = {
-            "tokens_per_s": Bt * args.steps / (ems / 1e3), "ms_per_step": ems / args.steps,
-            "kernel_avg_us": eag_ms / args.steps * 1e3,
-            "kernel_GBps": eager_bytes(wl) * Bt * H * args.steps / (eag_ms / 1e3) / 1e9,
-            "bytes_per_token": eager_bytes(wl) * H,
-        }
-        # Parity of the timed path on the whole batch: a fresh replay layer (the
-        # benchmark's schedule) and a fresh eager state run 2W steps side by side.
-        S.zero_()
-        chk = rss.ReplayLayer(cfg, A, dev)
-        chk.init_state()
-        num = den = 0.0
-        worst = 0.0
-        for k in range(2 * W):
-            i = k % T
-            if (k + 1) % W == 0 and fused:
-                chk.decode_flush_step(W, X[i], Bm[i], Cm[i], DT[i], y)
-            else:
-                chk.decode_step(X[i], Bm[i], Cm[i], DT[i], y)
-                if (k + 1) % W == 0:
-                    chk.flush_checkpoint(W)
-            rss.rss_eager_step(cfg, S, X[i], Bm[i], Cm[i], DT[i], A, ye)
-            d2 = float(torch.sum((y - ye).double() ** 2))
-            r2 = float(torch.sum(ye.double() ** 2))
-            num, den = num + d2, den + r2
-            worst = max(worst, (d2 / r2) ** 0.5)
-        assert chk.device_error() == 0
-        out_eager["parity_replay_vs_eager"] = {"steps": 2 * W, "run_rel_l2": (num / den) ** 0.5,
-                                               "worst_step_rel_l2": worst}
-        del S, chk
-
-    # Context: a plain device copy, 1 GiB read + 1 GiB written (torch's vectorised
-    # elementwise kernel multiplying by 1, the faster of torch's copy paths here).
-    csrc = torch.ones((1 << 28,), device=dev)
-    cdst = torch.empty_like(csrc)
-    torch.mul(csrc, 1.0, out=cdst)
-    copy_ms = _timed(torch, lambda j: torch.mul(csrc, 1.0, out=cdst), 10) / 10
-    copy_gbs = 2 * (1 << 30) / (copy_ms / 1e3) / 1e9
-    del csrc, cdst
-
+    main_run = run_main(torch, rss, dev, X, Bm, Cm, DT, A, args)
+    cfg, fused = main_run["cfg"], main_run["fused"]
+    out_eager = None if args.no_eager else run_eager(torch, rss, dev, X, Bm, Cm, DT, A, cfg,
+                                                     args.steps, args.warmup)
+    calib = run_calibration(torch, rss, dev)
     if args.calibrate_copy:
-        src = torch.ones((1 << 28,), device=dev)      # 1 GiB fp32
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calibrate_counters(torch, rss, dev)
 
     # Bytes per decoded token per layer (analytic): state tiles, and everything.
     st_eager = 2 * P * N * 4 * H
@@ -771,14 +843,16 @@ def main() -> int:
     c_fused, c_eager = counter_traffic("fused"), counter_traffic("eager")
     meas_replay = ((W - 1) * traffic + c_fused) / W / Bt if traffic and c_fused and fused else None
     meas_eager = c_eager / Bt if c_eager else None
+    kern = main_run["kernels"]
+    fk = "fused_decode_fold" if fused else "flush"
     rec = {
         "metric": METRIC,
-        "value": tok_s,
+        "value": main_run["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms / args.steps,
+        "ms_per_step": main_run["ms"] / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -788,25 +862,27 @@ def main() -> int:
                    "groups": G, "window": W, "xBC_storage": "bf16", "state": "f32",
                    "fold": "fused into the window-filling decode" if fused else "separate flush",
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": rep_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": rep_gbs / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "replay decode", "avg_launch_us": rep_avg_us,
-                     "algorithmic_bytes_per_launch": rep_bytes / n_rep},
-        "kernels": {
-            "replay_decode": {"avg_us": rep_avg_us, "GBps": rep_gbs},
-            ("fused_decode_fold" if fused else "flush"): {
-                "avg_us": fl_ms / max(n_fl, 1) * 1e3,
-                "GBps": fl_bytes / (fl_ms / 1e3) / 1e9 if n_fl else None, "launches": n_fl},
-        },
-        "step_us": {"median": float(np.median(step_us)), "max": float(np.max(step_us))},
-        "repeats_ms": reps_ms,
-        "context": {"device_copy_GBps": copy_gbs, "replay_frac_of_copy": rep_gbs / copy_gbs},
+        "roofline": {"bound": "hbm", "achieved": main_run["rep_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": main_run["rep_gbs"] / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "replay decode", "avg_launch_us": main_run["rep_us"],
+                     "algorithmic_bytes_per_launch": main_run["rep_bytes"]},
+        "steady_state_tokens_per_s": main_run["steady"]["tokens_per_s"],
+        "steady_state": main_run["steady"],
+        "kernels": kern,
+        "step_us": {"median": float(np.median(main_run["step_us"])),
+                    "max": float(np.max(main_run["step_us"]))},
+        "repeats_ms": main_run["reps_ms"],
+        "context": dict(calib, **{
+            "replay_frac_of_read_ceiling": main_run["rep_gbs"] / calib["read_ceiling_GBps"],
+            "fold_frac_of_copy_ceiling": kern[fk]["GBps"] / calib["copy_ceiling_GBps"],
+            "eager_frac_of_copy_ceiling": (out_eager["kernel_GBps"] / calib["copy_ceiling_GBps"]
+                                           if out_eager else None)}),
         "eager_baseline": out_eager,
         "bytes_per_token": {"replay_state": st_replay, "eager_state": st_eager,
                             "state_ratio": st_replay / st_eager, "replay_total": tot_replay,
                             "eager_total": eager_bytes(wl) * H,
                             "total_ratio": tot_replay / (eager_bytes(wl) * H),
-                            "replay_decode_launch_analytic": rep_bytes / n_rep / Bt,
+                            "replay_decode_launch_analytic": main_run["rep_bytes"] / Bt,
                             "replay_decode_launch_counters": traffic / Bt if traffic else None,
                             "replay_window_counters": meas_replay,
                             "eager_counters": meas_eager,
@@ -815,27 +891,27 @@ def main() -> int:
         "input_generation_s": gen_s,
     }
     if out_eager:
-        rec["speedup_vs_eager_gpu"] = tok_s / out_eager["tokens_per_s"]
+        rec["speedup_vs_eager_gpu"] = main_run["tokens_per_s"] / out_eager["tokens_per_s"]
+        rec["steady_state_speedup_vs_eager_gpu"] = (main_run["steady"]["tokens_per_s"] /
+                                                    out_eager["tokens_per_s"])
     if not args.no_extra:
-        rec["staggered_folds"] = run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, args.steps,
-                                             args.warmup)
-        rec["grouped_bc"] = run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
-        rec["dual_precision"] = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup)
-        # the dual-precision window sweep (W = 8, 16, 32; R = W), same inputs
+        sub = whole(args.steps, max(SWEEP_WINDOWS), 64)   # whole windows of every W swept
+        rec["sub_measurement_steps"] = sub
+        rec["staggered_folds"] = run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)
+        rec["grouped_bc"] = run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)
+        rec["dual_precision"] = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)
         rec["dual_precision"]["by_window"] = {
-            w: {k: v for k, v in run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup,
+            w: {k: v for k, v in run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup,
                                           window=w).items() if k != "workload"}
-            for w in (8, 16, 32)}
+            for w in SWEEP_WINDOWS}
         rec["low_precision"] = {
-            "bf16_checkpoint": run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, args.steps, args.warmup,
+            "bf16_checkpoint": run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup,
                                         mode="bf16_state"),
-            "eager_bf16_state": run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, args.steps,
-                                               args.warmup)}
-        rec["speculative"] = run_spec(torch, rss, dev, rounds=48, warmup=8, workers=workers)
-        rec["gated_deltanet"] = run_gdn(torch, rss, dev, steps=args.steps, warmup=args.warmup,
-                                        workers=workers)
-        rec["kimi_delta_attention"] = run_gdn(torch, rss, dev, steps=args.steps, warmup=args.warmup,
-                                              workers=workers, name="kda_b256_h32_d128_w16")
+            "eager_bf16_state": run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)}
+        rec["speculative"] = run_spec(torch, rss, dev)
+        rec["gated_deltanet"] = run_gdn(torch, rss, dev, sub, args.warmup)
+        rec["kimi_delta_attention"] = run_gdn(torch, rss, dev, sub, args.warmup,
+                                              name="kda_b256_h32_d128_w16")
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)

@@ -1,0 +1,45 @@
+/*
+ * rss_calib.h — bandwidth calibration kernels exported by librss (MI355X, gfx950).
+ *
+ * Not part of the decode path: a benchmark runs them beside the decode kernels
+ * to measure what HBM actually delivers with the decode kernels' own access
+ * pattern (16-byte non-temporal loads and stores, fully coalesced, grid-stride),
+ * so that each kernel's bandwidth can be quoted as a fraction of the achievable
+ * read or copy rate as well as of the data-sheet peak. The method's premise is
+ * that HBM traffic, not arithmetic, bounds the decode (P1, "La fiche qu'on
+ * réécrit à chaque token": the eager step reads and writes the whole state for
+ * very little arithmetic).
+ *
+ * Conventions as in rss.h: device pointers owned by the caller, 16-byte
+ * aligned; the call only enqueues work on `stream` (a hipStream_t, NULL = the
+ * null stream) and returns an rss_status: RSS_E_INVALID for a null or
+ * misaligned pointer, a size that is not a multiple of 16, or blocks < 0;
+ * RSS_E_HIP if the launch fails. bytes = 0 launches nothing.
+ */
+#ifndef RSS_CALIB_H_
+#define RSS_CALIB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rss.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Stream-read `bytes` from src (read only; nothing of it is written). sink: a
+ * device float the kernel may write (it stores only for one specific sum the
+ * inputs are not expected to produce, which keeps the loads from being
+ * removed). blocks: workgroups of 256 threads in the grid (0 = 4096). */
+int32_t rss_calib_read(const void* src, size_t bytes, float* sink, int32_t blocks, void* stream);
+
+/* Copy `bytes` from src to dst (non-overlapping): reads and writes `bytes`
+ * each. blocks as rss_calib_read. */
+int32_t rss_calib_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSS_CALIB_H_ */

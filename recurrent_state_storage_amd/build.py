@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librss.so")
 
-SOURCES = ["replay.hip", "flush.hip", "eager.hip", "gdn.hip", "rss_api.cpp"]
+SOURCES = ["replay.hip", "flush.hip", "eager.hip", "gdn.hip", "calib.hip", "rss_api.cpp"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 ARCH = "gfx950"

@@ -53,9 +53,37 @@ struct TileGeom {
   static constexpr int VEC = LOW ? 8 : 4;       // elements per 16-byte load
   static constexpr int TPR = N / VEC;            // threads per row
   static constexpr int RPP = NT / TPR;           // rows per pass (NT threads per workgroup)
+  static constexpr int SR = 64 / TPR;            // rows per pass in one wavefront
   static_assert(N % VEC == 0 && TPR >= 1 && TPR <= 64, "unsupported N");
   static_assert((TPR & (TPR - 1)) == 0, "N/VEC must be a power of two");
 };
+
+// Rows of a tile chunk held by one thread. A chunk is RPP * MP rows starting at
+// `base`; wavefront w owns its MP * SR consecutive rows starting at
+// base + w * MP * SR, and pass k of the wavefront covers the SR rows starting at
+// base + w * MP * SR + k * SR (lane / TPR picks the row). Each wavefront thus
+// loads whole, adjacent rows per 16-byte load (full cache lines) and its row
+// outputs are contiguous.
+template <int TPR, int MP>
+struct RowMap {
+  static constexpr int SR = 64 / TPR;
+  int off;   // row offset of this thread inside the chunk, pass 0
+  __device__ explicit RowMap(int tid) : off((tid >> 6) * MP * SR + (tid & 63) / TPR) {}
+  __device__ int row(int base, int k) const { return base + k * SR + off; }
+  // First row of pass k in this thread's wavefront (uniform across it).
+  __device__ int wave_row(int base, int k, int wave) const { return base + (wave * MP + k) * SR; }
+};
+
+// Workgroup -> tile index, XCD-aware. The dispatcher hands consecutive
+// workgroup ids to the eight XCDs in turn, each with its own L2; this bijection
+// on [0, n) gives XCD x one contiguous range of tiles instead, so neighbouring
+// (sequence, head) tiles, whose pointer words and ring entries share cache
+// lines, are written through the same L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int id, int n) {
+  const int x = id % kXcds, q = n / kXcds, r = n % kXcds;
+  return x * q + (x < r ? x : r) + id / kXcds;
+}
 
 // ---- cross-lane exchanges ----------------------------------------------------
 // xchg<BIT>(v) returns v of a partner lane whose id has the opposite bit BIT and

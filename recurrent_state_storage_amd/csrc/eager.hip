@@ -23,10 +23,11 @@
 
 namespace rss {
 
-template <int N, typename Tin, bool SB16>
+template <int N, typename Tin, bool SB16, bool POOL>
 __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
+  using Rows = RowMap<TPR, kMaxPass>;
 
   __shared__ float sa[kMaxNew];
   __shared__ float sdtv[kMaxNew];
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
 
   const int tid = threadIdx.x;
   const int H = a.H, P = a.P, G = a.G, T = a.T;
-  const int bh = blockIdx.x;
+  const int bh = xcd_tile(blockIdx.x, gridDim.x);
   const int b = bh / H, h = bh - b * H;
   const int g = h / (H / G);
   const size_t tile_elems = (size_t)P * N;
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
   float* const S = static_cast<float*>(a.S);
   if (SB16) {
     src = nullptr;
-  } else if (a.src_slot) {
+  } else if (POOL) {
     const int s = a.src_slot[b];
     if (s < 0 || s >= a.slots) {
       for (int e = tid; e < T * P; e += kThreads) {
@@ -58,15 +59,16 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
     src = S + (size_t)bh * tile_elems;
   }
 
-  const int col = tid % TPR, rsub = tid / TPR;
+  const int col = tid % TPR;
+  const Rows rows(tid);
   Frag<false> fr[kMaxPass];
   auto load_chunk = [&](int base) {
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
-      const int row = base + k * RPP + rsub;
+      const int row = rows.row(base, k);
       if (row >= P) fr[k].v = float4{};
-      else if constexpr (SB16) fr[k].v = ld8_bf16x4(srcb + (size_t)row * N + col * 4);
-      else fr[k].v = ld16(src + (size_t)row * N + col * 4);
+      else if constexpr (SB16) fr[k].v = ld8_bf16x4(srcb + row * N + col * 4);
+      else fr[k].v = ld16(src + row * N + col * 4);
     }
   };
   load_chunk(0);
@@ -94,58 +96,83 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
   }
   __syncthreads();
 
+  // Per token: every pass is updated (rows past P hold zeros, read a valid x
+  // row and are never stored, so the pass loop has no branch), each row's dot
+  // with C is reduce-scattered over the row's lanes (the replay's tree), and the
+  // writer lanes store y; a snapshot slot, when asked for, is written as it
+  // forms. In place, the state is stored once after the last token.
+  using RS = RowScatter<TPR>;
   for (int base = 0; base < P; base += RPP * kMaxPass) {
     if (base > 0) load_chunk(base);
+    int xrow[kMaxPass];
+#pragma unroll
+    for (int k = 0; k < kMaxPass; ++k) {
+      const int row = rows.row(base, k);
+      xrow[k] = row < P ? row : P - 1;
+    }
     for (int i = 0; i < T; ++i) {
       const float ai = sa[i], di = sdtv[i];
       const float4 bv = *reinterpret_cast<const float4*>(&Bs[i * N + col * 4]);
       const float4 cv = *reinterpret_cast<const float4*>(&Cs[i * N + col * 4]);
+      float part[kMaxPass];
 #pragma unroll
       for (int k = 0; k < kMaxPass; ++k) {
-        if (base + k * RPP >= P) break;
-        const int row = base + k * RPP + rsub;
-        const float u = row < P ? di * xs[i * P + row] : 0.f;
+        const float u = di * xs[i * P + xrow[k]];
         float4& s = fr[k].v;
         s.x = fmaf(u, bv.x, ai * s.x);
         s.y = fmaf(u, bv.y, ai * s.y);
         s.z = fmaf(u, bv.z, ai * s.z);
         s.w = fmaf(u, bv.w, ai * s.w);
-        float part = s.x * cv.x;
-        part = fmaf(s.y, cv.y, part);
-        part = fmaf(s.z, cv.z, part);
-        part = fmaf(s.w, cv.w, part);
-        part = row_sum<TPR>(part);
-        if (col == 0 && row < P) a.y[((size_t)(b * T + i) * H + h) * P + row] = part;
-        if (!SB16 && a.src_slot && row < P) {
-          float* dst = S + (((size_t)b * a.slots + i) * H + h) * tile_elems;
-          *reinterpret_cast<float4*>(dst + (size_t)row * N + col * 4) = s;
+        float acc = s.x * cv.x;
+        acc = fmaf(s.y, cv.y, acc);
+        acc = fmaf(s.z, cv.z, acc);
+        part[k] = fmaf(s.w, cv.w, acc);
+      }
+      if (!SB16 && POOL) {
+        float* dst = S + (((size_t)b * a.slots + i) * H + h) * tile_elems;
+#pragma unroll
+        for (int k = 0; k < kMaxPass; ++k) {
+          const int row = rows.row(base, k);
+          if (row < P) st16(dst + row * N + col * 4, fr[k].v);
+        }
+      }
+      int kbase;
+      RS::run(part, col, kbase);
+      if ((col & RS::WMASK) == 0) {
+        float* yo = a.y + ((size_t)(b * T + i) * H + h) * P;
+#pragma unroll
+        for (int m = 0; m < RS::NOUT; ++m) {
+          const int row = rows.row(base, kbase + m);
+          if (row < P) yo[row] = part[m];
         }
       }
     }
-    if (!a.src_slot) {
+    if (!POOL) {
 #pragma unroll
       for (int k = 0; k < kMaxPass; ++k) {
-        const int row = base + k * RPP + rsub;
+        const int row = rows.row(base, k);
         if (row >= P) continue;
-        if constexpr (SB16) st8_bf16x4(srcb + (size_t)row * N + col * 4, fr[k].v);
-        else *reinterpret_cast<float4*>(src + (size_t)row * N + col * 4) = fr[k].v;
+        if constexpr (SB16) st8_bf16x4(srcb + row * N + col * 4, fr[k].v);
+        else st16(src + row * N + col * 4, fr[k].v);
       }
     }
   }
 }
 
-template <int N, bool SB16>
+template <int N, bool SB16, bool POOL>
 static hipError_t eager_n(const EagerArgs& a, int batch, bool bf16_in, hipStream_t s) {
   const dim3 grid((unsigned)((size_t)batch * a.H)), block(kThreads);
   const size_t lds = (size_t)a.T * (a.P + 2 * N) * sizeof(float);
-  if (bf16_in) hipLaunchKernelGGL((eager_kernel<N, bf16_t, SB16>), grid, block, lds, s, a);
-  else hipLaunchKernelGGL((eager_kernel<N, float, SB16>), grid, block, lds, s, a);
+  if (bf16_in) hipLaunchKernelGGL((eager_kernel<N, bf16_t, SB16, POOL>), grid, block, lds, s, a);
+  else hipLaunchKernelGGL((eager_kernel<N, float, SB16, POOL>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
 template <int N>
 static hipError_t eager_s(const EagerArgs& a, int batch, bool bf16_in, bool bf16_state, hipStream_t s) {
-  return bf16_state ? eager_n<N, true>(a, batch, bf16_in, s) : eager_n<N, false>(a, batch, bf16_in, s);
+  if (a.src_slot) return eager_n<N, false, true>(a, batch, bf16_in, s);
+  return bf16_state ? eager_n<N, true, false>(a, batch, bf16_in, s)
+                    : eager_n<N, false, false>(a, batch, bf16_in, s);
 }
 
 hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, bool bf16_state,

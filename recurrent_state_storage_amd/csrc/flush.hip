@@ -22,6 +22,7 @@
 // Rollback (P2, "Un retour en arrière qui devient trivial") touches integers
 // only: len -= n_drop, n_tent = 0.
 #include "device.h"
+#include "fold.h"
 #include "launch.h"
 #include "lds.h"
 
@@ -30,11 +31,15 @@ namespace rss {
 constexpr int kFlushStage = 2;  // 16-byte B loads per thread per staging round
 
 
-template <int N, typename Tin, int MODE, bool PCD>
+// MF: the rank-n update runs on the matrix cores (fold.h); otherwise as fp32
+// FMAs, one entry at a time in ascending order.
+template <int N, typename Tin, int MODE, bool PCD, bool MF>
 __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   constexpr bool DUAL = MODE == kCkptDual, B16 = MODE == kCkptBf16;
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
+  using Rows = RowMap<TPR, kMaxPass>;
+  using Fold = MfmaFold<N, TPR, 4, kMaxPass>;
   constexpr int VE = V16<Tin>::VE;
   constexpr int NV = N / VE;
   using VT = typename V16<Tin>::T;
@@ -42,9 +47,10 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   extern __shared__ __align__(16) float lds[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, P = a.P, G = a.G, R = a.R;
-  const int bh = blockIdx.x;
+  const int bh = xcd_tile(blockIdx.x, gridDim.x);
   const int b = bh / H, h = bh - b * H;
   const int g = h / (H / G);
   const int4 pt = a.ptr[bh];
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (tid == 0) atomicOr(a.err, kDevUncommitted);
     return;
   }
-  const FlushLds lay(R, P, N, PCD);
+  const FlushLds lay(R, P, N, PCD, MF ? Fold::BUF : 0);
   const int RS = lay.RS;
   float* sXT = lds + lay.oXT;
   float* sB = lds + lay.oB;
@@ -72,7 +78,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   auto brow = [&](int j) { return rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N; };
 
   // 1. Tile loads (the fp32 master, or the bf16 checkpoint widened to fp32).
-  const int col = tid % TPR, rsub = tid / TPR;
+  const int col = tid % TPR;
+  const Rows rows(tid);
   float* tile = B16 ? nullptr : a.ckpt + (size_t)bh * P * N;
   bf16_t* tileb = B16 ? static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N : nullptr;
   Frag<false> fr[kMaxPass];
@@ -83,9 +90,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   auto load_chunk = [&](int base) {
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
-      const int r0 = base + k * RPP;
-      if (r0 + RPP <= P) fr[k].v = ld_row(r0 + rsub);
-      else if (r0 + rsub < P) fr[k].v = ld_row(r0 + rsub);
+      const int row = rows.row(base, k);
+      if (row < P) fr[k].v = ld_row(row);
       else fr[k].v = float4{};
     }
   };
@@ -164,50 +170,79 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     for (int v = 0; v < 4; ++v) Dc[v] = sDc[col * 4 + v];
   }
 
-  // 3. S <- D S + sum_j x_j outer (c_j B_j), j ascending, in place.
-  for (int base = 0; base < P; base += RPP * kMaxPass) {
-    if (base > 0) load_chunk(base);
-#pragma unroll
-    for (int k = 0; k < kMaxPass; ++k) {
-      fr[k].v.x *= Dc[0];
-      fr[k].v.y *= Dc[1];
-      fr[k].v.z *= Dc[2];
-      fr[k].v.w *= Dc[3];
-    }
-    // Rows past P read a valid row (results unused): every pass without a branch.
-    const float* xr[kMaxPass];
-#pragma unroll
-    for (int k = 0; k < kMaxPass; ++k) {
-      const int row = base + k * RPP + rsub;
-      xr[k] = sXT + (row < P ? row : P - 1) * RS;
-    }
-    for (int j = 0; j < n; ++j) {
-      const float cj = sCF[j];
-      const float4 t = *reinterpret_cast<const float4*>(&sB[j * N + col * 4]);
-      const float b0 = cj * t.x, b1 = cj * t.y, b2 = cj * t.z, b3 = cj * t.w;
-#pragma unroll
-      for (int k = 0; k < kMaxPass; ++k) {
-        const float xv = xr[k][j];
-        float4& s = fr[k].v;
-        s.x = fmaf(xv, b0, s.x); s.y = fmaf(xv, b1, s.y);
-        s.z = fmaf(xv, b2, s.z); s.w = fmaf(xv, b3, s.w);
+  // 3. S <- D S + sum_j x_j outer (c_j B_j), in place.
+  auto store_row = [&](int row, const float4& v) {
+    if constexpr (B16) {
+      st8_bf16x4(tileb + (size_t)row * N + col * 4, v);
+    } else {
+      st16(tile + (size_t)row * N + col * 4, v);
+      if (DUAL) {
+        bf16_t* lo = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N + (size_t)row * N + col * 4;
+        uint2 pk;
+        pk.x = pack_bf16x2(v.x, v.y);
+        pk.y = pack_bf16x2(v.z, v.w);
+        *reinterpret_cast<uint2*>(lo) = pk;
       }
     }
+  };
+  for (int base = 0; base < P; base += RPP * kMaxPass) {
+    if (base > 0) load_chunk(base);
+    if constexpr (MF) {
+      if (rows.wave_row(base, 0, wave) < P) {
+        Fold::run(rows.wave_row(base, 0, wave), P, n, lds + lay.oW + wave * Fold::BUF, lane, col,
+                  [&](int j, int c) { return sCF[j] * sB[j * N + c]; },
+                  [&](int j, int p) { return sXT[p * RS + j]; },
+                  [&](int k, const float (&d)[4]) {
+                    const float4 s = fr[k].v;
+                    const int row = rows.row(base, k);
+                    if (row < P)
+                      store_row(row, make_float4(fmaf(Dc[0], s.x, d[0]), fmaf(Dc[1], s.y, d[1]),
+                                                 fmaf(Dc[2], s.z, d[2]), fmaf(Dc[3], s.w, d[3])));
+                  });
+      }
+    } else {
 #pragma unroll
-    for (int k = 0; k < kMaxPass; ++k) {
-      const int row = base + k * RPP + rsub;
-      if (row < P) {
-        if constexpr (B16) {
-          st8_bf16x4(tileb + (size_t)row * N + col * 4, fr[k].v);
-          continue;
+      for (int k = 0; k < kMaxPass; ++k) {
+        fr[k].v.x *= Dc[0];
+        fr[k].v.y *= Dc[1];
+        fr[k].v.z *= Dc[2];
+        fr[k].v.w *= Dc[3];
+      }
+      // Rows past P read a valid row (results unused): every pass without a branch.
+      const float* xr[kMaxPass];
+#pragma unroll
+      for (int k = 0; k < kMaxPass; ++k) {
+        const int row = rows.row(base, k);
+        xr[k] = sXT + (row < P ? row : P - 1) * RS;
+      }
+      for (int j = 0; j < n; ++j) {
+        const float cj = sCF[j];
+        const float4 t = *reinterpret_cast<const float4*>(&sB[j * N + col * 4]);
+        const float b0 = cj * t.x, b1 = cj * t.y, b2 = cj * t.z, b3 = cj * t.w;
+#pragma unroll
+        for (int k = 0; k < kMaxPass; ++k) {
+          const float xv = xr[k][j];
+          float4& s = fr[k].v;
+          s.x = fmaf(xv, b0, s.x); s.y = fmaf(xv, b1, s.y);
+          s.z = fmaf(xv, b2, s.z); s.w = fmaf(xv, b3, s.w);
         }
-        st16(tile + (size_t)row * N + col * 4, fr[k].v);
-        if (DUAL) {
-          bf16_t* lo = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N + (size_t)row * N + col * 4;
-          uint2 pk;
-          pk.x = pack_bf16x2(fr[k].v.x, fr[k].v.y);
-          pk.y = pack_bf16x2(fr[k].v.z, fr[k].v.w);
-          *reinterpret_cast<uint2*>(lo) = pk;
+      }
+#pragma unroll
+      for (int k = 0; k < kMaxPass; ++k) {
+        const int row = rows.row(base, k);
+        if (row < P) {
+          if constexpr (B16) {
+            st8_bf16x4(tileb + (size_t)row * N + col * 4, fr[k].v);
+            continue;
+          }
+          st16(tile + (size_t)row * N + col * 4, fr[k].v);
+          if (DUAL) {
+            bf16_t* lo = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N + (size_t)row * N + col * 4;
+            uint2 pk;
+            pk.x = pack_bf16x2(fr[k].v.x, fr[k].v.y);
+            pk.y = pack_bf16x2(fr[k].v.z, fr[k].v.w);
+            *reinterpret_cast<uint2*>(lo) = pk;
+          }
         }
       }
     }
@@ -215,10 +250,11 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   if (tid == 0) a.ptr[bh] = make_int4(ring_slot(head, n, R), 0, 0, 0);
 }
 
-template <int N, typename Tin, int MODE, bool PCD = false>
+template <int N, typename Tin, int MODE, bool PCD, bool MF>
 static hipError_t flush_one(const FlushArgs& a, int batch, hipStream_t s) {
-  const size_t lds = (size_t)FlushLds(a.R, a.P, N, PCD).total * sizeof(float);
-  auto kern = flush_kernel<N, Tin, MODE, PCD>;
+  const size_t lds =
+      (size_t)FlushLds(a.R, a.P, N, PCD, MF ? fold_buf_floats(N, 4, kMaxPass) : 0).total * sizeof(float);
+  auto kern = flush_kernel<N, Tin, MODE, PCD, MF>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -228,34 +264,44 @@ static hipError_t flush_one(const FlushArgs& a, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The matrix-core fold serves the delta-rule layers (GDN, KDA) and the
+// bf16-stored checkpoint, whose decode kernels fold the same way; the fp32 and
+// dual-precision Mamba-2 checkpoints keep the FMA fold of their fused decode.
 template <int N, typename Tin>
-static hipError_t flush_t(const FlushArgs& a, int batch, int mode, hipStream_t s) {
+static hipError_t flush_t(const FlushArgs& a, int batch, int mode, bool delta, hipStream_t s) {
   switch (mode) {
-    case kCkptF32: return flush_one<N, Tin, kCkptF32>(a, batch, s);
-    case kCkptDual: return flush_one<N, Tin, kCkptDual>(a, batch, s);
-    case kCkptBf16: return flush_one<N, Tin, kCkptBf16>(a, batch, s);
+    case kCkptF32:
+      if (delta) return flush_one<N, Tin, kCkptF32, false, true>(a, batch, s);
+      return flush_one<N, Tin, kCkptF32, false, false>(a, batch, s);
+    case kCkptDual: return flush_one<N, Tin, kCkptDual, false, false>(a, batch, s);
+    case kCkptBf16: return flush_one<N, Tin, kCkptBf16, false, true>(a, batch, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int N>
-static hipError_t flush_n(const FlushArgs& a, int batch, bool bf16_in, int mode, bool pcd,
+static hipError_t flush_n(const FlushArgs& a, int batch, bool bf16_in, int mode, int kind,
                           hipStream_t s) {
-  if (pcd) {  // per-channel decay: fp32 rows and checkpoint only (Kimi Delta Attention)
+  if (kind == kFoldKda) {  // per-channel decay: fp32 rows and checkpoint only
     if (bf16_in || mode != kCkptF32) return hipErrorInvalidValue;
-    return flush_one<N, float, kCkptF32, true>(a, batch, s);
+    return flush_one<N, float, kCkptF32, true, true>(a, batch, s);
   }
-  return bf16_in ? flush_t<N, bf16_t>(a, batch, mode, s) : flush_t<N, float>(a, batch, mode, s);
+  if (kind == kFoldGdn) {
+    if (bf16_in || mode != kCkptF32) return hipErrorInvalidValue;
+    return flush_t<N, float>(a, batch, mode, true, s);
+  }
+  return bf16_in ? flush_t<N, bf16_t>(a, batch, mode, false, s)
+                 : flush_t<N, float>(a, batch, mode, false, s);
 }
 
-hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode,
-                        bool per_channel, hipStream_t s) {
+hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode, int kind,
+                        hipStream_t s) {
   switch (N) {
-    case 16: return flush_n<16>(a, batch, bf16_in, mode, per_channel, s);
-    case 32: return flush_n<32>(a, batch, bf16_in, mode, per_channel, s);
-    case 64: return flush_n<64>(a, batch, bf16_in, mode, per_channel, s);
-    case 128: return flush_n<128>(a, batch, bf16_in, mode, per_channel, s);
-    case 256: return flush_n<256>(a, batch, bf16_in, mode, per_channel, s);
+    case 16: return flush_n<16>(a, batch, bf16_in, mode, kind, s);
+    case 32: return flush_n<32>(a, batch, bf16_in, mode, kind, s);
+    case 64: return flush_n<64>(a, batch, bf16_in, mode, kind, s);
+    case 128: return flush_n<128>(a, batch, bf16_in, mode, kind, s);
+    case 256: return flush_n<256>(a, batch, bf16_in, mode, kind, s);
     default: return hipErrorInvalidValue;
   }
 }

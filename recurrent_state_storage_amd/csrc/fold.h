@@ -1,0 +1,119 @@
+// The checkpoint fold on the matrix cores.
+//
+// A fold rewrites a P x N tile with the window's F entries (P1, "Tenir le
+// journal plutôt que le solde": the checkpoint is rewritten once the buffer is
+// full):
+//
+//   S[p, n] <- D[n] * S[p, n] + dS[p, n],   dS = sum_{j < F} x_j[p] * a_j[n]
+//
+// with a_j = c_j B_j (Mamba-2, c_j = exp(lam_j) dt_j; GDN: c_j = exp(lam_j),
+// x -> u, B -> k) or the channel-decayed key (KDA, c_j = 1), and D the window's
+// decay (one value, or one per key channel). dS is a real contraction over the
+// window (K = F), so it runs on v_mfma_f32_16x16x4f32 (fp32 in, fp32
+// accumulate), four entries per instruction:
+//
+//   dS^T[n, p] (16 x 16 block) += A[n, j] (16 x 4) * X[j, p] (4 x 16)
+//
+// Lane l supplies A[n = l % 16][j = l / 16] and X[j = l / 16][p = l % 16], and
+// receives dS^T[n = 4 (l / 16) + v][p = l % 16] for v = 0..3: four adjacent
+// columns of one row of dS. Entries past F are zero.
+//
+// The tile itself stays in the layout its coalesced loads deliver (RowMap:
+// each wavefront holds MP * SR consecutive rows, a lane a 16-byte run of
+// columns per row), which is not the accumulator layout. Each wavefront hands
+// its dS blocks to its own lanes through a small LDS buffer (16 rows x 16 CBR
+// columns, padded so writes and reads spread over the banks), in rounds of CBR
+// column blocks, and every lane then finishes its own values with one fused
+// multiply-add: S = fma(D, S, dS). No other wavefront touches the buffer, so
+// the hand-over needs no barrier (a wavefront's LDS accesses complete in
+// order).
+//
+// The flush kernel and every kernel that folds inside a decode call this same
+// routine with the same operands in the same order, so a fold gives the same
+// bits wherever it runs.
+#pragma once
+
+#include "device.h"
+#include "lds.h"
+
+namespace rss {
+
+template <int N, int TPR, int VEC, int MP>
+struct MfmaFold {
+  static constexpr int SR = 64 / TPR;           // rows per pass in a wavefront
+  static constexpr int RW = MP * SR;            // rows of a wavefront per chunk
+  static constexpr int NRB = (RW + 15) / 16;    // 16-row blocks per wavefront per chunk
+  static constexpr int BR = RW < 16 ? RW : 16;  // buffer rows
+  static constexpr int NCB = N / 16;            // 16-column blocks
+  static constexpr int CBR = NCB < 4 ? NCB : 4; // column blocks per hand-over round
+  static constexpr int NRND = NCB / CBR;        // hand-over rounds per row block
+  static constexpr int LD = 16 * CBR + 4;       // buffer row stride, in floats
+  static constexpr int BUF = BR * LD;           // buffer floats per wavefront
+  static_assert(N % 16 == 0 && NCB % CBR == 0, "unsupported N");
+  static_assert(BUF == fold_buf_floats(N, VEC, MP), "LDS layout and fold disagree");
+
+  // Computes dS for the rows of this wavefront's chunk and hands this lane its
+  // share: fin(k, d) is called once per pass k of the lane whose row lies in a
+  // computed row block, with d[v] = dS at column col * VEC + v (fin finishes the
+  // tile values, S = fma(D, S, d), and may store them at once).
+  // R0: first row of the wavefront's chunk (R0 < P); F >= 1 entries. aop(j, n)
+  // and xop(j, p) read the window's operands; they are only called with
+  // 0 <= j < F, 0 <= n < N and R0 <= p < P. buf: this wavefront's BUF floats.
+  template <typename AOp, typename XOp, typename Fin>
+  __device__ static __forceinline__ void run(int R0, int P, int F, float* buf, int lane, int col,
+                                             AOp aop, XOp xop, Fin fin) {
+    const int l15 = lane & 15, lg = lane >> 4;
+    const int lrow = lane / TPR;
+    const int F4 = (F + 3) & ~3;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (R0 + rb * 16 >= P) break;  // uniform: the rest of the chunk lies past the tile
+      const int q = rb * 16 + l15;
+      const bool xrow_ok = q < RW && R0 + q < P;
+#pragma unroll
+      for (int r = 0; r < NRND; ++r) {
+        // dS for column blocks r*CBR .. r*CBR + CBR - 1, entries in ascending
+        // groups of four.
+        f32x4 acc[CBR];
+#pragma unroll
+        for (int c = 0; c < CBR; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < F4; e += 4) {
+          const int j = e + lg;
+          const int jc = j < F ? j : F - 1;              // a valid entry; its value is not used
+          const float xv = (j < F && xrow_ok) ? xop(jc, xrow_ok ? R0 + q : R0) : 0.f;
+#pragma unroll
+          for (int c = 0; c < CBR; ++c) {
+            const float av = j < F ? aop(jc, (r * CBR + c) * 16 + l15) : 0.f;
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv, acc[c], 0, 0, 0);
+          }
+        }
+        // Hand-over: the accumulators into the buffer, then each lane reads the
+        // values of its own rows and columns.
+        if (l15 < BR) {
+#pragma unroll
+          for (int c = 0; c < CBR; ++c)
+            *reinterpret_cast<f32x4*>(buf + l15 * LD + c * 16 + 4 * lg) = acc[c];
+        }
+        const int c0 = col * VEC - r * 16 * CBR;   // this lane's first column in the round
+        if (c0 >= 0 && c0 < 16 * CBR) {
+#pragma unroll
+          for (int k = 0; k < MP; ++k) {
+            const int qk = k * SR + lrow;
+            if ((qk >> 4) != rb) continue;
+            const float* src = buf + (qk - rb * 16) * LD + c0;
+            float d[VEC];
+#pragma unroll
+            for (int v4 = 0; v4 < VEC; v4 += 4) {
+              const f32x4 t = *reinterpret_cast<const f32x4*>(src + v4);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) d[v4 + v] = t[v];
+            }
+            fin(k, d);
+          }
+        }
+      }
+    }
+  }
+};
+
+}  // namespace rss

@@ -25,6 +25,7 @@
 // exp(Lam) * k_t and exp(Lam) * q_t, and the ring term uses the channel-scaled
 // keys k_j * exp(lam_j). The ring keeps log alpha_j as a row per entry.
 #include "device.h"
+#include "fold.h"
 #include "launch.h"
 #include "lds.h"
 
@@ -35,6 +36,7 @@ template <int N, int MP, bool KDA, bool FOLD>
 __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
+  using Rows = RowMap<TPR, MP>;
   constexpr int NV = N / 4;
   constexpr int EPL = N >= 64 ? N / 64 : 1;
   using RS = RowScatter<TPR>;
@@ -45,18 +47,17 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P, R = a.R;
-  const int bh = blockIdx.x;
+  const int bh = xcd_tile(blockIdx.x, gridDim.x);
 
   float* tile = a.ckpt + (size_t)bh * P * N;
-  const int col = tid % TPR, rsub = tid / TPR;
-  const int toff = rsub * N + col * 4;
+  const int col = tid % TPR;
+  const Rows rows(tid);
   Frag<false> fr[MP];
   auto load_chunk = [&](int base) {
 #pragma unroll
     for (int k = 0; k < MP; ++k) {
-      const int r0 = base + k * RPP;
-      if (r0 + RPP <= P) fr[k].v = ld16(tile + r0 * N + toff);
-      else if (r0 + rsub < P) fr[k].v = ld16(tile + r0 * N + toff);
+      const int row = rows.row(base, k);
+      if (row < P) fr[k].v = ld16(tile + row * N + col * 4);
       else fr[k].v = float4{};
     }
   };
@@ -80,7 +81,8 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   // separate flush's.
   const bool do_fold = FOLD && L >= a.fold_min_len && pt.z == 0;
 
-  const GdnLds lay(R, P, N, KDA);
+  using Fold = MfmaFold<N, TPR, 4, MP>;
+  const GdnLds lay(R, P, N, KDA, FOLD ? Fold::BUF : 0);
   float* sK = lds + lay.oK;
   float* sU = lds + lay.oU;
   float* sQ = lds + lay.oQ;
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     if (base > 0) load_chunk(base);
 #pragma unroll
     for (int g8 = 0; g8 < MP; g8 += 8) {
-      if (base + g8 * RPP >= P) break;
+      if (rows.wave_row(base, g8, wave) >= P) break;
       float pk[8], pq[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
       if ((col & RS::WMASK) == 0) {
 #pragma unroll
         for (int m = 0; m < RS::NOUT; ++m) {
-          const int row = base + (g8 + kb1 + m) * RPP + rsub;
+          const int row = rows.row(base, g8 + kb1 + m);
           if (row < P) {
             const float rk_ = (sS[0 * P + row] + sS[2 * P + row]) + (sS[4 * P + row] + sS[6 * P + row]);
             const float rq_ = (sS[1 * P + row] + sS[3 * P + row]) + (sS[5 * P + row] + sS[7 * P + row]);
@@ -269,41 +271,24 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     }
     if constexpr (FOLD) {
       __syncthreads();   // this chunk's new u rows are in LDS (do_fold is uniform)
-      if (do_fold) {
-        // S <- D S + sum_j u_j outer (c_j k_j), j ascending; KDA: D and the
-        // decays per key channel (the keys in LDS are already scaled, c_j = 1).
+      if (do_fold && rows.wave_row(base, 0, wave) < P) {
+        // S <- D S + sum_j u_j outer (c_j k_j) on the matrix cores (the flush's
+        // operands and order); KDA: D per key channel, and the keys in LDS are
+        // already decayed per channel (c_j = 1).
         float Dc[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) Dc[v] = KDA ? sD[col * 4 + v] : sFC[R];
-#pragma unroll
-        for (int k = 0; k < MP; ++k) {
-          fr[k].v.x *= Dc[0];
-          fr[k].v.y *= Dc[1];
-          fr[k].v.z *= Dc[2];
-          fr[k].v.w *= Dc[3];
-        }
-        for (int j = 0; j < L; ++j) {
-          const float cj = KDA ? 1.f : sFC[j];
-          float bv[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) bv[v] = cj * sK[j * N + col * 4 + v];
-#pragma unroll
-          for (int k = 0; k < MP; ++k) {
-            const int r0 = base + k * RPP;
-            if (r0 >= P) break;
-            const int row = r0 + rsub < P ? r0 + rsub : P - 1;   // rows past P: result unused
-            const float xv = sU[j * P + row];
-            fr[k].v.x = fmaf(xv, bv[0], fr[k].v.x);
-            fr[k].v.y = fmaf(xv, bv[1], fr[k].v.y);
-            fr[k].v.z = fmaf(xv, bv[2], fr[k].v.z);
-            fr[k].v.w = fmaf(xv, bv[3], fr[k].v.w);
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < MP; ++k) {
-          const int row = base + k * RPP + rsub;
-          if (row < P) st16(tile + row * N + col * 4, fr[k].v);
-        }
+        Fold::run(rows.wave_row(base, 0, wave), P, L, lds + lay.oW + wave * Fold::BUF, lane, col,
+                  [&](int j, int c) { return (KDA ? 1.f : sFC[j]) * sK[j * N + c]; },
+                  [&](int j, int p) { return sU[j * P + p]; },
+                  [&](int k, const float (&d)[4]) {
+                    const float4 s = fr[k].v;
+                    const int row = rows.row(base, k);
+                    if (row < P)
+                      st16(tile + row * N + col * 4,
+                           make_float4(fmaf(Dc[0], s.x, d[0]), fmaf(Dc[1], s.y, d[1]),
+                                       fmaf(Dc[2], s.z, d[2]), fmaf(Dc[3], s.w, d[3])));
+                  });
       }
     }
   }
@@ -319,6 +304,7 @@ template <int N, int MP, bool KDA>
 __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
   using Geo = TileGeom<N, false>;
   constexpr int TPR = Geo::TPR, RPP = Geo::RPP;
+  using Rows = RowMap<TPR, MP>;
   constexpr int EPL = N >= 64 ? N / 64 : 1;
   using RS = RowScatter<TPR>;
 
@@ -327,17 +313,16 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
-  const int bh = blockIdx.x;
+  const int bh = xcd_tile(blockIdx.x, gridDim.x);
   float* tile = a.S + (size_t)bh * P * N;
-  const int col = tid % TPR, rsub = tid / TPR;
-  const int toff = rsub * N + col * 4;
+  const int col = tid % TPR;
+  const Rows rows(tid);
   Frag<false> fr[MP];
   auto load_chunk = [&](int base) {
 #pragma unroll
     for (int k = 0; k < MP; ++k) {
-      const int r0 = base + k * RPP;
-      if (r0 + RPP <= P) fr[k].v = ld16(tile + r0 * N + toff);
-      else if (r0 + rsub < P) fr[k].v = ld16(tile + r0 * N + toff);
+      const int row = rows.row(base, k);
+      if (row < P) fr[k].v = ld16(tile + row * N + col * 4);
       else fr[k].v = float4{};
     }
   };
@@ -383,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
     const float kq = *skq;
 #pragma unroll
     for (int g8 = 0; g8 < MP; g8 += 8) {
-      if (base + g8 * RPP >= P) break;
+      if (rows.wave_row(base, g8, wave) >= P) break;
       float pk[8], pq[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -397,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
       if ((col & RS::WMASK) == 0) {
 #pragma unroll
         for (int m = 0; m < RS::NOUT; ++m) {
-          const int row = base + (g8 + kb1 + m) * RPP + rsub;
+          const int row = rows.row(base, g8 + kb1 + m);
           if (row < P) {
             const float u = beta * (vin[row] - alpha * pk[m]);
             su[row] = u;
@@ -409,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
     __syncthreads();  // u of every row in this chunk is in LDS
 #pragma unroll
     for (int k = 0; k < MP; ++k) {
-      const int row = base + k * RPP + rsub;
+      const int row = rows.row(base, k);
       if (row < P) {
         const float u = su[row];
         float4 s = fr[k].v;
@@ -425,7 +410,8 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
 
 template <int N, int MP, bool KDA, bool FOLD>
 static hipError_t gdn_replay_one(const GdnArgs& a, int batch, hipStream_t s) {
-  const size_t lds = (size_t)GdnLds(a.R, a.P, N, KDA).total * sizeof(float);
+  const size_t lds =
+      (size_t)GdnLds(a.R, a.P, N, KDA, FOLD ? fold_buf_floats(N, 4, MP) : 0).total * sizeof(float);
   auto kern = gdn_replay_kernel<N, MP, KDA, FOLD>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -438,9 +424,8 @@ static hipError_t gdn_replay_one(const GdnArgs& a, int batch, hipStream_t s) {
 
 template <int N, bool KDA, bool FOLD>
 static hipError_t gdn_replay_f(const GdnArgs& a, int batch, hipStream_t s) {
-  constexpr int RPP = TileGeom<N, false>::RPP;
-  return a.P > 8 * RPP ? gdn_replay_one<N, 16, KDA, FOLD>(a, batch, s)
-                       : gdn_replay_one<N, 8, KDA, FOLD>(a, batch, s);
+  return gdn_passes(a.P, N) == 16 ? gdn_replay_one<N, 16, KDA, FOLD>(a, batch, s)
+                                  : gdn_replay_one<N, 8, KDA, FOLD>(a, batch, s);
 }
 
 template <int N, bool KDA>
@@ -474,8 +459,8 @@ static hipError_t gdn_eager_one(const GdnEagerArgs& a, int batch, hipStream_t s)
 
 template <int N, bool KDA>
 static hipError_t gdn_eager_n(const GdnEagerArgs& a, int batch, hipStream_t s) {
-  constexpr int RPP = TileGeom<N, false>::RPP;
-  return a.P > 8 * RPP ? gdn_eager_one<N, 16, KDA>(a, batch, s) : gdn_eager_one<N, 8, KDA>(a, batch, s);
+  return gdn_passes(a.P, N) == 16 ? gdn_eager_one<N, 16, KDA>(a, batch, s)
+                                  : gdn_eager_one<N, 8, KDA>(a, batch, s);
 }
 
 template <int N>

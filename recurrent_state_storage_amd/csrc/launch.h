@@ -50,8 +50,11 @@ struct FlushArgs {
   int H, P, G, R, min_len;
   const int* min_len_dev;  // [Bt] per-sequence thresholds (overrides min_len), or null
 };
-hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode,
-                        bool per_channel, hipStream_t s);
+// Layer kinds for the fold: Mamba-2, Gated DeltaNet (matrix-core fold), Kimi
+// Delta Attention (matrix-core fold with per-channel decays).
+enum FoldKind { kFoldMamba2 = 0, kFoldGdn = 1, kFoldKda = 2 };
+hipError_t launch_flush(const FlushArgs& a, int batch, int N, bool bf16_in, int mode, int kind,
+                        hipStream_t s);
 
 // ckpt <- S0 (or 0), read copy <- bf16(ckpt), pointers and error word <- 0.
 struct InitArgs {

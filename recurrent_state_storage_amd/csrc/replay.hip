@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "device.h"
+#include "fold.h"
 #include "launch.h"
 #include "lds.h"
 
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   constexpr int NW = NT / 64;                                  // wavefronts per workgroup
   using Geo = TileGeom<N, LOW, NT>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, RPP = Geo::RPP;
+  using Rows = RowMap<TPR, kMaxPass>;
   constexpr int VE = V16<Tin>::VE;
   constexpr int NV = N / VE;                                   // 16-byte vectors per B or C row
   constexpr int kStageC = (NTMAX * NV + NT - 1) / NT;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, P = a.P, G = a.G, R = a.R, nt = a.nt;
-  const int bh = blockIdx.x;
+  const int bh = xcd_tile(blockIdx.x, gridDim.x);
   const int b = bh / H, h = bh - b * H;
   const int hpg = H / G, g = h / hpg;
 
@@ -75,16 +77,14 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   const TileT* tile = static_cast<const TileT*>(LOW ? a.ckpt_lo : static_cast<const void*>(a.ckpt)) +
                       (size_t)bh * P * N;
   const float Ah = a.A[h];
-  const int col = tid % TPR, rsub = tid / TPR;
-  const int toff = rsub * N + col * VEC;
+  const int col = tid % TPR;
+  const Rows rows(tid);
   Frag<LOW> fr[kMaxPass];
   auto load_chunk = [&](int base) {
 #pragma unroll
     for (int k = 0; k < kMaxPass; ++k) {
-      const int r0 = base + k * RPP;
-      const TileT* pk = tile + r0 * N;
-      if (r0 + RPP <= P) fr[k].v = ld16(pk + toff);  // whole pass in range
-      else if (r0 + rsub < P) fr[k].v = ld16(pk + toff);
+      const int row = rows.row(base, k);
+      if (row < P) fr[k].v = ld16(tile + row * N + col * VEC);
       else fr[k].v = decltype(fr[k].v){};
     }
   };
@@ -102,7 +102,9 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   // just before it would. Such a verify frees the committed slots for the new
   // entries, so its window may span up to R + K + 1 positions (all staged in
   // LDS before any slot is overwritten).
-  constexpr int XR = (FOLD && NTMAX > 1) ? NTMAX : 0;   // extra staged rows
+  // LDS is laid out for the nt tokens of this call (nt <= NTMAX).
+  const int NTL = NTMAX == 1 ? 1 : nt;
+  const int XR = (FOLD && NTMAX > 1) ? NTL : 0;         // extra staged rows
   const int RL = R + XR;                                 // staged rows (LDS layout)
   bool do_fold = false, tent = false;
   const int F = a.set_tent ? n0 : L;   // entries a fold takes
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   }
   if (tent && tid == 0) atomicOr(a.err, kDevUncommitted);  // never fold tentative entries
 
-  const ReplayLds lay(RL, P, N, NTMAX, (int)sizeof(Tin), NW, FOLD && LOW);
+  using Fold = MfmaFold<N, TPR, VEC, kMaxPass>;
+  const ReplayLds lay(RL, P, N, NTL, (int)sizeof(Tin), NW, (FOLD && LOW) ? Fold::BUF : 0);
   Tin* sX = reinterpret_cast<Tin*>(lds + lay.oX);
   Tin* sB = reinterpret_cast<Tin*>(lds + lay.oB);
   float* sC = lds + lay.oC;
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
 #pragma unroll
       for (int r = 0; r < kRowsPerLane; ++r) {
         if (r >= nrb) break;
-        if (r * 64 + lane < P) sRing[(wave * NTMAX + i) * P + r * 64 + lane] = share[r];
+        if (r * 64 + lane < P) sRing[(wave * NTL + i) * P + r * 64 + lane] = share[r];
       }
     }
   };
@@ -341,19 +344,6 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
     __syncthreads();
     ring_shares([&](int i, int j) { return sCF[i * RL + j]; });
   }
-  if constexpr (FOLD && LOW) {
-    if (do_fold) {  // the fold's operands widened once: x transposed, and c_j B_j
-      const int F4 = align4(F);                  // entries F..F4-1 are zero padding
-      float* sXT = lds + lay.oXT;
-      float* sCB = lds + lay.oCB;
-      for (int j = 0; j < F4; ++j)
-        for (int p = tid; p < P; p += NT) sXT[p * lay.RS + j] = j < F ? to_f32(sX[j * P + p]) : 0.f;
-      for (int e = tid; e < F4 * N; e += NT) {
-        const int j = e / N;
-        sCB[e] = j < F ? sFC[j] * to_f32(sB[e]) : 0.f;
-      }
-    }
-  }
   __syncthreads();
 
   // 4. Consume the tile: per pass a 16-byte fragment dot C_i, reduce-scattered
@@ -380,56 +370,35 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       if ((col & RS::WMASK) == 0) {
 #pragma unroll
         for (int m = 0; m < RS::NOUT; ++m) {
-          const int row = base + (kbase + m) * RPP + rsub;
+          const int row = rows.row(base, kbase + m);
           if (row < P) {
             float ring;
             if constexpr (NW == 4)
-              ring = (sRing[i * P + row] + sRing[(NTMAX + i) * P + row]) +
-                     (sRing[(2 * NTMAX + i) * P + row] + sRing[(3 * NTMAX + i) * P + row]);
+              ring = (sRing[i * P + row] + sRing[(NTL + i) * P + row]) +
+                     (sRing[(2 * NTL + i) * P + row] + sRing[(3 * NTL + i) * P + row]);
             else
-              ring = sRing[i * P + row] + sRing[(NTMAX + i) * P + row];
+              ring = sRing[i * P + row] + sRing[(NTL + i) * P + row];
             yout[i * xstr + row] = fmaf(sDC[i], part[m], ring);
           }
         }
       }
     }
     if constexpr (FOLD && LOW) {
-      if (do_fold) {  // bf16-stored checkpoint: the same fold in fp32 (the flush's
-                      // order, four entries per step), stored RNE-bf16
+      if (do_fold && rows.wave_row(base, 0, wave) < P) {
+        // bf16-stored checkpoint: widened to fp32, folded on the matrix cores
+        // (the flush's operands and order), stored RNE-bf16
         const float D = sFC[RL];
-        const float* sXT = lds + lay.oXT;
-        const float* sCB = lds + lay.oCB;
-        float sv[kMaxPass][8];
-        const float* xr[kMaxPass];
-        // Every pass is computed (rows past P read a valid row; their results
-        // are never stored), so the entry loop has no branches.
-#pragma unroll
-        for (int k = 0; k < kMaxPass; ++k) {
-#pragma unroll
-          for (int v = 0; v < 8; ++v) sv[k][v] = fr[k].get(v) * D;
-          const int row = base + k * RPP + rsub;
-          xr[k] = sXT + (row < P ? row : P - 1) * lay.RS;
-        }
-        for (int j4 = 0; j4 < F; j4 += 4) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float4 b0 = *reinterpret_cast<const float4*>(&sCB[(j4 + jj) * N + col * 8]);
-            const float4 b1 = *reinterpret_cast<const float4*>(&sCB[(j4 + jj) * N + col * 8 + 4]);
-            const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-            for (int k = 0; k < kMaxPass; ++k) {
-              const float x = xr[k][j4 + jj];
-#pragma unroll
-              for (int v = 0; v < 8; ++v) sv[k][v] = fmaf(x, bv[v], sv[k][v]);
-            }
-          }
-        }
         bf16_t* out = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N;
+        Fold::run(rows.wave_row(base, 0, wave), P, F, lds + lay.oW + wave * Fold::BUF, lane, col,
+                  [&](int j, int c) { return sFC[j] * to_f32(sB[j * N + c]); },
+                  [&](int j, int p) { return to_f32(sX[j * P + p]); },
+                  [&](int k, const float (&d)[8]) {
+                    float o[8];
 #pragma unroll
-        for (int k = 0; k < kMaxPass; ++k) {
-          const int row = base + k * RPP + rsub;
-          if (row < P) st16_bf16x8(out + row * N + col * 8, sv[k]);
-        }
+                    for (int v = 0; v < 8; ++v) o[v] = fmaf(D, fr[k].get(v), d[v]);
+                    const int row = rows.row(base, k);
+                    if (row < P) st16_bf16x8(out + row * N + col * 8, o);
+                  });
       }
     } else if constexpr (FOLD) {
       if (do_fold) {  // S <- exp(Lam) S + sum_j x_j outer (c_j B_j), j ascending
@@ -448,9 +417,9 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
           for (int v = 0; v < 4; ++v) bv[v] = cj * to_f32(sB[j * N + col * 4 + v]);
 #pragma unroll
           for (int k = 0; k < kMaxPass; ++k) {
-            const int r0 = base + k * RPP;
-            if (r0 >= P) break;
-            const int row = r0 + rsub < P ? r0 + rsub : P - 1;   // rows past P: result unused
+            if (rows.wave_row(base, k, wave) >= P) break;
+            const int r = rows.row(base, k);
+            const int row = r < P ? r : P - 1;   // rows past P: result unused
             const float xv = to_f32(sX[j * P + row]);
             fr[k].v.x = fmaf(xv, bv[0], fr[k].v.x);
             fr[k].v.y = fmaf(xv, bv[1], fr[k].v.y);
@@ -461,7 +430,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
         float* out = a.ckpt + (size_t)bh * P * N;
 #pragma unroll
         for (int k = 0; k < kMaxPass; ++k) {
-          const int row = base + k * RPP + rsub;
+          const int row = rows.row(base, k);
           if (row < P) st16(out + row * N + col * 4, fr[k].v);
         }
       }
@@ -476,9 +445,10 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
 
 template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD, int NT = kThreads>
 static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
+  constexpr int VEC = TileGeom<N, LOW, NT>::VEC;
   const size_t lds =
-      (size_t)ReplayLds(a.R + ((FOLD && NTMAX > 1) ? NTMAX : 0), a.P, N, NTMAX, (int)sizeof(Tin), NT / 64,
-                        FOLD && LOW)
+      (size_t)ReplayLds(a.R + ((FOLD && NTMAX > 1) ? a.nt : 0), a.P, N, a.nt, (int)sizeof(Tin), NT / 64,
+                        (FOLD && LOW) ? fold_buf_floats(N, VEC, kMaxPass) : 0)
           .total * sizeof(float);
   auto kern = replay_kernel<N, Tin, LOW, NTMAX, FOLD, NT>;
   if (lds > 64 * 1024) {

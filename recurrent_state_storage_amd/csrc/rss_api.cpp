@@ -40,12 +40,15 @@ size_t layer_lds_bytes(const rss_config* c) {
   if (c->kind == RSS_KIND_MAMBA2) {
     const int tin = c->in_dtype == RSS_DTYPE_BF16 ? 2 : 4;
     upd(rss::ReplayLds(R, P, N, 1, tin, c->read_copy == RSS_COPY_NONE ? 4 : 2).total);
-    if (c->max_draft > 0) upd(rss::ReplayLds(R, P, N, rss::kMaxNew, tin, 4).total);
-    upd(rss::FlushLds(R, P, N, false).total);
+    if (c->max_draft > 0) upd(rss::ReplayLds(R, P, N, c->max_draft + 1, tin, 4).total);
+    // the bf16-stored checkpoint folds on the matrix cores (a decode that would
+    // not fit runs its fold as the flush launch instead, so only the flush counts)
+    const bool mf = c->read_copy == RSS_STATE_BF16;
+    upd(rss::FlushLds(R, P, N, false, mf ? rss::fold_buf_floats(N, 4, rss::kMaxPass) : 0).total);
   } else {
     const bool kda = c->kind == RSS_KIND_KDA;
-    upd(rss::GdnLds(R, P, N, kda).total);
-    upd(rss::FlushLds(R, P, N, kda).total);
+    upd(rss::GdnLds(R, P, N, kda, rss::fold_buf_floats(N, 4, rss::gdn_passes(P, N))).total);
+    upd(rss::FlushLds(R, P, N, kda, rss::fold_buf_floats(N, 4, rss::kMaxPass)).total);
   }
   return m;
 }
@@ -227,7 +230,9 @@ static int32_t decode_fold(rss_layer* l, int32_t min_len, const int32_t* each, c
   bool separate = c.read_copy == RSS_COPY_BF16;
   if (c.read_copy == RSS_STATE_BF16) {
     const int tin = c.in_dtype == RSS_DTYPE_BF16 ? 2 : 4;
-    const size_t lds = (size_t)rss::ReplayLds(c.capacity, c.headdim, c.dstate, 1, tin, 2, true).total * 4;
+    const size_t lds = (size_t)rss::ReplayLds(c.capacity, c.headdim, c.dstate, 1, tin, 2,
+                                              rss::fold_buf_floats(c.dstate, 8, rss::kMaxPass))
+                           .total * 4;
     separate = lds > (size_t)rss::kMaxLdsBytes;
   }
   if (separate) {
@@ -282,8 +287,8 @@ int32_t rss_verify_k_tokens_fold(rss_layer* l, int32_t min_len, int32_t K, const
     // within the call: the window must fit R even before its fold.
     if (c.ngroups != c.nheads && c.capacity < min_len + 2 * K + 1) return RSS_E_CAPACITY;
     const int tin = c.in_dtype == RSS_DTYPE_BF16 ? 2 : 4;
-    const size_t lds = (size_t)rss::ReplayLds(c.capacity + rss::kMaxNew, c.headdim, c.dstate,
-                                              rss::kMaxNew, tin, 4).total * 4;
+    const size_t lds = (size_t)rss::ReplayLds(c.capacity + K + 1, c.headdim, c.dstate,
+                                              K + 1, tin, 4).total * 4;
     if (lds > (size_t)rss::kMaxLdsBytes) return RSS_E_SHAPE;
   }
   int32_t st;
@@ -344,9 +349,10 @@ static int32_t flush_call(rss_layer* l, int32_t min_len, const int32_t* each, vo
   a.min_len = min_len;
   a.min_len_dev = each;
   a.ring_g = c.kind == RSS_KIND_KDA ? l->dev.ring_dl : nullptr;
+  const int kind = c.kind == RSS_KIND_KDA ? rss::kFoldKda
+                   : c.kind == RSS_KIND_GDN ? rss::kFoldGdn : rss::kFoldMamba2;
   return launch_status(rss::launch_flush(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
-                                         c.read_copy, c.kind == RSS_KIND_KDA,
-                                         static_cast<hipStream_t>(stream)));
+                                         c.read_copy, kind, static_cast<hipStream_t>(stream)));
 }
 
 static int32_t delta_decode(rss_layer* l, int32_t kind, int32_t fold_min_len, const float* q,

@@ -19,6 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librss.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "rss.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(_HERE), "include", "rss_calib.h")]
 
 RSS_OK, RSS_E_INVALID, RSS_E_SHAPE, RSS_E_DTYPE, RSS_E_CAPACITY, RSS_E_ORDER, RSS_E_HIP = range(7)
 RSS_DTYPE_F32, RSS_DTYPE_BF16 = 0, 1
@@ -74,6 +75,8 @@ _SIGS = {
                        _I32),
     "rss_eager_verify": ([ctypes.POINTER(rss_config), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
                           _VP, _VP], _I32),
+    "rss_calib_read": ([_VP, ctypes.c_size_t, _VP, _I32, _VP], _I32),
+    "rss_calib_copy": ([_VP, _VP, ctypes.c_size_t, _I32, _VP], _I32),
 }
 
 _lib = None
@@ -101,9 +104,11 @@ def library() -> ctypes.CDLL:
 
 
 def declared_symbols() -> list:
-    """Every function the public header declares."""
-    with open(HEADER) as f:
-        text = f.read()
+    """Every function the public headers declare."""
+    text = ""
+    for h in HEADERS:
+        with open(h) as f:
+            text += f.read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*(rss_[a-z0-9_]+)\s*\(",
                                  text, flags=re.M)))
 
@@ -435,3 +440,29 @@ def rss_kda_decode_flush_step(layer: ReplayLayer, min_len: int, q, k, v, beta, a
     args = _delta_args(layer, q, k, v, beta, alpha, o, True)
     _check(library().rss_kda_decode_flush_step(layer.handle, int(min_len), *args, _stream(stream)),
            "rss_kda_decode_flush_step")
+
+
+# ---- bandwidth calibration kernels (include/rss_calib.h) ----------------------
+def rss_calib_read(src, sink, blocks: int = 0, stream=None) -> None:
+    """Stream-read the bytes of the contiguous device tensor `src`; `sink` is a
+    device float32 tensor of at least one element the kernel may write."""
+    if not (isinstance(src, torch.Tensor) and src.is_cuda and src.is_contiguous()):
+        raise ValueError("src: expected a contiguous device tensor")
+    if not (isinstance(sink, torch.Tensor) and sink.is_cuda and sink.dtype == torch.float32):
+        raise ValueError("sink: expected a device float32 tensor")
+    nbytes = src.numel() * src.element_size()
+    _check(library().rss_calib_read(src.data_ptr(), nbytes, sink.data_ptr(), int(blocks), _stream(stream)),
+           "rss_calib_read")
+
+
+def rss_calib_copy(src, dst, blocks: int = 0, stream=None) -> None:
+    """Copy the bytes of the contiguous device tensor `src` into `dst` (same
+    byte size, no overlap)."""
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{n}: expected a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst: byte size differs from src")
+    _check(library().rss_calib_copy(src.data_ptr(), dst.data_ptr(), nbytes, int(blocks), _stream(stream)),
+           "rss_calib_copy")

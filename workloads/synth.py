@@ -15,6 +15,12 @@ step or round can be regenerated on its own, in any order:
   stream 5, step t    gated-DeltaNet inputs (see ``gdn_step_inputs``)
   stream 6, step t    Kimi-Delta-Attention inputs (see ``kda_step_inputs``)
 
+Long runs whose inputs would take minutes to draw on the host (200 speculative
+rounds at batch 512 are 42 GB of inputs) draw them on the device instead, with
+torch's counter-based (Philox) generator seeded per round or step (streams 7-9,
+``device_*`` below): the same distributions, rounded to the same storage types.
+A consumer on the host (the oracle's tests) copies back the exact bits it needs.
+
 Inputs stored as bf16 are rounded from the float32 draw with round-to-nearest-
 even; the returned float32 arrays are the exact values of those bf16 numbers, so
 an fp64 consumer sees the very bits the device reads.
@@ -158,3 +164,48 @@ def kda_step_inputs(wl: Workload, t: int) -> dict:
         "beta": (1.0 / (1.0 + np.exp(-zb))).astype(np.float32),
         "alpha": np.exp(-_softplus64(za)).astype(np.float32),
     }
+
+
+# ---- device-side draws (torch, Philox), for long runs ---------------------------
+def _device_gen(seed: int, stream: int, idx: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1_000_003 + stream) * 1_000_003 + idx)
+    return g
+
+
+def device_draft_inputs(wl: Workload, r: int, device) -> dict:
+    """Speculative round r drawn on `device` (stream 7): x (Bt,K+1,H,P), B and
+    C (Bt,K+1,G,N) ~ N(0,1) drawn as float32 and rounded to the storage dtype
+    (bf16: round to nearest even), dt (Bt,K+1,H) = softplus(z - 2) with
+    z ~ N(0,1), computed in float32. Draw order: x, B, C, z."""
+    import torch
+    g = _device_gen(wl.seed, 7, r, device)
+    Bt, H, P, N, G, T = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.draft + 1
+    st = torch.bfloat16 if wl.in_dtype == "bf16" else torch.float32
+    out = {}
+    for k, shape in (("x", (Bt, T, H, P)), ("B", (Bt, T, G, N)), ("C", (Bt, T, G, N))):
+        out[k] = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(st)
+    z = torch.randn((Bt, T, H), generator=g, device=device, dtype=torch.float32)
+    out["dt"] = torch.nn.functional.softplus(z - 2.0)
+    return out
+
+
+def device_delta_inputs(wl: Workload, t: int, device) -> dict:
+    """Gated-DeltaNet (stream 8) or Kimi-Delta-Attention (stream 9) inputs of
+    step t drawn on `device`, float32, with the recipe of ``gdn_step_inputs`` /
+    ``kda_step_inputs`` evaluated in float32: q, k unit-L2-normalised N(0,1)
+    draws, v ~ N(0,1), beta = sigmoid(N(0,1)), alpha = exp(-softplus(N(0,1)))
+    (per key channel for KDA). Draw order: q, k, v, beta's normal, alpha's."""
+    import torch
+    kda = wl.kind == "kda"
+    g = _device_gen(wl.seed, 9 if kda else 8, t, device)
+    Bt, H, dk, dv = wl.batch, wl.nheads, wl.dstate, wl.headdim
+    f = torch.float32
+    q = torch.randn((Bt, H, dk), generator=g, device=device, dtype=f)
+    k = torch.randn((Bt, H, dk), generator=g, device=device, dtype=f)
+    v = torch.randn((Bt, H, dv), generator=g, device=device, dtype=f)
+    zb = torch.randn((Bt, H), generator=g, device=device, dtype=f)
+    za = torch.randn((Bt, H, dk) if kda else (Bt, H), generator=g, device=device, dtype=f)
+    return {"q": q / q.norm(dim=-1, keepdim=True), "k": k / k.norm(dim=-1, keepdim=True), "v": v,
+            "beta": torch.sigmoid(zb), "alpha": torch.exp(-torch.nn.functional.softplus(za))}
