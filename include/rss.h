@@ -52,7 +52,7 @@
  *    of which one gfx950 workgroup may hold 160 KiB: a configuration whose
  *    kernels would need more is refused with RSS_E_SHAPE. Only
  *    the largest shapes reach it: at P = N = 256, fp32 x/B/C with K_max > 0
- *    allow R <= 58 and a KDA layer R <= 49; bf16 x/B/C and GDN allow R = 64.
+ *    allow R <= 58 and a KDA layer R <= 48; bf16 x/B/C and GDN allow R = 64.
  */
 #ifndef RSS_H_
 #define RSS_H_

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     return;
   }
   const FlushLds lay(R, P, N, PCD, MF ? Fold::BUF : 0);
-  const int RS = lay.RS;
+  const int RS = lay.RS, LDB = lay.LDB, LDX = lay.LDX;
+  const int F4 = align4(n);   // the matrix-core fold reads entries in groups of four
   float* sXT = lds + lay.oXT;
   float* sB = lds + lay.oB;
   float* sCF = lds + lay.oCF;
@@ -119,15 +120,33 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
 #pragma unroll
     for (int m = 0; m < kFlushStage; ++m) {
       const int q = q0 + m * kThreads + tid;
-      if (q < totBV) st_lds_f32(sB + q * VE, vb[m]);
+      if (q < totBV) { const int j = q / NV; st_lds_f32(sB + j * LDB + (q - j * NV) * VE, vb[m]); }
     }
   }
-  // x: thread -> (entry j = tid mod JP, column block tid / JP), JP = 2^ceil(log2 n),
-  // so consecutive lanes write consecutive entries of a transposed row.
-  const int lgJP = n > 1 ? 32 - __clz(n - 1) : 0;
-  const int JP = 1 << lgJP;
-  const int jx = tid & (JP - 1);
-  if ((P % VE) == 0) {
+  if constexpr (MF) {
+    // x one entry per row; the rows from n up to the next multiple of four
+    // (read by the fold's last group of entries) are zero, in x and in B.
+    if ((P % VE) == 0) {
+      const int PV = P / VE;
+      for (int q = tid; q < n * PV; q += kThreads) {
+        const int j = q / PV, c = q - j * PV;
+        st_lds_f32(sXT + j * LDX + c * VE, ldv<Tin>(xrow(j) + c * VE));
+      }
+    } else {
+      for (int q = tid; q < n * P; q += kThreads) {
+        const int j = q / P, p = q - j * P;
+        sXT[j * LDX + p] = to_f32(xrow(j)[p]);
+      }
+    }
+    for (int q = tid; q < (F4 - n) * LDX; q += kThreads) sXT[n * LDX + q] = 0.f;
+    for (int q = tid; q < (F4 - n) * LDB; q += kThreads) sB[n * LDB + q] = 0.f;
+  } else if ((P % VE) == 0) {
+    // x: thread -> (entry j = tid mod JP, column block tid / JP), JP =
+    // 2^ceil(log2 n), so consecutive lanes write consecutive entries of a
+    // transposed row.
+    const int lgJP = n > 1 ? 32 - __clz(n - 1) : 0;
+    const int JP = 1 << lgJP;
+    const int jx = tid & (JP - 1);
     const int PV = P / VE;
     for (int c = tid >> lgJP; c < PV; c += kThreads >> lgJP) {
       if (jx < n) {
@@ -139,6 +158,9 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
       }
     }
   } else {
+    const int lgJP = n > 1 ? 32 - __clz(n - 1) : 0;
+    const int JP = 1 << lgJP;
+    const int jx = tid & (JP - 1);
     for (int p = tid >> lgJP; p < P; p += kThreads >> lgJP)
       if (jx < n) sXT[p * RS + jx] = to_f32(xrow(jx)[p]);
   }
@@ -146,16 +168,23 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     const float u = lane < n ? dl.y : 0.f;
     const float lam = wave_suffix_excl(u, lane);
     if (lane < n) sCF[lane] = expf(lam) * dl.x;
-    if (lane == 0) sCF[R] = expf(lam + u);
+    if (lane == 0) sCF[RS] = expf(lam + u);
   }
   __syncthreads();
+  if constexpr (MF && !PCD) {  // the fold's A operand: c_j B_j, scaled in place
+    for (int q = tid; q < n * N; q += kThreads) {
+      const int j = q / N, c = q - j * N;
+      sB[j * LDB + c] *= sCF[j];
+    }
+    __syncthreads();
+  }
   if constexpr (PCD) {
     // Channel c (one thread each): lam_j[c] from the newest entry back; the
     // decay goes into the staged key rows, exp(Lam[c]) scales tile column c.
     if (tid < N) {
       float acc = 0.f;
       for (int j = n - 1; j >= 0; --j) {
-        sB[j * N + tid] *= expf(acc);
+        sB[j * LDB + tid] *= expf(acc);
         acc += sG[j * N + tid];
       }
       sDc[tid] = expf(acc);
@@ -163,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (tid < n) sCF[tid] = 1.f;
     __syncthreads();
   }
-  const float D = PCD ? 1.f : sCF[R];
+  const float D = PCD ? 1.f : sCF[RS];
   float Dc[4] = {D, D, D, D};
   if constexpr (PCD) {
 #pragma unroll
@@ -189,9 +218,9 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (base > 0) load_chunk(base);
     if constexpr (MF) {
       if (rows.wave_row(base, 0, wave) < P) {
-        Fold::run(rows.wave_row(base, 0, wave), P, n, lds + lay.oW + wave * Fold::BUF, lane, col,
-                  [&](int j, int c) { return sCF[j] * sB[j * N + c]; },
-                  [&](int j, int p) { return sXT[p * RS + j]; },
+        Fold::run(rows.wave_row(base, 0, wave), P, F4, lds + lay.oW + wave * Fold::BUF, lane, col,
+                  [&](int j, int c) { return sB[j * LDB + c]; },
+                  [&](int j, int p) { return sXT[j * LDX + p]; },
                   [&](int k, const float (&d)[4]) {
                     const float4 s = fr[k].v;
                     const int row = rows.row(base, k);
@@ -217,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
       }
       for (int j = 0; j < n; ++j) {
         const float cj = sCF[j];
-        const float4 t = *reinterpret_cast<const float4*>(&sB[j * N + col * 4]);
+        const float4 t = *reinterpret_cast<const float4*>(&sB[j * LDB + col * 4]);
         const float b0 = cj * t.x, b1 = cj * t.y, b2 = cj * t.z, b3 = cj * t.w;
 #pragma unroll
         for (int k = 0; k < kMaxPass; ++k) {

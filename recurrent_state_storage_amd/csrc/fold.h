@@ -21,9 +21,10 @@
 // The tile itself stays in the layout its coalesced loads deliver (RowMap:
 // each wavefront holds MP * SR consecutive rows, a lane a 16-byte run of
 // columns per row), which is not the accumulator layout. Each wavefront hands
-// its dS blocks to its own lanes through a small LDS buffer (16 rows x 16 CBR
-// columns, padded so writes and reads spread over the banks), in rounds of CBR
-// column blocks, and every lane then finishes its own values with one fused
+// its dS blocks to its own lanes through a small LDS buffer (HR = 8 rows of N
+// columns, 4 rows at N = 256, padded so writes and reads spread over the
+// banks), HR rows at a time, and every lane then finishes its own values with
+// one fused
 // multiply-add: S = fma(D, S, dS). No other wavefront touches the buffer, so
 // the hand-over needs no barrier (a wavefront's LDS accesses complete in
 // order).
@@ -43,73 +44,66 @@ struct MfmaFold {
   static constexpr int SR = 64 / TPR;           // rows per pass in a wavefront
   static constexpr int RW = MP * SR;            // rows of a wavefront per chunk
   static constexpr int NRB = (RW + 15) / 16;    // 16-row blocks per wavefront per chunk
-  static constexpr int BR = RW < 16 ? RW : 16;  // buffer rows
   static constexpr int NCB = N / 16;            // 16-column blocks
-  static constexpr int CBR = NCB < 4 ? NCB : 4; // column blocks per hand-over round
-  static constexpr int NRND = NCB / CBR;        // hand-over rounds per row block
-  static constexpr int LD = 16 * CBR + 4;       // buffer row stride, in floats
-  static constexpr int BUF = BR * LD;           // buffer floats per wavefront
-  static_assert(N % 16 == 0 && NCB % CBR == 0, "unsupported N");
+  static constexpr int HR = N >= 256 ? 4 : 8;   // rows per hand-over round
+  static constexpr int LD = N + 4;              // buffer row stride, in floats
+  static constexpr int BUF = HR * LD;           // buffer floats per wavefront
+  static_assert(N % 16 == 0 && RW % HR == 0, "unsupported tile geometry");
   static_assert(BUF == fold_buf_floats(N, VEC, MP), "LDS layout and fold disagree");
 
   // Computes dS for the rows of this wavefront's chunk and hands this lane its
   // share: fin(k, d) is called once per pass k of the lane whose row lies in a
   // computed row block, with d[v] = dS at column col * VEC + v (fin finishes the
   // tile values, S = fma(D, S, d), and may store them at once).
-  // R0: first row of the wavefront's chunk (R0 < P); F >= 1 entries. aop(j, n)
-  // and xop(j, p) read the window's operands; they are only called with
-  // 0 <= j < F, 0 <= n < N and R0 <= p < P. buf: this wavefront's BUF floats.
+  // R0: first row of the wavefront's chunk (R0 < P). F4: the entry count
+  // rounded up to a multiple of 4. aop(j, n) and xop(j, p) read the window's
+  // operands for 0 <= j < F4 (entries at or past the true count must read as
+  // zero), 0 <= n < N and R0 <= p < P. buf: this wavefront's BUF floats.
   template <typename AOp, typename XOp, typename Fin>
-  __device__ static __forceinline__ void run(int R0, int P, int F, float* buf, int lane, int col,
+  __device__ static __forceinline__ void run(int R0, int P, int F4, float* buf, int lane, int col,
                                              AOp aop, XOp xop, Fin fin) {
     const int l15 = lane & 15, lg = lane >> 4;
     const int lrow = lane / TPR;
-    const int F4 = (F + 3) & ~3;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       if (R0 + rb * 16 >= P) break;  // uniform: the rest of the chunk lies past the tile
-      const int q = rb * 16 + l15;
-      const bool xrow_ok = q < RW && R0 + q < P;
+      // rows past the tile (or past this wavefront's rows) read a valid row;
+      // their results are never handed over
+      const int pr = R0 + rb * 16 + l15 < P ? R0 + rb * 16 + l15 : P - 1;
+      f32x4 acc[NCB];
 #pragma unroll
-      for (int r = 0; r < NRND; ++r) {
-        // dS for column blocks r*CBR .. r*CBR + CBR - 1, entries in ascending
-        // groups of four.
-        f32x4 acc[CBR];
+      for (int c = 0; c < NCB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < F4; e += 4) {
+        const int j = e + lg;
+        const float xv = xop(j, pr);
 #pragma unroll
-        for (int c = 0; c < CBR; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int e = 0; e < F4; e += 4) {
-          const int j = e + lg;
-          const int jc = j < F ? j : F - 1;              // a valid entry; its value is not used
-          const float xv = (j < F && xrow_ok) ? xop(jc, xrow_ok ? R0 + q : R0) : 0.f;
+        for (int c = 0; c < NCB; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop(j, c * 16 + l15), xv, acc[c], 0, 0, 0);
+      }
+      // Hand-over in rounds of HR rows: the accumulator rows of the round into
+      // the buffer, then every lane whose pass falls in those rows reads its
+      // own columns.
 #pragma unroll
-          for (int c = 0; c < CBR; ++c) {
-            const float av = j < F ? aop(jc, (r * CBR + c) * 16 + l15) : 0.f;
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv, acc[c], 0, 0, 0);
-          }
+      for (int h = 0; h < 16 / HR; ++h) {
+        if (rb * 16 + h * HR >= RW) break;
+        if (l15 / HR == h) {
+#pragma unroll
+          for (int c = 0; c < NCB; ++c)
+            *reinterpret_cast<f32x4*>(buf + (l15 % HR) * LD + c * 16 + 4 * lg) = acc[c];
         }
-        // Hand-over: the accumulators into the buffer, then each lane reads the
-        // values of its own rows and columns.
-        if (l15 < BR) {
 #pragma unroll
-          for (int c = 0; c < CBR; ++c)
-            *reinterpret_cast<f32x4*>(buf + l15 * LD + c * 16 + 4 * lg) = acc[c];
-        }
-        const int c0 = col * VEC - r * 16 * CBR;   // this lane's first column in the round
-        if (c0 >= 0 && c0 < 16 * CBR) {
+        for (int k = 0; k < MP; ++k) {
+          const int qk = k * SR + lrow;
+          if (qk / HR != rb * (16 / HR) + h) continue;
+          const float* src = buf + (qk % HR) * LD + col * VEC;
+          float d[VEC];
 #pragma unroll
-          for (int k = 0; k < MP; ++k) {
-            const int qk = k * SR + lrow;
-            if ((qk >> 4) != rb) continue;
-            const float* src = buf + (qk - rb * 16) * LD + c0;
-            float d[VEC];
+          for (int v4 = 0; v4 < VEC; v4 += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(src + v4);
 #pragma unroll
-            for (int v4 = 0; v4 < VEC; v4 += 4) {
-              const f32x4 t = *reinterpret_cast<const f32x4*>(src + v4);
-#pragma unroll
-              for (int v = 0; v < 4; ++v) d[v4 + v] = t[v];
-            }
-            fin(k, d);
+            for (int v = 0; v < 4; ++v) d[v4 + v] = t[v];
           }
+          fin(k, d);
         }
       }
     }

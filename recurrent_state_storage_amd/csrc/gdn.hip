@@ -152,11 +152,16 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
       const float g = lane < n0 ? dl.y : logf(alpha);
       const float u2 = lane < L ? g : 0.f;
       const float lam2 = wave_suffix_excl(u2, lane);
-      if (lane < L) sFC[lane] = expf(lam2) * 1.f;
-      if (lane == 0) sFC[R] = expf(lam2 + u2);
+      if (lane < lay.RS) sFC[lane] = lane < L ? expf(lam2) * 1.f : 0.f;
+      if (lane == 0) sFC[lay.RS] = expf(lam2 + u2);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
+  if (FOLD && do_fold) {  // the fold reads entries in groups of four: rows past the window are zero
+    const int F4 = align4(L);
+    for (int q = tid; q < (F4 - L) * N; q += kThreads) sK[L * N + q] = 0.f;
+    for (int q = tid; q < (F4 - L) * P; q += kThreads) sU[L * P + q] = 0.f;
+  }
   __syncthreads();
   // the new entry's (1, log alpha) after the wait: a store before it would be waited for too
   if (!KDA && tid == 0) rdl[ring_slot(head, n0, R)] = make_float2(1.f, logf(alpha));
@@ -277,9 +282,9 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
         // already decayed per channel (c_j = 1).
         float Dc[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) Dc[v] = KDA ? sD[col * 4 + v] : sFC[R];
-        Fold::run(rows.wave_row(base, 0, wave), P, L, lds + lay.oW + wave * Fold::BUF, lane, col,
-                  [&](int j, int c) { return (KDA ? 1.f : sFC[j]) * sK[j * N + c]; },
+        for (int v = 0; v < 4; ++v) Dc[v] = KDA ? sD[col * 4 + v] : sFC[lay.RS];
+        Fold::run(rows.wave_row(base, 0, wave), P, align4(L), lds + lay.oW + wave * Fold::BUF, lane,
+                  col, [&](int j, int c) { return KDA ? sK[j * N + c] : sFC[j] * sK[j * N + c]; },
                   [&](int j, int p) { return sU[j * P + p]; },
                   [&](int k, const float (&d)[4]) {
                     const float4 s = fr[k].v;
@@ -422,10 +427,12 @@ static hipError_t gdn_replay_one(const GdnArgs& a, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
+// A folding launch holds 8 passes per chunk: the fold's accumulators need the
+// registers the second half of a 16-pass chunk would take.
 template <int N, bool KDA, bool FOLD>
 static hipError_t gdn_replay_f(const GdnArgs& a, int batch, hipStream_t s) {
-  return gdn_passes(a.P, N) == 16 ? gdn_replay_one<N, 16, KDA, FOLD>(a, batch, s)
-                                  : gdn_replay_one<N, 8, KDA, FOLD>(a, batch, s);
+  return gdn_passes(a.P, N) == 16 && !FOLD ? gdn_replay_one<N, 16, KDA, FOLD>(a, batch, s)
+                                           : gdn_replay_one<N, 8, KDA, FOLD>(a, batch, s);
 }
 
 template <int N, bool KDA>

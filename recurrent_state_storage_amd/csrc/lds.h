@@ -10,51 +10,63 @@ namespace rss {
 constexpr int kMaxLdsBytes = 160 * 1024;  // LDS one gfx950 workgroup may allocate
 
 // Floats of the per-wavefront hand-over buffer of the matrix-core fold
-// (fold.h) for an N-column tile held as VEC columns per lane and MP passes:
-// up to 16 rows of 16 * min(N / 16, 4) columns, padded by 4 floats per row.
+// (fold.h) for an N-column tile: 8 rows (4 at N = 256) of N columns, padded by
+// 4 floats per row. (VEC and MP, the tile geometry, do not change it.)
 __host__ __device__ constexpr int fold_buf_floats(int N, int VEC, int MP) {
-  const int rw = MP * (64 / (N / VEC));
-  const int ncb = N / 16;
-  return (rw < 16 ? rw : 16) * (16 * (ncb < 4 ? ncb : 4) + 4);
+  return (VEC > 0 && MP > 0) ? (N >= 256 ? 4 : 8) * (N + 4) : 0;
 }
+
+// Row stride (floats) of a matrix-core fold operand staged in LDS: at least n,
+// and 16 more than a multiple of 64, so the four window entries one
+// instruction reads (one per group of 16 lanes) fall on different banks.
+__host__ __device__ constexpr int fold_ld(int n) { return n + ((16 - n) & 63); }
 
 // Dynamic LDS layout of the replay kernel, in 4-byte words. The window's x and
 // B rows are kept raw (input dtype), exactly as the direct global->LDS loads
-// deliver them; everything else is fp32.
+// deliver them; everything else is fp32. With a matrix-core fold (fold_buf >
+// 0) the window rows are allocated in multiples of four (the fold reads entries
+// in groups of four; the rows past the window are zeroed).
 struct ReplayLds {
-  int oX, oB, oC, oCF, oDC, oRing, oFC, oW, total;
+  int RA, oX, oB, oC, oCF, oDC, oRing, oFC, FD, oW, total;
   // fold_buf: floats of the matrix-core fold's hand-over buffer per wavefront
   // (0 when the kernel does not fold on the matrix cores).
   __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes, int nw,
                                 int fold_buf = 0) {
-    oX = 0;                                            // raw window x [R][P]
-    oB = align4((R * P * tin_bytes + 3) / 4);          // raw window B [R][N]
-    oC = oB + align4((R * N * tin_bytes + 3) / 4);     // new tokens' C [ntmax][N]
+    RA = fold_buf > 0 ? align4(R) : R;                 // allocated window rows
+    oX = 0;                                            // raw window x [RA][P]
+    oB = align4((RA * P * tin_bytes + 3) / 4);         // raw window B [RA][N]
+    oC = oB + align4((RA * N * tin_bytes + 3) / 4);    // new tokens' C [ntmax][N]
     oCF = oC + ntmax * N;                              // exp(lam) * dt [ntmax][R]
     oDC = oCF + ntmax * R;                             // exp(Lam) [ntmax]
     oRing = align4(oDC + ntmax);                       // ring shares [nw][ntmax][P]
-    oFC = oRing + nw * ntmax * P;                      // fused fold: c_j [R], then exp(Lam)
-    oW = align4(oFC + R + 1);                          // fold hand-over buffers [nw][fold_buf]
+    oFC = oRing + nw * ntmax * P;                      // fused fold: c_j [align4(R)], then exp(Lam)
+    FD = align4(R);                                    // index of exp(Lam) in the fold coefficients
+    oW = align4(oFC + FD + 1);                         // fold hand-over buffers [nw][fold_buf]
     total = oW + nw * fold_buf;
   }
 };
 
-// Dynamic LDS layout of the flush kernel, in floats. x is stored transposed
-// (row p holds entries j = 0..R-1 contiguously, rows padded to a multiple of 4
-// words), so the window's x values of one row sit together.
+// Dynamic LDS layout of the flush kernel, in floats. For the FMA fold, x is
+// stored transposed (row p holds entries j = 0..R-1 contiguously, rows padded
+// to a multiple of 4 words), so the window's x values of one row sit together;
+// for the matrix-core fold (fold_buf > 0) x and the scaled B rows are stored
+// one entry per row with fold_ld strides, the rows past the window zeroed.
 struct FlushLds {
-  int RS, oXT, oB, oCF, oDc, oG, oW, total;
+  int RS, LDX, LDB, oXT, oB, oCF, oDc, oG, oW, total;
   // fold_buf: floats of the matrix-core fold's hand-over buffer per wavefront
   // (0: the fold runs on the VALU). The per-channel log-decay rows are dead
   // once the decay walk has scaled the key rows, so the buffers share them.
   __host__ __device__ FlushLds(int R, int P, int N, bool pcd, int fold_buf = 0) {
     RS = align4(R);
-    oXT = 0;                 // x transposed  [P][RS]
-    oB = P * RS;             // window B rows [R][N]
-    oCF = oB + R * N;        // c_j = exp(lam_j) dt_j [R], then exp(Lam)
-    oDc = align4(oCF + R + 1);       // per-channel exp(Lam[n]) [N]
-    oG = align4(oDc + (pcd ? N : 0));  // per-channel log-decay rows [R][N]
-    oW = oG;                         // fold hand-over buffers [4 wavefronts][fold_buf]
+    const bool mf = fold_buf > 0;
+    LDX = mf ? fold_ld(P) : 0;
+    LDB = mf ? fold_ld(N) : N;
+    oXT = 0;                                   // x: transposed [P][RS], or [RS][LDX]
+    oB = mf ? RS * LDX : P * RS;               // window B rows [RS][LDB]
+    oCF = oB + RS * LDB;                       // c_j = exp(lam_j) dt_j [RS], then exp(Lam) at [RS]
+    oDc = align4(oCF + RS + 1);                // per-channel exp(Lam[n]) [N]
+    oG = align4(oDc + (pcd ? N : 0));          // per-channel log-decay rows [R][N]
+    oW = oG;                                   // fold hand-over buffers [4 wavefronts][fold_buf]
     const int g = pcd ? R * N : 0, w = kWaves * fold_buf;
     total = oG + (g > w ? g : w);
   }
@@ -66,19 +78,22 @@ __host__ __device__ constexpr int gdn_passes(int P, int N) { return P > 8 * (102
 
 // Dynamic LDS of the GDN / KDA replay kernel, in floats.
 struct GdnLds {
-  int oK, oU, oQ, oCF, oS, oD, oFC, oG, oW, total;
+  int RS, oK, oU, oQ, oCF, oS, oD, oFC, oG, oW, total;
   // fold_buf: floats of the matrix-core fold's hand-over buffer per wavefront
-  // (0 for a launch that does not fold). KDA's log-gate rows are dead once the
-  // decay walk has scaled the key rows, so the buffers share them.
+  // (0 for a launch that does not fold). The window rows are allocated in
+  // multiples of four (the fold reads entries in groups of four; the rows past
+  // the window are zeroed). KDA's log-gate rows are dead once the decay walk
+  // has scaled the key rows, so the buffers share them.
   __host__ __device__ GdnLds(int R, int P, int N, bool kda, int fold_buf = 0) {
-    oK = 0;                   // window k rows [R][N] (row n0 = k_t); KDA: scaled in place
-    oU = R * N;               // window u rows [R][P]
-    oQ = oU + R * P;          // q_t [N]
+    RS = align4(R);
+    oK = 0;                   // window k rows [RS][N] (row n0 = k_t); KDA: scaled in place
+    oU = RS * N;              // window u rows [RS][P]
+    oQ = oU + RS * P;         // q_t [N]
     oCF = oQ + N;             // exp(lam_j) [R], then exp(Lam), k_t . q_t
     oS = align4(oCF + R + 2); // shares [4 waves][2][P]: sum_j w u_j for z = k_t, q_t
     oD = oS + 8 * P;          // KDA: exp(Lam[n]) [N]
-    oFC = oD + (kda ? N : 0); // fused fold (GDN): c_j [R], then exp(Lam)
-    oG = align4(oFC + R + 1); // KDA: committed log-gate rows [R][N]
+    oFC = oD + (kda ? N : 0); // fused fold (GDN): c_j [RS], then exp(Lam) at [RS]
+    oG = align4(oFC + RS + 1); // KDA: committed log-gate rows [R][N]
     oW = oG;                  // fold hand-over buffers [4 wavefronts][fold_buf]
     const int g = kda ? R * N : 0, w = kWaves * fold_buf;
     total = oG + (g > w ? g : w);

@@ -247,15 +247,22 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       if (lane < L) sCF[i * RL + lane] = lane <= ti ? expf(lam) * dtj : 0.f;
       if (lane == 0) sDC[i] = expf(lam + u);
     }
-    if constexpr (FOLD) {  // the fold's coefficients: window entries 0..F-1
+    if constexpr (FOLD) {  // the fold's coefficients: window entries 0..F-1 (zero past them)
       const float u = lane < F ? lj : 0.f;
       const float lam = wave_suffix_excl(u, lane);
-      if (lane < RL) sFC[lane] = lane < F ? expf(lam) * dtj : 0.f;
-      if (lane == 0) sFC[RL] = expf(lam + u);
+      if (lane < lay.FD) sFC[lane] = lane < F ? expf(lam) * dtj : 0.f;
+      if (lane == 0) sFC[lay.FD] = expf(lam + u);
     }
     dl_new = make_float2(dtj, lj);
   }
   __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads have landed
+  if constexpr (FOLD && LOW) {
+    if (do_fold) {  // the fold reads entries in groups of four: rows past the window are zero
+      const int F4 = align4(F);
+      for (int q = tid; q < (F4 - F) * P; q += NT) sX[F * P + q] = Tin(0);
+      for (int q = tid; q < (F4 - F) * N; q += NT) sB[F * N + q] = Tin(0);
+    }
+  }
   __syncthreads();
   // The new tokens' (dt, l) into the ring, only now: on this target a store
   // counts in the same counter as the loads, so a store issued before the wait
@@ -387,9 +394,9 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       if (do_fold && rows.wave_row(base, 0, wave) < P) {
         // bf16-stored checkpoint: widened to fp32, folded on the matrix cores
         // (the flush's operands and order), stored RNE-bf16
-        const float D = sFC[RL];
+        const float D = sFC[lay.FD];
         bf16_t* out = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N;
-        Fold::run(rows.wave_row(base, 0, wave), P, F, lds + lay.oW + wave * Fold::BUF, lane, col,
+        Fold::run(rows.wave_row(base, 0, wave), P, align4(F), lds + lay.oW + wave * Fold::BUF, lane, col,
                   [&](int j, int c) { return sFC[j] * to_f32(sB[j * N + c]); },
                   [&](int j, int p) { return to_f32(sX[j * P + p]); },
                   [&](int k, const float (&d)[8]) {
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       }
     } else if constexpr (FOLD) {
       if (do_fold) {  // S <- exp(Lam) S + sum_j x_j outer (c_j B_j), j ascending
-        const float D = sFC[RL];
+        const float D = sFC[lay.FD];
 #pragma unroll
         for (int k = 0; k < kMaxPass; ++k) {
           fr[k].v.x *= D;

@@ -61,7 +61,7 @@ def test_largest_shapes_within_the_lds_budget_are_accepted():
                read_copy=rss.RSS_COPY_BF16),
           dict(kind=rss.RSS_KIND_GDN, headdim=256, dstate=256, window=64, capacity=64, max_draft=0,
                in_dtype=rss.RSS_DTYPE_F32),
-          dict(kind=rss.RSS_KIND_KDA, headdim=256, dstate=256, window=49, capacity=49, max_draft=0,
+          dict(kind=rss.RSS_KIND_KDA, headdim=256, dstate=256, window=48, capacity=48, max_draft=0,
                in_dtype=rss.RSS_DTYPE_F32)]
     for kw in ok:
         out = rss.rss_sizes()
@@ -109,7 +109,7 @@ def test_buffer_sizes():
     # LDS budget (160 KiB per workgroup) at the largest shapes
     (dict(headdim=256, dstate=256, window=57, capacity=64, max_draft=7, in_dtype=rss.RSS_DTYPE_F32),
      rss.RSS_E_SHAPE),
-    (dict(kind=rss.RSS_KIND_KDA, headdim=256, dstate=256, window=50, capacity=50, max_draft=0,
+    (dict(kind=rss.RSS_KIND_KDA, headdim=256, dstate=256, window=49, capacity=49, max_draft=0,
           in_dtype=rss.RSS_DTYPE_F32), rss.RSS_E_SHAPE),
 ])
 def test_config_validation(kw, status):

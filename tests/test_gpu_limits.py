@@ -1,5 +1,5 @@
 """The largest supported shapes on the GPU: P = N = 256 with the longest ring the
-LDS budget allows (R = 64, or 58 with fp32 x/B/C and drafts, 49 for KDA), the
+LDS budget allows (R = 64, or 58 with fp32 x/B/C and drafts, 48 for KDA), the
 longest draft (K = 7), a window that fills the ring, and head groups shared by
 two heads. Every output against the fp64 recurrence over the committed stream,
 pointers against the integer ring model."""
@@ -93,7 +93,7 @@ def test_mamba2_largest_shape(in_dtype, copy, R):
     assert L.device_error() == 0
 
 
-@pytest.mark.parametrize("kind,R", [("gdn", 64), ("kda", 49)])
+@pytest.mark.parametrize("kind,R", [("gdn", 64), ("kda", 48)])
 def test_delta_rule_largest_shape(kind, R):
     wl = workloads.get(f"{kind}_b256_h32_d128_w16").replace(
         batch=2, nheads=2, ngroups=2, headdim=256, dstate=256, window=R, capacity=R, s0="normal",
