@@ -276,6 +276,17 @@ __device__ __forceinline__ typename V16<Tin>::T ldv(const Tin* p) {
   return *reinterpret_cast<const typename V16<Tin>::T*>(p);
 }
 
+// A 16-byte vector of input elements widened to fp32 in registers.
+__device__ __forceinline__ void unpack16(const float4& v, float* d) {
+  d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+}
+__device__ __forceinline__ void unpack16(const uint4& v, float* d) {
+  d[0] = __uint_as_float(v.x << 16); d[1] = __uint_as_float(v.x & 0xffff0000u);
+  d[2] = __uint_as_float(v.y << 16); d[3] = __uint_as_float(v.y & 0xffff0000u);
+  d[4] = __uint_as_float(v.z << 16); d[5] = __uint_as_float(v.z & 0xffff0000u);
+  d[6] = __uint_as_float(v.w << 16); d[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
 __device__ __forceinline__ void st_lds_f32(float* d, const float4& v) {
   *reinterpret_cast<float4*>(d) = v;
 }

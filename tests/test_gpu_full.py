@@ -298,3 +298,73 @@ def test_bf16_tile_modes_b256_full_size(copy):
     log(f"  replay vs emulator {vs_emu:.2e}, vs exact {vs_exact:.2e}; eager bf16 vs emulator {eager_vs_emu:.2e}")
     assert vs_emu < 1e-3 and vs_exact < 2e-2 and eager_vs_emu < 1e-3
     assert layer.device_error() == 0
+
+
+def test_spec_b512_fold_verify_200_rounds():
+    """The speculative workload at its stated length: batch 512, K = 4, all 200
+    seeded rounds of the verify-with-fold + rollback schedule, each round with
+    its own draft inputs (drawn on the device by the workload's seeded
+    generator; the oracle reads back the sampled pairs' exact input bits) and
+    accepted lengths. After every round: all K+1 outputs of 24 sampled
+    (sequence, head) pairs against the fp64 recurrence on the committed stream
+    (<= 1e-5), every (sequence, head) pointer against the integer ring model
+    (bit-exact), and every folded checkpoint of a sampled pair against the
+    recurrence's state (<= 1e-5)."""
+    wl = workloads.get("mamba2_spec_b512_h128_p64_n128_w16_k4")
+    rounds = wl.rounds
+    log(f"[full] {wl.name}: {rounds} rounds, verify with fold + rollback")
+    cfg = cfg_of(wl)
+    A_np = synth.params(wl)["A"]
+    A = torch.from_numpy(A_np).to(DEV)
+    Bt, H, P, N, K, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.draft, wl.window
+    layer = rss.ReplayLayer(cfg, A, DEV)
+    layer.init_state()
+    pm = PointerModel(Bt, wl.capacity)
+    pg = PairGather(wl, sample_pairs(wl, 24, seed=17))
+    S_ref = np.zeros((1, len(pg.pairs), P, N))
+    A_pair = pg.A(A_np)
+    y = torch.empty((Bt, K + 1, H, P), device=DEV)
+    bidx, hidx = torch.as_tensor(pg.b, device=DEV), torch.as_tensor(pg.h, device=DEV)
+    gidx = torch.as_tensor(pg.g, device=DEV)
+
+    def host(t):  # (n, K+1, ...) device gather -> (1, K+1, n, ...) exact fp64 values
+        a = t.double().cpu().numpy()
+        return np.moveaxis(a, 1, 0)[None]
+
+    folds, worst = 0, 0.0
+    for r in range(rounds):
+        d = synth.device_draft_inputs(wl, r, DEV)
+        nacc = synth.accepted_drafts(wl, r)
+        folded = pm.len >= W
+        for b in np.nonzero(folded)[0]:
+            pm.flush(int(b), W)
+        layer.verify_k_tokens_fold(W, K, d["x"], d["B"], d["C"], d["dt"], y)
+        folds += int(folded.sum())
+        fp = folded[pg.b]
+        if fp.any():
+            ck = layer.ckpt[bidx, hidx].double().cpu().numpy()
+            assert rel_l2(ck[fp], S_ref[0][fp]) < 1e-5, r
+        px, pB, pC = host(d["x"][bidx, :, hidx]), host(d["B"][bidx, :, gidx]), host(d["C"][bidx, :, gidx])
+        pdt = host(d["dt"][bidx, :, hidx])
+        states, refs = [], []
+        S_run = S_ref
+        for i in range(K + 1):
+            S_run, yi = mamba2.eager_step(S_run, A_pair, px[:, i], pB[:, i], pC[:, i], pdt[:, i])
+            states.append(S_run)
+            refs.append(yi)
+        y_ref = np.stack(refs, axis=1)
+        got = y[bidx, :, hidx].permute(1, 0, 2).double().cpu().numpy()[None]
+        e = rel_l2(got, y_ref)
+        worst = max(worst, e)
+        assert e < 1e-5, r
+        layer.rollback(torch.from_numpy((K - nacc).astype(np.int32)).to(DEV))
+        pm.len += K + 1                     # verify appends K+1 tentative entries, the
+        pm.len -= K - nacc                  # rollback keeps the accepted ones (n_tent back to 0)
+        assert np.all(pm.len <= wl.capacity)
+        ptr = layer.ptr.cpu().numpy()
+        assert all(np.array_equal(ptr[:, h, :3], pm.as_array()) for h in range(H)), r
+        keep = nacc[pg.b]
+        S_ref = np.stack([states[keep[i]][0, i] for i in range(len(pg.pairs))])[None]
+    log(f"  {folds} sequence folds over {rounds} rounds; worst round rel-L2 {worst:.2e}")
+    assert folds > 10 * Bt
+    assert layer.device_error() == 0
