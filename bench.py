@@ -286,6 +286,26 @@ def run_calibration(torch, rss, dev):
     return out
 
 
+PHASES = ["main", "eager", "calibration", "staggered", "grouped", "dual", "dual_w8", "dual_w16",
+          "dual_w32", "bf16_checkpoint", "eager_bf16", "speculative", "gdn", "kda"]
+
+
+class PhaseMarker:
+    """With --phase-markers, a tiny launch of the library's read kernel before
+    each section, its grid size (1 + the section's index in PHASES) naming the
+    section, so a profiler's per-dispatch records can be split by workload."""
+
+    def __init__(self, torch, rss, dev, on):
+        self.on, self.rss = on, rss
+        if on:
+            self.src = torch.zeros((4,), device=dev)
+            self.sink = torch.zeros((4,), device=dev)
+
+    def __call__(self, name):
+        if self.on:
+            self.rss.rss_calib_read(self.src, self.sink, 1 + PHASES.index(name))
+
+
 def calibrate_counters(torch, rss, dev):
     """A plain 1 GiB -> 1 GiB copy by the library's copy kernel, run three
     times: the reference a profiler's HBM byte counters are scaled by."""
@@ -585,15 +605,15 @@ def run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup):
             "bytes_per_token": eager_bytes(wl, 2) * H}
 
 
-def run_spec(torch, rss, dev, warmup=8):
-    """Speculative rounds at batch 512, K = 4, over the workload's 200 rounds,
-    each with its own draft inputs (drawn on the device) and accepted lengths:
-    verify with the committed window's fold in the same pass + rollback, the
-    same with a separate flush launch, and the eager kernel with a state
-    snapshot per draft token."""
+def run_spec(torch, rss, dev, warmup=8, rounds=None):
+    """Speculative rounds at batch 512, K = 4, over the workload's 200 rounds
+    (or `rounds`), each with its own draft inputs (drawn on the device) and
+    accepted lengths: verify with the committed window's fold in the same pass
+    + rollback, the same with a separate flush launch, and the eager kernel
+    with a state snapshot per draft token."""
     wl = workloads.get("mamba2_spec_b512_h128_p64_n128_w16_k4")
     Bt, H, P, N, G, W, K = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window, wl.draft
-    R = wl.rounds
+    R = rounds or wl.rounds
     D = [synth.device_draft_inputs(wl, r, dev) for r in range(R)]
     NACC = [synth.accepted_drafts(wl, r) for r in range(R)]
     NDROP = [torch.from_numpy((K - n).astype(np.int32)).to(dev) for n in NACC]
@@ -793,6 +813,10 @@ def main() -> int:
                     help="fold with a separate flush launch instead of the fused decode+fold")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the further workloads (dual precision, speculative, GDN, ...)")
+    ap.add_argument("--spec-rounds", type=int, default=0,
+                    help="speculative rounds to run (default: the workload's 200)")
+    ap.add_argument("--phase-markers", action="store_true",
+                    help="launch a tiny marker kernel before each section (for profiler runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -822,10 +846,14 @@ def main() -> int:
     DT = torch.from_numpy(pool[3]).to(dev)
     A = torch.from_numpy(synth.params(wl)["A"]).to(dev)
 
+    mark = PhaseMarker(torch, rss, dev, args.phase_markers)
+    mark("main")
     main_run = run_main(torch, rss, dev, X, Bm, Cm, DT, A, args)
     cfg, fused = main_run["cfg"], main_run["fused"]
+    mark("eager")
     out_eager = None if args.no_eager else run_eager(torch, rss, dev, X, Bm, Cm, DT, A, cfg,
                                                      args.steps, args.warmup)
+    mark("calibration")
     calib = run_calibration(torch, rss, dev)
     if args.calibrate_copy:
         calibrate_counters(torch, rss, dev)
@@ -897,19 +925,29 @@ def main() -> int:
     if not args.no_extra:
         sub = whole(args.steps, max(SWEEP_WINDOWS), 64)   # whole windows of every W swept
         rec["sub_measurement_steps"] = sub
+        mark("staggered")
         rec["staggered_folds"] = run_stagger(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)
+        mark("grouped")
         rec["grouped_bc"] = run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)
+        mark("dual")
         rec["dual_precision"] = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)
-        rec["dual_precision"]["by_window"] = {
-            w: {k: v for k, v in run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup,
-                                          window=w).items() if k != "workload"}
-            for w in SWEEP_WINDOWS}
+        by_window = {}
+        for w in SWEEP_WINDOWS:
+            mark(f"dual_w{w}")
+            by_window[w] = {k: v for k, v in run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup,
+                                                      window=w).items() if k != "workload"}
+        rec["dual_precision"]["by_window"] = by_window
+        mark("bf16_checkpoint")
+        bf16_ckpt = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup, mode="bf16_state")
+        mark("eager_bf16")
         rec["low_precision"] = {
-            "bf16_checkpoint": run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup,
-                                        mode="bf16_state"),
+            "bf16_checkpoint": bf16_ckpt,
             "eager_bf16_state": run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)}
-        rec["speculative"] = run_spec(torch, rss, dev)
+        mark("speculative")
+        rec["speculative"] = run_spec(torch, rss, dev, rounds=args.spec_rounds or None)
+        mark("gdn")
         rec["gated_deltanet"] = run_gdn(torch, rss, dev, sub, args.warmup)
+        mark("kda")
         rec["kimi_delta_attention"] = run_gdn(torch, rss, dev, sub, args.warmup,
                                               name="kda_b256_h32_d128_w16")
     if cpu is not None:
