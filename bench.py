@@ -45,7 +45,8 @@ WORKLOAD = "mamba2_b256_h128_p64_n128_w16"
 METRIC = "SSM decode tokens/s per layer + achieved HBM GB/s (% of peak), batch 256"
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "replay_decode_b256_hbm_counters.txt")
-KERNEL_SOURCES = ["replay.hip", "device.h", "limits.h", "launch.h", "lds.h", "fold.h"]
+KERNEL_SOURCES = ["replay.hip", "device.h", "limits.h", "launch.h", "lds.h", "fold.h", "verify_mfma.h",
+                  "eager.hip"]
 SWEEP_WINDOWS = (8, 16, 32)
 
 

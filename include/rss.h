@@ -98,7 +98,7 @@ enum { RSS_COPY_NONE = 0, RSS_COPY_BF16 = 1, RSS_STATE_BF16 = 2 };
  * (u_t, k_t, (1, log alpha_t)) in ring_x, ring_B and ring_dl, and A is unused.
  * A Kimi Delta Attention layer (KDA, P1 "Des couches rapides sur le papier")
  * has the same rules and layout except that its gate has one value per key
- * channel: ring_dl then holds a log-gate row per entry, fp32 [Bt, H, R, N]. */
+ * channel: ring_dl then holds a log-gate row per entry, fp32 [Bt, R, H, N]. */
 enum { RSS_KIND_MAMBA2 = 0, RSS_KIND_GDN = 1, RSS_KIND_KDA = 2 };
 
 /* Bits of the sticky device error word. */
@@ -127,10 +127,15 @@ typedef struct rss_config {
  *   ckpt     fp32 [Bt, H, P, N]   checkpoint S_c (the fp32 master); bf16
  *                                 [Bt, H, P, N] when read_copy = RSS_STATE_BF16
  *   ckpt_lo  bf16 [Bt, H, P, N]   read copy; NULL unless read_copy = BF16
- *   ring_x   in_dtype [Bt, H, R, P]   buffered x_j
- *   ring_B   in_dtype [Bt, G, R, N]   buffered B_j (one copy per group)
- *   ring_dl  fp32 [Bt, H, R, 2]   buffered (dt_j, dt_j * A_h); KDA:
- *                                 fp32 [Bt, H, R, N] log-gate rows
+ *   ring_x   in_dtype [Bt, R, H, P]   buffered x_j
+ *   ring_B   in_dtype [Bt, R, G, N]   buffered B_j (one copy per group)
+ *   ring_dl  fp32 [Bt, R, H, 2]   buffered (dt_j, dt_j * A_h); KDA:
+ *                                 fp32 [Bt, R, H, N] log-gate rows
+ *            The ring is slot-major: slot s of every head (group) of a
+ *            sequence is contiguous, so the entries one call appends for all
+ *            heads of a sequence sit side by side. One sequence's ring,
+ *            R * H * max(P, N) elements, must stay below 2^31
+ *            (RSS_E_SHAPE otherwise).
  *   ptr      int32 [Bt, H, 4]     per (sequence, head): head slot, window
  *                                 length len, tentative count n_tent, 0.
  *                                 Every head of a sequence holds the same

@@ -75,8 +75,11 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   float* sDc = lds + lay.oDc;
   const Tin* rx = static_cast<const Tin*>(a.ring_x);
   const Tin* rB = static_cast<const Tin*>(a.ring_B);
-  auto xrow = [&](int j) { return rx + ((size_t)bh * R + ring_slot(head, j, R)) * P; };
-  auto brow = [&](int j) { return rB + (((size_t)b * G + g) * R + ring_slot(head, j, R)) * N; };
+  // slot-major ring: slot s of every head (group) of a sequence is contiguous
+  const Tin* rxh = rx + (size_t)b * R * H * P + h * P;
+  const Tin* rBg = rB + (size_t)b * R * G * N + g * N;
+  auto xrow = [&](int j) { return rxh + ring_slot(head, j, R) * (H * P); };
+  auto brow = [&](int j) { return rBg + ring_slot(head, j, R) * (G * N); };
 
   // 1. Tile loads (the fp32 master, or the bf16 checkpoint widened to fp32).
   const int col = tid % TPR;
@@ -100,13 +103,13 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
 
   // 2. Window B rows, x (transposed) and (dt, l), unpacked into LDS.
   float2 dl = make_float2(0.f, 0.f);
-  if (!PCD && tid < n) dl = a.ring_dl[(size_t)bh * R + ring_slot(head, tid, R)];
+  if (!PCD && tid < n) dl = a.ring_dl[(size_t)b * R * H + ring_slot(head, tid, R) * H + h];
   if constexpr (PCD) {  // the window's per-channel log-decay rows
-    const float* rg = a.ring_g + (size_t)bh * R * N;
+    const float* rg = a.ring_g + (size_t)b * R * H * N + h * N;
     for (int q = tid; q < n * (N / 4); q += kThreads) {
       const int j = q / (N / 4), c = q - j * (N / 4);
       *reinterpret_cast<float4*>(sG + j * N + c * 4) =
-          *reinterpret_cast<const float4*>(rg + ring_slot(head, j, R) * N + c * 4);
+          *reinterpret_cast<const float4*>(rg + ring_slot(head, j, R) * (H * N) + c * 4);
     }
   }
   const int totBV = n * NV;

@@ -46,8 +46,9 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int P = a.P, R = a.R;
+  const int H = a.H, P = a.P, R = a.R;
   const int bh = xcd_tile(blockIdx.x, gridDim.x);
+  const int b = bh / H, h = bh - b * H;
 
   float* tile = a.ckpt + (size_t)bh * P * N;
   const int col = tid % TPR;
@@ -91,10 +92,13 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   float* sG = lds + lay.oG;
   float* sD = lds + lay.oD;
   float* sFC = lds + lay.oFC;
-  float* rg = KDA ? a.ring_g + (size_t)bh * R * N : nullptr;
-  float* ru = a.ring_u + (size_t)bh * R * P;
-  float* rk = a.ring_k + (size_t)bh * R * N;
-  float2* rdl = a.ring_dl + (size_t)bh * R;
+  // slot-major ring (slot s of every head of a sequence contiguous): this
+  // head's rows at slot 0, then slot strides H P (u), H N (k, log-gates), H
+  const int sus = H * P, sks = H * N;
+  float* rg = KDA ? a.ring_g + (size_t)b * R * sks + h * N : nullptr;
+  float* ru = a.ring_u + (size_t)b * R * sus + h * P;
+  float* rk = a.ring_k + (size_t)b * R * sks + h * N;
+  float2* rdl = a.ring_dl + (size_t)b * R * H + h;
   const float* kin = a.k + (size_t)bh * N;
   const float* qin = a.q + (size_t)bh * N;
   const float* vin = a.v + (size_t)bh * P;
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     const int q = q0 + lane;
     if (q < totK) {
       const int j = q / NV;
-      const float* src = j < n0 ? rk + ring_slot(head, j, R) * N : kin;
+      const float* src = j < n0 ? rk + ring_slot(head, j, R) * sks : kin;
       dma16(src + (q - j * NV) * 4, sK + q0 * 4);
     }
   }
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
       const int q = q0 + lane;
       if (q < totU) {
         const int j = q / PV;
-        dma16(ru + ring_slot(head, j, R) * P + (q - j * PV) * 4, sU + q0 * 4);
+        dma16(ru + ring_slot(head, j, R) * sus + (q - j * PV) * 4, sU + q0 * 4);
       }
     }
   }
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
       const int q = q0 + lane;
       if (q < totG) {
         const int j = q / NV;
-        dma16(rg + ring_slot(head, j, R) * N + (q - j * NV) * 4, sG + q0 * 4);
+        dma16(rg + ring_slot(head, j, R) * sks + (q - j * NV) * 4, sG + q0 * 4);
       }
     }
   }
@@ -135,11 +139,11 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   if (tid < N) qv = qin[tid];
   if (KDA && tid < N) av = a.alpha[(size_t)bh * N + tid];
   float2 dl = make_float2(0.f, 0.f);
-  if (!KDA && tid < n0) dl = rdl[ring_slot(head, tid, R)];
+  if (!KDA && tid < n0) dl = rdl[ring_slot(head, tid, R) * H];
   if (!uvec) {
     for (int e = tid; e < n0 * P; e += kThreads) {
       const int j = e / P;
-      sU[e] = ru[ring_slot(head, j, R) * P + (e - j * P)];
+      sU[e] = ru[ring_slot(head, j, R) * sus + (e - j * P)];
     }
   }
   if (tid < N) sQ[tid] = qv;
@@ -164,13 +168,13 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   }
   __syncthreads();
   // the new entry's (1, log alpha) after the wait: a store before it would be waited for too
-  if (!KDA && tid == 0) rdl[ring_slot(head, n0, R)] = make_float2(1.f, logf(alpha));
+  if (!KDA && tid == 0) rdl[ring_slot(head, n0, R) * H] = make_float2(1.f, logf(alpha));
   if constexpr (KDA) {
     // Channel n (one thread each): lam_j[n] from the newest entry back, the new
     // token's gate included; scale the committed keys in place; exp(Lam[n]).
     if (tid < N) {
       const float gt = logf(av);
-      rg[ring_slot(head, n0, R) * N + tid] = gt;
+      rg[ring_slot(head, n0, R) * sks + tid] = gt;
       float acc = gt;
       for (int j = n0 - 1; j >= 0; --j) {
         sK[j * N + tid] *= expf(acc);
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   }
   // k_t into the ring (every head owns its k)
   for (int q = tid; q < NV; q += kThreads)
-    *reinterpret_cast<float4*>(rk + ring_slot(head, n0, R) * N + q * 4) =
+    *reinterpret_cast<float4*>(rk + ring_slot(head, n0, R) * sks + q * 4) =
         *reinterpret_cast<const float4*>(sK + n0 * N + q * 4);
   __syncthreads();
 
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     kc[v] = dn * sK[n0 * N + col * 4 + v];
     qc[v] = dn * sQ[col * 4 + v];
   }
-  float* unew = ru + ring_slot(head, n0, R) * P;
+  float* unew = ru + ring_slot(head, n0, R) * sus;
   for (int base = 0; base < P; base += RPP * MP) {
     if (base > 0) load_chunk(base);
 #pragma unroll

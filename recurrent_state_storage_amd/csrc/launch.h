@@ -14,9 +14,9 @@ struct ReplayArgs {
   float* ckpt;             // [Bt,H,P,N] fp32 master (written only by the fused fold)
   void* ckpt_lo;           // [Bt,H,P,N] bf16 read copy (dual mode), or the bf16-stored
                            // checkpoint (written only by its fused fold)
-  void* ring_x;            // [Bt,H,R,P]
-  void* ring_B;            // [Bt,G,R,N]
-  float2* ring_dl;         // [Bt,H,R] (dt, dt*A)
+  void* ring_x;            // [Bt,R,H,P] (slot-major)
+  void* ring_B;            // [Bt,R,G,N]
+  float2* ring_dl;         // [Bt,R,H] (dt, dt*A)
   int4* ptr;               // [Bt,H] (head, len, n_tent, 0)
   const float* A;          // [H]
   int* err;                // sticky device word
@@ -44,7 +44,7 @@ struct FlushArgs {
   const void* ring_x;
   const void* ring_B;
   const float2* ring_dl;
-  const float* ring_g;     // per-channel log-decay rows [Bt,H,R,N] (KDA), else unused
+  const float* ring_g;     // per-channel log-decay rows [Bt,R,H,N] (KDA), else unused
   int4* ptr;
   int* err;
   int H, P, G, R, min_len;
@@ -98,10 +98,10 @@ hipError_t launch_eager(const EagerArgs& a, int batch, int N, bool bf16_in, bool
 // Gated DeltaNet / KDA replay decode (one token) and the eager baselines.
 struct GdnArgs {
   float* ckpt;             // [Bt,H,P,N] fp32, P = d_v, N = d_k
-  float* ring_u;           // [Bt,H,R,P]
-  float* ring_k;           // [Bt,H,R,N]
-  float2* ring_dl;         // GDN: [Bt,H,R] (1, log alpha)
-  float* ring_g;           // KDA: [Bt,H,R,N] log alpha per channel
+  float* ring_u;           // [Bt,R,H,P] (slot-major)
+  float* ring_k;           // [Bt,R,H,N]
+  float2* ring_dl;         // GDN: [Bt,R,H] (1, log alpha)
+  float* ring_g;           // KDA: [Bt,R,H,N] log alpha per channel
   int4* ptr;               // [Bt,H]
   int* err;
   const float* q;          // [Bt,H,N]

@@ -27,7 +27,7 @@ __host__ __device__ constexpr int fold_ld(int n) { return n + ((16 - n) & 63); }
 // 0) the window rows are allocated in multiples of four (the fold reads entries
 // in groups of four; the rows past the window are zeroed).
 struct ReplayLds {
-  int RA, oX, oB, oC, oCF, oDC, oRing, oFC, FD, oW, total;
+  int RA, oX, oB, oC, oCF, oDC, oCR, oRing, oFC, FD, oW, total;
   // fold_buf: floats of the matrix-core fold's hand-over buffer per wavefront
   // (0 when the kernel does not fold on the matrix cores).
   __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes, int nw,
@@ -38,7 +38,8 @@ struct ReplayLds {
     oC = oB + align4((RA * N * tin_bytes + 3) / 4);    // new tokens' C [ntmax][N]
     oCF = oC + ntmax * N;                              // exp(lam) * dt [ntmax][R]
     oDC = oCF + ntmax * R;                             // exp(Lam) [ntmax]
-    oRing = align4(oDC + ntmax);                       // ring shares [nw][ntmax][P]
+    oCR = align4(oDC + ntmax);                         // several bf16 tokens: their raw C [ntmax][N]
+    oRing = oCR + (ntmax > 1 && tin_bytes == 2 ? align4((ntmax * N * 2 + 3) / 4) : 0);  // shares [nw][ntmax][P]
     oFC = oRing + nw * ntmax * P;                      // fused fold: c_j [align4(R)], then exp(Lam)
     FD = align4(R);                                    // index of exp(Lam) in the fold coefficients
     oW = align4(oFC + FD + 1);                         // fold hand-over buffers [nw][fold_buf]

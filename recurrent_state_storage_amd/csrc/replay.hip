@@ -42,6 +42,7 @@
 
 #include "device.h"
 #include "fold.h"
+#include "verify_mfma.h"
 #include "launch.h"
 #include "lds.h"
 
@@ -137,12 +138,20 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   float* sDC = lds + lay.oDC;
   float* sFC = lds + lay.oFC;
   float* sRing = lds + lay.oRing;
+  // Several bf16 tokens: the ring terms run on the matrix cores, from the raw C
+  // rows (a single token keeps the wavefront dots, bitwise the decode's).
+  constexpr bool kMfRing = NTMAX > 1 && std::is_same<Tin, bf16_t>::value;
+  const bool mf_ring = kMfRing && nt > 1;
+  bf16_t* sCr = reinterpret_cast<bf16_t*>(lds + lay.oCR);
 
   // Per-workgroup base pointers (uniform, held in scalar registers); every
-  // per-lane offset below is a 32-bit int.
-  Tin* rx = static_cast<Tin*>(a.ring_x) + (size_t)bh * R * P;           // this head's x rows
-  Tin* rB = static_cast<Tin*>(a.ring_B) + ((size_t)b * G + g) * R * N;   // this group's B rows
-  float2* rdl = a.ring_dl + (size_t)bh * R;
+  // per-lane offset below is a 32-bit int. The ring is slot-major: slot s of
+  // every head of a sequence is contiguous, so one call's appends of all heads
+  // land side by side.
+  const int slx = H * P, slb = G * N;                                    // slot strides of x and B
+  Tin* rx = static_cast<Tin*>(a.ring_x) + (size_t)b * R * slx + h * P;   // this head's x, slot 0
+  Tin* rB = static_cast<Tin*>(a.ring_B) + (size_t)b * R * slb + g * N;   // this group's B, slot 0
+  float2* rdl = a.ring_dl + (size_t)b * R * H + h;                       // (dt, l), slot stride H
   const Tin* xin = static_cast<const Tin*>(a.x) + ((size_t)b * nt * H + h) * P;
   const Tin* Bin = static_cast<const Tin*>(a.B) + ((size_t)b * nt * G + g) * N;
   const Tin* Cin = static_cast<const Tin*>(a.C) + ((size_t)b * nt * G + g) * N;
@@ -150,10 +159,10 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   float* yout = a.y + ((size_t)b * nt * H + h) * P;
   const int xstr = H * P, bstr = G * N;   // per-token strides of x and of B, C
   auto xrow = [&](int j) -> const Tin* {
-    return j < n0 ? rx + ring_slot(head, j, R) * P : xin + (j - n0) * xstr;
+    return j < n0 ? rx + ring_slot(head, j, R) * slx : xin + (j - n0) * xstr;
   };
   auto brow = [&](int j) -> const Tin* {
-    return j < n0 ? rB + ring_slot(head, j, R) * N : Bin + (j - n0) * bstr;
+    return j < n0 ? rB + ring_slot(head, j, R) * slb : Bin + (j - n0) * bstr;
   };
 
   // 2. Window rows straight into LDS (direct global->LDS 16-byte loads: lane l
@@ -205,12 +214,17 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   // in flight would serialise them.)
   float2 dl_ring = make_float2(0.f, 0.f);
   float dt_new = 0.f;
-  if (tid < n0) dl_ring = rdl[ring_slot(head, tid, R)];
+  if (tid < n0) dl_ring = rdl[ring_slot(head, tid, R) * H];
   if (tid >= n0 && tid < L) dt_new = dtin[(tid - n0) * H];
 #pragma unroll
   for (int m = 0; m < kStageC; ++m) {
     const int q = m * NT + tid;
-    if (q < totCV) st_lds_f32(sC + q * VE, vc[m]);
+    if (q < totCV) {
+      st_lds_f32(sC + q * VE, vc[m]);
+      if constexpr (kMfRing) {
+        if (mf_ring) *reinterpret_cast<VT*>(sCr + q * VE) = vc[m];
+      }
+    }
   }
   if (!xvec) {
 #pragma unroll
@@ -267,25 +281,25 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   // The new tokens' (dt, l) into the ring, only now: on this target a store
   // counts in the same counter as the loads, so a store issued before the wait
   // above would have been waited for too.
-  if (wave == 0 && lane >= n0 && lane < L) rdl[ring_slot2(head, lane, R)] = dl_new;
+  if (wave == 0 && lane >= n0 && lane < L) rdl[ring_slot2(head, lane, R) * H] = dl_new;
 
   // The new tokens' x and B rows go from LDS to the ring.
   if (xvec) {
     for (int q = tid; q < nt * PV; q += NT) {
       const int i = q / PV, c = q - i * PV;
-      *reinterpret_cast<VT*>(rx + ring_slot2(head, n0 + i, R) * P + c * VE) =
+      *reinterpret_cast<VT*>(rx + ring_slot2(head, n0 + i, R) * slx + c * VE) =
           *reinterpret_cast<const VT*>(sX + (n0 + i) * P + c * VE);
     }
   } else {
     for (int e = tid; e < nt * P; e += NT) {
       const int i = e / P, p = e - i * P;
-      rx[ring_slot2(head, n0 + i, R) * P + p] = sX[(n0 + i) * P + p];
+      rx[ring_slot2(head, n0 + i, R) * slx + p] = sX[(n0 + i) * P + p];
     }
   }
   if (h == g * hpg) {  // the group's first head keeps the group's B
     for (int q = tid; q < nt * NV; q += NT) {
       const int i = q / NV, c = q - i * NV;
-      *reinterpret_cast<VT*>(rB + ring_slot2(head, n0 + i, R) * N + c * VE) =
+      *reinterpret_cast<VT*>(rB + ring_slot2(head, n0 + i, R) * slb + c * VE) =
           *reinterpret_cast<const VT*>(sB + (n0 + i) * N + c * VE);
     }
   }
@@ -328,6 +342,10 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       }
       return sCF[i * RL + j] * wave_sum(part);
     });
+  } else if (mf_ring) {
+    verify_weights_mfma<N>(reinterpret_cast<const bf16_t*>(sB), sCr, sCF, RL, L, nt, wave, NW, lane);
+    __syncthreads();
+    verify_shares_mfma<Tin>(sX, sCF, sRing, RL, P, L, nt, wave, NW, lane);
   } else {
     // Several outputs: all (i, j) dots first, one 16-lane group per pair (16
     // pairs in flight per workgroup pass, each lane a contiguous slice of N
@@ -383,12 +401,30 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) cv[v] = sC[i * N + col * VEC + v];
       float part[kMaxPass];
+      if constexpr (LOW && std::is_same<Tin, bf16_t>::value) {
+        // bf16 tile, bf16 C (the stored inputs: exact as bf16): two exact
+        // products per v_dot2_f32_bf16, summed in fp32
+        uint32_t cp[VEC / 2];
 #pragma unroll
-      for (int k = 0; k < kMaxPass; ++k) {
-        float acc = 0.f;
+        for (int q = 0; q < VEC / 2; ++q) cp[q] = pack_bf16x2(cv[2 * q], cv[2 * q + 1]);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc = fmaf(fr[k].get(v), cv[v], acc);
-        part[k] = acc;
+        for (int k = 0; k < kMaxPass; ++k) {
+          const uint32_t w[4] = {fr[k].v.x, fr[k].v.y, fr[k].v.z, fr[k].v.w};
+          float acc = 0.f;
+#pragma unroll
+          for (int q = 0; q < VEC / 2; ++q)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[q]),
+                                                  __builtin_bit_cast(bf16x2_t, cp[q]), acc, false);
+          part[k] = acc;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kMaxPass; ++k) {
+          float acc = 0.f;
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc = fmaf(fr[k].get(v), cv[v], acc);
+          part[k] = acc;
+        }
       }
       int kbase;
       RS::run(part, col, kbase);
@@ -398,7 +434,9 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
           const int row = rows.row(base, kbase + m);
           if (row < P) {
             float ring;
-            if constexpr (NW == 4)
+            if (mf_ring)
+              ring = sRing[i * P + row];
+            else if constexpr (NW == 4)
               ring = (sRing[i * P + row] + sRing[(NTL + i) * P + row]) +
                      (sRing[(2 * NTL + i) * P + row] + sRing[(3 * NTL + i) * P + row]);
             else

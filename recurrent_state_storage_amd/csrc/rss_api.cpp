@@ -69,6 +69,10 @@ int32_t check_config(const rss_config* c) {
   if (c->window < 1 || c->capacity < c->window || c->capacity > rss::kMaxRing) return RSS_E_SHAPE;
   if (c->max_draft < 0 || c->max_draft > rss::kMaxNew - 1) return RSS_E_CAPACITY;
   if (c->capacity < c->window + c->max_draft) return RSS_E_CAPACITY;
+  // one sequence's ring rows (slot-major: R slots of H rows) stay within 32-bit
+  // element offsets, as the kernels index them
+  const int64_t row = c->headdim > c->dstate ? c->headdim : c->dstate;
+  if ((int64_t)c->capacity * c->nheads * row > 0x7fffffffLL) return RSS_E_SHAPE;
   if (layer_lds_bytes(c) > (size_t)rss::kMaxLdsBytes) return RSS_E_SHAPE;
   return RSS_OK;
 }

@@ -200,9 +200,10 @@ class ReplayLayer:
         self.ckpt = torch.empty((c.batch, c.nheads, c.headdim, c.dstate), dtype=_state_dtype(c), device=dev)
         self.ckpt_lo = (torch.empty((c.batch, c.nheads, c.headdim, c.dstate), dtype=torch.bfloat16, device=dev)
                         if c.read_copy == RSS_COPY_BF16 else None)
-        self.ring_x = torch.zeros((c.batch, c.nheads, c.capacity, c.headdim), dtype=idt, device=dev)
-        self.ring_B = torch.zeros((c.batch, c.ngroups, c.capacity, c.dstate), dtype=idt, device=dev)
-        self.ring_dl = torch.zeros((c.batch, c.nheads, c.capacity, c.dstate if c.kind == RSS_KIND_KDA else 2),
+        # slot-major ring: [batch, slot, head (group), row]
+        self.ring_x = torch.zeros((c.batch, c.capacity, c.nheads, c.headdim), dtype=idt, device=dev)
+        self.ring_B = torch.zeros((c.batch, c.capacity, c.ngroups, c.dstate), dtype=idt, device=dev)
+        self.ring_dl = torch.zeros((c.batch, c.capacity, c.nheads, c.dstate if c.kind == RSS_KIND_KDA else 2),
                                    dtype=torch.float32, device=dev)
         self.ptr = torch.zeros((c.batch, c.nheads, 4), dtype=torch.int32, device=dev)
         self.A = A

@@ -68,6 +68,14 @@ def test_largest_shapes_within_the_lds_budget_are_accepted():
         assert rss.library().rss_buffer_sizes(ctypes.byref(_cfg(**kw)), ctypes.byref(out)) == rss.RSS_OK, kw
 
 
+def test_largest_ring_per_sequence_is_accepted():
+    # R H max(P, N) = 2^31 - 64 * 256 * 1 ... just below the 32-bit offset bound
+    cfg = _cfg(batch=1, nheads=131071, ngroups=1, headdim=256, capacity=64, window=60)
+    out = rss.rss_sizes()
+    assert rss.library().rss_buffer_sizes(ctypes.byref(cfg), ctypes.byref(out)) == rss.RSS_OK
+    assert out.ring_x == 64 * 131071 * 256 * 2
+
+
 def test_buffer_sizes():
     cfg = _cfg()
     s = rss.rss_buffer_sizes(cfg)
@@ -111,6 +119,8 @@ def test_buffer_sizes():
      rss.RSS_E_SHAPE),
     (dict(kind=rss.RSS_KIND_KDA, headdim=256, dstate=256, window=49, capacity=49, max_draft=0,
           in_dtype=rss.RSS_DTYPE_F32), rss.RSS_E_SHAPE),
+    # one sequence's slot-major ring past 2^31 elements (R H max(P, N)): refused
+    (dict(batch=1, nheads=131072, ngroups=1, headdim=256, capacity=64, window=60), rss.RSS_E_SHAPE),
 ])
 def test_config_validation(kw, status):
     cfg = _cfg(**kw)

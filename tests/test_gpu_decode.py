@@ -92,8 +92,8 @@ def _run_decode(wl, steps, flush_every_step=True, check_ring=True, check_eager=T
                     src = hist[c + j]
                     xb = src["x_bits"] if wl.in_dtype == "bf16" else src["x"]
                     Bb = src["B_bits"] if wl.in_dtype == "bf16" else src["B"]
-                    assert np.array_equal(rx[b, :, slot].view(xb.dtype), xb[b]), (t, b, j)
-                    assert np.array_equal(rB[b, :, slot].view(Bb.dtype), Bb[b]), (t, b, j)
+                    assert np.array_equal(rx[b, slot].view(xb.dtype), xb[b]), (t, b, j)
+                    assert np.array_equal(rB[b, slot].view(Bb.dtype), Bb[b]), (t, b, j)
     assert layer.device_error() == 0
     worst["run"] = rel_l2(np.stack(ys), np.stack(yrefs))
     return worst, layer

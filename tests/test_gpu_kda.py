@@ -73,7 +73,7 @@ def _run(wl, steps, flush_every_step=True):
             slot = pm.slot(b, j)
             t = steps - int(pm.len[b]) + j
             want = np.log(synth.kda_step_inputs(wl, t)["alpha"][b].astype(np.float64))
-            assert np.allclose(g[b, :, slot], want, rtol=1e-6, atol=1e-6), (b, j)
+            assert np.allclose(g[b, slot], want, rtol=1e-6, atol=1e-6), (b, j)
     assert layer.device_error() == 0
     worst["run"] = rel_l2(np.stack(os_), np.stack(refs))
     worst["eager_state"] = rel_l2(S_eag.double().cpu().numpy(), S_ref)
