@@ -21,6 +21,8 @@
 //
 // Rollback (P2, "Un retour en arrière qui devient trivial") touches integers
 // only: len -= n_drop, n_tent = 0.
+#include <type_traits>
+
 #include "device.h"
 #include "fold.h"
 #include "launch.h"
@@ -65,7 +67,10 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (tid == 0) atomicOr(a.err, kDevUncommitted);
     return;
   }
-  const FlushLds lay(R, P, N, PCD, MF ? Fold::BUF : 0);
+  // A bf16-stored checkpoint with bf16 inputs folds on the bf16 matrix cores,
+  // exactly as the decode that folds it in the same pass (fold.h).
+  constexpr bool kB16Fold = MF && B16 && std::is_same<Tin, bf16_t>::value;
+  const FlushLds lay(R, P, N, PCD, MF ? Fold::BUF : 0, kB16Fold ? fold_bt_elems(N, R) : 0);
   const int RS = lay.RS, LDB = lay.LDB, LDX = lay.LDX;
   const int F4 = align4(n);   // the matrix-core fold reads entries in groups of four
   float* sXT = lds + lay.oXT;
@@ -174,7 +179,21 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (lane == 0) sCF[RS] = expf(lam + u);
   }
   __syncthreads();
-  if constexpr (MF && !PCD) {  // the fold's A operand: c_j B_j, scaled in place
+  bf16_t* bt = reinterpret_cast<bf16_t*>(lds + lay.oBT);
+  const int F16 = (n + 15) & ~15;
+  if constexpr (kB16Fold) {  // the bf16 fold's A operand: B rows transposed, bt[j / 16][c][j % 16] (zero for j >= n)
+    for (int q = tid; q < N * (F16 / 8); q += kThreads) {
+      const int c = q % N, j0 = (q / N) * 8;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ja = j0 + 2 * e, jb = ja + 1;
+        w[e] = pack_bf16x2(ja < n ? sB[ja * LDB + c] : 0.f, jb < n ? sB[jb * LDB + c] : 0.f);
+      }
+      *reinterpret_cast<u32x4*>(bt + ((j0 >> 4) * N + c) * 16 + (j0 & 15)) = w;
+    }
+    __syncthreads();
+  } else if constexpr (MF && !PCD) {  // the fold's A operand: c_j B_j, scaled in place
     for (int q = tid; q < n * N; q += kThreads) {
       const int j = q / N, c = q - j * N;
       sB[j * LDB + c] *= sCF[j];
@@ -221,16 +240,27 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (base > 0) load_chunk(base);
     if constexpr (MF) {
       if (rows.wave_row(base, 0, wave) < P) {
-        Fold::run(rows.wave_row(base, 0, wave), P, F4, lds + lay.oW + wave * Fold::BUF, lane, col,
-                  [&](int j, int c) { return sB[j * LDB + c]; },
-                  [&](int j, int p) { return sXT[j * LDX + p]; },
-                  [&](int k, const float (&d)[4]) {
-                    const float4 s = fr[k].v;
-                    const int row = rows.row(base, k);
-                    if (row < P)
-                      store_row(row, make_float4(fmaf(Dc[0], s.x, d[0]), fmaf(Dc[1], s.y, d[1]),
-                                                 fmaf(Dc[2], s.z, d[2]), fmaf(Dc[3], s.w, d[3])));
-                  });
+        auto fin = [&](int k, const float (&d)[4]) {
+          const float4 s = fr[k].v;
+          const int row = rows.row(base, k);
+          if (row < P)
+            store_row(row, make_float4(fmaf(Dc[0], s.x, d[0]), fmaf(Dc[1], s.y, d[1]),
+                                       fmaf(Dc[2], s.z, d[2]), fmaf(Dc[3], s.w, d[3])));
+        };
+        float* buf = lds + lay.oW + wave * Fold::BUF;
+        if constexpr (kB16Fold) {
+          Fold::run_b16(rows.wave_row(base, 0, wave), P, F16, bt, buf, lane, col,
+                        [&](int j, int p) {  // v_j[p] = c_j x_j[p], zero past the window
+                          const int jr = j < n ? j : 0;
+                          const float v = sCF[jr] * sXT[jr * LDX + p];
+                          return j < n ? v : 0.f;
+                        },
+                        fin);
+        } else {
+          Fold::run(rows.wave_row(base, 0, wave), P, F4, buf, lane, col,
+                    [&](int j, int c) { return sB[j * LDB + c]; },
+                    [&](int j, int p) { return sXT[j * LDX + p]; }, fin);
+        }
       }
     } else {
 #pragma unroll
@@ -284,8 +314,10 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
 
 template <int N, typename Tin, int MODE, bool PCD, bool MF>
 static hipError_t flush_one(const FlushArgs& a, int batch, hipStream_t s) {
-  const size_t lds =
-      (size_t)FlushLds(a.R, a.P, N, PCD, MF ? fold_buf_floats(N, 4, kMaxPass) : 0).total * sizeof(float);
+  constexpr bool kB16Fold = MF && MODE == kCkptBf16 && std::is_same<Tin, bf16_t>::value;
+  const size_t lds = (size_t)FlushLds(a.R, a.P, N, PCD, MF ? fold_buf_floats(N, 4, kMaxPass) : 0,
+                                      kB16Fold ? fold_bt_elems(N, a.R) : 0)
+                         .total * sizeof(float);
   auto kern = flush_kernel<N, Tin, MODE, PCD, MF>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

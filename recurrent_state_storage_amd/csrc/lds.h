@@ -16,6 +16,10 @@ __host__ __device__ constexpr int fold_buf_floats(int N, int VEC, int MP) {
   return (VEC > 0 && MP > 0) ? (N >= 256 ? 4 : 8) * (N + 4) : 0;
 }
 
+// bf16 elements of the transposed B rows the bf16 matrix-core fold reads
+// (fold.h): N rows of the window's entries, padded to a multiple of 16.
+__host__ __device__ constexpr int fold_bt_elems(int N, int R) { return N * ((R + 15) & ~15); }
+
 // Row stride (floats) of a matrix-core fold operand staged in LDS: at least n,
 // and 16 more than a multiple of 64, so the four window entries one
 // instruction reads (one per group of 16 lanes) fall on different banks.
@@ -27,11 +31,12 @@ __host__ __device__ constexpr int fold_ld(int n) { return n + ((16 - n) & 63); }
 // 0) the window rows are allocated in multiples of four (the fold reads entries
 // in groups of four; the rows past the window are zeroed).
 struct ReplayLds {
-  int RA, oX, oB, oC, oCF, oDC, oCR, oRing, oFC, FD, oW, total;
+  int RA, oX, oB, oC, oCF, oDC, oCR, oRing, oFC, FD, oW, oBT, total;
   // fold_buf: floats of the matrix-core fold's hand-over buffer per wavefront
-  // (0 when the kernel does not fold on the matrix cores).
+  // (0 when the kernel does not fold on the matrix cores); fold_bt: bf16
+  // elements of the transposed B rows of the bf16 fold (0 without it).
   __host__ __device__ ReplayLds(int R, int P, int N, int ntmax, int tin_bytes, int nw,
-                                int fold_buf = 0) {
+                                int fold_buf = 0, int fold_bt = 0) {
     RA = fold_buf > 0 ? align4(R) : R;                 // allocated window rows
     oX = 0;                                            // raw window x [RA][P]
     oB = align4((RA * P * tin_bytes + 3) / 4);         // raw window B [RA][N]
@@ -43,7 +48,8 @@ struct ReplayLds {
     oFC = oRing + nw * ntmax * P;                      // fused fold: c_j [align4(R)], then exp(Lam)
     FD = align4(R);                                    // index of exp(Lam) in the fold coefficients
     oW = align4(oFC + FD + 1);                         // fold hand-over buffers [nw][fold_buf]
-    total = oW + nw * fold_buf;
+    oBT = oW + nw * fold_buf;                          // bf16 fold: B rows transposed [align16(R)/16][N][16]
+    total = oBT + align4((fold_bt + 1) / 2);
   }
 };
 
@@ -53,11 +59,12 @@ struct ReplayLds {
 // for the matrix-core fold (fold_buf > 0) x and the scaled B rows are stored
 // one entry per row with fold_ld strides, the rows past the window zeroed.
 struct FlushLds {
-  int RS, LDX, LDB, oXT, oB, oCF, oDc, oG, oW, total;
+  int RS, LDX, LDB, oXT, oB, oCF, oDc, oG, oW, oBT, total;
   // fold_buf: floats of the matrix-core fold's hand-over buffer per wavefront
   // (0: the fold runs on the VALU). The per-channel log-decay rows are dead
   // once the decay walk has scaled the key rows, so the buffers share them.
-  __host__ __device__ FlushLds(int R, int P, int N, bool pcd, int fold_buf = 0) {
+  // fold_bt: bf16 elements of the transposed B rows of the bf16 fold.
+  __host__ __device__ FlushLds(int R, int P, int N, bool pcd, int fold_buf = 0, int fold_bt = 0) {
     RS = align4(R);
     const bool mf = fold_buf > 0;
     LDX = mf ? fold_ld(P) : 0;
@@ -69,7 +76,8 @@ struct FlushLds {
     oG = align4(oDc + (pcd ? N : 0));          // per-channel log-decay rows [R][N]
     oW = oG;                                   // fold hand-over buffers [4 wavefronts][fold_buf]
     const int g = pcd ? R * N : 0, w = kWaves * fold_buf;
-    total = oG + (g > w ? g : w);
+    oBT = oG + (g > w ? g : w);                // bf16 fold: B rows transposed [align16(R)/16][N][16]
+    total = oBT + align4((fold_bt + 1) / 2);
   }
 };
 

@@ -130,7 +130,11 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   if (tent && tid == 0) atomicOr(a.err, kDevUncommitted);  // never fold tentative entries
 
   using Fold = MfmaFold<N, TPR, VEC, kMaxPass>;
-  const ReplayLds lay(RL, P, N, NTL, (int)sizeof(Tin), NW, (FOLD && LOW) ? Fold::BUF : 0);
+  // A bf16-stored checkpoint with bf16 inputs folds on the bf16 matrix cores
+  // (fold.h), from the window's B rows transposed once per workgroup.
+  constexpr bool kB16Fold = FOLD && LOW && std::is_same<Tin, bf16_t>::value;
+  const ReplayLds lay(RL, P, N, NTL, (int)sizeof(Tin), NW, (FOLD && LOW) ? Fold::BUF : 0,
+                      kB16Fold ? fold_bt_elems(N, RL) : 0);
   Tin* sX = reinterpret_cast<Tin*>(lds + lay.oX);
   Tin* sB = reinterpret_cast<Tin*>(lds + lay.oB);
   float* sC = lds + lay.oC;
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
     dl_new = make_float2(dtj, lj);
   }
   __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads have landed
-  if constexpr (FOLD && LOW) {
+  if constexpr (FOLD && LOW && !kB16Fold) {
     if (do_fold) {  // the fold reads entries in groups of four: rows past the window are zero
       const int F4 = align4(F);
       for (int q = tid; q < (F4 - F) * P; q += NT) sX[F * P + q] = Tin(0);
@@ -306,6 +310,27 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
     for (int q = tid; q < nt * NV; q += NT) {
       const int i = q / NV, c = q - i * NV;
       put16(rB + ring_slot2(head, n0 + i, R) * slb + c * VE, sB + (n0 + i) * N + c * VE);
+    }
+  }
+
+  // The bf16 fold's A operand: the window's B rows transposed in groups of 16
+  // entries, bt[j / 16][n][j % 16] (zero for j >= F), 16-byte writes of eight.
+  bf16_t* bt = reinterpret_cast<bf16_t*>(lds + lay.oBT);
+  const int F16 = (F + 15) & ~15;
+  if constexpr (kB16Fold) {
+    if (do_fold) {
+      for (int q = tid; q < N * (F16 / 8); q += NT) {
+        const int n = q % N, j0 = (q / N) * 8;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ja = j0 + 2 * e, jb = ja + 1;
+          const uint32_t lo = ja < F ? (uint32_t)sB[ja * N + n] : 0u;
+          const uint32_t hi = jb < F ? (uint32_t)sB[jb * N + n] : 0u;
+          w[e] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(bt + ((j0 >> 4) * N + n) * 16 + (j0 & 15)) = w;
+      }
     }
   }
 
@@ -460,16 +485,27 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
         // (the flush's operands and order), stored RNE-bf16
         const float D = sFC[lay.FD];
         bf16_t* out = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N;
-        Fold::run(rows.wave_row(base, 0, wave), P, align4(F), lds + lay.oW + wave * Fold::BUF, lane, col,
-                  [&](int j, int c) { return sFC[j] * to_f32(sB[j * N + c]); },
-                  [&](int j, int p) { return to_f32(sX[j * P + p]); },
-                  [&](int k, const float (&d)[8]) {
-                    float o[8];
+        auto fin = [&](int k, const float (&d)[8]) {
+          float o[8];
 #pragma unroll
-                    for (int v = 0; v < 8; ++v) o[v] = fmaf(D, fr[k].get(v), d[v]);
-                    const int row = rows.row(base, k);
-                    if (row < P) st16_bf16x8(out + row * N + col * 8, o);
-                  });
+          for (int v = 0; v < 8; ++v) o[v] = fmaf(D, fr[k].get(v), d[v]);
+          const int row = rows.row(base, k);
+          if (row < P) st16_bf16x8(out + row * N + col * 8, o);
+        };
+        float* buf = lds + lay.oW + wave * Fold::BUF;
+        if constexpr (kB16Fold) {
+          Fold::run_b16(rows.wave_row(base, 0, wave), P, F16, bt, buf, lane, col,
+                        [&](int j, int p) {  // v_j[p] = c_j x_j[p], zero past the window
+                          const int jr = j < F ? j : 0;
+                          const float v = sFC[jr] * to_f32(sX[jr * P + p]);
+                          return j < F ? v : 0.f;
+                        },
+                        fin);
+        } else {
+          Fold::run(rows.wave_row(base, 0, wave), P, align4(F), buf, lane, col,
+                    [&](int j, int c) { return sFC[j] * to_f32(sB[j * N + c]); },
+                    [&](int j, int p) { return to_f32(sX[j * P + p]); }, fin);
+        }
       }
     } else if constexpr (FOLD) {
       if (do_fold) {  // S <- exp(Lam) S + sum_j x_j outer (c_j B_j), j ascending
@@ -517,9 +553,12 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
 template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD, int NT = kThreads>
 static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
   constexpr int VEC = TileGeom<N, LOW, NT>::VEC;
+  constexpr bool kB16Fold = FOLD && LOW && std::is_same<Tin, bf16_t>::value;
+  const int RL = a.R + ((FOLD && NTMAX > 1) ? a.nt : 0);
   const size_t lds =
-      (size_t)ReplayLds(a.R + ((FOLD && NTMAX > 1) ? a.nt : 0), a.P, N, a.nt, (int)sizeof(Tin), NT / 64,
-                        (FOLD && LOW) ? fold_buf_floats(N, VEC, kMaxPass) : 0)
+      (size_t)ReplayLds(RL, a.P, N, a.nt, (int)sizeof(Tin), NT / 64,
+                        (FOLD && LOW) ? fold_buf_floats(N, VEC, kMaxPass) : 0,
+                        kB16Fold ? fold_bt_elems(N, RL) : 0)
           .total * sizeof(float);
   auto kern = replay_kernel<N, Tin, LOW, NTMAX, FOLD, NT>;
   if (lds > 64 * 1024) {

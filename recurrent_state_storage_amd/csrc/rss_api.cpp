@@ -44,7 +44,8 @@ size_t layer_lds_bytes(const rss_config* c) {
     // the bf16-stored checkpoint folds on the matrix cores (a decode that would
     // not fit runs its fold as the flush launch instead, so only the flush counts)
     const bool mf = c->read_copy == RSS_STATE_BF16;
-    upd(rss::FlushLds(R, P, N, false, mf ? rss::fold_buf_floats(N, 4, rss::kMaxPass) : 0).total);
+    upd(rss::FlushLds(R, P, N, false, mf ? rss::fold_buf_floats(N, 4, rss::kMaxPass) : 0,
+                      mf && tin == 2 ? rss::fold_bt_elems(N, R) : 0).total);
   } else {
     const bool kda = c->kind == RSS_KIND_KDA;
     upd(rss::GdnLds(R, P, N, kda, rss::fold_buf_floats(N, 4, rss::gdn_passes(P, N))).total);
@@ -235,7 +236,8 @@ static int32_t decode_fold(rss_layer* l, int32_t min_len, const int32_t* each, c
   if (c.read_copy == RSS_STATE_BF16) {
     const int tin = c.in_dtype == RSS_DTYPE_BF16 ? 2 : 4;
     const size_t lds = (size_t)rss::ReplayLds(c.capacity, c.headdim, c.dstate, 1, tin, 2,
-                                              rss::fold_buf_floats(c.dstate, 8, rss::kMaxPass))
+                                              rss::fold_buf_floats(c.dstate, 8, rss::kMaxPass),
+                                              tin == 2 ? rss::fold_bt_elems(c.dstate, c.capacity) : 0)
                            .total * 4;
     separate = lds > (size_t)rss::kMaxLdsBytes;
   }
