@@ -117,7 +117,22 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
           *reinterpret_cast<const float4*>(rg + ring_slot(head, j, R) * (H * N) + c * 4);
     }
   }
-  const int totBV = n * NV;
+  bf16_t* bt = reinterpret_cast<bf16_t*>(lds + lay.oBT);
+  const int F16 = (n + 15) & ~15;
+  if constexpr (kB16Fold) {
+    // The bf16 fold's A operand straight from the ring: B rows transposed in
+    // groups of 16 entries, bt[j / 16][c][j % 16] (zero for j >= n);
+    // consecutive lanes take consecutive entries of one 8-column vector.
+    for (int q = tid; q < F16 * NV; q += kThreads) {
+      const int c8 = q / F16, j = q - c8 * F16;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j < n) v = __builtin_bit_cast(u32x4, ldv<Tin>(brow(j) + c8 * VE));
+      bf16_t* dst = bt + ((j >> 4) * N + c8 * VE) * 16 + (j & 15);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) dst[e * 16] = (bf16_t)((e & 1) ? v[e >> 1] >> 16 : v[e >> 1] & 0xffffu);
+    }
+  }
+  const int totBV = kB16Fold ? 0 : n * NV;
   for (int q0 = 0; q0 < totBV; q0 += kFlushStage * kThreads) {
     VT vb[kFlushStage];
 #pragma unroll
@@ -147,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
       }
     }
     for (int q = tid; q < (F4 - n) * LDX; q += kThreads) sXT[n * LDX + q] = 0.f;
-    for (int q = tid; q < (F4 - n) * LDB; q += kThreads) sB[n * LDB + q] = 0.f;
+    if constexpr (!kB16Fold)
+      for (int q = tid; q < (F4 - n) * LDB; q += kThreads) sB[n * LDB + q] = 0.f;
   } else if ((P % VE) == 0) {
     // x: thread -> (entry j = tid mod JP, column block tid / JP), JP =
     // 2^ceil(log2 n), so consecutive lanes write consecutive entries of a
@@ -179,21 +195,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
     if (lane == 0) sCF[RS] = expf(lam + u);
   }
   __syncthreads();
-  bf16_t* bt = reinterpret_cast<bf16_t*>(lds + lay.oBT);
-  const int F16 = (n + 15) & ~15;
-  if constexpr (kB16Fold) {  // the bf16 fold's A operand: B rows transposed, bt[j / 16][c][j % 16] (zero for j >= n)
-    for (int q = tid; q < N * (F16 / 8); q += kThreads) {
-      const int c = q % N, j0 = (q / N) * 8;
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ja = j0 + 2 * e, jb = ja + 1;
-        w[e] = pack_bf16x2(ja < n ? sB[ja * LDB + c] : 0.f, jb < n ? sB[jb * LDB + c] : 0.f);
-      }
-      *reinterpret_cast<u32x4*>(bt + ((j0 >> 4) * N + c) * 16 + (j0 & 15)) = w;
-    }
-    __syncthreads();
-  } else if constexpr (MF && !PCD) {  // the fold's A operand: c_j B_j, scaled in place
+  if constexpr (MF && !PCD && !kB16Fold) {  // the fold's A operand: c_j B_j, scaled in place
     for (int q = tid; q < n * N; q += kThreads) {
       const int j = q / N, c = q - j * N;
       sB[j * LDB + c] *= sCF[j];

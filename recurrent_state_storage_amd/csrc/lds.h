@@ -63,21 +63,24 @@ struct FlushLds {
   // fold_buf: floats of the matrix-core fold's hand-over buffer per wavefront
   // (0: the fold runs on the VALU). The per-channel log-decay rows are dead
   // once the decay walk has scaled the key rows, so the buffers share them.
-  // fold_bt: bf16 elements of the transposed B rows of the bf16 fold.
+  // fold_bt: bf16 elements of the transposed B rows of the bf16 fold (then the
+  // B rows are not staged in fp32).
   __host__ __device__ FlushLds(int R, int P, int N, bool pcd, int fold_buf = 0, int fold_bt = 0) {
     RS = align4(R);
     const bool mf = fold_buf > 0;
     LDX = mf ? fold_ld(P) : 0;
     LDB = mf ? fold_ld(N) : N;
     oXT = 0;                                   // x: transposed [P][RS], or [RS][LDX]
-    oB = mf ? RS * LDX : P * RS;               // window B rows [RS][LDB]
-    oCF = oB + RS * LDB;                       // c_j = exp(lam_j) dt_j [RS], then exp(Lam) at [RS]
+    oB = mf ? RS * LDX : P * RS;               // window B rows [RS][LDB] (fp32)
+    // the bf16 fold reads the B rows only transposed, bf16 [align16(R)/16][N][16],
+    // staged in place of the fp32 rows
+    oBT = oB;
+    oCF = oB + (fold_bt > 0 ? align4((fold_bt + 1) / 2) : RS * LDB);  // c_j [RS], then exp(Lam) at [RS]
     oDc = align4(oCF + RS + 1);                // per-channel exp(Lam[n]) [N]
     oG = align4(oDc + (pcd ? N : 0));          // per-channel log-decay rows [R][N]
     oW = oG;                                   // fold hand-over buffers [4 wavefronts][fold_buf]
     const int g = pcd ? R * N : 0, w = kWaves * fold_buf;
-    oBT = oG + (g > w ? g : w);                // bf16 fold: B rows transposed [align16(R)/16][N][16]
-    total = oBT + align4((fold_bt + 1) / 2);
+    total = oG + (g > w ? g : w);
   }
 };
 
