@@ -30,9 +30,17 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The replay kernels keep their few matrix-core accumulators
+# (a verify's ring terms) in ordinary VGPRs: with AGPRs the verify with the
+# committed-window fold needs 77 + 4 registers, one allocation granule past six
+# wavefronts per SIMD; in VGPR form it needs 77. (The folds in the flush and
+# delta-rule kernels, with 32 accumulators, are better off in AGPRs.)
+SOURCE_FLAGS = {"replay.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
