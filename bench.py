@@ -278,11 +278,19 @@ def run_calibration(torch, rss, dev):
         rss.rss_calib_copy(src, dst, g)
         ms = _timed(torch, lambda i: rss.rss_calib_copy(src, dst, g), 10) / 10
         copy[g] = rate(2 * nbytes, ms * 1e3)
+    write = {}
+    for g in (4096, 8192, 16384):
+        rss.rss_calib_write(dst, g)
+        ms = _timed(torch, lambda i: rss.rss_calib_write(dst, g), 10) / 10
+        write[g] = rate(nbytes, ms * 1e3)
     torch.mul(src, 1.0, out=dst)
     ms = _timed(torch, lambda i: torch.mul(src, 1.0, out=dst), 10) / 10
     out = {"read_ceiling_GBps": max(read.values()), "copy_ceiling_GBps": max(copy.values()),
-           "read_by_grid": read, "copy_by_grid": copy, "torch_elementwise_copy_GBps": rate(2 * nbytes, ms * 1e3),
-           "how": "rss_calib_read / rss_calib_copy over 1 GiB, best of grids of 256-thread workgroups"}
+           "write_ceiling_GBps": max(write.values()),
+           "read_by_grid": read, "copy_by_grid": copy, "write_by_grid": write,
+           "torch_elementwise_copy_GBps": rate(2 * nbytes, ms * 1e3),
+           "how": "rss_calib_read / rss_calib_copy / rss_calib_write over 1 GiB, best of grids of 256-thread "
+                  "workgroups"}
     del src, dst, sink
     return out
 
@@ -690,6 +698,8 @@ def run_spec(torch, rss, dev, warmup=8, rounds=None):
     torch.cuda.synchronize()
     e_us = lt2.us("e")
     ebytes = H * Bt * ((K + 2) * P * N * 4 + (K + 1) * (2 * P + 4 * N + 4 + 4 * P) + 4)
+    # of which written: a state snapshot and a y row per token
+    ewrite = H * Bt * (K + 1) * (P * N * 4 + 4 * P)
     del pool, D
     return {"workload": wl.name, "rounds": R, "inputs": "fresh draws every round (device generator)",
             "committed_tokens": committed,
@@ -703,7 +713,8 @@ def run_spec(torch, rss, dev, warmup=8, rounds=None):
             "verify_fold_avg_us": float(np.mean(vf_us)), "verify_fold_GBps": rate(vfbytes, sum(vf_us)),
             "verify_fold_frac_of_peak": rate(vfbytes, sum(vf_us)) / PEAK_HBM_GBS,
             "eager_verify_avg_us": float(np.mean(e_us)),
-            "eager_verify_GBps": rate(ebytes * len(e_us), sum(e_us))}
+            "eager_verify_GBps": rate(ebytes * len(e_us), sum(e_us)),
+            "eager_verify_read_bytes": ebytes - ewrite, "eager_verify_write_bytes": ewrite}
 
 
 def run_gdn(torch, rss, dev, steps, warmup, name="gdn_b256_h32_d128_w16"):
@@ -945,7 +956,12 @@ def main() -> int:
             "bf16_checkpoint": bf16_ckpt,
             "eager_bf16_state": run_eager_bf16(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)}
         mark("speculative")
-        rec["speculative"] = run_spec(torch, rss, dev, rounds=args.spec_rounds or None)
+        rec["speculative"] = sp = run_spec(torch, rss, dev, rounds=args.spec_rounds or None)
+        # the eager verify writes ~4.6x what it reads: its bound is the read
+        # bytes at the read ceiling plus the written bytes at the write ceiling
+        bound_us = (sp["eager_verify_read_bytes"] / calib["read_ceiling_GBps"] +
+                    sp["eager_verify_write_bytes"] / calib["write_ceiling_GBps"]) / 1e3
+        sp["eager_verify_frac_of_read_write_ceilings"] = bound_us / sp["eager_verify_avg_us"]
         mark("gdn")
         rec["gated_deltanet"] = run_gdn(torch, rss, dev, sub, args.warmup)
         mark("kda")

@@ -5,7 +5,7 @@
  * to measure what HBM actually delivers with the decode kernels' own access
  * pattern (16-byte non-temporal loads and stores, fully coalesced, grid-stride),
  * so that each kernel's bandwidth can be quoted as a fraction of the achievable
- * read or copy rate as well as of the data-sheet peak. The method's premise is
+ * read, write or copy rate as well as of the data-sheet peak. The method's premise is
  * that HBM traffic, not arithmetic, bounds the decode (P1, "La fiche qu'on
  * réécrit à chaque token": the eager step reads and writes the whole state for
  * very little arithmetic).
@@ -37,6 +37,12 @@ int32_t rss_calib_read(const void* src, size_t bytes, float* sink, int32_t block
 /* Copy `bytes` from src to dst (non-overlapping): reads and writes `bytes`
  * each. blocks as rss_calib_read. */
 int32_t rss_calib_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* stream);
+
+/* Stream-write `bytes` to dst (nothing is read): 16-byte vector i holds the
+ * floats (i mod 2^24, 1, 2, 3). blocks as rss_calib_read. The write ceiling
+ * bounds the write-heavy baselines (an eager verify that writes one state
+ * snapshot per draft token). */
+int32_t rss_calib_write(void* dst, size_t bytes, int32_t blocks, void* stream);
 
 #ifdef __cplusplus
 }

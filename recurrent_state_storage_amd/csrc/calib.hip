@@ -1,5 +1,5 @@
-// Bandwidth calibration kernels: the achievable HBM read and copy rates of
-// this GPU, measured with the access pattern the decode kernels use (16-byte
+// Bandwidth calibration kernels: the achievable HBM read, write and copy rates
+// of this GPU, measured with the access pattern the decode kernels use (16-byte
 // non-temporal loads and stores, fully coalesced). The decode path never calls
 // them; a benchmark times them beside the decode kernels so that a kernel's
 // bandwidth can be read against what the memory system delivers, not only
@@ -53,6 +53,20 @@ __global__ __launch_bounds__(kCalibThreads) void calib_copy_kernel(const f32x4* 
   }
 }
 
+// Writes `n` 16-byte vectors of a fixed pattern (the value of each float is
+// its vector index modulo 2^24 in the first lane, then 1, 2, 3), so a caller
+// can check what was written.
+__global__ __launch_bounds__(kCalibThreads) void calib_write_kernel(f32x4* dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * kCalibThreads * kCalibUnroll;
+  for (size_t i = (size_t)blockIdx.x * kCalibThreads * kCalibUnroll + threadIdx.x; i < n; i += stride) {
+#pragma unroll
+    for (int u = 0; u < kCalibUnroll; ++u) {
+      const size_t k = i + (size_t)u * kCalibThreads;
+      if (k < n) __builtin_nontemporal_store(f32x4{(float)(k & 0xffffffu), 1.f, 2.f, 3.f}, dst + k);
+    }
+  }
+}
+
 }  // namespace rss
 
 namespace {
@@ -77,6 +91,14 @@ int32_t rss_calib_copy(const void* src, void* dst, size_t bytes, int32_t blocks,
   hipLaunchKernelGGL(rss::calib_copy_kernel, dim3(grid_of(blocks)), dim3(rss::kCalibThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const rss::f32x4*>(src),
                      static_cast<rss::f32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? RSS_OK : RSS_E_HIP;
+}
+
+int32_t rss_calib_write(void* dst, size_t bytes, int32_t blocks, void* stream) {
+  if (!dst || !aligned16(dst) || bytes % 16 || blocks < 0) return RSS_E_INVALID;
+  if (bytes == 0) return RSS_OK;
+  hipLaunchKernelGGL(rss::calib_write_kernel, dim3(grid_of(blocks)), dim3(rss::kCalibThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<rss::f32x4*>(dst), bytes / 16);
   return hipGetLastError() == hipSuccess ? RSS_OK : RSS_E_HIP;
 }
 

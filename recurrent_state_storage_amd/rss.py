@@ -77,6 +77,7 @@ _SIGS = {
                           _VP, _VP], _I32),
     "rss_calib_read": ([_VP, ctypes.c_size_t, _VP, _I32, _VP], _I32),
     "rss_calib_copy": ([_VP, _VP, ctypes.c_size_t, _I32, _VP], _I32),
+    "rss_calib_write": ([_VP, ctypes.c_size_t, _I32, _VP], _I32),
 }
 
 _lib = None
@@ -467,3 +468,12 @@ def rss_calib_copy(src, dst, blocks: int = 0, stream=None) -> None:
         raise ValueError("dst: byte size differs from src")
     _check(library().rss_calib_copy(src.data_ptr(), dst.data_ptr(), nbytes, int(blocks), _stream(stream)),
            "rss_calib_copy")
+
+
+def rss_calib_write(dst, blocks: int = 0, stream=None) -> None:
+    """Stream-write the bytes of the contiguous device tensor `dst` (16-byte
+    vector i holds the floats (i mod 2^24, 1, 2, 3))."""
+    if not (isinstance(dst, torch.Tensor) and dst.is_cuda and dst.is_contiguous()):
+        raise ValueError("dst: expected a contiguous device tensor")
+    nbytes = dst.numel() * dst.element_size()
+    _check(library().rss_calib_write(dst.data_ptr(), nbytes, int(blocks), _stream(stream)), "rss_calib_write")

@@ -260,3 +260,21 @@ def test_binding_rejects_host_tensors():
         rss.rss_eager_step(cfg, torch.zeros(1, 2, 16, 16), torch.zeros(1, 1, 2, 16),
                            torch.zeros(1, 1, 2, 16), torch.zeros(1, 1, 2, 16), torch.zeros(1, 1, 2),
                            torch.zeros(2), torch.zeros(1, 1, 2, 16))
+
+
+def test_calibration_calls_validate_before_launch():
+    lib = rss.library()
+    ok = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100004)
+    for st in (lib.rss_calib_read(None, 16, ok, 0, None), lib.rss_calib_read(odd, 16, ok, 0, None),
+               lib.rss_calib_read(ok, 24, ok, 0, None), lib.rss_calib_read(ok, 16, None, 0, None),
+               lib.rss_calib_read(ok, 16, ok, -1, None),
+               lib.rss_calib_copy(ok, None, 16, 0, None), lib.rss_calib_copy(ok, odd, 16, 0, None),
+               lib.rss_calib_copy(ok, ok, 8, 0, None),
+               lib.rss_calib_write(None, 16, 0, None), lib.rss_calib_write(odd, 16, 0, None),
+               lib.rss_calib_write(ok, 20, 0, None), lib.rss_calib_write(ok, 16, -2, None)):
+        assert st == rss.RSS_E_INVALID
+    # zero bytes launch nothing
+    assert lib.rss_calib_read(ok, 0, ok, 0, None) == rss.RSS_OK
+    assert lib.rss_calib_copy(ok, ok, 0, 0, None) == rss.RSS_OK
+    assert lib.rss_calib_write(ok, 0, 0, None) == rss.RSS_OK
