@@ -12,8 +12,10 @@
 // also refreshes the bf16 read copy from the new fp32 master (P2, "Deux
 // précisions pour le prix d'une"); the fold reads the master only. With a
 // bf16-only checkpoint (the single low-precision checkpoint the dual mode is
-// compared with) it folds from the bf16 values in fp32 and stores the RNE-bf16
-// result: one rounding per window (P1, "Tenir le journal plutôt que le solde").
+// compared with) it folds from the bf16 values on the matrix cores (fold.h:
+// with bf16 inputs c_j x_j enters as a bf16 hi/lo pair, 2^-18 relative) and
+// stores the RNE-bf16 result: one rounding per window (P1, "Tenir le journal
+// plutôt que le solde").
 //
 // With per-channel decays (Kimi Delta Attention) the scalars become vectors
 // over the key channels n: S_c[:, n] <- exp(Lam[n]) S_c[:, n] + sum_j u_j

@@ -20,11 +20,13 @@
 //   2. issue, all at once, the window's x and B rows (direct global->LDS loads,
 //      kept raw), the new tokens' C and the window's (dt, l) pairs; scan the
 //      log-decays in one wavefront (a reverse tree sum: no prefix differences);
-//   3. per (i, j) pair, one wavefront: w_ij = exp(lam) dt (B_j . C_i), and the
-//      wavefront's share of sum_j w_ij x_j (wavefront w takes j = w mod the
-//      number of wavefronts);
-//   4. consume the tile: per pass a 16-byte fragment dot C_i, reduce-scattered
-//      over the lanes sharing the row, y = exp(Lam) * dot + the ring shares.
+//   3. w_ij = exp(lam) dt (B_j . C_i) and sum_j w_ij x_j: for one token, per
+//      entry j one wavefront (wavefront w takes j = w mod the number of
+//      wavefronts) forms w_j and its share of the sum; for several bf16 tokens
+//      both products run on the matrix cores (verify_mfma.h);
+//   4. consume the tile: per pass a 16-byte fragment dot C_i (v_dot2_f32_bf16
+//      for a bf16 tile), reduce-scattered over the lanes sharing the row,
+//      y = exp(Lam) * dot + the ring shares.
 // The new tokens' x and B rows are copied from LDS to the ring, and their
 // (dt, l) pairs stored, after the loads have landed (a store issued before that
 // wait would be waited for too). The checkpoint tile is read exactly once per
@@ -36,8 +38,9 @@
 // The threshold may differ per sequence, so that sequences whose windows are
 // out of phase fold on different steps (a staggered schedule). A verify
 // launched with a threshold folds the committed window it starts from instead.
-// A bf16-stored checkpoint is folded the same way by the two-wavefront decode
-// (widened to fp32, folded, stored RNE-bf16, as its separate flush does).
+// A bf16-stored checkpoint is folded the same way by the two-wavefront decode,
+// on the matrix cores (fold.h) and stored RNE-bf16, as its separate flush does.
+// The ring is slot-major (slot s of all heads of a sequence contiguous).
 #include <type_traits>
 
 #include "device.h"
