@@ -59,6 +59,12 @@ SHAPES = [
     (128, 128, 2, 2, 8, 8, "bf16", "bf16_state"),
     (256, 64, 1, 1, 3, 3, "bf16", "bf16_state"),
     (1, 16, 1, 1, 1, 1, "f32", "bf16_state"),
+    # windows past 16 entries: the bf16 fold's second and third groups of 16,
+    # a grouped layer, N = 256 (4-row hand-over), and the fp32-input fold
+    (64, 128, 2, 2, 20, 20, "bf16", "bf16_state"),
+    (48, 64, 2, 1, 40, 44, "bf16", "bf16_state"),
+    (256, 256, 1, 1, 24, 24, "bf16", "bf16_state"),
+    (64, 128, 2, 2, 20, 20, "f32", "bf16_state"),
 ]
 
 
