@@ -38,7 +38,22 @@ def _eager_round(S, A, r_in, b_sel=None):
 
 @pytest.mark.parametrize("copy", ["none", "bf16"])
 def test_verify_rollback_matches_committed_stream(copy):
-    wl = _spec_wl(read_copy=copy)
+    _rounds_against_oracle(_spec_wl(read_copy=copy))
+
+
+# The matrix-core ring terms of a bf16 verify at the shapes their blocking
+# meets: N = 16 (half of each 32-wide K slice empty), N = 256, row counts that
+# leave a partial 16-row block (P = 17, 100, 1), K + 1 = 8 outputs, a window
+# of 27 positions (two 16-entry blocks), and grouped B rows.
+@pytest.mark.parametrize("P,N,H,G,W,R,K", [(17, 16, 2, 1, 6, 14, 7), (100, 256, 2, 2, 5, 10, 3),
+                                           (64, 128, 3, 3, 20, 27, 7), (1, 32, 2, 1, 1, 3, 2)])
+def test_verify_ring_term_shapes(P, N, H, G, W, R, K):
+    _rounds_against_oracle(_spec_wl(headdim=P, dstate=N, nheads=H, ngroups=G, window=W, capacity=R,
+                                    max_draft=K, draft=K, rounds=8, batch=3, seed=4100 + P + N))
+
+
+def _rounds_against_oracle(wl):
+    copy = wl.read_copy
     log(f"[spec] {wl} ")
     cfg = cfg_of(wl)
     A_np = synth.params(wl)["A"]
