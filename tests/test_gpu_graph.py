@@ -18,12 +18,16 @@ from gpu_util import DEV, cfg_of, dev_inputs, log
 pytestmark = pytest.mark.gpu
 
 
-def test_captured_window_replays_match_eager_calls():
+# every checkpoint precision: fp32 (fold fused into the replay), dual (replay of
+# the bf16 copy, then the flush of the master), a bf16-stored checkpoint (folded
+# on the bf16 matrix cores inside the two-wavefront decode)
+@pytest.mark.parametrize("copy", ["none", "bf16", "bf16_state"])
+def test_captured_window_replays_match_eager_calls(copy):
     wl = workloads.get("tiny_b2_h4_p16_n16_w8").replace(
         name="graph", batch=4, nheads=4, ngroups=2, headdim=64, dstate=128, window=4, capacity=4,
-        in_dtype="bf16", s0="normal", seed=9100)
+        in_dtype="bf16", read_copy=copy, s0="normal", seed=9100)
     W = wl.window
-    log(f"[graph] capture {W} decode steps (the last fused with the fold), replay 3 times")
+    log(f"[graph] {copy}: capture {W} decode steps (the last fused with the fold), replay 3 times")
     cfg = cfg_of(wl)
     A = torch.from_numpy(synth.params(wl)["A"]).to(DEV)
     S0 = torch.from_numpy(synth.initial_state(wl)).to(DEV)
@@ -68,6 +72,8 @@ def test_captured_window_replays_match_eager_calls():
         for t in range(W):
             assert torch.equal(ys[t], y_ref[t]), (rep, t)
         assert torch.equal(cap.ckpt, ref.ckpt), rep
+        if copy == "bf16":
+            assert torch.equal(cap.ckpt_lo, ref.ckpt_lo), rep
         assert torch.equal(cap.ptr, ref.ptr), rep
         assert torch.equal(cap.ring_x, ref.ring_x) and torch.equal(cap.ring_B, ref.ring_B), rep
         _ = torch.ones(1000, device=DEV).sum().item()   # eager work between replays
