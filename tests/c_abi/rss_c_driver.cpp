@@ -1,17 +1,22 @@
 // A plain C++ caller of librss: no torch, no Python. It allocates every buffer
-// itself from rss_buffer_sizes, binds a layer, runs a decode loop through the C
-// entry points and writes the outputs, the final checkpoint and the pointers
-// to a file, so that a test can check them against the fp64 oracle.
+// itself from rss_buffer_sizes, binds a layer, runs a decode loop and then
+// speculative rounds through the C entry points, and writes the outputs, the
+// final checkpoint and the pointers to a file, so that a test can check them
+// against the fp64 oracle.
 //
 // usage: rss_c_driver <input> <output>
-//   input  (little-endian): int32 header[11] = {magic 0x52535331, Bt, H, P, N,
-//          G, W, R, T, has_S0, fused}; fp32 A[H]; fp32 S0[Bt*H*P*N] if has_S0;
-//          then per step t < T: fp32 x[Bt*H*P], B[Bt*G*N], C[Bt*G*N], dt[Bt*H].
-//   output: fp32 y[T][Bt*H*P]; fp32 ckpt[Bt*H*P*N]; int32 ptr[Bt*H*4];
-//          int32 device error word.
+//   input  (little-endian): int32 header[14] = {magic 0x52535332, Bt, H, P, N,
+//          G, W, R, T, has_S0, fused, K, rounds, bf16}; fp32 A[H]; fp32
+//          S0[Bt*H*P*N] if has_S0; then per step t < T: x[Bt*H*P],
+//          B[Bt*G*N], C[Bt*G*N] (fp32, or raw bf16 bits if bf16), fp32
+//          dt[Bt*H]; then per round: x[Bt*(K+1)*H*P], B and C[Bt*(K+1)*G*N]
+//          (same element type), fp32 dt[Bt*(K+1)*H], int32 n_drop[Bt].
+//   output: fp32 y[T][Bt*H*P]; fp32 yr[rounds][Bt*(K+1)*H*P]; fp32
+//          ckpt[Bt*H*P*N]; int32 ptr[Bt*H*4]; int32 device error word.
 // fused = 0 runs rss_decode_step then rss_flush_checkpoint(W) every step;
-// fused = 1 runs rss_decode_flush_step(W). Exit status 0 only if every call
-// returned RSS_OK.
+// fused = 1 runs rss_decode_flush_step(W). A round is
+// rss_verify_k_tokens_fold(W, K) then rss_rollback(n_drop). Exit status 0 only
+// if every call returned RSS_OK.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -48,21 +53,26 @@ int main(int argc, char** argv) {
   }
   FILE* in = std::fopen(argv[1], "rb");
   if (!in) return fail("open input", -1);
-  int32_t hd[11];
-  if (!read_all(in, hd, sizeof(hd)) || hd[0] != 0x52535331) return fail("input header", -1);
+  int32_t hd[14];
+  if (!read_all(in, hd, sizeof(hd)) || hd[0] != 0x52535332) return fail("input header", -1);
   const int Bt = hd[1], H = hd[2], P = hd[3], N = hd[4], G = hd[5], W = hd[6], R = hd[7],
-            T = hd[8], has_s0 = hd[9], fused = hd[10];
+            T = hd[8], has_s0 = hd[9], fused = hd[10], K = hd[11], rounds = hd[12], bf16 = hd[13];
+  const size_t es = bf16 ? 2 : 4;  // bytes per x, B, C element
   const size_t nS = (size_t)Bt * H * P * N, nx = (size_t)Bt * H * P, nB = (size_t)Bt * G * N,
                ndt = (size_t)Bt * H;
+  const size_t step_bytes = (nx + 2 * nB) * es + ndt * 4;
+  const size_t round_bytes = (size_t)(K + 1) * step_bytes + (size_t)Bt * 4;
 
-  rss_config cfg = {Bt, H, P, N, G, W, R, 0, RSS_DTYPE_F32, RSS_COPY_NONE, RSS_KIND_MAMBA2};
+  rss_config cfg = {Bt, H, P, N, G, W, R, K, bf16 ? RSS_DTYPE_BF16 : RSS_DTYPE_F32, RSS_COPY_NONE,
+                    RSS_KIND_MAMBA2};
   rss_sizes sz;
   int st = rss_buffer_sizes(&cfg, &sz);
   if (st != RSS_OK) return fail("rss_buffer_sizes", st);
 
-  std::vector<float> A(H), S0(has_s0 ? nS : 0), steps((size_t)T * (nx + 2 * nB + ndt));
+  std::vector<float> A(H), S0(has_s0 ? nS : 0);
+  std::vector<unsigned char> steps((size_t)T * step_bytes), rnds((size_t)rounds * round_bytes);
   if (!read_all(in, A.data(), A.size() * 4) || !read_all(in, S0.data(), S0.size() * 4) ||
-      !read_all(in, steps.data(), steps.size() * 4))
+      !read_all(in, steps.data(), steps.size()) || !read_all(in, rnds.data(), rnds.size()))
     return fail("input body", -1);
   std::fclose(in);
 
@@ -81,16 +91,21 @@ int main(int argc, char** argv) {
   dev.dev_err = static_cast<int32_t*>(p[7]);
   HIP_OK(hipMemcpy(p[6], A.data(), sz.A, hipMemcpyHostToDevice));
 
-  float *dS0 = nullptr, *dx, *dB, *dC, *ddt, *dy;
+  // input buffers sized for a round of K + 1 tokens (a decode step uses the first)
+  const size_t nt = (size_t)K + 1;
+  float *dS0 = nullptr, *ddt, *dy;
+  void *dx, *dB, *dC;
+  int32_t* dndrop;
   if (has_s0) {
     HIP_OK(hipMalloc(&dS0, nS * 4));
     HIP_OK(hipMemcpy(dS0, S0.data(), nS * 4, hipMemcpyHostToDevice));
   }
-  HIP_OK(hipMalloc(&dx, nx * 4));
-  HIP_OK(hipMalloc(&dB, nB * 4));
-  HIP_OK(hipMalloc(&dC, nB * 4));
-  HIP_OK(hipMalloc(&ddt, ndt * 4));
-  HIP_OK(hipMalloc(&dy, nx * 4));
+  HIP_OK(hipMalloc(&dx, nt * nx * es));
+  HIP_OK(hipMalloc(&dB, nt * nB * es));
+  HIP_OK(hipMalloc(&dC, nt * nB * es));
+  HIP_OK(hipMalloc(&ddt, nt * ndt * 4));
+  HIP_OK(hipMalloc(&dy, nt * nx * 4));
+  HIP_OK(hipMalloc(&dndrop, (size_t)Bt * 4 + 16));
 
   rss_layer* layer = nullptr;
   st = rss_layer_bind(&cfg, &dev, &layer);
@@ -100,14 +115,14 @@ int main(int argc, char** argv) {
   st = rss_init_state(layer, dS0, s);
   if (st != RSS_OK) return fail("rss_init_state", st);
 
-  std::vector<float> y((size_t)T * nx);
-  const float* src = steps.data();
+  std::vector<float> y((size_t)T * nx), yr((size_t)rounds * nt * nx);
+  const unsigned char* src = steps.data();
   for (int t = 0; t < T; ++t) {
-    HIP_OK(hipMemcpyAsync(dx, src, nx * 4, hipMemcpyHostToDevice, s));
-    HIP_OK(hipMemcpyAsync(dB, src + nx, nB * 4, hipMemcpyHostToDevice, s));
-    HIP_OK(hipMemcpyAsync(dC, src + nx + nB, nB * 4, hipMemcpyHostToDevice, s));
-    HIP_OK(hipMemcpyAsync(ddt, src + nx + 2 * nB, ndt * 4, hipMemcpyHostToDevice, s));
-    src += nx + 2 * nB + ndt;
+    HIP_OK(hipMemcpyAsync(dx, src, nx * es, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dB, src + nx * es, nB * es, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dC, src + (nx + nB) * es, nB * es, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(ddt, src + (nx + 2 * nB) * es, ndt * 4, hipMemcpyHostToDevice, s));
+    src += step_bytes;
     if (fused) {
       st = rss_decode_flush_step(layer, W, dx, dB, dC, ddt, dy, s);
       if (st != RSS_OK) return fail("rss_decode_flush_step", st);
@@ -118,6 +133,20 @@ int main(int argc, char** argv) {
       if (st != RSS_OK) return fail("rss_flush_checkpoint", st);
     }
     HIP_OK(hipMemcpyAsync(y.data() + (size_t)t * nx, dy, nx * 4, hipMemcpyDeviceToHost, s));
+  }
+  src = rnds.data();
+  for (int r = 0; r < rounds; ++r) {
+    HIP_OK(hipMemcpyAsync(dx, src, nt * nx * es, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dB, src + nt * nx * es, nt * nB * es, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dC, src + nt * (nx + nB) * es, nt * nB * es, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(ddt, src + nt * (nx + 2 * nB) * es, nt * ndt * 4, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dndrop, src + nt * step_bytes, (size_t)Bt * 4, hipMemcpyHostToDevice, s));
+    src += round_bytes;
+    st = rss_verify_k_tokens_fold(layer, W, K, dx, dB, dC, ddt, dy, s);
+    if (st != RSS_OK) return fail("rss_verify_k_tokens_fold", st);
+    st = rss_rollback(layer, dndrop, s);
+    if (st != RSS_OK) return fail("rss_rollback", st);
+    HIP_OK(hipMemcpyAsync(yr.data() + (size_t)r * nt * nx, dy, nt * nx * 4, hipMemcpyDeviceToHost, s));
   }
   int32_t err = -1;
   st = rss_get_device_error(layer, &err, s);  // synchronises the stream
@@ -130,6 +159,7 @@ int main(int argc, char** argv) {
   FILE* out = std::fopen(argv[2], "wb");
   if (!out) return fail("open output", -1);
   const bool ok = std::fwrite(y.data(), 4, y.size(), out) == y.size() &&
+                  std::fwrite(yr.data(), 4, yr.size(), out) == yr.size() &&
                   std::fwrite(ck.data(), 4, ck.size(), out) == ck.size() &&
                   std::fwrite(ptr.data(), 4, ptr.size(), out) == ptr.size() &&
                   std::fwrite(&err, 4, 1, out) == 1;
@@ -140,7 +170,7 @@ int main(int argc, char** argv) {
   HIP_OK(hipStreamDestroy(s));
   for (void* q : p)
     if (q) HIP_OK(hipFree(q));
-  for (float* q : {dS0, dx, dB, dC, ddt, dy})
+  for (void* q : {(void*)dS0, dx, dB, dC, (void*)ddt, (void*)dy, (void*)dndrop})
     if (q) HIP_OK(hipFree(q));
   return 0;
 }

@@ -1,8 +1,9 @@
 """The C ABI from a plain C++ caller: tests/c_abi/rss_c_driver (built by
 __graft_entry__.build(); no torch, no Python) allocates every buffer from
-rss_buffer_sizes with hipMalloc, binds a layer and runs init + decode (+ fold)
-through the C entry points. Its outputs, final checkpoint and pointers are
-checked here against the fp64 oracle and the integer ring model."""
+rss_buffer_sizes with hipMalloc, binds a layer and runs init + decode (+ fold),
+then speculative rounds (verify with fold, rollback), through the C entry
+points. Its outputs, final checkpoint and pointers are checked here against
+the fp64 oracle and the integer ring model."""
 import os
 import subprocess
 
@@ -21,21 +22,38 @@ DRIVER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "rss_
 BASE = workloads.get("tiny_b2_h4_p16_n16_w8")
 
 
-def _run_driver(tmp_path, wl, T, fused):
+def _write_tokens(f, s, bf16):
+    for k in ("x", "B", "C"):
+        if bf16:
+            f.write(np.ascontiguousarray(s[k + "_bits"]).astype(np.uint16).tobytes())
+        else:
+            f.write(np.ascontiguousarray(s[k], dtype=np.float32).tobytes())
+    f.write(np.ascontiguousarray(s["dt"], dtype=np.float32).tobytes())
+
+
+def _run_driver(tmp_path, wl, T, fused, rounds=0):
+    """Run the C++ caller: T decode steps, then `rounds` speculative rounds of
+    wl.draft drafts with the seeded acceptances."""
     A = synth.params(wl)["A"].astype(np.float32)
     S0 = synth.initial_state(wl).astype(np.float32)
     has_s0 = int(np.any(S0 != 0))
-    hdr = np.array([0x52535331, wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window,
-                    wl.capacity, T, has_s0, int(fused)], dtype=np.int32)
+    bf16 = int(wl.in_dtype == "bf16")
+    K = wl.draft if rounds else 0
+    hdr = np.array([0x52535332, wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window,
+                    wl.capacity, T, has_s0, int(fused), K, rounds, bf16], dtype=np.int32)
     steps = [synth.step_inputs(wl, t) for t in range(T)]
+    rins = [synth.draft_inputs(wl, r) for r in range(rounds)]
+    naccs = [synth.accepted_drafts(wl, r) for r in range(rounds)]
     with open(tmp_path / "in.bin", "wb") as f:
         f.write(hdr.tobytes())
         f.write(A.tobytes())
         if has_s0:
             f.write(np.ascontiguousarray(S0).tobytes())
         for s in steps:
-            for k in ("x", "B", "C", "dt"):
-                f.write(np.ascontiguousarray(s[k], dtype=np.float32).tobytes())
+            _write_tokens(f, s, bf16)
+        for rin, nacc in zip(rins, naccs):
+            _write_tokens(f, rin, bf16)
+            f.write((K - nacc).astype(np.int32).tobytes())
     if not os.path.exists(DRIVER):
         pytest.fail(f"{DRIVER} is not built; run __graft_entry__.build() first")
     r = subprocess.run([DRIVER, str(tmp_path / "in.bin"), str(tmp_path / "out.bin")],
@@ -43,12 +61,14 @@ def _run_driver(tmp_path, wl, T, fused):
     assert r.returncode == 0, r.stderr
     Bt, H, P, N = wl.batch, wl.nheads, wl.headdim, wl.dstate
     raw = open(tmp_path / "out.bin", "rb").read()
-    ny, nS, nptr = T * Bt * H * P, Bt * H * P * N, Bt * H * 4
+    ny, nyr, nS, nptr = T * Bt * H * P, rounds * Bt * (K + 1) * H * P, Bt * H * P * N, Bt * H * 4
+    assert len(raw) == 4 * (ny + nyr + nS + nptr + 1)
     y = np.frombuffer(raw, np.float32, ny).reshape(T, Bt, H, P)
-    ck = np.frombuffer(raw, np.float32, nS, offset=4 * ny).reshape(Bt, H, P, N)
-    ptr = np.frombuffer(raw, np.int32, nptr, offset=4 * (ny + nS)).reshape(Bt, H, 4)
-    err = int(np.frombuffer(raw, np.int32, 1, offset=4 * (ny + nS + nptr))[0])
-    return steps, A, S0, y, ck, ptr, err
+    yr = np.frombuffer(raw, np.float32, nyr, offset=4 * ny).reshape(rounds, Bt, K + 1, H, P)
+    ck = np.frombuffer(raw, np.float32, nS, offset=4 * (ny + nyr)).reshape(Bt, H, P, N)
+    ptr = np.frombuffer(raw, np.int32, nptr, offset=4 * (ny + nyr + nS)).reshape(Bt, H, 4)
+    err = int(np.frombuffer(raw, np.int32, 1, offset=4 * (ny + nyr + nS + nptr))[0])
+    return dict(steps=steps, rins=rins, naccs=naccs, A=A, S0=S0, y=y, yr=yr, ck=ck, ptr=ptr, err=err)
 
 
 @pytest.mark.parametrize("shape,fused", [
@@ -63,8 +83,9 @@ def test_c_caller_matches_oracle(tmp_path, shape, fused):
                       capacity=R, s0="normal", seed=7000 + P + N + G)
     T = 3 * W + 2
     log(f"[c-abi] Bt={Bt} H={H} P={P} N={N} G={G} W={W} R={R} fused={fused}, {T} steps")
-    steps, A, S0, y, ck, ptr, err = _run_driver(tmp_path, wl, T, fused)
-    assert err == 0
+    out = _run_driver(tmp_path, wl, T, fused)
+    steps, A, S0, y, ck, ptr = (out[k] for k in ("steps", "A", "S0", "y", "ck", "ptr"))
+    assert out["err"] == 0
     S = S0.astype(np.float64)
     pm = PointerModel(Bt, R)
     worst, ys, refs = 0.0, [], []
@@ -86,3 +107,65 @@ def test_c_caller_matches_oracle(tmp_path, shape, fused):
     for s in steps[:T - T % W]:
         S_f, _ = mamba2.eager_step(S_f, A, s["x"], s["B"], s["C"], s["dt"])
     assert rel_l2(ck.astype(np.float64), S_f) < 1e-5
+
+
+# Decode steps, then speculative rounds of rss_verify_k_tokens_fold(W, K) and
+# rss_rollback from the C++ caller. bf16 inputs take the matrix-core ring
+# terms; grouped B rows need R >= W + 2K + 1, one B row set per head R >= W + K.
+@pytest.mark.parametrize("shape,in_dtype", [
+    ((2, 4, 16, 16, 4, 8, 12, 4), "f32"),
+    ((3, 4, 64, 128, 2, 8, 15, 3), "bf16"),
+    ((2, 3, 37, 32, 3, 5, 12, 7), "bf16"),
+    ((2, 2, 64, 128, 1, 16, 25, 4), "f32"),
+], ids=["tiny-f32", "P64N128-G2-bf16", "P37N32-K7-bf16", "P64N128-G1-f32"])
+def test_c_caller_speculative_rounds(tmp_path, shape, in_dtype):
+    Bt, H, P, N, G, W, R, K = shape
+    wl = BASE.replace(name="c-abi-spec", batch=Bt, nheads=H, headdim=P, dstate=N, ngroups=G, window=W,
+                      capacity=R, max_draft=K, draft=K, in_dtype=in_dtype, s0="normal",
+                      seed=7100 + P + N + G + K)
+    T, rounds = W + 3, 10
+    log(f"[c-abi spec] Bt={Bt} H={H} P={P} N={N} G={G} W={W} R={R} K={K} {in_dtype}, "
+        f"{T} steps + {rounds} rounds")
+    out = _run_driver(tmp_path, wl, T, True, rounds)
+    assert out["err"] == 0
+    A = out["A"]
+    S = out["S0"].astype(np.float64)
+    hist = [[S[b]] for b in range(Bt)]     # committed states of each sequence
+    pm = PointerModel(Bt, R)
+    ys, refs = [], []
+    for t, s in enumerate(out["steps"]):
+        S, y_ref = mamba2.eager_step(S, A, s["x"], s["B"], s["C"], s["dt"])
+        ys.append(out["y"][t])
+        refs.append(y_ref)
+        for b in range(Bt):
+            hist[b].append(S[b])
+            pm.append(b, 1)
+            pm.flush(b, W)
+    worst = 0.0
+    for r, (rin, nacc) in enumerate(zip(out["rins"], out["naccs"])):
+        states, y_ref = [], []
+        Sr = S
+        for i in range(K + 1):
+            Sr, yi = mamba2.eager_step(Sr, A, rin["x"][:, i], rin["B"][:, i], rin["C"][:, i], rin["dt"][:, i])
+            states.append(Sr)
+            y_ref.append(yi)
+        y_ref = np.stack(y_ref, axis=1)
+        worst = max(worst, rel_l2(out["yr"][r].astype(np.float64), y_ref))
+        ys.append(out["yr"][r])
+        refs.append(y_ref)
+        S = np.stack([states[nacc[b]][b] for b in range(Bt)])
+        for b in range(Bt):
+            pm.flush(b, W)
+            pm.append(b, K + 1)
+            pm.mark_tentative(b, K + 1)
+            pm.rollback(b, int(K - nacc[b]))
+            hist[b].extend(states[i][b] for i in range(nacc[b] + 1))
+    run = rel_l2(np.concatenate([a.ravel() for a in ys]).astype(np.float64),
+                 np.concatenate([a.ravel() for a in refs]))
+    log(f"  worst round {worst:.2e}, run {run:.2e}")
+    assert worst < 1e-5 and run < 1e-5
+    for h in range(H):
+        assert np.array_equal(out["ptr"][:, h, :3], pm.as_array())
+    # each checkpoint holds the state before its sequence's open window
+    ck_ref = np.stack([hist[b][len(hist[b]) - 1 - int(pm.len[b])] for b in range(Bt)])
+    assert rel_l2(out["ck"].astype(np.float64), ck_ref) < 1e-5
