@@ -5,14 +5,16 @@
 // against the fp64 oracle.
 //
 // usage: rss_c_driver <input> <output>
-//   input  (little-endian): int32 header[14] = {magic 0x52535332, Bt, H, P, N,
-//          G, W, R, T, has_S0, fused, K, rounds, bf16}; fp32 A[H]; fp32
+//   input  (little-endian): int32 header[15] = {magic 0x52535333, Bt, H, P, N,
+//          G, W, R, T, has_S0, fused, K, rounds, bf16, read_copy}; fp32 A[H]; fp32
 //          S0[Bt*H*P*N] if has_S0; then per step t < T: x[Bt*H*P],
 //          B[Bt*G*N], C[Bt*G*N] (fp32, or raw bf16 bits if bf16), fp32
 //          dt[Bt*H]; then per round: x[Bt*(K+1)*H*P], B and C[Bt*(K+1)*G*N]
 //          (same element type), fp32 dt[Bt*(K+1)*H], int32 n_drop[Bt].
-//   output: fp32 y[T][Bt*H*P]; fp32 yr[rounds][Bt*(K+1)*H*P]; fp32
-//          ckpt[Bt*H*P*N]; int32 ptr[Bt*H*4]; int32 device error word.
+//   output: fp32 y[T][Bt*H*P]; fp32 yr[rounds][Bt*(K+1)*H*P]; the ckpt
+//          buffer's bytes (fp32, or bf16 with read_copy = RSS_STATE_BF16);
+//          the ckpt_lo buffer's bytes (bf16, read_copy = RSS_COPY_BF16 only);
+//          int32 ptr[Bt*H*4]; int32 device error word.
 // fused = 0 runs rss_decode_step then rss_flush_checkpoint(W) every step;
 // fused = 1 runs rss_decode_flush_step(W). A round is
 // rss_verify_k_tokens_fold(W, K) then rss_rollback(n_drop). Exit status 0 only
@@ -53,17 +55,18 @@ int main(int argc, char** argv) {
   }
   FILE* in = std::fopen(argv[1], "rb");
   if (!in) return fail("open input", -1);
-  int32_t hd[14];
-  if (!read_all(in, hd, sizeof(hd)) || hd[0] != 0x52535332) return fail("input header", -1);
+  int32_t hd[15];
+  if (!read_all(in, hd, sizeof(hd)) || hd[0] != 0x52535333) return fail("input header", -1);
   const int Bt = hd[1], H = hd[2], P = hd[3], N = hd[4], G = hd[5], W = hd[6], R = hd[7],
-            T = hd[8], has_s0 = hd[9], fused = hd[10], K = hd[11], rounds = hd[12], bf16 = hd[13];
+            T = hd[8], has_s0 = hd[9], fused = hd[10], K = hd[11], rounds = hd[12], bf16 = hd[13],
+            copy = hd[14];
   const size_t es = bf16 ? 2 : 4;  // bytes per x, B, C element
   const size_t nS = (size_t)Bt * H * P * N, nx = (size_t)Bt * H * P, nB = (size_t)Bt * G * N,
                ndt = (size_t)Bt * H;
   const size_t step_bytes = (nx + 2 * nB) * es + ndt * 4;
   const size_t round_bytes = (size_t)(K + 1) * step_bytes + (size_t)Bt * 4;
 
-  rss_config cfg = {Bt, H, P, N, G, W, R, K, bf16 ? RSS_DTYPE_BF16 : RSS_DTYPE_F32, RSS_COPY_NONE,
+  rss_config cfg = {Bt, H, P, N, G, W, R, K, bf16 ? RSS_DTYPE_BF16 : RSS_DTYPE_F32, copy,
                     RSS_KIND_MAMBA2};
   rss_sizes sz;
   int st = rss_buffer_sizes(&cfg, &sz);
@@ -151,16 +154,18 @@ int main(int argc, char** argv) {
   int32_t err = -1;
   st = rss_get_device_error(layer, &err, s);  // synchronises the stream
   if (st != RSS_OK) return fail("rss_get_device_error", st);
-  std::vector<float> ck(nS);
+  std::vector<unsigned char> ck(sz.ckpt), cl(sz.ckpt_lo);
   std::vector<int32_t> ptr((size_t)Bt * H * 4);
-  HIP_OK(hipMemcpy(ck.data(), p[0], nS * 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(ck.data(), p[0], sz.ckpt, hipMemcpyDeviceToHost));
+  if (sz.ckpt_lo) HIP_OK(hipMemcpy(cl.data(), p[1], sz.ckpt_lo, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(ptr.data(), p[5], ptr.size() * 4, hipMemcpyDeviceToHost));
 
   FILE* out = std::fopen(argv[2], "wb");
   if (!out) return fail("open output", -1);
   const bool ok = std::fwrite(y.data(), 4, y.size(), out) == y.size() &&
                   std::fwrite(yr.data(), 4, yr.size(), out) == yr.size() &&
-                  std::fwrite(ck.data(), 4, ck.size(), out) == ck.size() &&
+                  std::fwrite(ck.data(), 1, ck.size(), out) == ck.size() &&
+                  std::fwrite(cl.data(), 1, cl.size(), out) == cl.size() &&
                   std::fwrite(ptr.data(), 4, ptr.size(), out) == ptr.size() &&
                   std::fwrite(&err, 4, 1, out) == 1;
   std::fclose(out);

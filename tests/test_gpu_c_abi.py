@@ -2,7 +2,7 @@
 __graft_entry__.build(); no torch, no Python) allocates every buffer from
 rss_buffer_sizes with hipMalloc, binds a layer and runs init + decode (+ fold),
 then speculative rounds (verify with fold, rollback), through the C entry
-points. Its outputs, final checkpoint and pointers are checked here against
+points, for each checkpoint precision. Its outputs, final checkpoint and pointers are checked here against
 the fp64 oracle and the integer ring model."""
 import os
 import subprocess
@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import mamba2
+from oracle.lowp import round_bf16_from_f32
 from oracle.ring import PointerModel
 import workloads
 from workloads import synth
@@ -20,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 DRIVER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "rss_c_driver")
 BASE = workloads.get("tiny_b2_h4_p16_n16_w8")
+COPY = {"none": 0, "bf16": 1, "bf16_state": 2}   # rss_config.read_copy codes (include/rss.h)
 
 
 def _write_tokens(f, s, bf16):
@@ -39,8 +41,9 @@ def _run_driver(tmp_path, wl, T, fused, rounds=0):
     has_s0 = int(np.any(S0 != 0))
     bf16 = int(wl.in_dtype == "bf16")
     K = wl.draft if rounds else 0
-    hdr = np.array([0x52535332, wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window,
-                    wl.capacity, T, has_s0, int(fused), K, rounds, bf16], dtype=np.int32)
+    copy = COPY[wl.read_copy]
+    hdr = np.array([0x52535333, wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window,
+                    wl.capacity, T, has_s0, int(fused), K, rounds, bf16, copy], dtype=np.int32)
     steps = [synth.step_inputs(wl, t) for t in range(T)]
     rins = [synth.draft_inputs(wl, r) for r in range(rounds)]
     naccs = [synth.accepted_drafts(wl, r) for r in range(rounds)]
@@ -62,13 +65,22 @@ def _run_driver(tmp_path, wl, T, fused, rounds=0):
     Bt, H, P, N = wl.batch, wl.nheads, wl.headdim, wl.dstate
     raw = open(tmp_path / "out.bin", "rb").read()
     ny, nyr, nS, nptr = T * Bt * H * P, rounds * Bt * (K + 1) * H * P, Bt * H * P * N, Bt * H * 4
-    assert len(raw) == 4 * (ny + nyr + nS + nptr + 1)
+    ck_bytes = nS * (2 if copy == 2 else 4)       # fp32 checkpoint, or the bf16-stored one
+    lo_bytes = nS * 2 if copy == 1 else 0         # bf16 read copy
+    assert len(raw) == 4 * (ny + nyr + nptr + 1) + ck_bytes + lo_bytes
     y = np.frombuffer(raw, np.float32, ny).reshape(T, Bt, H, P)
     yr = np.frombuffer(raw, np.float32, nyr, offset=4 * ny).reshape(rounds, Bt, K + 1, H, P)
-    ck = np.frombuffer(raw, np.float32, nS, offset=4 * (ny + nyr)).reshape(Bt, H, P, N)
-    ptr = np.frombuffer(raw, np.int32, nptr, offset=4 * (ny + nyr + nS)).reshape(Bt, H, 4)
-    err = int(np.frombuffer(raw, np.int32, 1, offset=4 * (ny + nyr + nS + nptr))[0])
-    return dict(steps=steps, rins=rins, naccs=naccs, A=A, S0=S0, y=y, yr=yr, ck=ck, ptr=ptr, err=err)
+    o = 4 * (ny + nyr)
+
+    def bf16_at(off):  # bf16 words -> float32 values
+        return (np.frombuffer(raw, np.uint16, nS, offset=off).astype(np.uint32) << 16).view(np.float32)
+    ck = bf16_at(o) if copy == 2 else np.frombuffer(raw, np.float32, nS, offset=o)
+    ck_lo = bf16_at(o + ck_bytes).reshape(Bt, H, P, N) if copy == 1 else None
+    o += ck_bytes + lo_bytes
+    ptr = np.frombuffer(raw, np.int32, nptr, offset=o).reshape(Bt, H, 4)
+    err = int(np.frombuffer(raw, np.int32, 1, offset=o + 4 * nptr)[0])
+    return dict(steps=steps, rins=rins, naccs=naccs, A=A, S0=S0, y=y, yr=yr, ck=ck.reshape(Bt, H, P, N),
+                ck_lo=ck_lo, ptr=ptr, err=err)
 
 
 @pytest.mark.parametrize("shape,fused", [
@@ -123,9 +135,41 @@ def test_c_caller_speculative_rounds(tmp_path, shape, in_dtype):
     wl = BASE.replace(name="c-abi-spec", batch=Bt, nheads=H, headdim=P, dstate=N, ngroups=G, window=W,
                       capacity=R, max_draft=K, draft=K, in_dtype=in_dtype, s0="normal",
                       seed=7100 + P + N + G + K)
+    out = _spec_run(tmp_path, wl)
+    assert out["worst"] < 1e-5 and out["run"] < 1e-5
+    assert rel_l2(out["ck"].astype(np.float64), out["ck_ref"]) < 1e-5
+
+
+# The other checkpoint precisions through the same raw-pointer calls: dual
+# precision (fp32 master for the fold, bf16 read copy for the outputs) and a
+# single bf16-stored checkpoint. Outputs against the exact recurrence at the
+# bf16-read bar (2e-2); the dual master at the fp32 bar and its read copy
+# bit for bit the round-to-nearest-even of the master.
+@pytest.mark.parametrize("copy,in_dtype", [("bf16", "bf16"), ("bf16", "f32"), ("bf16_state", "bf16"),
+                                           ("bf16_state", "f32")])
+def test_c_caller_checkpoint_precisions(tmp_path, copy, in_dtype):
+    Bt, H, P, N, G, W, R, K = 2, 4, 64, 128, 2, 8, 15, 3
+    wl = BASE.replace(name="c-abi-prec", batch=Bt, nheads=H, headdim=P, dstate=N, ngroups=G, window=W,
+                      capacity=R, max_draft=K, draft=K, in_dtype=in_dtype, read_copy=copy, s0="normal",
+                      seed=7200 + COPY[copy] + (in_dtype == "bf16"))
+    out = _spec_run(tmp_path, wl)
+    assert out["run"] < 2e-2
+    if copy == "bf16":
+        assert rel_l2(out["ck"].astype(np.float64), out["ck_ref"]) < 1e-5
+        assert np.array_equal(out["ck_lo"], round_bf16_from_f32(out["ck"]).astype(np.float32))
+    else:
+        assert rel_l2(out["ck"].astype(np.float64), out["ck_ref"]) < 2e-2
+
+
+def _spec_run(tmp_path, wl):
+    """W + 3 decode steps, then 10 rounds of verify-with-fold and rollback, from
+    the C++ caller; returns its outputs with the oracle's errors: worst round
+    and whole-run rel-L2 of the outputs, and each sequence's state just before
+    its open window (ck_ref). Pointers are checked against the ring model."""
+    Bt, H, R, K, W = wl.batch, wl.nheads, wl.capacity, wl.draft, wl.window
     T, rounds = W + 3, 10
-    log(f"[c-abi spec] Bt={Bt} H={H} P={P} N={N} G={G} W={W} R={R} K={K} {in_dtype}, "
-        f"{T} steps + {rounds} rounds")
+    log(f"[c-abi spec] Bt={Bt} H={H} P={wl.headdim} N={wl.dstate} G={wl.ngroups} W={W} R={R} K={K} "
+        f"{wl.in_dtype} read_copy={wl.read_copy}, {T} steps + {rounds} rounds")
     out = _run_driver(tmp_path, wl, T, True, rounds)
     assert out["err"] == 0
     A = out["A"]
@@ -163,9 +207,9 @@ def test_c_caller_speculative_rounds(tmp_path, shape, in_dtype):
     run = rel_l2(np.concatenate([a.ravel() for a in ys]).astype(np.float64),
                  np.concatenate([a.ravel() for a in refs]))
     log(f"  worst round {worst:.2e}, run {run:.2e}")
-    assert worst < 1e-5 and run < 1e-5
     for h in range(H):
         assert np.array_equal(out["ptr"][:, h, :3], pm.as_array())
     # each checkpoint holds the state before its sequence's open window
-    ck_ref = np.stack([hist[b][len(hist[b]) - 1 - int(pm.len[b])] for b in range(Bt)])
-    assert rel_l2(out["ck"].astype(np.float64), ck_ref) < 1e-5
+    out["ck_ref"] = np.stack([hist[b][len(hist[b]) - 1 - int(pm.len[b])] for b in range(Bt)])
+    out["worst"], out["run"] = worst, run
+    return out
