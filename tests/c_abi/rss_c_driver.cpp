@@ -5,18 +5,22 @@
 // against the fp64 oracle.
 //
 // usage: rss_c_driver <input> <output>
-//   input  (little-endian): int32 header[15] = {magic 0x52535333, Bt, H, P, N,
-//          G, W, R, T, has_S0, fused, K, rounds, bf16, read_copy}; fp32 A[H]; fp32
-//          S0[Bt*H*P*N] if has_S0; then per step t < T: x[Bt*H*P],
-//          B[Bt*G*N], C[Bt*G*N] (fp32, or raw bf16 bits if bf16), fp32
-//          dt[Bt*H]; then per round: x[Bt*(K+1)*H*P], B and C[Bt*(K+1)*G*N]
-//          (same element type), fp32 dt[Bt*(K+1)*H], int32 n_drop[Bt].
+//   input  (little-endian): int32 header[16] = {magic 0x52535334, Bt, H, P, N,
+//          G, W, R, T, has_S0, fused, K, rounds, bf16, read_copy, kind}; fp32
+//          A[H]; fp32 S0[Bt*H*P*N] if has_S0; then per step t < T:
+//          Mamba-2: x[Bt*H*P], B[Bt*G*N], C[Bt*G*N] (fp32, or raw bf16 bits if
+//          bf16), fp32 dt[Bt*H]; Gated DeltaNet / KDA (fp32, K = rounds = 0):
+//          q[Bt*H*N], k[Bt*H*N], v[Bt*H*P], beta[Bt*H], alpha[Bt*H] (GDN) or
+//          [Bt*H*N] (KDA); then per round: x[Bt*(K+1)*H*P], B and
+//          C[Bt*(K+1)*G*N] (same element type), fp32 dt[Bt*(K+1)*H], int32
+//          n_drop[Bt].
 //   output: fp32 y[T][Bt*H*P]; fp32 yr[rounds][Bt*(K+1)*H*P]; the ckpt
 //          buffer's bytes (fp32, or bf16 with read_copy = RSS_STATE_BF16);
 //          the ckpt_lo buffer's bytes (bf16, read_copy = RSS_COPY_BF16 only);
 //          int32 ptr[Bt*H*4]; int32 device error word.
 // fused = 0 runs rss_decode_step then rss_flush_checkpoint(W) every step;
-// fused = 1 runs rss_decode_flush_step(W). A round is
+// fused = 1 runs rss_decode_flush_step(W) (the rss_gdn_ / rss_kda_ forms for
+// those kinds). A round is
 // rss_verify_k_tokens_fold(W, K) then rss_rollback(n_drop). Exit status 0 only
 // if every call returned RSS_OK.
 #include <hip/hip_runtime.h>
@@ -55,19 +59,22 @@ int main(int argc, char** argv) {
   }
   FILE* in = std::fopen(argv[1], "rb");
   if (!in) return fail("open input", -1);
-  int32_t hd[15];
-  if (!read_all(in, hd, sizeof(hd)) || hd[0] != 0x52535333) return fail("input header", -1);
+  int32_t hd[16];
+  if (!read_all(in, hd, sizeof(hd)) || hd[0] != 0x52535334) return fail("input header", -1);
   const int Bt = hd[1], H = hd[2], P = hd[3], N = hd[4], G = hd[5], W = hd[6], R = hd[7],
             T = hd[8], has_s0 = hd[9], fused = hd[10], K = hd[11], rounds = hd[12], bf16 = hd[13],
-            copy = hd[14];
+            copy = hd[14], kind = hd[15];
+  const bool delta = kind != RSS_KIND_MAMBA2;
+  if (delta && (K || rounds || bf16 || copy)) return fail("input header (delta-rule layer)", -1);
   const size_t es = bf16 ? 2 : 4;  // bytes per x, B, C element
   const size_t nS = (size_t)Bt * H * P * N, nx = (size_t)Bt * H * P, nB = (size_t)Bt * G * N,
                ndt = (size_t)Bt * H;
-  const size_t step_bytes = (nx + 2 * nB) * es + ndt * 4;
+  // delta rules: q, k [Bt*H*N], v [Bt*H*P], beta [Bt*H], alpha [Bt*H] or [Bt*H*N]
+  const size_t nq = (size_t)Bt * H * N, nal = kind == RSS_KIND_KDA ? nq : ndt;
+  const size_t step_bytes = delta ? (2 * nq + nx + ndt + nal) * 4 : (nx + 2 * nB) * es + ndt * 4;
   const size_t round_bytes = (size_t)(K + 1) * step_bytes + (size_t)Bt * 4;
 
-  rss_config cfg = {Bt, H, P, N, G, W, R, K, bf16 ? RSS_DTYPE_BF16 : RSS_DTYPE_F32, copy,
-                    RSS_KIND_MAMBA2};
+  rss_config cfg = {Bt, H, P, N, G, W, R, K, bf16 ? RSS_DTYPE_BF16 : RSS_DTYPE_F32, copy, kind};
   rss_sizes sz;
   int st = rss_buffer_sizes(&cfg, &sz);
   if (st != RSS_OK) return fail("rss_buffer_sizes", st);
@@ -92,7 +99,7 @@ int main(int argc, char** argv) {
   dev.ptr = static_cast<int32_t*>(p[5]);
   dev.A = static_cast<const float*>(p[6]);
   dev.dev_err = static_cast<int32_t*>(p[7]);
-  HIP_OK(hipMemcpy(p[6], A.data(), sz.A, hipMemcpyHostToDevice));
+  if (sz.A) HIP_OK(hipMemcpy(p[6], A.data(), sz.A, hipMemcpyHostToDevice));
 
   // input buffers sized for a round of K + 1 tokens (a decode step uses the first)
   const size_t nt = (size_t)K + 1;
@@ -109,6 +116,14 @@ int main(int argc, char** argv) {
   HIP_OK(hipMalloc(&ddt, nt * ndt * 4));
   HIP_OK(hipMalloc(&dy, nt * nx * 4));
   HIP_OK(hipMalloc(&dndrop, (size_t)Bt * 4 + 16));
+  float *dq = nullptr, *dk = nullptr, *dv = nullptr, *dbeta = nullptr, *dalpha = nullptr;
+  if (delta) {
+    HIP_OK(hipMalloc(&dq, nq * 4));
+    HIP_OK(hipMalloc(&dk, nq * 4));
+    HIP_OK(hipMalloc(&dv, nx * 4));
+    HIP_OK(hipMalloc(&dbeta, ndt * 4));
+    HIP_OK(hipMalloc(&dalpha, nal * 4));
+  }
 
   rss_layer* layer = nullptr;
   st = rss_layer_bind(&cfg, &dev, &layer);
@@ -120,7 +135,29 @@ int main(int argc, char** argv) {
 
   std::vector<float> y((size_t)T * nx), yr((size_t)rounds * nt * nx);
   const unsigned char* src = steps.data();
-  for (int t = 0; t < T; ++t) {
+  for (int t = 0; t < T && delta; ++t) {
+    const float* f = reinterpret_cast<const float*>(src);
+    HIP_OK(hipMemcpyAsync(dq, f, nq * 4, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dk, f + nq, nq * 4, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dv, f + 2 * nq, nx * 4, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dbeta, f + 2 * nq + nx, ndt * 4, hipMemcpyHostToDevice, s));
+    HIP_OK(hipMemcpyAsync(dalpha, f + 2 * nq + nx + ndt, nal * 4, hipMemcpyHostToDevice, s));
+    src += step_bytes;
+    const bool kda = kind == RSS_KIND_KDA;
+    if (fused) {
+      st = kda ? rss_kda_decode_flush_step(layer, W, dq, dk, dv, dbeta, dalpha, dy, s)
+               : rss_gdn_decode_flush_step(layer, W, dq, dk, dv, dbeta, dalpha, dy, s);
+      if (st != RSS_OK) return fail("rss_*_decode_flush_step", st);
+    } else {
+      st = kda ? rss_kda_decode_step(layer, dq, dk, dv, dbeta, dalpha, dy, s)
+               : rss_gdn_decode_step(layer, dq, dk, dv, dbeta, dalpha, dy, s);
+      if (st != RSS_OK) return fail("rss_*_decode_step", st);
+      st = rss_flush_checkpoint(layer, W, s);
+      if (st != RSS_OK) return fail("rss_flush_checkpoint", st);
+    }
+    HIP_OK(hipMemcpyAsync(y.data() + (size_t)t * nx, dy, nx * 4, hipMemcpyDeviceToHost, s));
+  }
+  for (int t = 0; t < T && !delta; ++t) {
     HIP_OK(hipMemcpyAsync(dx, src, nx * es, hipMemcpyHostToDevice, s));
     HIP_OK(hipMemcpyAsync(dB, src + nx * es, nB * es, hipMemcpyHostToDevice, s));
     HIP_OK(hipMemcpyAsync(dC, src + (nx + nB) * es, nB * es, hipMemcpyHostToDevice, s));
@@ -175,7 +212,8 @@ int main(int argc, char** argv) {
   HIP_OK(hipStreamDestroy(s));
   for (void* q : p)
     if (q) HIP_OK(hipFree(q));
-  for (void* q : {(void*)dS0, dx, dB, dC, (void*)ddt, (void*)dy, (void*)dndrop})
+  for (void* q : {(void*)dS0, dx, dB, dC, (void*)ddt, (void*)dy, (void*)dndrop, (void*)dq, (void*)dk,
+                  (void*)dv, (void*)dbeta, (void*)dalpha})
     if (q) HIP_OK(hipFree(q));
   return 0;
 }

@@ -10,7 +10,7 @@ import subprocess
 import numpy as np
 import pytest
 
-from oracle import mamba2
+from oracle import gdn, kda, mamba2
 from oracle.lowp import round_bf16_from_f32
 from oracle.ring import PointerModel
 import workloads
@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 DRIVER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "rss_c_driver")
 BASE = workloads.get("tiny_b2_h4_p16_n16_w8")
 COPY = {"none": 0, "bf16": 1, "bf16_state": 2}   # rss_config.read_copy codes (include/rss.h)
+KIND = {"mamba2": 0, "gdn": 1, "kda": 2}           # rss_config.kind codes
 
 
 def _write_tokens(f, s, bf16):
@@ -36,15 +37,17 @@ def _write_tokens(f, s, bf16):
 def _run_driver(tmp_path, wl, T, fused, rounds=0):
     """Run the C++ caller: T decode steps, then `rounds` speculative rounds of
     wl.draft drafts with the seeded acceptances."""
-    A = synth.params(wl)["A"].astype(np.float32)
+    delta = wl.kind in ("gdn", "kda")
+    A = np.zeros(wl.nheads, np.float32) if delta else synth.params(wl)["A"].astype(np.float32)
     S0 = synth.initial_state(wl).astype(np.float32)
     has_s0 = int(np.any(S0 != 0))
     bf16 = int(wl.in_dtype == "bf16")
     K = wl.draft if rounds else 0
     copy = COPY[wl.read_copy]
-    hdr = np.array([0x52535333, wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window,
-                    wl.capacity, T, has_s0, int(fused), K, rounds, bf16, copy], dtype=np.int32)
-    steps = [synth.step_inputs(wl, t) for t in range(T)]
+    hdr = np.array([0x52535334, wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.window,
+                    wl.capacity, T, has_s0, int(fused), K, rounds, bf16, copy, KIND[wl.kind]], dtype=np.int32)
+    gen = {"gdn": synth.gdn_step_inputs, "kda": synth.kda_step_inputs}.get(wl.kind, synth.step_inputs)
+    steps = [gen(wl, t) for t in range(T)]
     rins = [synth.draft_inputs(wl, r) for r in range(rounds)]
     naccs = [synth.accepted_drafts(wl, r) for r in range(rounds)]
     with open(tmp_path / "in.bin", "wb") as f:
@@ -53,7 +56,11 @@ def _run_driver(tmp_path, wl, T, fused, rounds=0):
         if has_s0:
             f.write(np.ascontiguousarray(S0).tobytes())
         for s in steps:
-            _write_tokens(f, s, bf16)
+            if delta:
+                for k in ("q", "k", "v", "beta", "alpha"):
+                    f.write(np.ascontiguousarray(s[k], dtype=np.float32).tobytes())
+            else:
+                _write_tokens(f, s, bf16)
         for rin, nacc in zip(rins, naccs):
             _write_tokens(f, rin, bf16)
             f.write((K - nacc).astype(np.int32).tobytes())
@@ -213,3 +220,38 @@ def _spec_run(tmp_path, wl):
     out["ck_ref"] = np.stack([hist[b][len(hist[b]) - 1 - int(pm.len[b])] for b in range(Bt)])
     out["worst"], out["run"] = worst, run
     return out
+
+
+# The delta rules through their own C entry points: Gated DeltaNet (scalar gate)
+# and Kimi Delta Attention (one gate per key channel), decode with the fold in
+# the same pass or a separate flush each step. Outputs at every step and the
+# final checkpoint against the fp64 eager rule; pointers against the ring model.
+@pytest.mark.parametrize("kind,fused", [("gdn", True), ("gdn", False), ("kda", True), ("kda", False)])
+def test_c_caller_delta_rules(tmp_path, kind, fused):
+    Bt, H, P, N, W = 2, 3, 64, 128, 6
+    wl = workloads.get("gdn_b256_h32_d128_w16").replace(
+        name="c-abi-delta", kind=kind, batch=Bt, nheads=H, ngroups=H, headdim=P, dstate=N, window=W,
+        capacity=W, s0="normal", seed=7300 + KIND[kind] + int(fused))
+    T = 3 * W + 2
+    log(f"[c-abi {kind}] Bt={Bt} H={H} dv={P} dk={N} W={W} fused={fused}, {T} steps")
+    out = _run_driver(tmp_path, wl, T, fused)
+    assert out["err"] == 0
+    rule = gdn if kind == "gdn" else kda
+    S = out["S0"].astype(np.float64)
+    pm = PointerModel(Bt, W)
+    worst, ys, refs, S_fold = 0.0, [], [], S
+    for t, s in enumerate(out["steps"]):
+        S, o_ref = rule.eager_step(S, s["q"], s["k"], s["v"], s["beta"], s["alpha"])
+        worst = max(worst, rel_l2(out["y"][t].astype(np.float64), o_ref))
+        ys.append(out["y"][t])
+        refs.append(o_ref)
+        for b in range(Bt):
+            pm.append(b, 1)
+            if pm.flush(b, W) and b == 0:
+                S_fold = S
+    run = rel_l2(np.stack(ys).astype(np.float64), np.stack(refs))
+    log(f"  worst step {worst:.2e}, run {run:.2e}")
+    assert worst < 1e-5 and run < 1e-5
+    for h in range(H):
+        assert np.array_equal(out["ptr"][:, h, :3], pm.as_array())
+    assert rel_l2(out["ck"].astype(np.float64), S_fold) < 1e-5
