@@ -285,13 +285,30 @@ def run_calibration(torch, rss, dev):
         write[g] = rate(nbytes, ms * 1e3)
     torch.mul(src, 1.0, out=dst)
     ms = _timed(torch, lambda i: torch.mul(src, 1.0, out=dst), 10) / 10
+    # The replay's shape of work without its arithmetic: one workgroup per
+    # checkpoint tile, then the bytes a replay writes per tile (y, the appended
+    # ring entry, the pointer word), rounded up to whole 16-byte vectors.
+    wl = workloads.get(WORKLOAD)
+    P, N = wl.headdim, wl.dstate
+    tile = P * N * 4
+    ntile = nbytes // tile
+    wb = -(-(4 * P + (2 * P + 2 * N + 8) + 16) // 16) * 16
+    wdst = torch.empty((ntile * wb // 4,), device=dev)
+    rss.rss_calib_tiles(src, tile, ntile)
+    ms_t = _timed(torch, lambda i: rss.rss_calib_tiles(src, tile, ntile), 10) / 10
+    rss.rss_calib_tiles(src, tile, ntile, wdst, wb)
+    ms_tw = _timed(torch, lambda i: rss.rss_calib_tiles(src, tile, ntile, wdst, wb), 10) / 10
     out = {"read_ceiling_GBps": max(read.values()), "copy_ceiling_GBps": max(copy.values()),
            "write_ceiling_GBps": max(write.values()),
+           "tile_read_GBps": rate(nbytes, ms_t * 1e3),
+           "tile_read_write_GBps": rate(nbytes + ntile * wb, ms_tw * 1e3),
+           "tile_read_write_bytes_per_tile": [tile, wb],
            "read_by_grid": read, "copy_by_grid": copy, "write_by_grid": write,
            "torch_elementwise_copy_GBps": rate(2 * nbytes, ms * 1e3),
            "how": "rss_calib_read / rss_calib_copy / rss_calib_write over 1 GiB, best of grids of 256-thread "
-                  "workgroups"}
-    del src, dst, sink
+                  "workgroups; rss_calib_tiles over the same 1 GiB as 32 KiB tiles, one workgroup each, "
+                  "without and with the replay's bytes written per tile"}
+    del src, dst, sink, wdst
     return out
 
 
@@ -914,6 +931,7 @@ def main() -> int:
         "repeats_ms": main_run["reps_ms"],
         "context": dict(calib, **{
             "replay_frac_of_read_ceiling": main_run["rep_gbs"] / calib["read_ceiling_GBps"],
+            "replay_frac_of_tile_read_write": main_run["rep_gbs"] / calib["tile_read_write_GBps"],
             "fold_frac_of_copy_ceiling": kern[fk]["GBps"] / calib["copy_ceiling_GBps"],
             "eager_frac_of_copy_ceiling": (out_eager["kernel_GBps"] / calib["copy_ceiling_GBps"]
                                            if out_eager else None)}),

@@ -44,6 +44,21 @@ int32_t rss_calib_copy(const void* src, void* dst, size_t bytes, int32_t blocks,
  * snapshot per draft token). */
 int32_t rss_calib_write(void* dst, size_t bytes, int32_t blocks, void* stream);
 
+/* The decode kernels' shape of work without their arithmetic: one 256-thread
+ * workgroup per tile reads a tile of `tile_bytes` (4096, 8192, 16384, 32768
+ * or 65536) from src, all of its 16-byte loads issued at once, then writes
+ * `write_bytes` (a multiple of 16, at most 4096; 0 = none) per tile to dst.
+ * n_tiles tiles, src holding n_tiles * tile_bytes bytes and dst n_tiles *
+ * write_bytes. Tile t's 16-byte vector i in dst holds (s, i, t mod 2^24, 1),
+ * s = the sum, in fp32, of the floats thread i read (vectors i, i + 256, ...
+ * of the tile, added vector by vector, then the four lanes in order). Reading
+ * with writes of a decode's bytes per tile, it measures what HBM delivers for
+ * a decode's mix of a large streaming read and small writes. dst may be NULL
+ * when write_bytes = 0. RSS_E_INVALID also for n_tiles < 0 or an unsupported
+ * tile size. */
+int32_t rss_calib_tiles(const void* src, size_t tile_bytes, int32_t n_tiles, void* dst,
+                        int32_t write_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,31 @@ __global__ __launch_bounds__(kCalibThreads) void calib_write_kernel(f32x4* dst, 
   }
 }
 
+// One workgroup per tile, the decode kernels' shape of work: the tile's
+// 16-byte non-temporal loads all issued at once (thread i takes vectors
+// i, i + 256, ...), then `wvec` 16-byte vectors written per tile at
+// dst[t * wvec + i], each carrying its thread's sum of the tile, so that the
+// writes follow the reads as a decode's outputs and ring entries do. Tiles are
+// dealt to the XCDs in contiguous ranges, as the decode kernels deal theirs.
+template <int L>  // 16-byte loads per thread: tile bytes / 4096
+__global__ __launch_bounds__(kCalibThreads) void calib_tiles_kernel(const f32x4* src, f32x4* dst,
+                                                                    int wvec) {
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const f32x4* tile = src + (size_t)t * (L * kCalibThreads);
+  f32x4 v[L];
+#pragma unroll
+  for (int k = 0; k < L; ++k) v[k] = __builtin_nontemporal_load(tile + k * kCalibThreads + threadIdx.x);
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int k = 1; k < L; ++k) acc += v[k];
+  const float s = acc.x + acc.y + acc.z + acc.w;
+  // Every thread's loads are used here: without this the compiler moves them
+  // into the branch below, and threads that write nothing would read nothing.
+  asm volatile("" ::"v"(s));
+  if ((int)threadIdx.x < wvec)
+    dst[(size_t)t * wvec + threadIdx.x] = f32x4{s, (float)threadIdx.x, (float)(t & 0xffffff), 1.f};
+}
+
 }  // namespace rss
 
 namespace {
@@ -99,6 +124,30 @@ int32_t rss_calib_write(void* dst, size_t bytes, int32_t blocks, void* stream) {
   if (bytes == 0) return RSS_OK;
   hipLaunchKernelGGL(rss::calib_write_kernel, dim3(grid_of(blocks)), dim3(rss::kCalibThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<rss::f32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? RSS_OK : RSS_E_HIP;
+}
+
+int32_t rss_calib_tiles(const void* src, size_t tile_bytes, int32_t n_tiles, void* dst,
+                        int32_t write_bytes, void* stream) {
+  if (!src || !aligned16(src) || n_tiles < 0 || write_bytes < 0 || write_bytes % 16 ||
+      write_bytes > 4096 || (write_bytes > 0 && (!dst || !aligned16(dst))))
+    return RSS_E_INVALID;
+  if (tile_bytes != 4096 && tile_bytes != 8192 && tile_bytes != 16384 && tile_bytes != 32768 &&
+      tile_bytes != 65536)
+    return RSS_E_INVALID;
+  if (n_tiles == 0) return RSS_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const rss::f32x4* in = static_cast<const rss::f32x4*>(src);
+  rss::f32x4* out = static_cast<rss::f32x4*>(dst);
+  const int wvec = write_bytes / 16;
+  const dim3 grid((unsigned)n_tiles), block(rss::kCalibThreads);
+  switch (tile_bytes / 4096) {
+    case 1: hipLaunchKernelGGL(rss::calib_tiles_kernel<1>, grid, block, 0, s, in, out, wvec); break;
+    case 2: hipLaunchKernelGGL(rss::calib_tiles_kernel<2>, grid, block, 0, s, in, out, wvec); break;
+    case 4: hipLaunchKernelGGL(rss::calib_tiles_kernel<4>, grid, block, 0, s, in, out, wvec); break;
+    case 8: hipLaunchKernelGGL(rss::calib_tiles_kernel<8>, grid, block, 0, s, in, out, wvec); break;
+    default: hipLaunchKernelGGL(rss::calib_tiles_kernel<16>, grid, block, 0, s, in, out, wvec); break;
+  }
   return hipGetLastError() == hipSuccess ? RSS_OK : RSS_E_HIP;
 }
 
