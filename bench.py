@@ -298,16 +298,26 @@ def run_calibration(torch, rss, dev):
     ms_t = _timed(torch, lambda i: rss.rss_calib_tiles(src, tile, ntile), 10) / 10
     rss.rss_calib_tiles(src, tile, ntile, wdst, wb)
     ms_tw = _timed(torch, lambda i: rss.rss_calib_tiles(src, tile, ntile, wdst, wb), 10) / 10
+    # the same with a verify's bytes written per tile (K + 1 outputs and
+    # appended entries of the speculative workload, and the pointer word)
+    sw = workloads.get("mamba2_spec_b512_h128_p64_n128_w16_k4")
+    wbv = -(-((sw.draft + 1) * (4 * P + 2 * P + 2 * N + 8) + 16) // 16) * 16
+    del wdst
+    wdst = torch.empty((ntile * wbv // 4,), device=dev)
+    rss.rss_calib_tiles(src, tile, ntile, wdst, wbv)
+    ms_tv = _timed(torch, lambda i: rss.rss_calib_tiles(src, tile, ntile, wdst, wbv), 10) / 10
     out = {"read_ceiling_GBps": max(read.values()), "copy_ceiling_GBps": max(copy.values()),
            "write_ceiling_GBps": max(write.values()),
            "tile_read_GBps": rate(nbytes, ms_t * 1e3),
            "tile_read_write_GBps": rate(nbytes + ntile * wb, ms_tw * 1e3),
            "tile_read_write_bytes_per_tile": [tile, wb],
+           "tile_read_verify_writes_GBps": rate(nbytes + ntile * wbv, ms_tv * 1e3),
+           "tile_read_verify_writes_bytes_per_tile": [tile, wbv],
            "read_by_grid": read, "copy_by_grid": copy, "write_by_grid": write,
            "torch_elementwise_copy_GBps": rate(2 * nbytes, ms * 1e3),
            "how": "rss_calib_read / rss_calib_copy / rss_calib_write over 1 GiB, best of grids of 256-thread "
                   "workgroups; rss_calib_tiles over the same 1 GiB as 32 KiB tiles, one workgroup each, "
-                  "without and with the replay's bytes written per tile"}
+                  "without and with the replay's (or a verify's) bytes written per tile"}
     del src, dst, sink, wdst
     return out
 
@@ -980,6 +990,7 @@ def main() -> int:
         bound_us = (sp["eager_verify_read_bytes"] / calib["read_ceiling_GBps"] +
                     sp["eager_verify_write_bytes"] / calib["write_ceiling_GBps"]) / 1e3
         sp["eager_verify_frac_of_read_write_ceilings"] = bound_us / sp["eager_verify_avg_us"]
+        sp["verify_frac_of_tile_read_verify_writes"] = sp["verify_GBps"] / calib["tile_read_verify_writes_GBps"]
         mark("gdn")
         rec["gated_deltanet"] = run_gdn(torch, rss, dev, sub, args.warmup)
         mark("kda")
