@@ -103,7 +103,7 @@ def gdn_bytes(wl, n0: int) -> dict:
         entry = 4 * N + 4 * P + 8                   # k, u, (1, log alpha)
         inputs = 4 * N * 2 + 4 * P + 8              # q, k, v, beta, alpha
     replay = P * N * 4 + n0 * entry + inputs + 4 * P + entry + 32
-    return {"replay": replay,
+    return {"replay": replay, "inputs": inputs,
             "fused": P * N * 4 * 2 + (wl.window - 1) * entry + inputs + 4 * P + entry + 32,
             "flush": 2 * P * N * 4 + wl.window * entry + 32,
             "eager": 2 * P * N * 4 + inputs + 4 * P}
@@ -306,6 +306,18 @@ def run_calibration(torch, rss, dev):
     wdst = torch.empty((ntile * wbv // 4,), device=dev)
     rss.rss_calib_tiles(src, tile, ntile, wdst, wbv)
     ms_tv = _timed(torch, lambda i: rss.rss_calib_tiles(src, tile, ntile, wdst, wbv), 10) / 10
+    # Gated DeltaNet / KDA replays: 64 KiB tiles (d = 128 fp32), and the bytes
+    # each writes per tile (output, appended k / u (/ log-gate) rows, pointer)
+    delta = {}
+    for name in ("gdn_b256_h32_d128_w16", "kda_b256_h32_d128_w16"):
+        dw = workloads.get(name)
+        dt_ = dw.headdim * dw.dstate * 4
+        g = gdn_bytes(dw, 0)
+        wbd = -(-(g["replay"] - dt_ - g["inputs"] - 16) // 16) * 16   # y + appended entry + pointer write
+        nd = nbytes // dt_
+        rss.rss_calib_tiles(src, dt_, nd, wdst, wbd)
+        ms_d = _timed(torch, lambda i: rss.rss_calib_tiles(src, dt_, nd, wdst, wbd), 10) / 10
+        delta[dw.kind] = {"GBps": rate(nbytes + nd * wbd, ms_d * 1e3), "bytes_per_tile": [dt_, wbd]}
     out = {"read_ceiling_GBps": max(read.values()), "copy_ceiling_GBps": max(copy.values()),
            "write_ceiling_GBps": max(write.values()),
            "tile_read_GBps": rate(nbytes, ms_t * 1e3),
@@ -313,6 +325,7 @@ def run_calibration(torch, rss, dev):
            "tile_read_write_bytes_per_tile": [tile, wb],
            "tile_read_verify_writes_GBps": rate(nbytes + ntile * wbv, ms_tv * 1e3),
            "tile_read_verify_writes_bytes_per_tile": [tile, wbv],
+           "tile_read_delta_rule_writes": delta,
            "read_by_grid": read, "copy_by_grid": copy, "write_by_grid": write,
            "torch_elementwise_copy_GBps": rate(2 * nbytes, ms * 1e3),
            "how": "rss_calib_read / rss_calib_copy / rss_calib_write over 1 GiB, best of grids of 256-thread "
@@ -996,6 +1009,9 @@ def main() -> int:
         mark("kda")
         rec["kimi_delta_attention"] = run_gdn(torch, rss, dev, sub, args.warmup,
                                               name="kda_b256_h32_d128_w16")
+        for key, kind in (("gated_deltanet", "gdn"), ("kimi_delta_attention", "kda")):
+            rec[key]["replay_frac_of_tile_read_write"] = (rec[key]["replay_GBps"] /
+                                                          calib["tile_read_delta_rule_writes"][kind]["GBps"])
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
