@@ -3,9 +3,11 @@
  *
  * Not part of the decode path: a benchmark runs them beside the decode kernels
  * to measure what HBM actually delivers with the decode kernels' own access
- * pattern (16-byte non-temporal loads and stores, fully coalesced, grid-stride),
- * so that each kernel's bandwidth can be quoted as a fraction of the achievable
- * read, write or copy rate as well as of the data-sheet peak. The method's premise is
+ * pattern (16-byte non-temporal loads and stores, fully coalesced: grid-stride
+ * streams, and one workgroup per tile as the decode kernels work), so that each
+ * kernel's bandwidth can be quoted as a fraction of the achievable read, write
+ * or copy rate, or of a traffic-only kernel of its own shape, as well as of the
+ * data-sheet peak. The method's premise is
  * that HBM traffic, not arithmetic, bounds the decode (P1, "La fiche qu'on
  * réécrit à chaque token": the eager step reads and writes the whole state for
  * very little arithmetic).
