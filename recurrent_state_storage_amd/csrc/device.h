@@ -310,6 +310,13 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_wave_base, 16, 0, 0);
 }
+// The same, marked non-temporal (read once: a call's own inputs). Lanes of one
+// wavefront may mix the two forms under complementary exec masks: each writes
+// its own lane's 16 bytes.
+constexpr int kCachePolicyNt = 2;
+__device__ __forceinline__ void dma16_nt(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_wave_base, 16, 0, kCachePolicyNt);
+}
 
 // Ring slot of window position j (0 <= head < R, 0 <= j < R).
 __device__ __forceinline__ int ring_slot(int head, int j, int R) {
