@@ -275,6 +275,11 @@ template <typename Tin>
 __device__ __forceinline__ typename V16<Tin>::T ldv(const Tin* p) {
   return *reinterpret_cast<const typename V16<Tin>::T*>(p);
 }
+// The same, non-temporal: for data read for the last time (a fold's ring rows).
+template <typename Tin>
+__device__ __forceinline__ typename V16<Tin>::T ldv_nt(const Tin* p) {
+  return __builtin_bit_cast(typename V16<Tin>::T, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
 
 // A 16-byte vector of input elements widened to fp32 in registers.
 __device__ __forceinline__ void unpack16(const float4& v, float* d) {

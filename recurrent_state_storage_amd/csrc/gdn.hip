@@ -103,18 +103,26 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   const float* qin = a.q + (size_t)bh * N;
   const float* vin = a.v + (size_t)bh * P;
 
-  // Window k rows (ring, then k_t as row n0) and u rows straight into LDS;
-  // q_t and the log-decays through registers.
+  // Window k rows (ring, then k_t as row n0), u rows and v_t straight into
+  // LDS; q_t and the log-decays through registers. The step's own inputs are
+  // read once, so they go non-temporal; ring rows stay cached.
   const int totK = L * NV;
   for (int q0 = wave * 64; q0 < totK; q0 += kThreads) {
     const int q = q0 + lane;
     if (q < totK) {
       const int j = q / NV;
-      const float* src = j < n0 ? rk + ring_slot(head, j, R) * sks : kin;
-      dma16(src + (q - j * NV) * 4, sK + q0 * 4);
+      if (j < n0) dma16(rk + ring_slot(head, j, R) * sks + (q - j * NV) * 4, sK + q0 * 4);
+      else dma16_nt(kin + (q - j * NV) * 4, sK + q0 * 4);
     }
   }
   const bool uvec = (P % 4) == 0;
+  float* sV = lds + lay.oV;
+  if (uvec) {  // v_t, read by the writer lanes at the end of each tile chunk
+    for (int q0 = wave * 64; q0 < P / 4; q0 += kThreads)
+      if (q0 + lane < P / 4) dma16_nt(vin + (q0 + lane) * 4, sV + q0 * 4);
+  } else {
+    for (int p = tid; p < P; p += kThreads) sV[p] = __builtin_nontemporal_load(vin + p);
+  }
   if (uvec) {
     const int PV = P / 4, totU = n0 * PV;
     for (int q0 = wave * 64; q0 < totU; q0 += kThreads) {
@@ -136,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
     }
   }
   float qv = 0.f, av = 1.f;
-  if (tid < N) qv = qin[tid];
-  if (KDA && tid < N) av = a.alpha[(size_t)bh * N + tid];
+  if (tid < N) qv = __builtin_nontemporal_load(qin + tid);
+  if (KDA && tid < N) av = __builtin_nontemporal_load(a.alpha + (size_t)bh * N + tid);
   float2 dl = make_float2(0.f, 0.f);
   if (!KDA && tid < n0) dl = rdl[ring_slot(head, tid, R) * H];
   if (!uvec) {
@@ -270,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
             const float rq_ = (sS[1 * P + row] + sS[3 * P + row]) + (sS[5 * P + row] + sS[7 * P + row]);
             const float Sk = fmaf(D, pk[m], rk_);
             const float Sq = fmaf(D, pq[m], rq_);
-            const float u = beta * (vin[row] - alpha * Sk);
+            const float u = beta * (sV[row] - alpha * Sk);
             unew[row] = u;
             if (FOLD) sU[n0 * P + row] = u;
             oout[row] = fmaf(alpha, Sq, kq * u);

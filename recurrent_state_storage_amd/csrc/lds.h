@@ -90,7 +90,7 @@ __host__ __device__ constexpr int gdn_passes(int P, int N) { return P > 8 * (102
 
 // Dynamic LDS of the GDN / KDA replay kernel, in floats.
 struct GdnLds {
-  int RS, oK, oU, oQ, oCF, oS, oD, oFC, oG, oW, total;
+  int RS, oK, oU, oQ, oV, oCF, oS, oD, oFC, oG, oW, total;
   // fold_buf: floats of the matrix-core fold's hand-over buffer per wavefront
   // (0 for a launch that does not fold). The window rows are allocated in
   // multiples of four (the fold reads entries in groups of four; the rows past
@@ -101,7 +101,8 @@ struct GdnLds {
     oK = 0;                   // window k rows [RS][N] (row n0 = k_t); KDA: scaled in place
     oU = RS * N;              // window u rows [RS][P]
     oQ = oU + RS * P;         // q_t [N]
-    oCF = oQ + N;             // exp(lam_j) [R], then exp(Lam), k_t . q_t
+    oV = align4(oQ + N);      // v_t [P] (the replay decode; 16-byte aligned)
+    oCF = oV + P;             // exp(lam_j) [R], then exp(Lam), k_t . q_t
     oS = align4(oCF + R + 2); // shares [4 waves][2][P]: sum_j w u_j for z = k_t, q_t
     oD = oS + 8 * P;          // KDA: exp(Lam[n]) [N]
     oFC = oD + (kda ? N : 0); // fused fold (GDN): c_j [RS], then exp(Lam) at [RS]
