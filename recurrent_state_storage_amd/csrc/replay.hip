@@ -176,7 +176,10 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   // of a wavefront lands at the wavefront's LDS base + 16 l), C and (dt, l)
   // through registers. All issued before any wait. The call's own inputs are
   // read once, so they go non-temporal (measured: decode 185.0 -> 184.3 us at
-  // batch 256); the ring rows, read again by the next calls, stay cached.
+  // batch 256); the ring rows, read again by the next calls, stay cached, except
+  // in a verify that folds them (verify + fold 558.5 -> 555.3 us at batch 512;
+  // a decode's fold did not gain).
+  const bool last_read = NTMAX > 1 && do_fold;
   const bool xvec = (P % VE) == 0;
   const int PV = xvec ? P / VE : 0;
   auto xdiv = [&](int q) { return (int)(((uint64_t)(uint32_t)q * a.xdiv) >> 32); };
@@ -185,8 +188,8 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
     const int q = q0 + lane;
     if (q < totBV) {
       const int j = q / NV;
-      if (j < n0) dma16(brow(j) + (q - j * NV) * VE, sB + q0 * VE);
-      else dma16_nt(brow(j) + (q - j * NV) * VE, sB + q0 * VE);   // this call's input: read once
+      if (j < n0 && !last_read) dma16(brow(j) + (q - j * NV) * VE, sB + q0 * VE);
+      else dma16_nt(brow(j) + (q - j * NV) * VE, sB + q0 * VE);   // read for the last time
     }
   }
   Tin sxs[kStageS];
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
       const int q = q0 + lane;
       if (q < totXV) {
         const int j = xdiv(q);
-        if (j < n0) dma16(xrow(j) + (q - j * PV) * VE, sX + q0 * VE);
+        if (j < n0 && !last_read) dma16(xrow(j) + (q - j * PV) * VE, sX + q0 * VE);
         else dma16_nt(xrow(j) + (q - j * PV) * VE, sX + q0 * VE);
       }
     }
