@@ -306,6 +306,11 @@ def run_calibration(torch, rss, dev):
     wdst = torch.empty((ntile * wbv // 4,), device=dev)
     rss.rss_calib_tiles(src, tile, ntile, wdst, wbv)
     ms_tv = _timed(torch, lambda i: rss.rss_calib_tiles(src, tile, ntile, wdst, wbv), 10) / 10
+    # whole tiles read and written back (eager step, folds)
+    del wdst
+    wdst = torch.empty_like(src)
+    rss.rss_calib_tiles(src, tile, ntile, wdst, tile)
+    ms_tc = _timed(torch, lambda i: rss.rss_calib_tiles(src, tile, ntile, wdst, tile), 10) / 10
     # Gated DeltaNet / KDA replays: 64 KiB tiles (d = 128 fp32), and the bytes
     # each writes per tile (output, appended k / u (/ log-gate) rows, pointer)
     delta = {}
@@ -326,11 +331,12 @@ def run_calibration(torch, rss, dev):
            "tile_read_verify_writes_GBps": rate(nbytes + ntile * wbv, ms_tv * 1e3),
            "tile_read_verify_writes_bytes_per_tile": [tile, wbv],
            "tile_read_delta_rule_writes": delta,
+           "tile_copy_GBps": rate(2 * nbytes, ms_tc * 1e3),
            "read_by_grid": read, "copy_by_grid": copy, "write_by_grid": write,
            "torch_elementwise_copy_GBps": rate(2 * nbytes, ms * 1e3),
            "how": "rss_calib_read / rss_calib_copy / rss_calib_write over 1 GiB, best of grids of 256-thread "
                   "workgroups; rss_calib_tiles over the same 1 GiB as 32 KiB tiles, one workgroup each, "
-                  "without and with the replay's (or a verify's) bytes written per tile"}
+                  "without and with the replay's (or a verify's) bytes written per tile, and each tile copied back"}
     del src, dst, sink, wdst
     return out
 
@@ -957,7 +963,10 @@ def main() -> int:
             "replay_frac_of_tile_read_write": main_run["rep_gbs"] / calib["tile_read_write_GBps"],
             "fold_frac_of_copy_ceiling": kern[fk]["GBps"] / calib["copy_ceiling_GBps"],
             "eager_frac_of_copy_ceiling": (out_eager["kernel_GBps"] / calib["copy_ceiling_GBps"]
-                                           if out_eager else None)}),
+                                           if out_eager else None),
+            "fold_frac_of_tile_copy": kern[fk]["GBps"] / calib["tile_copy_GBps"],
+            "eager_frac_of_tile_copy": (out_eager["kernel_GBps"] / calib["tile_copy_GBps"]
+                                        if out_eager else None)}),
         "eager_baseline": out_eager,
         "bytes_per_token": {"replay_state": st_replay, "eager_state": st_eager,
                             "state_ratio": st_replay / st_eager, "replay_total": tot_replay,

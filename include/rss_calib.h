@@ -55,9 +55,12 @@ int32_t rss_calib_write(void* dst, size_t bytes, int32_t blocks, void* stream);
  * s = the sum, in fp32, of the floats thread i read (vectors i, i + 256, ...
  * of the tile, added vector by vector, then the four lanes in order). Reading
  * with writes of a decode's bytes per tile, it measures what HBM delivers for
- * a decode's mix of a large streaming read and small writes. dst may be NULL
- * when write_bytes = 0. RSS_E_INVALID also for n_tiles < 0 or an unsupported
- * tile size. */
+ * a decode's mix of a large streaming read and small writes. write_bytes =
+ * tile_bytes instead copies each tile to dst at t * tile_bytes (each thread
+ * stores the vectors it read, non-temporal): a read-then-write-back of whole
+ * state tiles, as the eager step and the folds do. dst may be NULL when
+ * write_bytes = 0. RSS_E_INVALID also for n_tiles < 0 or an unsupported tile
+ * size. */
 int32_t rss_calib_tiles(const void* src, size_t tile_bytes, int32_t n_tiles, void* dst,
                         int32_t write_bytes, void* stream);
 

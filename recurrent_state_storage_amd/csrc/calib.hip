@@ -73,7 +73,9 @@ __global__ __launch_bounds__(kCalibThreads) void calib_write_kernel(f32x4* dst, 
 // dst[t * wvec + i], each carrying its thread's sum of the tile, so that the
 // writes follow the reads as a decode's outputs and ring entries do. Tiles are
 // dealt to the XCDs in contiguous ranges, as the decode kernels deal theirs.
-template <int L>  // 16-byte loads per thread: tile bytes / 4096
+// COPY: the tile itself is written to dst (each thread stores the vectors it
+// loaded, non-temporal), a decode kernel's read-then-write-back of a state tile.
+template <int L, bool COPY>  // L: 16-byte loads per thread (tile bytes / 4096)
 __global__ __launch_bounds__(kCalibThreads) void calib_tiles_kernel(const f32x4* src, f32x4* dst,
                                                                     int wvec) {
   const int t = xcd_tile(blockIdx.x, gridDim.x);
@@ -81,6 +83,12 @@ __global__ __launch_bounds__(kCalibThreads) void calib_tiles_kernel(const f32x4*
   f32x4 v[L];
 #pragma unroll
   for (int k = 0; k < L; ++k) v[k] = __builtin_nontemporal_load(tile + k * kCalibThreads + threadIdx.x);
+  if constexpr (COPY) {
+    f32x4* out = dst + (size_t)t * (L * kCalibThreads);
+#pragma unroll
+    for (int k = 0; k < L; ++k) __builtin_nontemporal_store(v[k], out + k * kCalibThreads + threadIdx.x);
+    return;
+  }
   f32x4 acc = v[0];
 #pragma unroll
   for (int k = 1; k < L; ++k) acc += v[k];
@@ -129,11 +137,12 @@ int32_t rss_calib_write(void* dst, size_t bytes, int32_t blocks, void* stream) {
 
 int32_t rss_calib_tiles(const void* src, size_t tile_bytes, int32_t n_tiles, void* dst,
                         int32_t write_bytes, void* stream) {
-  if (!src || !aligned16(src) || n_tiles < 0 || write_bytes < 0 || write_bytes % 16 ||
-      write_bytes > 4096 || (write_bytes > 0 && (!dst || !aligned16(dst))))
-    return RSS_E_INVALID;
   if (tile_bytes != 4096 && tile_bytes != 8192 && tile_bytes != 16384 && tile_bytes != 32768 &&
       tile_bytes != 65536)
+    return RSS_E_INVALID;
+  const bool copy = (size_t)write_bytes == tile_bytes;
+  if (!src || !aligned16(src) || n_tiles < 0 || write_bytes < 0 || write_bytes % 16 ||
+      (write_bytes > 4096 && !copy) || (write_bytes > 0 && (!dst || !aligned16(dst))))
     return RSS_E_INVALID;
   if (n_tiles == 0) return RSS_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -141,13 +150,19 @@ int32_t rss_calib_tiles(const void* src, size_t tile_bytes, int32_t n_tiles, voi
   rss::f32x4* out = static_cast<rss::f32x4*>(dst);
   const int wvec = write_bytes / 16;
   const dim3 grid((unsigned)n_tiles), block(rss::kCalibThreads);
+#define RSS_CALIB_TILES(L_)                                                             \
+  do {                                                                                   \
+    if (copy) hipLaunchKernelGGL((rss::calib_tiles_kernel<L_, true>), grid, block, 0, s, in, out, wvec); \
+    else hipLaunchKernelGGL((rss::calib_tiles_kernel<L_, false>), grid, block, 0, s, in, out, wvec);     \
+  } while (0)
   switch (tile_bytes / 4096) {
-    case 1: hipLaunchKernelGGL(rss::calib_tiles_kernel<1>, grid, block, 0, s, in, out, wvec); break;
-    case 2: hipLaunchKernelGGL(rss::calib_tiles_kernel<2>, grid, block, 0, s, in, out, wvec); break;
-    case 4: hipLaunchKernelGGL(rss::calib_tiles_kernel<4>, grid, block, 0, s, in, out, wvec); break;
-    case 8: hipLaunchKernelGGL(rss::calib_tiles_kernel<8>, grid, block, 0, s, in, out, wvec); break;
-    default: hipLaunchKernelGGL(rss::calib_tiles_kernel<16>, grid, block, 0, s, in, out, wvec); break;
+    case 1: RSS_CALIB_TILES(1); break;
+    case 2: RSS_CALIB_TILES(2); break;
+    case 4: RSS_CALIB_TILES(4); break;
+    case 8: RSS_CALIB_TILES(8); break;
+    default: RSS_CALIB_TILES(16); break;
   }
+#undef RSS_CALIB_TILES
   return hipGetLastError() == hipSuccess ? RSS_OK : RSS_E_HIP;
 }
 

@@ -284,3 +284,5 @@ def test_calibration_calls_validate_before_launch():
     assert lib.rss_calib_copy(ok, ok, 0, 0, None) == rss.RSS_OK
     assert lib.rss_calib_write(ok, 0, 0, None) == rss.RSS_OK
     assert lib.rss_calib_tiles(ok, 32768, 0, ok, 16, None) == rss.RSS_OK
+    assert lib.rss_calib_tiles(ok, 32768, 0, ok, 32768, None) == rss.RSS_OK   # tile copy
+    assert lib.rss_calib_tiles(ok, 32768, 4, None, 32768, None) == rss.RSS_E_INVALID

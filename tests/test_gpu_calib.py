@@ -54,3 +54,14 @@ def test_calibration_tiles(tile_bytes, n_tiles, write_bytes):
     want[..., 2] = np.arange(n_tiles)[:, None]
     want[..., 3] = 1.0
     assert np.array_equal(dst.cpu().numpy().reshape(n_tiles, wv, 4), want)
+
+
+@pytest.mark.parametrize("tile_bytes,n_tiles", [(32768, 37), (4096, 9), (65536, 5)])
+def test_calibration_tile_copy(tile_bytes, n_tiles):
+    """write_bytes = tile_bytes copies every tile to the same place in dst."""
+    src = torch.randn((n_tiles * tile_bytes // 4,), device=DEV)
+    keep = src.clone()
+    dst = torch.full_like(src, float("nan"))
+    rss.rss_calib_tiles(src, tile_bytes, n_tiles, dst, tile_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(src, keep) and torch.equal(dst, src)
