@@ -59,10 +59,13 @@ int32_t rss_calib_write(void* dst, size_t bytes, int32_t blocks, void* stream);
  * tile_bytes instead copies each tile to dst at t * tile_bytes (each thread
  * stores the vectors it read, non-temporal): a read-then-write-back of whole
  * state tiles, as the eager step and the folds do. dst may be NULL when
- * write_bytes = 0. RSS_E_INVALID also for n_tiles < 0 or an unsupported tile
- * size. */
+ * write_bytes = 0. order: 0 = the decode kernels' workgroup-to-tile order (each
+ * XCD takes runs of consecutive tiles of up to 512 KiB, the eight XCDs side by
+ * side), 1 = one contiguous range of tiles per XCD; which of the two HBM serves
+ * faster depends on the traffic. RSS_E_INVALID also for n_tiles < 0, an
+ * unsupported tile size or another order. */
 int32_t rss_calib_tiles(const void* src, size_t tile_bytes, int32_t n_tiles, void* dst,
-                        int32_t write_bytes, void* stream);
+                        int32_t write_bytes, int32_t order, void* stream);
 
 #ifdef __cplusplus
 }

@@ -72,13 +72,22 @@ __global__ __launch_bounds__(kCalibThreads) void calib_write_kernel(f32x4* dst, 
 // i, i + 256, ...), then `wvec` 16-byte vectors written per tile at
 // dst[t * wvec + i], each carrying its thread's sum of the tile, so that the
 // writes follow the reads as a decode's outputs and ring entries do. Tiles are
-// dealt to the XCDs in contiguous ranges, as the decode kernels deal theirs.
+// dealt to the XCDs in runs of up to 512 KiB, as the decode kernels deal theirs
+// (order 0), or in one contiguous range per XCD (order 1).
 // COPY: the tile itself is written to dst (each thread stores the vectors it
 // loaded, non-temporal), a decode kernel's read-then-write-back of a state tile.
+// The other order a calibration may take: XCD x works through one contiguous
+// range of tiles, x-th of eight, in address order.
+__device__ __forceinline__ int xcd_range(int id, int n) {
+  const int x = id % kXcds, q = n / kXcds, r = n % kXcds;
+  return x * q + (x < r ? x : r) + id / kXcds;
+}
+
 template <int L, bool COPY>  // L: 16-byte loads per thread (tile bytes / 4096)
 __global__ __launch_bounds__(kCalibThreads) void calib_tiles_kernel(const f32x4* src, f32x4* dst,
-                                                                    int wvec) {
-  const int t = xcd_tile(blockIdx.x, gridDim.x);
+                                                                    int wvec, int order) {
+  const int t = order ? xcd_range(blockIdx.x, gridDim.x)
+                      : xcd_tile(blockIdx.x, gridDim.x, L * kCalibThreads * 16);
   const f32x4* tile = src + (size_t)t * (L * kCalibThreads);
   f32x4 v[L];
 #pragma unroll
@@ -136,13 +145,14 @@ int32_t rss_calib_write(void* dst, size_t bytes, int32_t blocks, void* stream) {
 }
 
 int32_t rss_calib_tiles(const void* src, size_t tile_bytes, int32_t n_tiles, void* dst,
-                        int32_t write_bytes, void* stream) {
+                        int32_t write_bytes, int32_t order, void* stream) {
   if (tile_bytes != 4096 && tile_bytes != 8192 && tile_bytes != 16384 && tile_bytes != 32768 &&
       tile_bytes != 65536)
     return RSS_E_INVALID;
   const bool copy = (size_t)write_bytes == tile_bytes;
   if (!src || !aligned16(src) || n_tiles < 0 || write_bytes < 0 || write_bytes % 16 ||
-      (write_bytes > 4096 && !copy) || (write_bytes > 0 && (!dst || !aligned16(dst))))
+      (write_bytes > 4096 && !copy) || (write_bytes > 0 && (!dst || !aligned16(dst))) ||
+      (order != 0 && order != 1))
     return RSS_E_INVALID;
   if (n_tiles == 0) return RSS_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -152,8 +162,8 @@ int32_t rss_calib_tiles(const void* src, size_t tile_bytes, int32_t n_tiles, voi
   const dim3 grid((unsigned)n_tiles), block(rss::kCalibThreads);
 #define RSS_CALIB_TILES(L_)                                                             \
   do {                                                                                   \
-    if (copy) hipLaunchKernelGGL((rss::calib_tiles_kernel<L_, true>), grid, block, 0, s, in, out, wvec); \
-    else hipLaunchKernelGGL((rss::calib_tiles_kernel<L_, false>), grid, block, 0, s, in, out, wvec);     \
+    if (copy) hipLaunchKernelGGL((rss::calib_tiles_kernel<L_, true>), grid, block, 0, s, in, out, wvec, order); \
+    else hipLaunchKernelGGL((rss::calib_tiles_kernel<L_, false>), grid, block, 0, s, in, out, wvec, order);     \
   } while (0)
   switch (tile_bytes / 4096) {
     case 1: RSS_CALIB_TILES(1); break;

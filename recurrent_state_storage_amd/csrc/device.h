@@ -75,14 +75,23 @@ struct RowMap {
 };
 
 // Workgroup -> tile index, XCD-aware. The dispatcher hands consecutive
-// workgroup ids to the eight XCDs in turn, each with its own L2; this bijection
-// on [0, n) gives XCD x one contiguous range of tiles instead, so neighbouring
-// (sequence, head) tiles, whose pointer words and ring entries share cache
-// lines, are written through the same L2.
+// workgroup ids to the eight XCDs in turn, each with its own L2. This bijection
+// on [0, n) takes the ids in groups of 8 runs of 2^lc tiles, a run being the
+// largest power-of-two number of tiles within 512 KiB: inside a group XCD x
+// works through the x-th run. So each XCD streams runs of consecutive tiles
+// (neighbouring heads, whose pointer words and ring entries share cache lines,
+// go through one L2), while the eight XCDs together stay on one 4 MiB stretch
+// of the state at a time. Measured on MI355X against one contiguous range per
+// XCD (every tile of XCD x before those of XCD x + 1 in address order), 512 KiB
+// runs beat both that and shorter or longer runs. Ids past the last whole group
+// map to themselves.
 constexpr int kXcds = 8;
-__device__ __forceinline__ int xcd_tile(int id, int n) {
-  const int x = id % kXcds, q = n / kXcds, r = n % kXcds;
-  return x * q + (x < r ? x : r) + id / kXcds;
+__device__ __forceinline__ int xcd_tile(int id, int n, int tile_bytes) {
+  const int cl = tile_bytes > 1 ? 32 - __builtin_clz((unsigned)tile_bytes - 1u) : 0;  // ceil(log2)
+  const int lc = cl < 19 ? 19 - cl : 0;                     // run of 2^lc tiles <= 512 KiB
+  const int grp = kXcds << lc;                              // ids per group (a power of two)
+  if (id >= (n & -grp)) return id;
+  return (id & -grp) | ((id % kXcds) << lc) | ((id / kXcds) & ((1 << lc) - 1));
 }
 
 // ---- cross-lane exchanges ----------------------------------------------------

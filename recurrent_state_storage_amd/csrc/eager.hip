@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void eager_kernel(EagerArgs a) {
 
   const int tid = threadIdx.x;
   const int H = a.H, P = a.P, G = a.G, T = a.T;
-  const int bh = xcd_tile(blockIdx.x, gridDim.x);
+  const int bh = xcd_tile(blockIdx.x, gridDim.x, P * N * 4);
   const int b = bh / H, h = bh - b * H;
   const int g = h / (H / G);
   const size_t tile_elems = (size_t)P * N;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kEagerLowThreads) void eager_bf16_kernel(EagerArgs 
 
   const int tid = threadIdx.x;
   const int H = a.H, P = a.P, G = a.G, T = a.T;
-  const int bh = xcd_tile(blockIdx.x, gridDim.x);
+  const int bh = xcd_tile(blockIdx.x, gridDim.x, P * N * 2);
   const int b = bh / H, h = bh - b * H;
   const int g = h / (H / G);
   bf16_t* st = static_cast<bf16_t*>(a.S) + (size_t)bh * P * N;

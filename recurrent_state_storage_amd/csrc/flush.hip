@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(FlushArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, P = a.P, G = a.G, R = a.R;
-  const int bh = xcd_tile(blockIdx.x, gridDim.x);
+  const int bh = xcd_tile(blockIdx.x, gridDim.x, a.P * N * (B16 ? 2 : 4));
   const int b = bh / H, h = bh - b * H;
   const int g = h / (H / G);
   const int4 pt = a.ptr[bh];

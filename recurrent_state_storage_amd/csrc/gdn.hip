@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void gdn_replay_kernel(GdnArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, P = a.P, R = a.R;
-  const int bh = xcd_tile(blockIdx.x, gridDim.x);
+  const int bh = xcd_tile(blockIdx.x, gridDim.x, a.P * N * 4);
   const int b = bh / H, h = bh - b * H;
 
   float* tile = a.ckpt + (size_t)bh * P * N;
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void gdn_eager_kernel(GdnEagerArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.P;
-  const int bh = xcd_tile(blockIdx.x, gridDim.x);
+  const int bh = xcd_tile(blockIdx.x, gridDim.x, a.P * N * 4);
   float* tile = a.S + (size_t)bh * P * N;
   const int col = tid % TPR;
   const Rows rows(tid);

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, P = a.P, G = a.G, R = a.R, nt = a.nt;
-  const int bh = xcd_tile(blockIdx.x, gridDim.x);
+  const int bh = xcd_tile(blockIdx.x, gridDim.x, a.P * N * (int)sizeof(TileT));
   const int b = bh / H, h = bh - b * H;
   const int hpg = H / G, g = h / hpg;
 

@@ -78,7 +78,7 @@ _SIGS = {
     "rss_calib_read": ([_VP, ctypes.c_size_t, _VP, _I32, _VP], _I32),
     "rss_calib_copy": ([_VP, _VP, ctypes.c_size_t, _I32, _VP], _I32),
     "rss_calib_write": ([_VP, ctypes.c_size_t, _I32, _VP], _I32),
-    "rss_calib_tiles": ([_VP, ctypes.c_size_t, _I32, _VP, _I32, _VP], _I32),
+    "rss_calib_tiles": ([_VP, ctypes.c_size_t, _I32, _VP, _I32, _I32, _VP], _I32),
 }
 
 _lib = None
@@ -480,9 +480,11 @@ def rss_calib_write(dst, blocks: int = 0, stream=None) -> None:
     _check(library().rss_calib_write(dst.data_ptr(), nbytes, int(blocks), _stream(stream)), "rss_calib_write")
 
 
-def rss_calib_tiles(src, tile_bytes: int, n_tiles: int, dst=None, write_bytes: int = 0, stream=None) -> None:
+def rss_calib_tiles(src, tile_bytes: int, n_tiles: int, dst=None, write_bytes: int = 0, order: int = 0,
+                    stream=None) -> None:
     """One workgroup per tile: read n_tiles tiles of tile_bytes from the
-    contiguous device tensor `src`, then write write_bytes per tile to `dst`."""
+    contiguous device tensor `src`, then write write_bytes per tile to `dst`;
+    tiles in the decode kernels' order (0) or one contiguous range per XCD (1)."""
     if not (isinstance(src, torch.Tensor) and src.is_cuda and src.is_contiguous()):
         raise ValueError("src: expected a contiguous device tensor")
     if src.numel() * src.element_size() < n_tiles * tile_bytes:
@@ -495,4 +497,4 @@ def rss_calib_tiles(src, tile_bytes: int, n_tiles: int, dst=None, write_bytes: i
             raise ValueError("dst: smaller than n_tiles * write_bytes")
         dptr = dst.data_ptr()
     _check(library().rss_calib_tiles(src.data_ptr(), int(tile_bytes), int(n_tiles), dptr, int(write_bytes),
-                                     _stream(stream)), "rss_calib_tiles")
+                                     int(order), _stream(stream)), "rss_calib_tiles")

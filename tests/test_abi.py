@@ -273,16 +273,18 @@ def test_calibration_calls_validate_before_launch():
                lib.rss_calib_copy(ok, ok, 8, 0, None),
                lib.rss_calib_write(None, 16, 0, None), lib.rss_calib_write(odd, 16, 0, None),
                lib.rss_calib_write(ok, 20, 0, None), lib.rss_calib_write(ok, 16, -2, None),
-               lib.rss_calib_tiles(None, 32768, 4, ok, 16, None), lib.rss_calib_tiles(odd, 32768, 4, ok, 16, None),
-               lib.rss_calib_tiles(ok, 12288, 4, ok, 16, None), lib.rss_calib_tiles(ok, 32768, -1, ok, 16, None),
-               lib.rss_calib_tiles(ok, 32768, 4, None, 16, None), lib.rss_calib_tiles(ok, 32768, 4, odd, 16, None),
-               lib.rss_calib_tiles(ok, 32768, 4, ok, 24, None), lib.rss_calib_tiles(ok, 32768, 4, ok, 4112, None),
-               lib.rss_calib_tiles(ok, 32768, 4, ok, -16, None)):
+               lib.rss_calib_tiles(None, 32768, 4, ok, 16, 0, None), lib.rss_calib_tiles(odd, 32768, 4, ok, 16, 0, None),
+               lib.rss_calib_tiles(ok, 12288, 4, ok, 16, 0, None), lib.rss_calib_tiles(ok, 32768, -1, ok, 16, 0, None),
+               lib.rss_calib_tiles(ok, 32768, 4, None, 16, 0, None), lib.rss_calib_tiles(ok, 32768, 4, odd, 16, 0, None),
+               lib.rss_calib_tiles(ok, 32768, 4, ok, 24, 0, None), lib.rss_calib_tiles(ok, 32768, 4, ok, 4112, 0, None),
+               lib.rss_calib_tiles(ok, 32768, 4, ok, -16, 0, None), lib.rss_calib_tiles(ok, 32768, 4, ok, 16, 2, None),
+               lib.rss_calib_tiles(ok, 32768, 4, ok, 16, -1, None)):
         assert st == rss.RSS_E_INVALID
     # zero bytes launch nothing
     assert lib.rss_calib_read(ok, 0, ok, 0, None) == rss.RSS_OK
     assert lib.rss_calib_copy(ok, ok, 0, 0, None) == rss.RSS_OK
     assert lib.rss_calib_write(ok, 0, 0, None) == rss.RSS_OK
-    assert lib.rss_calib_tiles(ok, 32768, 0, ok, 16, None) == rss.RSS_OK
-    assert lib.rss_calib_tiles(ok, 32768, 0, ok, 32768, None) == rss.RSS_OK   # tile copy
-    assert lib.rss_calib_tiles(ok, 32768, 4, None, 32768, None) == rss.RSS_E_INVALID
+    assert lib.rss_calib_tiles(ok, 32768, 0, ok, 16, 0, None) == rss.RSS_OK
+    assert lib.rss_calib_tiles(ok, 32768, 0, ok, 32768, 0, None) == rss.RSS_OK   # tile copy
+    assert lib.rss_calib_tiles(ok, 32768, 0, ok, 16, 1, None) == rss.RSS_OK     # the other order
+    assert lib.rss_calib_tiles(ok, 32768, 4, None, 32768, 0, None) == rss.RSS_E_INVALID

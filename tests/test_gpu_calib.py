@@ -29,11 +29,16 @@ def test_calibration_read_copy_write(nvec, blocks):
     assert torch.equal(out, want)
 
 
+@pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("tile_bytes,n_tiles,write_bytes", [(32768, 37, 672), (4096, 9, 16), (65536, 5, 4096),
-                                                            (8192, 3, 0)])
-def test_calibration_tiles(tile_bytes, n_tiles, write_bytes):
+                                                            (8192, 3, 0), (32768, 300, 672), (65536, 77, 16),
+                                                            (4096, 1100, 16)])
+def test_calibration_tiles(tile_bytes, n_tiles, write_bytes, order):
     """Tile t's 16-byte vector i: (sum of thread i's floats, i, t, 1). The
-    source holds small integers, so every fp32 sum is exact in any order."""
+    source holds small integers, so every fp32 sum is exact in any order. The
+    larger cases span whole groups of the decode kernels' tile order (8 runs of
+    up to 512 KiB) and a ragged tail, so every tile being served exactly once
+    checks that order's workgroup-to-tile map."""
     L = tile_bytes // 4096
     g = np.random.default_rng(tile_bytes + n_tiles)
     host = g.integers(0, 8, size=(n_tiles, L, 256, 4)).astype(np.float32)
@@ -41,7 +46,7 @@ def test_calibration_tiles(tile_bytes, n_tiles, write_bytes):
     keep = src.clone()
     wv = write_bytes // 16
     dst = torch.full((max(n_tiles * wv, 1), 4), float("nan"), device=DEV)
-    rss.rss_calib_tiles(src, tile_bytes, n_tiles, dst if write_bytes else None, write_bytes)
+    rss.rss_calib_tiles(src, tile_bytes, n_tiles, dst if write_bytes else None, write_bytes, order)
     torch.cuda.synchronize()
     assert torch.equal(src, keep)
     if not write_bytes:
@@ -56,12 +61,13 @@ def test_calibration_tiles(tile_bytes, n_tiles, write_bytes):
     assert np.array_equal(dst.cpu().numpy().reshape(n_tiles, wv, 4), want)
 
 
-@pytest.mark.parametrize("tile_bytes,n_tiles", [(32768, 37), (4096, 9), (65536, 5)])
-def test_calibration_tile_copy(tile_bytes, n_tiles):
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("tile_bytes,n_tiles", [(32768, 37), (4096, 9), (65536, 5), (32768, 300), (16384, 531)])
+def test_calibration_tile_copy(tile_bytes, n_tiles, order):
     """write_bytes = tile_bytes copies every tile to the same place in dst."""
     src = torch.randn((n_tiles * tile_bytes // 4,), device=DEV)
     keep = src.clone()
     dst = torch.full_like(src, float("nan"))
-    rss.rss_calib_tiles(src, tile_bytes, n_tiles, dst, tile_bytes)
+    rss.rss_calib_tiles(src, tile_bytes, n_tiles, dst, tile_bytes, order)
     torch.cuda.synchronize()
     assert torch.equal(src, keep) and torch.equal(dst, src)

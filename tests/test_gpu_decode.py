@@ -128,6 +128,11 @@ SHAPES = [
     (1, 16, 1, 1, 1, 1, "f32", "none"),
     (64, 32, 8, 2, 8, 12, "bf16", "none"),
     (48, 256, 2, 1, 7, 8, "bf16", "bf16"),
+    # tile counts past whole groups of the workgroup-to-tile order (8 runs of up
+    # to 512 KiB of tiles) with a ragged tail: 144 fp32 tiles of 32 KiB (one
+    # group of 128), 288 bf16 read-copy tiles of 16 KiB (one group of 256)
+    (64, 128, 48, 48, 8, 8, "bf16", "none"),
+    (64, 128, 96, 96, 8, 8, "bf16", "bf16"),
 ]
 
 

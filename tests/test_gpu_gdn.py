@@ -76,6 +76,7 @@ SHAPES = [
     (100, 64, 2, 6, 6, "normal"),
     (64, 256, 2, 4, 4, "normal"),
     (256, 32, 1, 3, 4, "normal"),
+    (128, 128, 24, 5, 6, "normal"),   # 72 tiles of 64 KiB: one group of the tile order (64) + a tail
 ]
 
 
