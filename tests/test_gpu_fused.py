@@ -65,6 +65,10 @@ SHAPES = [
     (48, 64, 2, 1, 40, 44, "bf16", "bf16_state"),
     (256, 256, 1, 1, 24, 24, "bf16", "bf16_state"),
     (64, 128, 2, 2, 20, 20, "f32", "bf16_state"),
+    # tile counts past whole groups of the workgroup-to-tile order with a ragged
+    # tail: 144 fp32 tiles (groups of 128), 288 bf16 tiles (groups of 256)
+    (64, 128, 48, 48, 8, 8, "bf16", "none"),
+    (64, 128, 96, 96, 8, 8, "bf16", "bf16_state"),
 ]
 
 

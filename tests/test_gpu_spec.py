@@ -44,9 +44,12 @@ def test_verify_rollback_matches_committed_stream(copy):
 # The matrix-core ring terms of a bf16 verify at the shapes their blocking
 # meets: N = 16 (half of each 32-wide K slice empty), N = 256, row counts that
 # leave a partial 16-row block (P = 17, 100, 1), K + 1 = 8 outputs, a window
-# of 27 positions (two 16-entry blocks), and grouped B rows.
+# of 27 positions (two 16-entry blocks), and grouped B rows; and 144 tiles of
+# 32 KiB (batch 3 x 48 heads), past one whole group of the workgroup-to-tile
+# order (8 runs of 16 tiles) with a ragged tail.
 @pytest.mark.parametrize("P,N,H,G,W,R,K", [(17, 16, 2, 1, 6, 14, 7), (100, 256, 2, 2, 5, 10, 3),
-                                           (64, 128, 3, 3, 20, 27, 7), (1, 32, 2, 1, 1, 3, 2)])
+                                           (64, 128, 3, 3, 20, 27, 7), (1, 32, 2, 1, 1, 3, 2),
+                                           (64, 128, 48, 48, 8, 12, 4)])
 def test_verify_ring_term_shapes(P, N, H, G, W, R, K):
     _rounds_against_oracle(_spec_wl(headdim=P, dstate=N, nheads=H, ngroups=G, window=W, capacity=R,
                                     max_draft=K, draft=K, rounds=8, batch=3, seed=4100 + P + N))
