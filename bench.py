@@ -77,6 +77,14 @@ def fused_bytes(wl) -> int:
     return replay_bytes(wl, wl.window - 1) + wl.headdim * wl.dstate * sb
 
 
+def dual_fused_bytes(wl) -> int:
+    """Dual precision, the token that fills every window folded in one pass from
+    the fp32 master: the replay's bytes with the master tile read instead of the
+    bf16 copy, plus the new master and the new copy written."""
+    P, N = wl.headdim, wl.dstate
+    return replay_bytes(wl.replace(read_copy="none"), wl.window - 1) + P * N * 4 + P * N * 2
+
+
 def eager_bytes(wl, state_bytes: int = 4) -> int:
     P, N, ib = wl.headdim, wl.dstate, 2 if wl.in_dtype == "bf16" else 4
     return 2 * P * N * state_bytes + P * ib + 2 * N * ib + 4 + P * 4 + 4
@@ -588,12 +596,14 @@ def run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, groups=1):
             "eager_tokens_per_s": Bt * steps / (ms_e / 1e3), "speedup": ms_e / ms}
 
 
-def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16", window=16):
+def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16", window=16, separate=False):
     """Replay with a bf16 tile read, W = window, same inputs: dual precision
-    (fp32 master + bf16 read copy, mode "bf16"; the fold of the master is a
-    separate flush launch) or a single bf16 checkpoint ("bf16_state"; folded
-    inside the decode that fills the window). `steps` is a whole number of
-    windows, and the timed region starts at a window boundary."""
+    (fp32 master + bf16 read copy, mode "bf16"; the token that fills every
+    window is decoded and folded in one pass from the fp32 master) or a single
+    bf16 checkpoint ("bf16_state"; folded inside the two-wavefront decode that
+    fills the window). `steps` is a whole number of windows, and the timed
+    region starts at a window boundary. separate=True times the dual mode's
+    other plan instead: the replay of the copy, then the flush launch."""
     wl = workloads.get(f"mamba2_dual_b256_h128_p64_n128_w{window}").replace(read_copy=mode)
     Bt, H, P, N, W = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.window
     assert steps % W == 0
@@ -603,7 +613,7 @@ def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16", wind
     layer.init_state()
     y = torch.empty((Bt, H, P), device=dev)
     T = X.shape[0]
-    fused = mode == "bf16_state"
+    fused = not separate
 
     def step(k, lt=None):
         i = k % T
@@ -638,13 +648,15 @@ def run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, steps, warmup, mode="bf16", wind
         r_b += len(d) * replay_bytes(wl, n0) * Bt * H
         n_r += len(d)
     f_us = lt.us("f")
-    per_fold = fused_bytes(wl) if fused else flush_bytes(wl, W)
+    per_fold = (fused_bytes(wl) if mode == "bf16_state" else dual_fused_bytes(wl)) if fused else flush_bytes(wl, W)
     assert layer.device_error() == 0
     return {"workload": wl.name if mode == "bf16" else wl.name + " with a bf16-only checkpoint",
             "steps": steps, "folds_timed": steps // W,
             "tokens_per_s": Bt * steps / (ms / 1e3),
             "replay_avg_us": r_us / n_r, "replay_GBps": rate(r_b, r_us),
-            "fold": "fused into the decode that fills the window" if fused else "separate flush launch",
+            "fold": ("fused into the decode that fills the window" if mode == "bf16_state" else
+                     "one pass from the fp32 master on the token that fills every window") if fused
+                    else "separate flush launch",
             "fold_avg_us": float(np.mean(f_us)),
             "fold_GBps": rate(per_fold * Bt * H * len(f_us), sum(f_us)),
             "fold_frac_of_peak": rate(per_fold * Bt * H * len(f_us), sum(f_us)) / PEAK_HBM_GBS}
@@ -1005,6 +1017,10 @@ def main() -> int:
         rec["grouped_bc"] = run_grouped(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)
         mark("dual")
         rec["dual_precision"] = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup)
+        sep_dual = run_lowp(torch, rss, dev, X, Bm, Cm, DT, A, sub, args.warmup, separate=True)
+        rec["dual_precision"]["separate_flush"] = {
+            k: sep_dual[k] for k in ("tokens_per_s", "replay_avg_us", "fold", "fold_avg_us", "fold_GBps",
+                                     "fold_frac_of_peak")}
         by_window = {}
         for w in SWEEP_WINDOWS:
             mark(f"dual_w{w}")

@@ -204,12 +204,21 @@ int32_t rss_decode_step(rss_layer* layer, const void* x, const void* B, const vo
  * folded while its checkpoint tile is already loaded for the output, and the
  * new checkpoint is written, so the flush's second read of the tile is saved
  * (the fold writes the state only once per window, P1 "Tenir le journal plutôt
- * que le solde"). Results equal the two separate calls bit for bit. A
- * bf16-stored checkpoint (RSS_STATE_BF16) is folded in the same pass too,
- * unless its fold operands, widened to fp32 in LDS, would not fit the budget
- * (P = N = 256 with a long window): then, as always with read_copy = BF16
- * (the replay reads the bf16 copy while the fold needs the fp32 master), the
- * fold runs as the separate flush launch, with the same results. On steps
+ * que le solde"). Results equal the two separate calls bit for bit (dual
+ * precision: outputs up to rounding, see below). A bf16-stored checkpoint
+ * (RSS_STATE_BF16) is folded in the same pass too, unless its fold operands,
+ * widened to fp32 in LDS, would not fit the budget (P = N = 256 with a long
+ * window): then the fold runs as the separate flush launch, with the same
+ * results. With read_copy = BF16 the replay reads the bf16 copy while the fold
+ * needs the fp32 master. When the handle knows that this token fills every
+ * window (all sequences in step: since rss_init_state or an
+ * rss_flush_checkpoint(1), only plain decodes and folds of every window, no
+ * verify round and no per-sequence thresholds), one pass reads the fp32 master
+ * instead of the copy: the outputs come from the master's RNE-bf16 rounding,
+ * bit for bit the copy's values, summed in another order (equal to the
+ * separate calls' up to rounding), and the new master and copy are written,
+ * bit for bit as the flush writes them. Otherwise the dual-precision fold is
+ * the separate flush launch after the replay of the copy. On steps
  * where no sequence folds the call costs what rss_decode_step does, so a
  * caller may simply use it for every token. min_len >= 1; errors as
  * rss_decode_step, plus RSS_DEV_UNCOMMITTED if a window to fold still holds

@@ -30,6 +30,8 @@ struct ReplayArgs {
   const int* fold_min_len_dev;  // [Bt] per-sequence fold thresholds (overrides fold_min_len), or null
   uint64_t xdiv;           // ceil(2^32 / d): q / d == (q * xdiv) >> 32 for q < 2^16,
                            // d = P/VE (16-byte x vectors per row) or P (element path)
+  int dual_fold;           // decode of a dual-precision layer with a fold: read the fp32
+                           // master (outputs from its bf16 rounding), write master + copy
 };
 hipError_t launch_replay(const ReplayArgs& a, int batch, int N, bool bf16_in, bool low_copy,
                          hipStream_t s);

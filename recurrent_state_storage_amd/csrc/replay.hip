@@ -53,8 +53,14 @@ namespace rss {
 
 constexpr int kStageS = 4;  // scalar loads per thread and round (x rows when P % VE != 0)
 
-template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD, int NT>
+// FOLD: 0 = no fold; 1 = fold windows that reach the threshold; 2 = the same for
+// a dual-precision layer, from its fp32 master: the tile read is the master, the
+// outputs use its RNE-bf16 rounding (bit for bit the read copy's values), and
+// the fold writes the new master and its RNE-bf16 copy (decode only).
+template <int N, typename Tin, bool LOW, int NTMAX, int FOLD, int NT>
 __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
+  constexpr bool kDual = FOLD == 2;
+  static_assert(!kDual || (!LOW && NTMAX == 1), "dual fold: fp32 master tile, decode only");
   constexpr int NW = NT / 64;                                  // wavefronts per workgroup
   using Geo = TileGeom<N, LOW, NT>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, RPP = Geo::RPP;
@@ -457,6 +463,18 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
                                                   __builtin_bit_cast(bf16x2_t, cp[q]), acc, false);
           part[k] = acc;
         }
+      } else if constexpr (kDual) {
+        // the read copy's values: RNE-bf16 of the master, two per packed conversion
+#pragma unroll
+        for (int k = 0; k < kMaxPass; ++k) {
+          const uint32_t lo = pack_bf16x2(fr[k].v.x, fr[k].v.y), hi = pack_bf16x2(fr[k].v.z, fr[k].v.w);
+          const float q[4] = {__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                              __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+          float acc = 0.f;
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc = fmaf(q[v], cv[v], acc);
+          part[k] = acc;
+        }
       } else {
 #pragma unroll
         for (int k = 0; k < kMaxPass; ++k) {
@@ -550,6 +568,14 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
           const int row = rows.row(base, k);
           if (row < P) st16(out + row * N + col * 4, fr[k].v);
         }
+        if constexpr (kDual) {  // the new read copy: RNE-bf16 of the new master
+          bf16_t* lo = static_cast<bf16_t*>(a.ckpt_lo) + (size_t)bh * P * N;
+#pragma unroll
+          for (int k = 0; k < kMaxPass; ++k) {
+            const int row = rows.row(base, k);
+            if (row < P) st8_bf16x4(lo + row * N + col * 4, fr[k].v);
+          }
+        }
       }
     }
   }
@@ -560,7 +586,7 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   }
 }
 
-template <int N, typename Tin, bool LOW, int NTMAX, bool FOLD, int NT = kThreads>
+template <int N, typename Tin, bool LOW, int NTMAX, int FOLD, int NT = kThreads>
 static hipError_t launch_one(const ReplayArgs& a, int batch, hipStream_t s) {
   constexpr int VEC = TileGeom<N, LOW, NT>::VEC;
   constexpr bool kB16Fold = FOLD && LOW && std::is_same<Tin, bf16_t>::value;
@@ -585,11 +611,11 @@ static hipError_t launch_nt(const ReplayArgs& a, int batch, hipStream_t s) {
   const bool fold = a.fold_min_len > 0 || a.fold_min_len_dev;
   if (a.nt != 1 || (fold && a.set_tent)) {   // verify (a folding verify of one token too)
     if constexpr (!LOW) {
-      if (fold) return launch_one<N, Tin, LOW, kMaxNew, true>(a, batch, s);
+      if (fold) return launch_one<N, Tin, LOW, kMaxNew, 1>(a, batch, s);
     } else {
       if (fold) return hipErrorInvalidValue;
     }
-    return launch_one<N, Tin, LOW, kMaxNew, false>(a, batch, s);
+    return launch_one<N, Tin, LOW, kMaxNew, 0>(a, batch, s);
   }
   if constexpr (LOW) {
     // A bf16 tile is half the bytes: two wavefronts per (sequence, head) hold
@@ -597,11 +623,12 @@ static hipError_t launch_nt(const ReplayArgs& a, int batch, hipStream_t s) {
     // a CU, so twice the bytes are in flight. A fold writes the bf16 tile back:
     // only for a bf16-stored checkpoint (a dual-precision layer folds its fp32
     // master, which this kernel never reads).
-    if (fold) return launch_one<N, Tin, LOW, 1, true, 128>(a, batch, s);
-    return launch_one<N, Tin, LOW, 1, false, 128>(a, batch, s);
+    if (fold) return launch_one<N, Tin, LOW, 1, 1, 128>(a, batch, s);
+    return launch_one<N, Tin, LOW, 1, 0, 128>(a, batch, s);
   } else {
-    if (fold) return launch_one<N, Tin, LOW, 1, true>(a, batch, s);
-    return launch_one<N, Tin, LOW, 1, false>(a, batch, s);
+    if (fold && a.dual_fold) return launch_one<N, Tin, LOW, 1, 2>(a, batch, s);
+    if (fold) return launch_one<N, Tin, LOW, 1, 1>(a, batch, s);
+    return launch_one<N, Tin, LOW, 1, 0>(a, batch, s);
   }
 }
 

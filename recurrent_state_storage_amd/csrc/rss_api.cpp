@@ -13,7 +13,29 @@ struct rss_layer {
   rss_config cfg;
   rss_buffers dev;
   int pending_verify;  // a verify round is waiting for its rollback
+  // What the host knows of the windows: lock_len >= 0 when every sequence's
+  // window holds exactly lock_len committed entries and none tentative (from
+  // rss_init_state on, through plain decodes and folds of every window), -1 when
+  // unknown (after speculative rounds or per-sequence thresholds). It only picks
+  // a launch plan: every fold is still decided on the device from the pointers.
+  int lock_len;
 };
+
+// A decode appended one entry to every window, and folded those that reached
+// min_len (0: no fold).
+static void lock_decode(rss_layer* l, int32_t min_len) {
+  if (l->lock_len < 0 || l->lock_len >= l->cfg.capacity) {  // unknown, or the ring overflows
+    l->lock_len = -1;
+    return;
+  }
+  const int n = l->lock_len + 1;
+  l->lock_len = (min_len > 0 && n >= min_len) ? 0 : n;
+}
+
+// A flush folded every window holding at least min_len entries.
+static void lock_flush(rss_layer* l, int32_t min_len) {
+  if (min_len == 1 || (l->lock_len >= 0 && l->lock_len >= min_len)) l->lock_len = 0;
+}
 
 namespace {
 
@@ -153,6 +175,7 @@ int32_t rss_layer_bind(const rss_config* c, const rss_buffers* d, rss_layer** ou
   l->dev = *d;
   if (c->read_copy != RSS_COPY_BF16) l->dev.ckpt_lo = nullptr;
   l->pending_verify = 0;
+  l->lock_len = -1;
   *out = l;
   return RSS_OK;
 }
@@ -175,12 +198,13 @@ int32_t rss_init_state(rss_layer* l, const float* S0, void* stream) {
   a.n_state = (size_t)c.batch * c.nheads * c.headdim * c.dstate;
   a.n_ptr = (size_t)c.batch * c.nheads;
   l->pending_verify = 0;
+  l->lock_len = 0;
   return launch_status(rss::launch_init(a, static_cast<hipStream_t>(stream)));
 }
 
 static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len,
                            const int32_t* fold_each, const void* x, const void* B, const void* C,
-                           const float* dt, float* y, void* stream) {
+                           const float* dt, float* y, void* stream, int dual_fold = 0) {
   const rss_config& c = l->cfg;
   if (c.batch == 0) return RSS_OK;
   rss::ReplayArgs a;
@@ -208,8 +232,10 @@ static int32_t replay_call(rss_layer* l, int nt, int set_tent, int fold_min_len,
   const int ve = c.in_dtype == RSS_DTYPE_BF16 ? 8 : 4;  // elements per 16-byte vector
   const uint64_t d = c.headdim % ve == 0 ? (uint64_t)(c.headdim / ve) : (uint64_t)c.headdim;
   a.xdiv = ((1ull << 32) + d - 1) / d;
+  a.dual_fold = dual_fold;
+  // a dual fold reads the fp32 master in the fp32 tile geometry
   return launch_status(rss::launch_replay(a, c.batch, c.dstate, c.in_dtype == RSS_DTYPE_BF16,
-                                          c.read_copy != RSS_COPY_NONE,
+                                          !dual_fold && c.read_copy != RSS_COPY_NONE,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -218,10 +244,19 @@ int32_t rss_decode_step(rss_layer* l, const void* x, const void* B, const void* 
   if (!l || l->cfg.kind != RSS_KIND_MAMBA2) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && !inputs_ok(x, B, C, dt, y)) return RSS_E_INVALID;
   if (l->pending_verify) return RSS_E_ORDER;
-  return replay_call(l, 1, 0, 0, nullptr, x, B, C, dt, y, stream);
+  const int32_t st = replay_call(l, 1, 0, 0, nullptr, x, B, C, dt, y, stream);
+  if (st == RSS_OK) lock_decode(l, 0);
+  return st;
 }
 
 static int32_t flush_call(rss_layer* l, int32_t min_len, const int32_t* each, void* stream);
+
+// The fp32-geometry decode of a dual fold (four wavefronts) within the LDS budget.
+static bool dual_fold_fits(const rss_config& c) {
+  const int tin = c.in_dtype == RSS_DTYPE_BF16 ? 2 : 4;
+  return (size_t)rss::ReplayLds(c.capacity, c.headdim, c.dstate, 1, tin, 4, 0, 0).total * 4 <=
+         (size_t)rss::kMaxLdsBytes;
+}
 
 static int32_t decode_fold(rss_layer* l, int32_t min_len, const int32_t* each, const void* x,
                            const void* B, const void* C, const float* dt, float* y, void* stream) {
@@ -241,11 +276,24 @@ static int32_t decode_fold(rss_layer* l, int32_t min_len, const int32_t* each, c
                            .total * 4;
     separate = lds > (size_t)rss::kMaxLdsBytes;
   }
-  if (separate) {
-    const int32_t st = replay_call(l, 1, 0, 0, nullptr, x, B, C, dt, y, stream);
-    return st ? st : flush_call(l, min_len, each, stream);
+  int32_t st;
+  if (separate && c.read_copy == RSS_COPY_BF16 && !each && l->lock_len >= 0 &&
+      l->lock_len < c.capacity && l->lock_len + 1 >= min_len && dual_fold_fits(c)) {
+    // Dual precision, every window filled by this token: one pass reads the fp32
+    // master (which the fold needs anyway) instead of the copy, takes the outputs
+    // from its RNE-bf16 rounding (the copy's values) and writes master and copy.
+    st = replay_call(l, 1, 0, min_len, nullptr, x, B, C, dt, y, stream, 1);
+  } else if (separate) {
+    st = replay_call(l, 1, 0, 0, nullptr, x, B, C, dt, y, stream);
+    if (st == RSS_OK) st = flush_call(l, min_len, each, stream);
+  } else {
+    st = replay_call(l, 1, 0, min_len, each, x, B, C, dt, y, stream);
   }
-  return replay_call(l, 1, 0, min_len, each, x, B, C, dt, y, stream);
+  if (st == RSS_OK) {
+    if (each) l->lock_len = -1;
+    else lock_decode(l, min_len);
+  }
+  return st;
 }
 
 int32_t rss_decode_flush_step(rss_layer* l, int32_t min_len, const void* x, const void* B,
@@ -270,7 +318,10 @@ int32_t rss_verify_k_tokens(rss_layer* l, int32_t K, const void* x, const void* 
   if (K > l->cfg.max_draft) return RSS_E_CAPACITY;
   if (l->pending_verify) return RSS_E_ORDER;
   const int32_t st = replay_call(l, K + 1, 1, 0, nullptr, x, B, C, dt, y, stream);
-  if (st == RSS_OK) l->pending_verify = 1;
+  if (st == RSS_OK) {
+    l->pending_verify = 1;
+    l->lock_len = -1;
+  }
   return st;
 }
 
@@ -304,7 +355,10 @@ int32_t rss_verify_k_tokens_fold(rss_layer* l, int32_t min_len, int32_t K, const
   } else {
     st = replay_call(l, K + 1, 1, min_len, nullptr, x, B, C, dt, y, stream);
   }
-  if (st == RSS_OK) l->pending_verify = 1;
+  if (st == RSS_OK) {
+    l->pending_verify = 1;
+    l->lock_len = -1;
+  }
   return st;
 }
 
@@ -327,13 +381,17 @@ int32_t rss_rollback(rss_layer* l, const int32_t* n_drop, void* stream) {
 int32_t rss_flush_checkpoint(rss_layer* l, int32_t min_len, void* stream) {
   if (!l) return RSS_E_INVALID;
   if (min_len < 1) return RSS_E_INVALID;
-  return flush_call(l, min_len, nullptr, stream);
+  const int32_t st = flush_call(l, min_len, nullptr, stream);
+  if (st == RSS_OK) lock_flush(l, min_len);
+  return st;
 }
 
 int32_t rss_flush_checkpoint_each(rss_layer* l, const int32_t* min_len, void* stream) {
   if (!l) return RSS_E_INVALID;
   if (l->cfg.batch > 0 && (!min_len || !aligned16(min_len))) return RSS_E_INVALID;
-  return flush_call(l, 1, min_len, stream);
+  const int32_t st = flush_call(l, 1, min_len, stream);
+  if (st == RSS_OK) l->lock_len = -1;
+  return st;
 }
 
 static int32_t flush_call(rss_layer* l, int32_t min_len, const int32_t* each, void* stream) {
@@ -388,8 +446,10 @@ static int32_t delta_decode(rss_layer* l, int32_t kind, int32_t fold_min_len, co
   a.P = c.headdim;
   a.R = c.capacity;
   a.fold_min_len = fold_min_len;
-  return launch_status(rss::launch_gdn_replay(a, c.batch, c.dstate, kind == RSS_KIND_KDA,
-                                              static_cast<hipStream_t>(stream)));
+  const int32_t st = launch_status(rss::launch_gdn_replay(a, c.batch, c.dstate, kind == RSS_KIND_KDA,
+                                                          static_cast<hipStream_t>(stream)));
+  if (st == RSS_OK) lock_decode(l, fold_min_len);
+  return st;
 }
 
 int32_t rss_gdn_decode_step(rss_layer* l, const float* q, const float* k, const float* v,

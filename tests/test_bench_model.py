@@ -34,6 +34,16 @@ def test_replay_bytes_by_hand():
         assert bench.replay_bytes(WL, n0) == want == 34096 + 392 * n0
 
 
+def test_dual_one_pass_fold_bytes_by_hand():
+    # the window-filling token of a dual-precision layer (W = 16): the fp32
+    # master tile read, 15 ring entries, the inputs, y, the appended entry,
+    # pointers and A, then the new master (fp32) and copy (bf16) written
+    wl = workloads.get("mamba2_dual_b256_h128_p64_n128_w16")
+    entry = 64 * 2 + 128 * 2 + 8
+    want = 64 * 128 * 4 + 15 * entry + (64 * 2 + 128 * 2 * 2 + 4) + 64 * 4 + entry + 32 + 4 + 64 * 128 * (4 + 2)
+    assert bench.dual_fused_bytes(wl) == want == 89128
+
+
 def test_replay_launch_bytes_of_the_fused_schedule():
     # plain replays run at n0 = 0..W-2; the window-filling token is the fused launch
     per_launch = sum(bench.replay_bytes(WL, n0) for n0 in range(WL.window - 1)) / (WL.window - 1)

@@ -80,6 +80,70 @@ def test_captured_window_replays_match_eager_calls(copy):
     assert cap.device_error() == 0 and ref.device_error() == 0
 
 
+def test_captured_dual_fold_step_replayed_at_every_phase():
+    """A dual-precision rss_decode_flush_step captured on the token that fills
+    every window (so the one-pass fold from the fp32 master is recorded), then
+    replayed on every token: the kernel decides each fold on the device, so on
+    the replays where no window fills it only decodes. Checkpoint, copy, ring
+    and pointers equal rss_decode_step + rss_flush_checkpoint bit for bit after
+    every replay; outputs up to rounding (the copy's values, summed in the fp32
+    kernel's order)."""
+    wl = workloads.get("tiny_b2_h4_p16_n16_w8").replace(
+        name="graph-dual", batch=4, nheads=4, ngroups=4, headdim=64, dstate=128, window=4, capacity=4,
+        in_dtype="bf16", read_copy="bf16", s0="normal", seed=9300)
+    W = wl.window
+    cfg = cfg_of(wl)
+    A = torch.from_numpy(synth.params(wl)["A"]).to(DEV)
+    S0 = torch.from_numpy(synth.initial_state(wl)).to(DEV)
+    ref, cap = rss.ReplayLayer(cfg, A, DEV), rss.ReplayLayer(cfg, A, DEV)
+    Bt, H, P = wl.batch, wl.nheads, wl.headdim
+    inp = dev_inputs(synth.step_inputs(wl, 0), "bf16")
+    y = torch.empty((Bt, H, P), device=DEV)
+
+    def lead_in(layer):                      # W - 1 plain decodes: the next token fills every window
+        layer.init_state(S0)
+        for t in range(W - 1):
+            d = dev_inputs(synth.step_inputs(wl, t), "bf16")
+            layer.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lead_in(cap)
+        cap.decode_flush_step(W, inp["x"], inp["B"], inp["C"], inp["dt"], y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    lead_in(cap)
+    lead_in(ref)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap.decode_flush_step(W, inp["x"], inp["B"], inp["C"], inp["dt"], y)
+    torch.cuda.synchronize()
+    folds = 0
+    for t in range(W - 1, W - 1 + 3 * W + 2):
+        fresh = dev_inputs(synth.step_inputs(wl, t), "bf16")
+        for k in inp:
+            inp[k].copy_(fresh[k])
+        g.replay()
+        y_ref = torch.empty_like(y)
+        ref.decode_step(fresh["x"], fresh["B"], fresh["C"], fresh["dt"], y_ref)
+        ref.flush_checkpoint(W)
+        torch.cuda.synchronize()
+        folds += int((ref.ptr[:, 0, 1] == 0).all())
+        rel = float(torch.linalg.vector_norm(y - y_ref) / torch.linalg.vector_norm(y_ref))
+        assert rel < 1e-5, (t, rel)
+        assert torch.equal(cap.ckpt, ref.ckpt), t
+        assert torch.equal(cap.ckpt_lo, ref.ckpt_lo), t
+        assert torch.equal(cap.ptr, ref.ptr), t
+        assert torch.equal(cap.ring_x, ref.ring_x) and torch.equal(cap.ring_B, ref.ring_B), t
+        assert torch.equal(cap.ring_dl, ref.ring_dl), t
+        _ = torch.ones(1000, device=DEV).sum().item()   # eager work between replays
+    log(f"[graph] dual one-pass fold step replayed {3 * W + 2} times, {folds} of them folding")
+    assert folds >= 3
+    assert cap.device_error() == 0 and ref.device_error() == 0
+
+
 def test_captured_speculative_round_replays_match_eager_calls():
     """One speculative round (verify K+1 tokens with the committed-window fold,
     then rollback by a device n_drop array) captured once and replayed for eight
