@@ -20,6 +20,7 @@ namespace {
 int g_fail = 0;
 int g_launches = 0;
 rss::ReplayArgs g_last_replay;
+bool g_last_replay_low = false;   // the replay launcher was asked for the bf16 tile geometry
 rss::FlushArgs g_last_flush;
 int g_last_flush_kind = -1;
 }  // namespace
@@ -34,9 +35,10 @@ int g_last_flush_kind = -1;
 
 // ---- stub launchers (same signatures as launch.h) ----------------------------
 namespace rss {
-hipError_t launch_replay(const ReplayArgs& a, int, int, bool, bool, hipStream_t) {
+hipError_t launch_replay(const ReplayArgs& a, int, int, bool, bool low, hipStream_t) {
   ++g_launches;
   g_last_replay = a;
+  g_last_replay_low = low;
   return hipSuccess;
 }
 hipError_t launch_flush(const FlushArgs& a, int, int, bool, int, int kind, hipStream_t) {
@@ -312,6 +314,54 @@ int main() {
     CHECK(rss_verify_k_tokens(h, 2, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == RSS_OK);
     CHECK(rss_rollback(h, nullptr, nullptr) == RSS_OK);
     CHECK(g_launches == before);
+    CHECK(rss_layer_free(h) == RSS_OK);
+  }
+
+  // dual precision: the one-pass fold from the fp32 master only on a token the
+  // handle knows fills every window; the replay of the copy + the flush otherwise
+  {
+    rss_config c = cfg_base();
+    c.read_copy = RSS_COPY_BF16;
+    const int W = c.window;
+    rss_buffers b = bufs_for(c);
+    rss_layer* h = nullptr;
+    CHECK(rss_layer_bind(&c, &b, &h) == RSS_OK);
+    void* A = fake(9);
+    const float* dt = static_cast<const float*>(A);
+    float* y = static_cast<float*>(fake(10));
+    const int32_t* dev_i = static_cast<const int32_t*>(fake(11));
+    auto fused = [&](int min_len, bool one_pass) {
+      const int before = g_launches;
+      CHECK(rss_decode_flush_step(h, min_len, A, A, A, dt, y, nullptr) == RSS_OK);
+      if (one_pass) {
+        CHECK(g_launches == before + 1);
+        CHECK(g_last_replay.dual_fold == 1 && !g_last_replay_low && g_last_replay.fold_min_len == min_len);
+        CHECK(g_last_replay.ckpt == b.ckpt && g_last_replay.ckpt_lo == b.ckpt_lo);
+      } else {
+        CHECK(g_launches == before + 2);   // the replay of the copy, then the flush
+        CHECK(g_last_replay.dual_fold == 0 && g_last_replay_low && g_last_replay.fold_min_len == 0);
+        CHECK(g_last_flush.min_len == min_len);
+      }
+    };
+    fused(W, false);                          // bound, never initialised: windows unknown
+    CHECK(rss_init_state(h, nullptr, nullptr) == RSS_OK);
+    for (int t = 0; t < W - 1; ++t) CHECK(rss_decode_step(h, A, A, A, dt, y, nullptr) == RSS_OK);
+    fused(W, true);                           // the W-th token fills every window
+    for (int t = 0; t < W - 1; ++t) fused(W, false);
+    fused(W, true);
+    fused(1, true);                           // a fold every token
+    CHECK(rss_verify_k_tokens(h, 4, A, A, A, dt, y, nullptr) == RSS_OK);
+    CHECK(rss_rollback(h, dev_i, nullptr) == RSS_OK);
+    for (int t = 0; t < 2 * W; ++t) fused(W, false);   // windows uneven after the round
+    CHECK(rss_flush_checkpoint(h, 1, nullptr) == RSS_OK);  // every window folded: in step
+    for (int t = 0; t < W - 1; ++t) fused(W, false);
+    fused(W, true);
+    CHECK(rss_decode_flush_step_each(h, dev_i, A, A, A, dt, y, nullptr) == RSS_OK);
+    CHECK(g_last_replay.dual_fold == 0);
+    for (int t = 0; t < 2 * W; ++t) fused(W, false);   // per-sequence thresholds: unknown again
+    CHECK(rss_init_state(h, nullptr, nullptr) == RSS_OK);
+    for (int t = 0; t < c.capacity; ++t) CHECK(rss_decode_step(h, A, A, A, dt, y, nullptr) == RSS_OK);
+    fused(W, false);                          // the ring is full: that token would overflow
     CHECK(rss_layer_free(h) == RSS_OK);
   }
 
