@@ -302,6 +302,15 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
   // counts in the same counter as the loads, so a store issued before the wait
   // above would have been waited for too.
   if (wave == 0 && lane >= n0 && lane < L) rdl[ring_slot2(head, lane, R) * H] = dl_new;
+  // The new pointer word (this workgroup's own copy, read only at its start). A
+  // verify stores it as soon as the loads have landed (measured at batch 512,
+  // K = 4: 430 -> 424 us); a decode stores it last (183.1 against 182.6 us).
+  if constexpr (NTMAX > 1) {
+    if (tid == 0) {
+      if (do_fold) a.ptr[bh] = make_int4(ring_slot(head, F, R), L - F, a.set_tent ? nt : 0, 0);
+      else a.ptr[bh] = make_int4(head, L, a.set_tent ? nt : pt.z, 0);
+    }
+  }
 
   // The new tokens' x and B rows go from LDS to the ring. A verify's K + 1
   // rows per head go out non-temporal (measured at batch 512, K = 4: verify
@@ -580,9 +589,11 @@ __global__ __launch_bounds__(NT) void replay_kernel(ReplayArgs a) {
     }
   }
 
-  if (tid == 0) {
-    if (do_fold) a.ptr[bh] = make_int4(ring_slot(head, F, R), L - F, a.set_tent ? nt : 0, 0);
-    else a.ptr[bh] = make_int4(head, L, a.set_tent ? nt : pt.z, 0);
+  if constexpr (NTMAX == 1) {
+    if (tid == 0) {
+      if (do_fold) a.ptr[bh] = make_int4(ring_slot(head, F, R), L - F, a.set_tent ? nt : 0, 0);
+      else a.ptr[bh] = make_int4(head, L, a.set_tent ? nt : pt.z, 0);
+    }
   }
 }
 
