@@ -151,9 +151,12 @@ def test_shapes(shape):
     assert w["ckpt"] < 1e-5       # the fp32 master is exact in both modes
 
 
-def test_dual_master_equals_fp32_checkpoint():
+@pytest.mark.parametrize("fused", [False, True], ids=["decode+flush", "fused"])
+def test_dual_master_equals_fp32_checkpoint(fused):
     """The bf16 read copy never feeds back: the dual-mode master is bitwise the
-    fp32-mode checkpoint after the same tokens."""
+    fp32-mode checkpoint after the same tokens, and the copy is RNE-bf16 of it;
+    also through the fused entry point, where a dual-precision layer in step
+    folds the window-filling token in one pass from the master."""
     base = TINY.replace(name="dual", batch=4, headdim=64, dstate=128, nheads=4, ngroups=4,
                         window=8, capacity=8, in_dtype="bf16", s0="normal", seed=3001)
     layers = {}
@@ -168,11 +171,16 @@ def test_dual_master_equals_fp32_checkpoint():
     for t in range(27):
         d = dev_inputs(synth.step_inputs(base, t), "bf16")
         for L, _ in layers.values():
-            L.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
-            L.flush_checkpoint(8)
+            if fused:
+                L.decode_flush_step(8, d["x"], d["B"], d["C"], d["dt"], y)
+            else:
+                L.decode_step(d["x"], d["B"], d["C"], d["dt"], y)
+                L.flush_checkpoint(8)
     torch.cuda.synchronize()
-    assert torch.equal(layers["none"][0].ckpt, layers["bf16"][0].ckpt)
-    assert torch.equal(layers["none"][0].ptr, layers["bf16"][0].ptr)
+    master, dual = layers["none"][0], layers["bf16"][0]
+    assert torch.equal(master.ckpt, dual.ckpt)
+    assert torch.equal(master.ptr, dual.ptr)
+    assert torch.equal(dual.ckpt_lo, dual.ckpt.to(torch.bfloat16))   # torch's cast rounds to nearest even
 
 
 def test_deterministic():
